@@ -1,0 +1,383 @@
+/*
+ * moe_oracle.c -- plain, slow, fp64 CPU model of the routed-expert MoE layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg load this library.  The GPU library never
+ * includes, links or calls anything in this directory, and this file shares
+ * no source with it.
+ *
+ * Every function is the plain definition of one step, evaluated in double
+ * precision with plain loops (threads only split independent tokens or
+ * token-expert slots; each slot's arithmetic runs sequentially in the order
+ * written).  Sources:
+ *   - LazyLoRA README (github heyobi/LazyLora), "The engine": K3 has 896
+ *     routed experts per MoE layer, top-16 routing, MXFP4 expert weights;
+ *     "Routed experts": the routed experts form one unit whose backward
+ *     returns the gradient with respect to the latent input; "Arithmetic":
+ *     expert sums accumulate in fp32 or wider; "File map": top-16 gating with
+ *     a score-correction bias, and a routing record holds the chosen experts
+ *     with their combining weights; "LoRA": the expert shape 3584->3072->3584.
+ *   - WASTE README (hackernews.jp story 49123386), section on 3 bits per
+ *     expert weight: residual VQ with 3 stages of 256-entry codebooks over
+ *     8-dimensional vectors.
+ *   - OCP Microscaling Formats (MX) v1.0: the E2M1 element and E8M0 scale.
+ * Readings where the pages are silent (SwiGLU with the gate as the SiLU
+ * branch, softmax over the selected logits, ties to the lower expert id,
+ * nibble order, block direction, RVQ vector orientation) are the ones listed
+ * in the design notes; each is restated beside the code that takes it.
+ *
+ * Parity pins: every function here is checked by tests against closed forms,
+ * brute force, library routines or finite differences; none is "unpinned".
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "moe_oracle.h"
+
+/* ------------------------------------------------------------------ */
+/* element formats                                                     */
+/* ------------------------------------------------------------------ */
+
+/* OCP MX v1.0 FP4 (E2M1): bit 3 sign, bits 2..1 exponent with bias 1,
+ * bit 0 mantissa; exponent field 0 is subnormal (0 or 0.5). */
+double oracle_e2m1(unsigned code)
+{
+    unsigned sign = (code >> 3) & 1u, ef = (code >> 1) & 3u, mf = code & 1u;
+    double mag = (ef == 0) ? 0.5 * (double)mf : ldexp(1.0 + 0.5 * (double)mf, (int)ef - 1);
+    return sign ? -mag : mag;
+}
+
+/* OCP MX v1.0 E8M0 scale: 2^(b-127); the byte 0xFF encodes NaN. */
+double oracle_e8m0(unsigned b)
+{
+    return (b == 255u) ? NAN : ldexp(1.0, (int)b - 127);
+}
+
+/* IEEE binary16 from its bit fields. */
+double oracle_fp16(uint16_t h)
+{
+    unsigned sign = (h >> 15) & 1u, ef = (h >> 10) & 31u, mf = h & 1023u;
+    double v;
+    if (ef == 0)
+        v = ldexp((double)mf, -24);
+    else if (ef == 31)
+        v = mf ? NAN : INFINITY;
+    else
+        v = ldexp(1024.0 + (double)mf, (int)ef - 25);
+    return sign ? -v : v;
+}
+
+/* ------------------------------------------------------------------ */
+/* weight access                                                       */
+/* ------------------------------------------------------------------ */
+
+static void mat_shape(int mat, int H, int I, int *rows, int *cols)
+{
+    /* gate and up map the latent (in = H) to the intermediate (out = I);
+     * down maps I back to H.  Stored [out][in], `in` contiguous. */
+    if (mat == ORACLE_MAT_DOWN) { *rows = H; *cols = I; }
+    else                        { *rows = I; *cols = H; }
+}
+
+/* Decode row `row` of matrix `mat` of expert `e` into out[cols] (exact). */
+void oracle_decode_row(const oracle_weights *W, int mat, int e, int H, int I, int row, double *out)
+{
+    int rows, cols;
+    mat_shape(mat, H, I, &rows, &cols);
+    if (W->fmt == ORACLE_FMT_MXFP4) {
+        /* codes [E][rows][cols/2]: byte j holds element 2j in its low nibble
+         * and element 2j+1 in its high nibble; scales [E][rows][cols/32]:
+         * one E8M0 byte per 32 consecutive elements along `in`. */
+        const uint8_t *c = W->codes[mat] + ((size_t)e * rows + row) * (size_t)(cols / 2);
+        const uint8_t *s = W->scales[mat] + ((size_t)e * rows + row) * (size_t)(cols / 32);
+        for (int i = 0; i < cols; i++) {
+            unsigned byte = c[i / 2];
+            unsigned code = (i & 1) ? (byte >> 4) : (byte & 15u);
+            out[i] = oracle_e2m1(code) * oracle_e8m0(s[i / 32]);
+        }
+    } else {
+        /* RVQ3: idx [E][3][rows][cols/8] (stage-planar), codebooks
+         * [E][3][256][8] fp16.  Elements 8v..8v+7 of a row form vector v and
+         * equal the sum over the three stages of codebook_s[idx_s[row][v]]. */
+        for (int v = 0; v < cols / 8; v++) {
+            for (int d = 0; d < 8; d++) out[8 * v + d] = 0.0;
+            for (int st = 0; st < 3; st++) {
+                const uint8_t *ip = W->rvq_idx[mat] + (((size_t)e * 3 + st) * rows + row) * (size_t)(cols / 8);
+                const uint16_t *cb = W->rvq_cb[mat] + (((size_t)e * 3 + st) * 256 + ip[v]) * 8;
+                for (int d = 0; d < 8; d++) out[8 * v + d] += oracle_fp16(cb[d]);
+            }
+        }
+    }
+}
+
+void oracle_decode_matrix(const oracle_weights *W, int mat, int e, int H, int I, double *out)
+{
+    int rows, cols;
+    mat_shape(mat, H, I, &rows, &cols);
+    for (int r = 0; r < rows; r++) oracle_decode_row(W, mat, e, H, I, r, out + (size_t)r * cols);
+}
+
+/* ------------------------------------------------------------------ */
+/* a minimal thread pool over independent items                        */
+/* ------------------------------------------------------------------ */
+
+typedef void (*item_fn)(void *ctx, long item);
+typedef struct { item_fn fn; void *ctx; long n; long next; pthread_mutex_t mu; } pool_t;
+
+static void *pool_worker(void *arg)
+{
+    pool_t *p = (pool_t *)arg;
+    for (;;) {
+        pthread_mutex_lock(&p->mu);
+        long it = p->next++;
+        pthread_mutex_unlock(&p->mu);
+        if (it >= p->n) break;
+        p->fn(p->ctx, it);
+    }
+    return NULL;
+}
+
+static void parallel_for(long n, int nthreads, item_fn fn, void *ctx)
+{
+    pool_t p = { fn, ctx, n, 0, PTHREAD_MUTEX_INITIALIZER };
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > 256) nthreads = 256;
+    if (nthreads > n) nthreads = (int)(n > 0 ? n : 1);
+    pthread_t th[256];
+    for (int i = 0; i < nthreads; i++) pthread_create(&th[i], NULL, pool_worker, &p);
+    for (int i = 0; i < nthreads; i++) pthread_join(th[i], NULL);
+}
+
+/* ------------------------------------------------------------------ */
+/* router                                                              */
+/* ------------------------------------------------------------------ */
+
+/* l[t][e] = sum_i x[t][i] * Wr[e][i], summed sequentially in i, plus b[e]
+ * when a bias is given (the score-correction bias added to the logits). */
+typedef struct { int H, E; const double *x, *wr, *bias; double *logits; } logit_ctx;
+
+static void logits_token(void *vctx, long t)
+{
+    logit_ctx *c = (logit_ctx *)vctx;
+    for (int e = 0; e < c->E; e++) {
+        double acc = 0.0;
+        for (int i = 0; i < c->H; i++) acc += c->x[(size_t)t * c->H + i] * c->wr[(size_t)e * c->H + i];
+        if (c->bias) acc += c->bias[e];
+        c->logits[(size_t)t * c->E + e] = acc;
+    }
+}
+
+void oracle_router_logits(int T, int H, int E, const double *x, const double *wr, const double *bias,
+                          double *logits, int nthreads)
+{
+    logit_ctx c = { H, E, x, wr, bias, logits };
+    parallel_for(T, nthreads, logits_token, &c);
+}
+
+/* Expert a ranks ahead of expert b: larger logit first; equal logits (+0 and
+ * -0 compare equal) go to the lower expert id. */
+static int ranks_before(double la, int a, double lb, int b)
+{
+    return la > lb || (la == lb && a < b);
+}
+
+/* Top-k selection and softmax over the selected logits.
+ * ids[t][j] in rank order; w[t][j] = exp(l_j - l_max) / sum_j' exp(l_j' - l_max).
+ * Returns 0, or -1 on a non-finite logit or bad arguments. */
+int oracle_topk_softmax(int T, int E, int k, const double *logits, int32_t *ids, double *w)
+{
+    if (k < 1 || k > E) return -1;
+    char *taken = (char *)malloc((size_t)E);
+    if (!taken) return -1;
+    for (int t = 0; t < T; t++) {
+        const double *l = logits + (size_t)t * E;
+        for (int e = 0; e < E; e++)
+            if (!isfinite(l[e])) { free(taken); return -1; }
+        memset(taken, 0, (size_t)E);
+        for (int j = 0; j < k; j++) {
+            int best = -1;
+            for (int e = 0; e < E; e++)
+                if (!taken[e] && (best < 0 || ranks_before(l[e], e, l[best], best))) best = e;
+            taken[best] = 1;
+            ids[(size_t)t * k + j] = best;
+        }
+        double lmax = l[ids[(size_t)t * k]];
+        double den = 0.0;
+        for (int j = 0; j < k; j++) den += exp(l[ids[(size_t)t * k + j]] - lmax);
+        for (int j = 0; j < k; j++) w[(size_t)t * k + j] = exp(l[ids[(size_t)t * k + j]] - lmax) / den;
+    }
+    free(taken);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* grouping                                                            */
+/* ------------------------------------------------------------------ */
+
+/* Token-to-expert grouping.  counts[e] = number of slots (t,j) routed to e;
+ * offsets = exclusive prefix sum (E+1 entries); perm lists slot indices
+ * t*k+j ordered by (expert asc, token asc, j asc); inv is its inverse;
+ * active lists the experts with a nonzero count in ascending order and
+ * *n_active is their number. */
+void oracle_group(int T, int k, int E, const int32_t *ids, int32_t *counts, int32_t *offsets, int32_t *perm,
+                  int32_t *inv, int32_t *active, int32_t *n_active)
+{
+    long S = (long)T * k;
+    for (int e = 0; e < E; e++) counts[e] = 0;
+    for (long s = 0; s < S; s++) counts[ids[s]]++;
+    offsets[0] = 0;
+    for (int e = 0; e < E; e++) offsets[e + 1] = offsets[e] + counts[e];
+    long r = 0;
+    for (int e = 0; e < E; e++)
+        for (long s = 0; s < S; s++)
+            if (ids[s] == e) { perm[r] = (int32_t)s; inv[s] = (int32_t)r; r++; }
+    int u = 0;
+    for (int e = 0; e < E; e++)
+        if (counts[e] > 0) active[u++] = e;
+    *n_active = u;
+}
+
+/* ------------------------------------------------------------------ */
+/* experts                                                             */
+/* ------------------------------------------------------------------ */
+
+static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
+
+/* One expert on one token: g = Wg x, u = Wu x, h = silu(g) * u with
+ * silu(g) = g * sigmoid(g), o = Wd h.  Any output pointer may be NULL. */
+void oracle_expert_forward(const oracle_weights *W, int e, int H, int I, const double *x, double *g_out,
+                           double *u_out, double *h_out, double *o_out)
+{
+    int wmax = H > I ? H : I;
+    double *row = (double *)malloc(sizeof(double) * (size_t)wmax);
+    double *h = (double *)malloc(sizeof(double) * (size_t)I);
+    for (int n = 0; n < I; n++) {
+        double g = 0.0, u = 0.0;
+        oracle_decode_row(W, ORACLE_MAT_GATE, e, H, I, n, row);
+        for (int i = 0; i < H; i++) g += row[i] * x[i];
+        oracle_decode_row(W, ORACLE_MAT_UP, e, H, I, n, row);
+        for (int i = 0; i < H; i++) u += row[i] * x[i];
+        h[n] = g * sigmoid(g) * u;
+        if (g_out) g_out[n] = g;
+        if (u_out) u_out[n] = u;
+    }
+    if (h_out) memcpy(h_out, h, sizeof(double) * (size_t)I);
+    if (o_out)
+        for (int m = 0; m < H; m++) {
+            double o = 0.0;
+            oracle_decode_row(W, ORACLE_MAT_DOWN, e, H, I, m, row);
+            for (int n = 0; n < I; n++) o += row[n] * h[n];
+            o_out[m] = o;
+        }
+    free(h);
+    free(row);
+}
+
+typedef struct {
+    const oracle_weights *W;
+    int H, I, k;
+    const double *x, *dy, *wr, *w;
+    const int32_t *ids;
+    double *o;      /* [slots][H] forward expert outputs */
+    double *dxs;    /* [slots][H] backward per-slot input gradient */
+    double *dp;     /* [slots] */
+} slot_ctx;
+
+static void fwd_slot(void *vctx, long s)
+{
+    slot_ctx *c = (slot_ctx *)vctx;
+    long t = s / c->k;
+    oracle_expert_forward(c->W, c->ids[s], c->H, c->I, c->x + (size_t)t * c->H, NULL, NULL, NULL,
+                          c->o + (size_t)s * c->H);
+}
+
+/* y[t] = sum over j in rank order of w[t][j] * expert_{ids[t][j]}(x[t]). */
+void oracle_forward(int T, int H, int I, int k, const double *x, const int32_t *ids, const double *w,
+                    const oracle_weights *W, double *y, int nthreads)
+{
+    long S = (long)T * k;
+    double *o = (double *)malloc(sizeof(double) * (size_t)S * H);
+    slot_ctx c = { W, H, I, k, x, NULL, NULL, w, ids, o, NULL, NULL };
+    parallel_for(S, nthreads, fwd_slot, &c);
+    for (int t = 0; t < T; t++)
+        for (int m = 0; m < H; m++) {
+            double acc = 0.0;
+            for (int j = 0; j < k; j++) acc += w[(size_t)t * k + j] * o[((size_t)t * k + j) * H + m];
+            y[(size_t)t * H + m] = acc;
+        }
+    free(o);
+}
+
+/* Backward through one slot (t, j, e) with the upstream gradient dy[t]:
+ *   a  = Wd^T dy                (reduces over the down matrix's rows)
+ *   dp = <a, h>                 (= <dy, o>, the gradient w.r.t. the weight p)
+ *   dh = p a
+ *   dg = dh * u * s * (1 + g (1 - s)),  du = dh * g * s,   s = sigmoid(g)
+ *   dx = Wg^T dg + Wu^T du      (reduces over the gate/up rows). */
+static void bwd_slot(void *vctx, long s)
+{
+    slot_ctx *c = (slot_ctx *)vctx;
+    int H = c->H, I = c->I, e = c->ids[s];
+    long t = s / c->k;
+    double p = c->w[s];
+    const double *x = c->x + (size_t)t * H, *dy = c->dy + (size_t)t * H;
+    int wmax = H > I ? H : I;
+    double *g = (double *)malloc(sizeof(double) * (size_t)I);
+    double *u = (double *)malloc(sizeof(double) * (size_t)I);
+    double *h = (double *)malloc(sizeof(double) * (size_t)I);
+    double *a = (double *)calloc((size_t)I, sizeof(double));
+    double *row = (double *)malloc(sizeof(double) * (size_t)wmax);
+    double *dx = c->dxs + (size_t)s * H;
+    oracle_expert_forward(c->W, e, H, I, x, g, u, h, NULL);
+    for (int m = 0; m < H; m++) {
+        oracle_decode_row(c->W, ORACLE_MAT_DOWN, e, H, I, m, row);
+        for (int n = 0; n < I; n++) a[n] += row[n] * dy[m];
+    }
+    double dp = 0.0;
+    for (int n = 0; n < I; n++) dp += a[n] * h[n];
+    c->dp[s] = dp;
+    for (int i = 0; i < H; i++) dx[i] = 0.0;
+    for (int n = 0; n < I; n++) {
+        double sg = sigmoid(g[n]);
+        double dh = p * a[n];
+        double dg = dh * u[n] * sg * (1.0 + g[n] * (1.0 - sg));
+        double du = dh * g[n] * sg;
+        oracle_decode_row(c->W, ORACLE_MAT_GATE, e, H, I, n, row);
+        for (int i = 0; i < H; i++) dx[i] += row[i] * dg;
+        oracle_decode_row(c->W, ORACLE_MAT_UP, e, H, I, n, row);
+        for (int i = 0; i < H; i++) dx[i] += row[i] * du;
+    }
+    free(g); free(u); free(h); free(a); free(row);
+}
+
+/* dX[t] = sum_j dx_tj + sum_j dl_tj * Wr[e_j], with the router term
+ * dl_tj = p_tj (dp_tj - sum_j' p_tj' dp_tj') (softmax over the selected
+ * logits; the selection itself is piecewise constant and has no gradient;
+ * the bias does not depend on x). */
+void oracle_backward_input(int T, int H, int I, int k, const double *x, const double *dy, const int32_t *ids,
+                           const double *w, const double *wr, const oracle_weights *W, double *dx, int nthreads)
+{
+    long S = (long)T * k;
+    double *dxs = (double *)malloc(sizeof(double) * (size_t)S * H);
+    double *dp = (double *)malloc(sizeof(double) * (size_t)S);
+    slot_ctx c = { W, H, I, k, x, dy, wr, w, ids, NULL, dxs, dp };
+    parallel_for(S, nthreads, bwd_slot, &c);
+    for (int t = 0; t < T; t++) {
+        double pdp = 0.0;
+        for (int j = 0; j < k; j++) pdp += w[(size_t)t * k + j] * dp[(size_t)t * k + j];
+        for (int i = 0; i < H; i++) {
+            double acc = 0.0;
+            for (int j = 0; j < k; j++) {
+                size_t s = (size_t)t * k + j;
+                double dl = w[s] * (dp[s] - pdp);
+                acc += dxs[s * H + i] + dl * wr[(size_t)ids[s] * H + i];
+            }
+            dx[(size_t)t * H + i] = acc;
+        }
+    }
+    free(dxs);
+    free(dp);
+}

@@ -1,0 +1,36 @@
+/*
+ * moe_oracle.h -- declarations of the fp64 CPU oracle (test infrastructure
+ * only; the GPU library never includes this header).
+ */
+#ifndef MOE_ORACLE_H
+#define MOE_ORACLE_H
+#include <stdint.h>
+
+enum { ORACLE_FMT_MXFP4 = 0, ORACLE_FMT_RVQ3 = 1 };
+enum { ORACLE_MAT_GATE = 0, ORACLE_MAT_UP = 1, ORACLE_MAT_DOWN = 2 };
+
+typedef struct {
+    int fmt;
+    const uint8_t *codes[3];     /* MXFP4: [E][rows][cols/2]  */
+    const uint8_t *scales[3];    /* MXFP4: [E][rows][cols/32] */
+    const uint8_t *rvq_idx[3];   /* RVQ3:  [E][3][rows][cols/8] */
+    const uint16_t *rvq_cb[3];   /* RVQ3:  [E][3][256][8] fp16 bits */
+} oracle_weights;
+
+double oracle_e2m1(unsigned code);
+double oracle_e8m0(unsigned b);
+double oracle_fp16(uint16_t h);
+void oracle_decode_row(const oracle_weights *W, int mat, int e, int H, int I, int row, double *out);
+void oracle_decode_matrix(const oracle_weights *W, int mat, int e, int H, int I, double *out);
+void oracle_router_logits(int T, int H, int E, const double *x, const double *wr, const double *bias,
+                          double *logits, int nthreads);
+int oracle_topk_softmax(int T, int E, int k, const double *logits, int32_t *ids, double *w);
+void oracle_group(int T, int k, int E, const int32_t *ids, int32_t *counts, int32_t *offsets, int32_t *perm,
+                  int32_t *inv, int32_t *active, int32_t *n_active);
+void oracle_expert_forward(const oracle_weights *W, int e, int H, int I, const double *x, double *g_out,
+                           double *u_out, double *h_out, double *o_out);
+void oracle_forward(int T, int H, int I, int k, const double *x, const int32_t *ids, const double *w,
+                    const oracle_weights *W, double *y, int nthreads);
+void oracle_backward_input(int T, int H, int I, int k, const double *x, const double *dy, const int32_t *ids,
+                           const double *w, const double *wr, const oracle_weights *W, double *dx, int nthreads);
+#endif

@@ -1,0 +1,214 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert MoE layer (Kimi-K3 shape) on one MI355X.
+
+Default workload: single-token decode, H 3584, I 3072, 896 MXFP4 experts resident in HBM,
+top-16.  A step is one pass of the layer's forward hot path for one batch: router logits,
+top-k + softmax, grouping, dequant gate/up + SwiGLU, down + weighted combine.  Consecutive
+steps take consecutive tokens from a pool of 64 seeded tokens, so they route to different
+experts and the 256 MB last-level cache cannot serve the expert bytes of a repeated call.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode) / MFMA util (prefill), K3 shape"
+HBM_PEAK_GBPS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2500.0
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("expert_fwd.hip", "expert_frag.h", "common.h"):
+        h.update(open(os.path.join(ROOT, "quantized_moe_route_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_record(workload: str):
+    """HBM bytes per gate/up launch from committed rocprofv3 counter runs, if they were taken
+    on the current kernel source; else None."""
+    p = os.path.join(ROOT, "profiles", f"gateup_{workload}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p))
+    if rec.get("kernel_source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, x_pool, wr, bias, codes, scales, budget_s: float):
+    """The fp64 oracle as it stands, on the first tokens of the same pool (route + forward)."""
+    import oracle
+    nthreads = oracle.default_threads()
+    W = oracle.Weights(w.H, w.I, codes=codes, scales=scales)
+    n, t0 = 0, time.perf_counter()
+    while True:
+        xb = oracle.to_f64(x_pool[n], "bf16")
+        oracle.layer_forward(xb, wr, bias, w.k, W, nthreads=nthreads)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or n >= x_pool.shape[0]:
+            break
+    toks = n * w.T
+    return {"value": toks / el, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
+            "sample": f"{n} steps of {w.T} token(s) from the same 64-batch pool (route + group + "
+                      f"{w.k}-expert forward each), {el:.1f} s of fp64 CPU work"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode1", choices=["decode1", "decode64", "rvq16"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--breakdown", action="store_true", help="also time every kernel family (stderr)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (every box here has one GPU, "
+              "and the layer's multi-GPU sharding is a design, not a build)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_synth as syn
+    import quantized_moe_route_amd as q
+    from quantized_moe_route_amd import _lib as C
+
+    assert torch.cuda.is_available(), "no GPU visible"
+    torch.cuda.set_device(0)
+    w = syn.WORKLOADS[args.workload]
+    POOL = 64
+    log(f"workload {w.name}: T={w.T} H={w.H} I={w.I} E={w.E} k={w.k} {w.wfmt}; generating weights")
+    wr, bias = syn.router_weight(w), syn.router_bias(w)
+    kw = dict(hidden=w.H, inter=w.I, n_experts=w.E, top_k=w.k, max_tokens=w.T, router_w=q.to_device(wr),
+              router_b=None if bias is None else q.to_device(bias))
+    if w.wfmt == "mxfp4":
+        codes, scales = syn.mxfp4_layer(w)
+        kw["codes"] = [q.to_device(a) for a in codes]
+        kw["scales"] = [q.to_device(a) for a in scales]
+        expert_bytes = sum(a[0].nbytes for a in codes) + sum(a[0].nbytes for a in scales)
+        gateup_bytes_per_expert = sum(a[0].nbytes for a in codes[:2]) + sum(a[0].nbytes for a in scales[:2])
+    else:
+        codes = scales = None
+        idx, cb = syn.rvq3_layer(w)
+        kw["rvq_idx"] = [q.to_device(a) for a in idx]
+        kw["rvq_cb"] = [q.to_device(a) for a in cb]
+        expert_bytes = sum(a[0].nbytes for a in idx) + sum(a[0].nbytes for a in cb)
+        gateup_bytes_per_expert = sum(a[0].nbytes for a in idx[:2]) + sum(a[0].nbytes for a in cb[:2])
+    L = q.MoELayer(**kw)
+    x_host = syn.activations(w, w.T * POOL).reshape(POOL, w.T, w.H)
+    x_pool = q.bf16_tensor(x_host.reshape(-1, w.H)).reshape(POOL, w.T, w.H)
+    r = L.new_routing(w.T)
+    y = torch.empty((w.T, w.H), dtype=torch.float32, device="cuda")
+
+    # active experts per pool entry (device routing, read once before any timing)
+    U = []
+    for i in range(POOL):
+        L.route(x_pool[i], r)
+        U.append(int(r.n_active.item()))
+    log(f"active experts per step: min {min(U)} max {max(U)}")
+
+    def step(i):
+        xi = x_pool[i % POOL]
+        L.route(xi, r)
+        L.forward(xi, r, y=y)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    L.prof_enable([C.PROF_GATEUP], max_launches=args.steps)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end)
+    gu_ms, gu_n = L.prof_read(C.PROF_GATEUP)
+    L.prof_enable([])
+    assert gu_n == args.steps
+
+    steps_U = [U[(args.warmup + i) % POOL] for i in range(args.steps)]
+    S = w.T * w.k
+    x_bytes = w.T * w.H * 2
+    gu_alg = [u * gateup_bytes_per_expert + x_bytes + S * w.I * 4 for u in steps_U]
+    gu_bytes = sum(gu_alg) / len(gu_alg)
+    gu_avg_s = gu_ms / gu_n / 1e3
+    achieved = gu_bytes / gu_avg_s / 1e9
+    step_bytes = [u * expert_bytes + wr.nbytes + x_bytes + w.T * w.H * 4 for u in steps_U]
+    step_s = ms / 1e3 / args.steps
+    tokens_per_s = w.T * args.steps / (ms / 1e3)
+    traffic = traffic_record(w.name)
+    log(f"{args.steps} steps in {ms:.2f} ms (wall {wall * 1e3:.1f} ms): {step_s * 1e6:.1f} us/step, "
+        f"{tokens_per_s:.0f} tokens/s; gate/up kernel {gu_avg_s * 1e6:.1f} us avg, {achieved:.0f} GB/s")
+
+    detail = {"step_hbm_GBps": sum(step_bytes) / len(step_bytes) / step_s / 1e9,
+              "step_alg_bytes": sum(step_bytes) / len(step_bytes),
+              "active_experts_mean": sum(steps_U) / len(steps_U),
+              "gateup_us": gu_avg_s * 1e6}
+    if args.breakdown:
+        fams = list(range(len(C.PROF_NAMES)))
+        L.prof_enable(fams, max_launches=args.steps)
+        for i in range(args.steps):
+            step(i)
+        torch.cuda.synchronize()
+        for f in fams:
+            tot, n = L.prof_read(f)
+            if n:
+                detail[f"{C.PROF_NAMES[f]}_us"] = tot / n * 1e3
+        L.prof_enable([])
+        log("breakdown " + json.dumps(detail))
+
+    base = None
+    if not args.no_cpu_baseline:
+        log("CPU baseline: fp64 oracle")
+        base = cpu_baseline(w, x_host, wr, bias, codes, scales, args.cpu_seconds) if codes is not None else None
+
+    out = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms / args.steps,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: K3-shaped routed-expert layer, {w.T} token(s) per step, H {w.H}, "
+                               f"I {w.I}, {w.E} {w.wfmt} experts resident, top-{w.k}, bf16 activations, "
+                               "forward (route + group + experts + combine)",
+                   "T": w.T, "H": w.H, "I": w.I, "E": w.E, "k": w.k, "weights": w.wfmt},
+        "roofline": {"bound": "hbm", "kernel": "k_gateup (dequant + gate/up + SwiGLU)", "achieved": achieved,
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
+                     "traffic": traffic},
+        "cpu_baseline": base,
+        "detail": detail,
+    }
+    print(json.dumps(out), flush=True)
+    L.close()
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,182 @@
+/*
+ * moe.h -- C ABI of the routed-expert MoE layer for AMD Instinct MI355X (gfx950).
+ *
+ * The layer: a router picks the top-k of E experts per token, the tokens are
+ * grouped by expert, each routed expert applies a SwiGLU MLP whose gate, up
+ * and down matrices are stored quantized (MXFP4, or 3-bit residual VQ), and
+ * the expert outputs are combined with the routing weights.  The input
+ * gradient through the frozen experts and the router is also provided.
+ *
+ * Sources (cited by page and section):
+ *  - LazyLoRA README (github heyobi/LazyLora), "The engine": Kimi K3 has 896
+ *    routed experts per MoE layer, top-16 routing and MXFP4 expert weights;
+ *    the routed experts are one differentiable unit whose backward returns
+ *    the gradient with respect to the latent input ("Routed experts");
+ *    expert sums accumulate in fp32 ("Arithmetic"); a tensor that is missing
+ *    raises instead of being replaced ("Three rules the engine is built
+ *    around").  "File map": top-16 gating with a score-correction bias; a
+ *    routing record holds the chosen experts and their combining weights.
+ *    "LoRA": the expert shape 3584 -> 3072 -> 3584 in the MoE latent space.
+ *  - WASTE README (hackernews.jp story 49123386): an embeddable C API whose
+ *    open call returns a status and fills an out-handle, a config struct with
+ *    an init function for defaults, and a close call; experts stored as
+ *    3-bit residual VQ, 3 stages of 256-entry codebooks over 8-dim vectors.
+ *  - OCP Microscaling Formats (MX) v1.0: E2M1 elements, E8M0 block scales.
+ *
+ * Conventions
+ *  - Every tensor argument is a DEVICE pointer allocated by the caller
+ *    (typically through PyTorch); the library allocates no device memory.
+ *  - Every call that takes a stream only enqueues work on it (a hipStream_t
+ *    passed as void*; NULL = the null stream) and returns without waiting.
+ *    Data-dependent sizes (per-expert token counts, number of active
+ *    experts) stay on the device; no call synchronizes with the host.
+ *  - Argument checks run on the host, synchronously, before anything is
+ *    enqueued; on failure nothing is enqueued and no output is touched.
+ *  - No C++ exception crosses this interface.  A failed kernel launch
+ *    returns MOE_ERR_DEVICE; faults inside kernels surface at the caller's
+ *    next stream synchronization.
+ *  - One layer handle may be used from one stream at a time (its workspace
+ *    is shared by all calls on it).
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,   /* a null pointer, a bad size, a bad dtype, misalignment */
+    MOE_ERR_UNSUPPORTED = 2,   /* a valid request this build does not implement */
+    MOE_ERR_WORKSPACE = 3,     /* workspace smaller than moe_workspace_size() */
+    MOE_ERR_DEVICE = 4,        /* a HIP call failed; text in moe_last_error() */
+    MOE_ERR_INTERNAL = 5
+} moe_status;
+
+typedef enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1 } moe_dtype;
+typedef enum { MOE_W_MXFP4 = 0, MOE_W_RVQ3 = 1 } moe_wfmt;
+typedef enum { MOE_ACT_SWIGLU = 0 } moe_act;
+
+/* flags */
+enum {
+    MOE_F_DETERMINISTIC = 1u  /* combine and gradient reductions in a fixed order (always on in this build) */
+};
+
+/* Layer description.  moe_desc_init() fills the K3 defaults. */
+typedef struct {
+    int32_t hidden;      /* H: latent width (K3: 3584); multiple of 32 */
+    int32_t inter;       /* I: expert intermediate width (K3: 3072); multiple of 32 */
+    int32_t n_experts;   /* E: routed experts (K3: 896); 1..2048 */
+    int32_t top_k;       /* k: experts per token (K3: 16); 1..min(E, 64) */
+    int32_t max_tokens;  /* largest T any call on this layer will pass; sizes the workspace */
+    int32_t wfmt;        /* moe_wfmt */
+    int32_t act;         /* moe_act (SwiGLU: h = silu(gate) * up) */
+    int32_t bias_mode;   /* 0: no router bias; 1: bias added to the logits (selection and weights) */
+    uint32_t flags;
+} moe_desc;
+
+/* Expert and router weights: BORROWED device pointers.  The caller keeps
+ * them alive and unchanged until moe_destroy().  Matrices are stored
+ * [out][in] row-major with `in` contiguous: gate and up are [I][H], down is
+ * [H][I]; index 0 = gate, 1 = up, 2 = down.
+ *
+ * MXFP4 (wfmt = MOE_W_MXFP4): codes[m] is [E][out][in/2] bytes, byte j of a
+ *   row holding element 2j in its low nibble and 2j+1 in its high nibble
+ *   (E2M1: bit 3 sign, bits 2..1 exponent with bias 1, bit 0 mantissa);
+ *   scales[m] is [E][out][in/32] E8M0 bytes, one per 32 consecutive `in`
+ *   elements, value 2^(byte-127).  Element = E2M1(code) * 2^(scale-127).
+ *   codes must be 16-byte aligned.  Scale bytes must lie in 1..254 (the
+ *   all-ones byte means NaN in the format and is not supported).
+ * RVQ3 (wfmt = MOE_W_RVQ3): rvq_idx[m] is [E][3][out][in/8] bytes (stage-
+ *   planar); rvq_cb[m] is [E][3][256][8] fp16 codewords.  Elements 8v..8v+7
+ *   of a row equal the sum over the three stages s of
+ *   rvq_cb[m][e][s][rvq_idx[m][e][s][row][v]].  Both 16-byte aligned.
+ * router_w is [E][H] fp32; router_b is [E] fp32 or NULL (required when
+ * bias_mode = 1). */
+typedef struct {
+    const float *router_w;
+    const float *router_b;
+    const uint8_t *codes[3];
+    const uint8_t *scales[3];
+    const uint8_t *rvq_idx[3];
+    const uint16_t *rvq_cb[3];
+} moe_weights;
+
+/* Routing record, caller-owned device buffers written by moe_route() and
+ * read by moe_forward() / moe_backward_input():
+ *   ids      [T][k] int32  chosen experts, ranked by logit (larger first;
+ *                          equal logits rank the lower expert id first)
+ *   w        [T][k] fp32   combining weights: softmax over the k chosen logits
+ *   counts   [E]    int32  slots routed to each expert
+ *   offsets  [E+1]  int32  exclusive prefix sum of counts
+ *   perm     [T*k]  int32  slot indices t*k+j ordered by (expert, token)
+ *   inv      [T*k]  int32  inverse of perm (grouped row of each slot)
+ *   active   [E]    int32  experts with a nonzero count, ascending (first
+ *                          *n_active entries are meaningful)
+ *   n_active [1]    int32  number of active experts */
+typedef struct {
+    int32_t *ids;
+    float *w;
+    int32_t *counts;
+    int32_t *offsets;
+    int32_t *perm;
+    int32_t *inv;
+    int32_t *active;
+    int32_t *n_active;
+} moe_routing;
+
+typedef struct moe_layer moe_layer;
+
+/* Fill *d with the K3 layer: H 3584, I 3072, E 896, k 16, max_tokens 4096,
+ * MXFP4, SwiGLU, no bias, deterministic. */
+void moe_desc_init(moe_desc *d);
+
+/* Bytes of device workspace the layer needs for d->max_tokens tokens. */
+moe_status moe_workspace_size(const moe_desc *d, size_t *bytes);
+
+/* Validate d and w, and create a host-side handle that borrows the weights
+ * and the workspace (a device buffer of at least moe_workspace_size() bytes,
+ * 256-byte aligned, owned by the caller until moe_destroy()).  Copies *d. */
+moe_status moe_layer_create(const moe_desc *d, const moe_weights *w, void *workspace, size_t ws_bytes,
+                            moe_layer **out);
+
+/* Router and grouping.  x is [T][H] of dtype xt (fp32 or bf16), 16-byte
+ * aligned.  Fills every buffer of *r.  Logits are formed in fp32; tokens whose
+ * ranking is not certain under a rigorous fp32 error bound are re-ranked from
+ * fp64 logits, so the selection equals the one made on fp64 logits.
+ * T = 0 is a no-op.  0 <= T <= max_tokens. */
+moe_status moe_route(moe_layer *L, const void *x, int32_t xt, int32_t T, const moe_routing *r, void *stream);
+
+/* Expert forward and combine: y[T][H] fp32 = sum_j w[t][j] * expert_{ids[t][j]}(x[t]).
+ * r must come from moe_route() on the same x and T.  If saved_gu is not
+ * NULL it receives the gate and up pre-activations [T*k][2][I] fp32 in
+ * grouped row order (row = inv[t*k+j]) for moe_backward_input(). */
+moe_status moe_forward(moe_layer *L, const void *x, int32_t xt, int32_t T, const moe_routing *r, float *y,
+                       float *saved_gu, void *stream);
+
+/* Input gradient through the frozen experts and the router:
+ * dx[T][H] fp32 = d/dx of sum_t <dy[t], y[t]> with the routing held fixed
+ * (the expert selection is piecewise constant; the gradient flows through
+ * the experts and through the softmax weights into the router logits).
+ * dy is [T][H] of dtype dyt.  saved_gu from moe_forward() on the same
+ * inputs, or NULL to recompute it. */
+moe_status moe_backward_input(moe_layer *L, const void *x, int32_t xt, const void *dy, int32_t dyt, int32_t T,
+                              const moe_routing *r, const float *saved_gu, float *dx, void *stream);
+
+/* Release the handle (NULL is a no-op).  Borrowed memory is not freed. */
+void moe_destroy(moe_layer *L);
+
+/* Static text of a status code. */
+const char *moe_status_string(moe_status s);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char *moe_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H */

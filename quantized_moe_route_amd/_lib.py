@@ -1,0 +1,91 @@
+"""ctypes declarations of the C ABI in include/moe.h (argument marshalling only)."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from .build import LIB_PATH
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE, MOE_ERR_INTERNAL = range(6)
+MOE_DT_F32, MOE_DT_BF16 = 0, 1
+MOE_W_MXFP4, MOE_W_RVQ3 = 0, 1
+MOE_ACT_SWIGLU = 0
+MOE_F_DETERMINISTIC = 1
+
+EXPORTED = (
+    "moe_desc_init", "moe_workspace_size", "moe_layer_create", "moe_route", "moe_forward",
+    "moe_backward_input", "moe_destroy", "moe_status_string", "moe_last_error",
+    "moe_prof_enable", "moe_prof_read",
+)
+
+# kernel families of include/moe_prof.h
+PROF_ROUTER_LOGITS, PROF_ROUTER_TOPK, PROF_GROUP, PROF_GATEUP, PROF_DOWN, PROF_COMBINE, PROF_BWD_DOWN, \
+    PROF_BWD_GATEUP, PROF_BWD_FINAL = range(9)
+PROF_NAMES = ("router_logits", "router_topk", "group", "gateup", "down", "combine", "bwd_down", "bwd_gateup",
+              "bwd_final")
+
+
+class MoeDesc(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("n_experts", ctypes.c_int32),
+                ("top_k", ctypes.c_int32), ("max_tokens", ctypes.c_int32), ("wfmt", ctypes.c_int32),
+                ("act", ctypes.c_int32), ("bias_mode", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+
+
+class MoeWeights(ctypes.Structure):
+    _fields_ = [("router_w", ctypes.c_void_p), ("router_b", ctypes.c_void_p),
+                ("codes", ctypes.c_void_p * 3), ("scales", ctypes.c_void_p * 3),
+                ("rvq_idx", ctypes.c_void_p * 3), ("rvq_cb", ctypes.c_void_p * 3)]
+
+
+class MoeRouting(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("ids", "w", "counts", "offsets", "perm", "inv", "active", "n_active")]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, fn: str, detail: str):
+        super().__init__(f"{fn}: status {status} ({detail})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load the in-tree gfx950 library; there is no other implementation to fall back to."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first (quantized_moe_route_amd.build.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, st = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int
+        L.moe_desc_init.argtypes = [ctypes.POINTER(MoeDesc)]
+        L.moe_desc_init.restype = None
+        L.moe_workspace_size.argtypes = [ctypes.POINTER(MoeDesc), ctypes.POINTER(ctypes.c_size_t)]
+        L.moe_workspace_size.restype = st
+        L.moe_layer_create.argtypes = [ctypes.POINTER(MoeDesc), ctypes.POINTER(MoeWeights), vp, ctypes.c_size_t,
+                                       ctypes.POINTER(vp)]
+        L.moe_layer_create.restype = st
+        L.moe_route.argtypes = [vp, vp, i32, i32, ctypes.POINTER(MoeRouting), vp]
+        L.moe_route.restype = st
+        L.moe_forward.argtypes = [vp, vp, i32, i32, ctypes.POINTER(MoeRouting), vp, vp, vp]
+        L.moe_forward.restype = st
+        L.moe_backward_input.argtypes = [vp, vp, i32, vp, i32, i32, ctypes.POINTER(MoeRouting), vp, vp, vp]
+        L.moe_backward_input.restype = st
+        L.moe_destroy.argtypes = [vp]
+        L.moe_destroy.restype = None
+        L.moe_status_string.argtypes = [st]
+        L.moe_status_string.restype = ctypes.c_char_p
+        L.moe_last_error.argtypes = []
+        L.moe_last_error.restype = ctypes.c_char_p
+        L.moe_prof_enable.argtypes = [vp, ctypes.c_uint32, i32]
+        L.moe_prof_enable.restype = st
+        L.moe_prof_read.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]
+        L.moe_prof_read.restype = st
+        _lib = L
+    return _lib
+
+
+def check(status: int, fn: str) -> None:
+    if status != MOE_OK:
+        L = lib()
+        raise MoeError(status, fn, (L.moe_last_error() or b"").decode() or L.moe_status_string(status).decode())

@@ -1,0 +1,417 @@
+// moe_api.hip -- the C ABI declared in include/moe.h: argument validation,
+// workspace carving and kernel launches on the caller's stream.
+//
+// API shape after the WASTE README (hackernews.jp story 49123386): a config
+// struct with an init function for defaults, a create call that returns a
+// status and fills an out-handle, and a destroy call.  A missing input is an
+// error, never replaced (LazyLoRA README, "Three rules the engine is built
+// around").
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+
+#include "moe.h"
+#include "moe_internal.h"
+#include "moe_prof.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+moe_status fail(moe_status s, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return s;
+}
+
+constexpr int kMaxExperts = 2048;
+constexpr int kMaxTopK = 64;
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct Layout {
+    size_t logits, beta, h, ybuf, gu, dgdu, dp, total;
+};
+
+Layout layout_of(const moe_desc &d)
+{
+    const size_t T = (size_t)d.max_tokens, S = T * (size_t)d.top_k;
+    const size_t H = (size_t)d.hidden, I = (size_t)d.inter, E = (size_t)d.n_experts;
+    Layout L{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += align256(bytes);
+        return at;
+    };
+    L.logits = take(T * E * 4);
+    L.beta = take(T * E * 4);
+    L.h = take(S * I * 4);
+    L.ybuf = take(S * H * 4);
+    L.gu = take(S * 2 * I * 4);
+    L.dgdu = take(S * 2 * I * 4);
+    L.dp = take(S * (size_t)moe::dp_tiles((int)I) * 4);
+    L.total = off;
+    return L;
+}
+
+moe_status check_desc(const moe_desc *d)
+{
+    if (!d) return fail(MOE_ERR_INVALID_ARG, "desc is NULL");
+    if (d->hidden <= 0 || d->hidden % 32) return fail(MOE_ERR_INVALID_ARG, "hidden=%d must be a positive multiple of 32", d->hidden);
+    if (d->inter <= 0 || d->inter % 32) return fail(MOE_ERR_INVALID_ARG, "inter=%d must be a positive multiple of 32", d->inter);
+    if (d->n_experts < 1 || d->n_experts > kMaxExperts)
+        return fail(MOE_ERR_INVALID_ARG, "n_experts=%d must be in 1..%d", d->n_experts, kMaxExperts);
+    if (d->top_k < 1 || d->top_k > d->n_experts || d->top_k > kMaxTopK)
+        return fail(MOE_ERR_INVALID_ARG, "top_k=%d must be in 1..min(n_experts, %d)", d->top_k, kMaxTopK);
+    if (d->max_tokens < 0) return fail(MOE_ERR_INVALID_ARG, "max_tokens=%d is negative", d->max_tokens);
+    if ((long long)d->max_tokens * d->top_k > (1LL << 30))
+        return fail(MOE_ERR_INVALID_ARG, "max_tokens*top_k exceeds 2^30");
+    if (d->wfmt != MOE_W_MXFP4 && d->wfmt != MOE_W_RVQ3) return fail(MOE_ERR_INVALID_ARG, "unknown wfmt %d", d->wfmt);
+    if (d->act != MOE_ACT_SWIGLU) return fail(MOE_ERR_UNSUPPORTED, "activation %d is not implemented", d->act);
+    if (d->bias_mode != 0 && d->bias_mode != 1)
+        return fail(MOE_ERR_UNSUPPORTED, "bias_mode %d is not implemented", d->bias_mode);
+    return MOE_OK;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+moe_status check_dtype(int32_t dt, const char *what)
+{
+    if (dt != MOE_DT_F32 && dt != MOE_DT_BF16) return fail(MOE_ERR_INVALID_ARG, "%s dtype %d is not f32/bf16", what, dt);
+    return MOE_OK;
+}
+
+moe_status device_status(hipError_t e, const char *where)
+{
+    if (e == hipSuccess) return MOE_OK;
+    return fail(MOE_ERR_DEVICE, "%s: %s", where, hipGetErrorString(e));
+}
+
+}  // namespace
+
+struct moe_layer {
+    moe_desc d;
+    moe_weights w;
+    char *ws;
+    size_t ws_bytes;
+    Layout lay;
+    moe::Prof prof;
+};
+
+namespace {
+
+void prof_release(moe::Prof &p)
+{
+    for (int k = 0; k < moe::PK_N; k++) {
+        for (hipEvent_t e : p.ev[k])
+            if (e) hipEventDestroy(e);
+        p.ev[k].clear();
+        p.n[k] = 0;
+    }
+    p.mask = 0;
+    p.cap = 0;
+}
+
+}  // namespace
+
+namespace {
+
+moe_status check_layer(const moe_layer *L)
+{
+    if (!L) return fail(MOE_ERR_INVALID_ARG, "layer is NULL");
+    return MOE_OK;
+}
+
+moe_status check_routing(const moe_routing *r)
+{
+    if (!r) return fail(MOE_ERR_INVALID_ARG, "routing is NULL");
+    if (!r->ids || !r->w || !r->counts || !r->offsets || !r->perm || !r->inv || !r->active || !r->n_active)
+        return fail(MOE_ERR_INVALID_ARG, "a routing buffer is NULL");
+    return MOE_OK;
+}
+
+moe_status check_tokens(const moe_layer *L, int32_t T)
+{
+    if (T < 0 || T > L->d.max_tokens)
+        return fail(MOE_ERR_INVALID_ARG, "T=%d must be in 0..max_tokens=%d", T, L->d.max_tokens);
+    return MOE_OK;
+}
+
+moe::MatW matw(const moe_weights &w, int m)
+{
+    moe::MatW r;
+    r.codes = w.codes[m];
+    r.scales = w.scales[m];
+    r.idx = w.rvq_idx[m];
+    r.cb = w.rvq_cb[m];
+    return r;
+}
+
+}  // namespace
+
+extern "C" {
+
+void moe_desc_init(moe_desc *d)
+{
+    if (!d) return;
+    std::memset(d, 0, sizeof *d);
+    d->hidden = 3584;
+    d->inter = 3072;
+    d->n_experts = 896;
+    d->top_k = 16;
+    d->max_tokens = 4096;
+    d->wfmt = MOE_W_MXFP4;
+    d->act = MOE_ACT_SWIGLU;
+    d->bias_mode = 0;
+    d->flags = MOE_F_DETERMINISTIC;
+}
+
+moe_status moe_workspace_size(const moe_desc *d, size_t *bytes)
+{
+    g_last_error.clear();
+    moe_status st = check_desc(d);
+    if (st != MOE_OK) return st;
+    if (!bytes) return fail(MOE_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = layout_of(*d).total;
+    return MOE_OK;
+}
+
+moe_status moe_layer_create(const moe_desc *d, const moe_weights *w, void *workspace, size_t ws_bytes,
+                            moe_layer **out)
+{
+    g_last_error.clear();
+    moe_status st = check_desc(d);
+    if (st != MOE_OK) return st;
+    if (!w) return fail(MOE_ERR_INVALID_ARG, "weights is NULL");
+    if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
+    if (!w->router_w) return fail(MOE_ERR_INVALID_ARG, "router_w is NULL");
+    if (!aligned(w->router_w, 16)) return fail(MOE_ERR_INVALID_ARG, "router_w must be 16-byte aligned");
+    if (d->bias_mode == 1 && !w->router_b) return fail(MOE_ERR_INVALID_ARG, "bias_mode=1 needs router_b");
+    static const char *names[3] = {"gate", "up", "down"};
+    for (int m = 0; m < 3; m++) {
+        if (d->wfmt == MOE_W_MXFP4) {
+            if (!w->codes[m] || !w->scales[m]) return fail(MOE_ERR_INVALID_ARG, "%s codes/scales missing", names[m]);
+            if (!aligned(w->codes[m], 16)) return fail(MOE_ERR_INVALID_ARG, "%s codes must be 16-byte aligned", names[m]);
+        } else {
+            if (!w->rvq_idx[m] || !w->rvq_cb[m]) return fail(MOE_ERR_INVALID_ARG, "%s rvq_idx/rvq_cb missing", names[m]);
+            if (!aligned(w->rvq_idx[m], 16) || !aligned(w->rvq_cb[m], 16))
+                return fail(MOE_ERR_INVALID_ARG, "%s rvq_idx/rvq_cb must be 16-byte aligned", names[m]);
+        }
+    }
+    const Layout lay = layout_of(*d);
+    if (!workspace && lay.total > 0) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
+    if (ws_bytes < lay.total) return fail(MOE_ERR_WORKSPACE, "workspace %zu bytes < required %zu", ws_bytes, lay.total);
+    if (!aligned(workspace, 256)) return fail(MOE_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    moe_layer *L = new (std::nothrow) moe_layer;
+    if (!L) return fail(MOE_ERR_INTERNAL, "out of host memory");
+    L->d = *d;
+    L->w = *w;
+    L->ws = (char *)workspace;
+    L->ws_bytes = ws_bytes;
+    L->lay = lay;
+    *out = L;
+    return MOE_OK;
+}
+
+moe_status moe_route(moe_layer *L, const void *x, int32_t xt, int32_t T, const moe_routing *r, void *stream)
+{
+    g_last_error.clear();
+    moe_status st;
+    if ((st = check_layer(L)) != MOE_OK || (st = check_tokens(L, T)) != MOE_OK || (st = check_dtype(xt, "x")) != MOE_OK)
+        return st;
+    if (T == 0) return MOE_OK;
+    if ((st = check_routing(r)) != MOE_OK) return st;
+    if (!x) return fail(MOE_ERR_INVALID_ARG, "x is NULL");
+    if (!aligned(x, 16)) return fail(MOE_ERR_INVALID_ARG, "x must be 16-byte aligned");
+    hipStream_t s = (hipStream_t)stream;
+    moe::RouteArgs a{};
+    a.x = x;
+    a.xt = xt;
+    a.wr = L->w.router_w;
+    a.bias = L->d.bias_mode == 1 ? L->w.router_b : nullptr;
+    a.T = T;
+    a.H = L->d.hidden;
+    a.E = L->d.n_experts;
+    a.k = L->d.top_k;
+    a.logits = (float *)(L->ws + L->lay.logits);
+    a.beta = (float *)(L->ws + L->lay.beta);
+    a.ids = r->ids;
+    a.w = r->w;
+    a.refined = nullptr;
+    a.prof = &L->prof;
+    if ((st = device_status(moe::launch_router(a, s), "router")) != MOE_OK) return st;
+    moe::GroupArgs gq{};
+    gq.ids = r->ids;
+    gq.T = T;
+    gq.k = a.k;
+    gq.E = a.E;
+    gq.counts = r->counts;
+    gq.offsets = r->offsets;
+    gq.perm = r->perm;
+    gq.inv = r->inv;
+    gq.active = r->active;
+    gq.n_active = r->n_active;
+    gq.prof = &L->prof;
+    return device_status(moe::launch_group(gq, s), "group");
+}
+
+moe_status moe_forward(moe_layer *L, const void *x, int32_t xt, int32_t T, const moe_routing *r, float *y,
+                       float *saved_gu, void *stream)
+{
+    g_last_error.clear();
+    moe_status st;
+    if ((st = check_layer(L)) != MOE_OK || (st = check_tokens(L, T)) != MOE_OK || (st = check_dtype(xt, "x")) != MOE_OK)
+        return st;
+    if (T == 0) return MOE_OK;
+    if ((st = check_routing(r)) != MOE_OK) return st;
+    if (!x || !y) return fail(MOE_ERR_INVALID_ARG, "x or y is NULL");
+    if (!aligned(x, 16) || !aligned(y, 16)) return fail(MOE_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
+    if (saved_gu && !aligned(saved_gu, 16)) return fail(MOE_ERR_INVALID_ARG, "saved_gu must be 16-byte aligned");
+    moe::ExpertFwdArgs a{};
+    a.wfmt = L->d.wfmt;
+    a.gate = matw(L->w, 0);
+    a.up = matw(L->w, 1);
+    a.down = matw(L->w, 2);
+    a.x = x;
+    a.xt = xt;
+    a.T = T;
+    a.H = L->d.hidden;
+    a.I = L->d.inter;
+    a.E = L->d.n_experts;
+    a.k = L->d.top_k;
+    a.offsets = r->offsets;
+    a.perm = r->perm;
+    a.active = r->active;
+    a.n_active = r->n_active;
+    a.w = r->w;
+    a.h = (float *)(L->ws + L->lay.h);
+    a.gu = saved_gu;
+    a.ybuf = (float *)(L->ws + L->lay.ybuf);
+    a.y = y;
+    a.prof = &L->prof;
+    return device_status(moe::launch_expert_forward(a, (hipStream_t)stream), "forward");
+}
+
+moe_status moe_backward_input(moe_layer *L, const void *x, int32_t xt, const void *dy, int32_t dyt, int32_t T,
+                              const moe_routing *r, const float *saved_gu, float *dx, void *stream)
+{
+    g_last_error.clear();
+    moe_status st;
+    if ((st = check_layer(L)) != MOE_OK || (st = check_tokens(L, T)) != MOE_OK || (st = check_dtype(xt, "x")) != MOE_OK ||
+        (st = check_dtype(dyt, "dy")) != MOE_OK)
+        return st;
+    if (T == 0) return MOE_OK;
+    if ((st = check_routing(r)) != MOE_OK) return st;
+    if (!x || !dy || !dx) return fail(MOE_ERR_INVALID_ARG, "x, dy or dx is NULL");
+    if (!aligned(x, 16) || !aligned(dy, 16) || !aligned(dx, 16))
+        return fail(MOE_ERR_INVALID_ARG, "x, dy and dx must be 16-byte aligned");
+    if (saved_gu && !aligned(saved_gu, 16)) return fail(MOE_ERR_INVALID_ARG, "saved_gu must be 16-byte aligned");
+    moe::ExpertBwdArgs a{};
+    a.wfmt = L->d.wfmt;
+    a.gate = matw(L->w, 0);
+    a.up = matw(L->w, 1);
+    a.down = matw(L->w, 2);
+    a.x = x;
+    a.xt = xt;
+    a.dy = dy;
+    a.dyt = dyt;
+    a.T = T;
+    a.H = L->d.hidden;
+    a.I = L->d.inter;
+    a.E = L->d.n_experts;
+    a.k = L->d.top_k;
+    a.ids = r->ids;
+    a.offsets = r->offsets;
+    a.perm = r->perm;
+    a.inv = r->inv;
+    a.active = r->active;
+    a.n_active = r->n_active;
+    a.w = r->w;
+    a.wr = L->w.router_w;
+    a.gu = saved_gu;
+    a.h = (float *)(L->ws + L->lay.h);
+    a.gu_scratch = (float *)(L->ws + L->lay.gu);
+    a.dgdu = (float *)(L->ws + L->lay.dgdu);
+    a.dp_part = (float *)(L->ws + L->lay.dp);
+    a.dxs = (float *)(L->ws + L->lay.ybuf);
+    a.dx = dx;
+    a.prof = &L->prof;
+    return device_status(moe::launch_expert_backward(a, (hipStream_t)stream), "backward_input");
+}
+
+void moe_destroy(moe_layer *L)
+{
+    if (!L) return;
+    prof_release(L->prof);
+    delete L;
+}
+
+moe_status moe_prof_enable(moe_layer *L, uint32_t mask, int32_t max_launches)
+{
+    g_last_error.clear();
+    if (!L) return fail(MOE_ERR_INVALID_ARG, "layer is NULL");
+    prof_release(L->prof);
+    if (mask == 0) return MOE_OK;
+    if (max_launches < 1 || max_launches > 65536)
+        return fail(MOE_ERR_INVALID_ARG, "max_launches=%d must be in 1..65536", max_launches);
+    mask &= (1u << moe::PK_N) - 1u;
+    for (int k = 0; k < moe::PK_N; k++) {
+        if (!((mask >> k) & 1u)) continue;
+        L->prof.ev[k].assign((size_t)2 * max_launches, nullptr);
+        for (auto &e : L->prof.ev[k]) {
+            hipError_t err = hipEventCreate(&e);
+            if (err != hipSuccess) {
+                prof_release(L->prof);
+                return device_status(err, "hipEventCreate");
+            }
+        }
+    }
+    L->prof.cap = max_launches;
+    L->prof.mask = mask;
+    return MOE_OK;
+}
+
+moe_status moe_prof_read(moe_layer *L, int32_t family, double *total_ms, int32_t *launches)
+{
+    g_last_error.clear();
+    if (!L || !total_ms || !launches) return fail(MOE_ERR_INVALID_ARG, "NULL argument");
+    if (family < 0 || family >= moe::PK_N) return fail(MOE_ERR_INVALID_ARG, "unknown kernel family %d", family);
+    const moe::Prof &p = L->prof;
+    double tot = 0.0;
+    for (int i = 0; i < p.n[family]; i++) {
+        hipError_t err = hipEventSynchronize(p.ev[family][2 * i + 1]);
+        if (err != hipSuccess) return device_status(err, "hipEventSynchronize");
+        float ms = 0.f;
+        err = hipEventElapsedTime(&ms, p.ev[family][2 * i], p.ev[family][2 * i + 1]);
+        if (err != hipSuccess) return device_status(err, "hipEventElapsedTime");
+        tot += ms;
+    }
+    *total_ms = tot;
+    *launches = p.n[family];
+    return MOE_OK;
+}
+
+const char *moe_status_string(moe_status s)
+{
+    switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_DEVICE: return "device error";
+    case MOE_ERR_INTERNAL: return "internal error";
+    }
+    return "unknown status";
+}
+
+const char *moe_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

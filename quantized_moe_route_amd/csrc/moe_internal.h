@@ -1,0 +1,118 @@
+// moe_internal.h -- launch interfaces between the C ABI (moe_api.hip) and the
+// kernel files.  Host-side only declarations; no torch, no oracle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <vector>
+
+namespace moe {
+
+// Optional per-kernel timing (include/moe_prof.h): two events per launch on the launch stream.
+enum { PK_ROUTER_LOGITS = 0, PK_ROUTER_TOPK, PK_GROUP, PK_GATEUP, PK_DOWN, PK_COMBINE, PK_BWD_DOWN, PK_BWD_GATEUP,
+       PK_BWD_FINAL, PK_N };
+
+struct Prof {
+    uint32_t mask = 0;
+    int cap = 0;
+    std::vector<hipEvent_t> ev[PK_N];  // 2 * cap events per family
+    int n[PK_N] = {};
+};
+
+class ProfScope {
+  public:
+    ProfScope(Prof *p, int kid, hipStream_t s) : p_(p), kid_(kid), s_(s)
+    {
+        on_ = p_ && ((p_->mask >> kid_) & 1u) && p_->n[kid_] < p_->cap;
+        if (on_) hipEventRecord(p_->ev[kid_][2 * p_->n[kid_]], s_);
+    }
+    ~ProfScope()
+    {
+        if (on_) {
+            hipEventRecord(p_->ev[kid_][2 * p_->n[kid_] + 1], s_);
+            p_->n[kid_]++;
+        }
+    }
+
+  private:
+    Prof *p_;
+    int kid_;
+    hipStream_t s_;
+    bool on_;
+};
+
+struct RouteArgs {
+    Prof *prof;
+    const void *x;
+    int xt;
+    const float *wr;
+    const float *bias;
+    int T, H, E, k;
+    float *logits;  // [T][E] workspace
+    float *beta;    // [T][E] workspace
+    int32_t *ids;
+    float *w;
+    int32_t *refined;  // device counter of re-ranked tokens (may be null)
+};
+
+struct GroupArgs {
+    Prof *prof;
+    const int32_t *ids;
+    int T, k, E;
+    int32_t *counts, *offsets, *perm, *inv, *active, *n_active;
+};
+
+// Weights of one matrix (gate, up or down) in either format.
+struct MatW {
+    const uint8_t *codes;     // MXFP4 [E][rows][cols/2]
+    const uint8_t *scales;    // MXFP4 [E][rows][cols/32]
+    const uint8_t *idx;       // RVQ3  [E][3][rows][cols/8]
+    const uint16_t *cb;       // RVQ3  [E][3][256][8] fp16
+};
+
+struct ExpertFwdArgs {
+    Prof *prof;
+    int wfmt;
+    MatW gate, up, down;
+    const void *x;
+    int xt;
+    int T, H, I, E, k;
+    const int32_t *offsets, *perm, *active, *n_active;
+    const float *w;      // routing weights [T][k]
+    float *h;            // [S][I] grouped rows: silu(g) * u
+    float *gu;           // [S][2][I] grouped rows (g, u) or null
+    float *ybuf;         // [S][H] slot rows: w * expert output
+    float *y;            // [T][H]
+};
+
+struct ExpertBwdArgs {
+    Prof *prof;
+    int wfmt;
+    MatW gate, up, down;
+    const void *x;
+    int xt;
+    const void *dy;
+    int dyt;
+    int T, H, I, E, k;
+    const int32_t *ids, *offsets, *perm, *inv, *active, *n_active;
+    const float *w;
+    const float *wr;
+    const float *gu;     // [S][2][I] grouped (g, u)
+    float *h;            // scratch for recomputation [S][I]
+    float *gu_scratch;   // [S][2][I] when gu must be recomputed
+    float *dgdu;         // [S][2][I] grouped (dg, du)
+    float *dp_part;      // [S][ntile] partial <a, h>
+    float *dxs;          // [S][H] slot rows
+    float *dx;           // [T][H]
+};
+
+hipError_t launch_router(const RouteArgs &a, hipStream_t s);
+hipError_t launch_group(const GroupArgs &a, hipStream_t s);
+hipError_t launch_expert_forward(const ExpertFwdArgs &a, hipStream_t s);
+hipError_t launch_expert_backward(const ExpertBwdArgs &a, hipStream_t s);
+
+// number of I-column tiles whose partial <a, h> sums the backward stores per row
+__host__ __device__ inline int dp_tiles(int I) { return (I + 63) / 64; }
+
+}  // namespace moe

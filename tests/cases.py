@@ -1,0 +1,95 @@
+"""Shared helpers for the parity tests: build a workload on host and device, run the
+oracle on the same host arrays, compare."""
+from __future__ import annotations
+
+import sys
+import time
+from dataclasses import dataclass
+from typing import List, Optional
+
+import numpy as np
+
+import moe_synth as syn
+import oracle
+
+
+def log(msg: str) -> None:
+    print(f"[{time.strftime('%H:%M:%S')}] {msg}", flush=True)
+
+
+@dataclass
+class HostCase:
+    w: syn.Workload
+    x: np.ndarray            # fp32 or bf16 bits
+    wr: np.ndarray
+    bias: Optional[np.ndarray]
+    dy: Optional[np.ndarray]
+    codes: Optional[List[np.ndarray]] = None
+    scales: Optional[List[np.ndarray]] = None
+    idx: Optional[List[np.ndarray]] = None
+    cb: Optional[List[np.ndarray]] = None
+
+    @property
+    def x64(self):
+        return oracle.to_f64(self.x, self.w.x_dtype)
+
+    @property
+    def dy64(self):
+        return oracle.to_f64(self.dy, self.w.x_dtype)
+
+    def oracle_weights(self):
+        if self.codes is not None:
+            return oracle.Weights(self.w.H, self.w.I, codes=self.codes, scales=self.scales)
+        return oracle.Weights(self.w.H, self.w.I, idx=self.idx, cb=self.cb)
+
+
+def host_case(w: syn.Workload, T: Optional[int] = None, with_dy: Optional[bool] = None) -> HostCase:
+    T = w.T if T is None else T
+    c = HostCase(w, syn.activations(w, T), syn.router_weight(w), syn.router_bias(w),
+                 syn.upstream_grad(w, T) if (w.with_dy if with_dy is None else with_dy) else None)
+    if w.wfmt == "mxfp4":
+        c.codes, c.scales = syn.mxfp4_layer(w)
+    else:
+        c.idx, c.cb = syn.rvq3_layer(w)
+    return c
+
+
+def act_tensor(a: np.ndarray, dtype: str):
+    import quantized_moe_route_amd as q
+    return q.bf16_tensor(a) if dtype == "bf16" else q.to_device(np.asarray(a, np.float32))
+
+
+def device_layer(c: HostCase, max_tokens: int):
+    import quantized_moe_route_amd as q
+    w = c.w
+    kw = dict(hidden=w.H, inter=w.I, n_experts=w.E, top_k=w.k, max_tokens=max_tokens,
+              router_w=q.to_device(c.wr), router_b=None if c.bias is None else q.to_device(c.bias))
+    if c.codes is not None:
+        kw["codes"] = [q.to_device(a) for a in c.codes]
+        kw["scales"] = [q.to_device(a) for a in c.scales]
+    else:
+        kw["rvq_idx"] = [q.to_device(a) for a in c.idx]
+        kw["rvq_cb"] = [q.to_device(a) for a in c.cb]
+    return q.MoELayer(**kw)
+
+
+def rel_err(got: np.ndarray, ref: np.ndarray) -> float:
+    """max |got - ref| / max |ref| (the parity metric; 0 for an all-zero reference matched exactly)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    den = np.abs(ref).max() if ref.size else 0.0
+    num = np.abs(got - ref).max() if ref.size else 0.0
+    if den == 0.0:
+        return 0.0 if num == 0.0 else np.inf
+    return float(num / den)
+
+
+TOL = 1e-4
+
+
+def fnv1a32(a: np.ndarray) -> int:
+    """FNV-1a over the bytes of an array (determinism gate)."""
+    h = 0x811C9DC5
+    for b in np.ascontiguousarray(a).view(np.uint8).tobytes():
+        h = ((h ^ b) * 0x01000193) & 0xFFFFFFFF
+    return h

@@ -1,0 +1,164 @@
+"""Host-side checks of the C ABI: the library loads, exports every declared entry point, and
+rejects bad arguments synchronously without touching the device (no compute calls here)."""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import quantized_moe_route_amd as q
+from quantized_moe_route_amd import _lib as C
+
+INCLUDE = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include")
+
+
+def _declared():
+    names = set()
+    for h in glob.glob(os.path.join(INCLUDE, "*.h")):
+        src = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"\b(moe_[a-z_]+)\s*\(", src))
+    return sorted(names)
+
+
+def test_header_declares_the_boundary():
+    assert _declared() == sorted(C.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    L = C.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def _desc(**kw):
+    d = C.MoeDesc()
+    C.lib().moe_desc_init(ctypes.byref(d))
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+def test_desc_defaults_are_the_k3_layer():
+    d = _desc()
+    assert (d.hidden, d.inter, d.n_experts, d.top_k, d.max_tokens) == (3584, 3072, 896, 16, 4096)
+    assert d.wfmt == C.MOE_W_MXFP4 and d.act == C.MOE_ACT_SWIGLU and d.bias_mode == 0
+
+
+def test_workspace_size_and_desc_validation():
+    L = C.lib()
+    n = ctypes.c_size_t()
+    assert L.moe_workspace_size(ctypes.byref(_desc(max_tokens=1)), ctypes.byref(n)) == C.MOE_OK
+    small = n.value
+    assert L.moe_workspace_size(ctypes.byref(_desc(max_tokens=64)), ctypes.byref(n)) == C.MOE_OK
+    assert n.value > small
+    bad = [dict(hidden=100), dict(inter=0), dict(n_experts=0), dict(n_experts=5000), dict(top_k=0),
+           dict(top_k=65), dict(n_experts=8, top_k=9), dict(max_tokens=-1), dict(wfmt=7), dict(bias_mode=3)]
+    for kw in bad:
+        st = L.moe_workspace_size(ctypes.byref(_desc(**kw)), ctypes.byref(n))
+        assert st in (C.MOE_ERR_INVALID_ARG, C.MOE_ERR_UNSUPPORTED), kw
+        assert L.moe_last_error()
+    assert L.moe_workspace_size(None, ctypes.byref(n)) == C.MOE_ERR_INVALID_ARG
+
+
+def _fake_weights(wfmt=C.MOE_W_MXFP4, align=256):
+    # host-side validation only reads the pointer values; nothing dereferences them here
+    w = C.MoeWeights()
+    w.router_w = 0x10000
+    for m in range(3):
+        if wfmt == C.MOE_W_MXFP4:
+            w.codes[m] = 0x20000 + m * align
+            w.scales[m] = 0x30000 + m * 256
+        else:
+            w.rvq_idx[m] = 0x20000 + m * align
+            w.rvq_cb[m] = 0x30000 + m * 256
+    return w
+
+
+def _create(d, w, ws=0x100000, ws_bytes=None):
+    L = C.lib()
+    if ws_bytes is None:
+        n = ctypes.c_size_t()
+        L.moe_workspace_size(ctypes.byref(d), ctypes.byref(n))
+        ws_bytes = n.value
+    h = ctypes.c_void_p()
+    st = L.moe_layer_create(ctypes.byref(d), ctypes.byref(w), ws, ws_bytes, ctypes.byref(h))
+    return st, h
+
+
+def test_create_validation_and_destroy():
+    L = C.lib()
+    d = _desc(max_tokens=8)
+    st, h = _create(d, _fake_weights())
+    assert st == C.MOE_OK and h.value
+    L.moe_destroy(h)
+    L.moe_destroy(None)
+    w = _fake_weights()
+    w.codes[1] = None
+    assert _create(d, w)[0] == C.MOE_ERR_INVALID_ARG and b"up" in L.moe_last_error()
+    assert _create(d, _fake_weights(align=8))[0] == C.MOE_ERR_INVALID_ARG  # codes not 16-byte aligned
+    w = _fake_weights()
+    w.router_w = None
+    assert _create(d, w)[0] == C.MOE_ERR_INVALID_ARG
+    assert _create(_desc(max_tokens=8, bias_mode=1), _fake_weights())[0] == C.MOE_ERR_INVALID_ARG
+    assert _create(d, _fake_weights(), ws_bytes=16)[0] == C.MOE_ERR_WORKSPACE
+    assert _create(d, _fake_weights(), ws=0x100010)[0] == C.MOE_ERR_WORKSPACE
+    assert _create(_desc(max_tokens=8, wfmt=C.MOE_W_RVQ3), _fake_weights())[0] == C.MOE_ERR_INVALID_ARG
+    st, h = _create(_desc(max_tokens=8, wfmt=C.MOE_W_RVQ3), _fake_weights(C.MOE_W_RVQ3))
+    assert st == C.MOE_OK
+    L.moe_destroy(h)
+
+
+def test_calls_reject_bad_arguments_before_enqueueing():
+    L = C.lib()
+    d = _desc(max_tokens=8)
+    st, h = _create(d, _fake_weights())
+    assert st == C.MOE_OK
+    r = C.MoeRouting()
+    for i, n in enumerate(("ids", "w", "counts", "offsets", "perm", "inv", "active", "n_active")):
+        setattr(r, n, 0x40000 + 256 * i)
+    x, y = 0x50000, 0x60000
+    # T beyond max_tokens, negative T, bad dtype, null routing, null/misaligned x
+    assert L.moe_route(h, x, C.MOE_DT_BF16, 9, ctypes.byref(r), None) == C.MOE_ERR_INVALID_ARG
+    assert L.moe_route(h, x, C.MOE_DT_BF16, -1, ctypes.byref(r), None) == C.MOE_ERR_INVALID_ARG
+    assert L.moe_route(h, x, 5, 1, ctypes.byref(r), None) == C.MOE_ERR_INVALID_ARG
+    assert L.moe_route(h, x, C.MOE_DT_BF16, 1, None, None) == C.MOE_ERR_INVALID_ARG
+    assert L.moe_route(h, None, C.MOE_DT_BF16, 1, ctypes.byref(r), None) == C.MOE_ERR_INVALID_ARG
+    assert L.moe_route(h, x + 2, C.MOE_DT_BF16, 1, ctypes.byref(r), None) == C.MOE_ERR_INVALID_ARG
+    assert L.moe_route(None, x, C.MOE_DT_BF16, 1, ctypes.byref(r), None) == C.MOE_ERR_INVALID_ARG
+    r2 = C.MoeRouting()
+    ctypes.memmove(ctypes.byref(r2), ctypes.byref(r), ctypes.sizeof(r))
+    r2.perm = None
+    assert L.moe_route(h, x, C.MOE_DT_BF16, 1, ctypes.byref(r2), None) == C.MOE_ERR_INVALID_ARG
+    assert L.moe_forward(h, x, C.MOE_DT_BF16, 1, ctypes.byref(r), None, None, None) == C.MOE_ERR_INVALID_ARG
+    assert L.moe_forward(h, x, C.MOE_DT_BF16, 1, ctypes.byref(r), y + 4, None, None) == C.MOE_ERR_INVALID_ARG
+    assert L.moe_backward_input(h, x, C.MOE_DT_BF16, None, C.MOE_DT_BF16, 1, ctypes.byref(r), None, y,
+                                None) == C.MOE_ERR_INVALID_ARG
+    assert L.moe_backward_input(h, x, C.MOE_DT_BF16, x, 9, 1, ctypes.byref(r), None, y, None) == C.MOE_ERR_INVALID_ARG
+    # T = 0 is a valid no-op that touches nothing
+    assert L.moe_route(h, None, C.MOE_DT_BF16, 0, ctypes.byref(r), None) == C.MOE_OK
+    assert L.moe_forward(h, None, C.MOE_DT_BF16, 0, ctypes.byref(r), None, None, None) == C.MOE_OK
+    assert L.moe_backward_input(h, None, C.MOE_DT_BF16, None, C.MOE_DT_BF16, 0, ctypes.byref(r), None, None,
+                                None) == C.MOE_OK
+    assert L.moe_route(h, None, C.MOE_DT_BF16, 0, None, None) == C.MOE_OK  # empty buffers may be NULL
+    assert L.moe_status_string(C.MOE_ERR_DEVICE) == b"device error"
+    L.moe_destroy(h)
+
+
+def test_prof_argument_checks():
+    L = C.lib()
+    st, h = _create(_desc(max_tokens=8), _fake_weights())
+    assert L.moe_prof_enable(None, 1, 4) == C.MOE_ERR_INVALID_ARG
+    assert L.moe_prof_enable(h, 1, 0) == C.MOE_ERR_INVALID_ARG
+    assert L.moe_prof_enable(h, 0, 0) == C.MOE_OK  # disable needs no events
+    ms, n = ctypes.c_double(), ctypes.c_int32()
+    assert L.moe_prof_read(h, 99, ctypes.byref(ms), ctypes.byref(n)) == C.MOE_ERR_INVALID_ARG
+    assert L.moe_prof_read(h, 3, ctypes.byref(ms), ctypes.byref(n)) == C.MOE_OK and n.value == 0
+    L.moe_destroy(h)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(C, "_lib", None)
+    monkeypatch.setattr(C, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        C.lib()

@@ -1,0 +1,176 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle on the same seeded
+inputs.  Routing ids, grouping and permutations must be bit-exact; y, dX and the routing
+weights within max|err| / max|ref| <= 1e-4."""
+import numpy as np
+import pytest
+
+import moe_synth as syn
+import oracle
+from cases import TOL, act_tensor, device_layer, fnv1a32, host_case, log, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+def _np(t):
+    return t.detach().cpu().numpy()
+
+
+def check_routing(r, ids, p, E, name):
+    _sync()
+    gids = _np(r.ids)
+    assert np.array_equal(gids, ids), f"{name}: routing ids differ at {np.argwhere(gids != ids)[:5]}"
+    assert rel_err(_np(r.w), p) <= TOL, f"{name}: routing weights"
+    g = oracle.group(ids, E)
+    for key in ("counts", "offsets", "perm", "inv"):
+        assert np.array_equal(_np(getattr(r, key))[: g[key].size], g[key]), f"{name}: {key}"
+    n = int(_np(r.n_active)[0])
+    assert n == g["n_active"] and np.array_equal(_np(r.active)[:n], g["active"][:n]), f"{name}: active"
+
+
+def run_small(c, T=None, saved=True, name=""):
+    """Full comparison of route, forward and (when dY is present) backward."""
+    w = c.w
+    T = w.T if T is None else T
+    log(f"case {name}: T={T} H={w.H} I={w.I} E={w.E} k={w.k} fmt={w.wfmt} x={w.x_dtype}")
+    L = device_layer(c, max_tokens=max(T, 1))
+    x = act_tensor(c.x, w.x_dtype)
+    r = L.route(x)
+    ids, p, _ = oracle.route(c.x64, c.wr, c.bias, w.k)
+    check_routing(r, ids, p, w.E, name)
+    W = c.oracle_weights()
+    y_ref = oracle.forward(c.x64, ids, p, W)
+    gu = L.new_saved_gu(T) if saved else None
+    y = L.forward(x, r, saved_gu=gu)
+    _sync()
+    e = rel_err(_np(y), y_ref)
+    log(f"  y rel err {e:.3e}")
+    assert e <= TOL, f"{name}: y rel err {e}"
+    if c.dy is not None:
+        dy = act_tensor(c.dy, w.x_dtype)
+        dx_ref = oracle.backward_input(c.x64, c.dy64, ids, p, c.wr, W)
+        for g in ([gu, None] if saved else [None]):
+            dx = L.backward_input(x, dy, r, saved_gu=g)
+            _sync()
+            e = rel_err(_np(dx), dx_ref)
+            log(f"  dX rel err {e:.3e} (saved_gu={'yes' if g is not None else 'no'})")
+            assert e <= TOL, f"{name}: dX rel err {e}"
+    return L, x, r, y
+
+
+TINY = syn.WORKLOADS["tiny"]
+
+
+def test_tiny_config_full():
+    run_small(host_case(TINY), name="tiny")
+
+
+def test_tiny_bf16_activations_and_bias():
+    w = syn.shrink(TINY, x_dtype="bf16", bias_sd=0.5, x_key=7)
+    run_small(host_case(w), name="tiny-bf16-bias")
+
+
+def test_ragged_shapes_span_tiles():
+    # H, I multiples of 32 but not of 64 or 256; T, E, k odd-sized
+    w = syn.shrink(TINY, T=37, H=160, I=96, E=20, k=3, x_key=8)
+    run_small(host_case(w), name="ragged")
+
+
+def test_many_tokens_per_expert_uses_multi_tile_path():
+    # T > 64 selects the 4-tile token path; 8 experts with k=4 give ~50 tokens per expert
+    w = syn.shrink(TINY, T=100, E=8, k=4, x_dtype="bf16", x_key=9)
+    run_small(host_case(w), name="multi-tile")
+
+
+def test_rvq3_small():
+    w = syn.shrink(syn.WORKLOADS["rvq16"], T=24, H=256, I=128, E=12, k=3, with_dy=True)
+    run_small(host_case(w), name="rvq3-small")
+
+
+def test_single_token_and_k1():
+    w = syn.shrink(TINY, T=1, k=1, x_key=10)
+    run_small(host_case(w), name="T1-k1")
+
+
+def test_all_tokens_to_one_expert_max_skew():
+    w = syn.shrink(TINY, T=64, x_dtype="bf16", x_key=11)
+    c = host_case(w)
+    c.bias = np.zeros(w.E, np.float32)
+    c.bias[5] = 100.0  # every token ranks expert 5 first
+    run_small(c, name="skew")
+
+
+def test_exact_ties_from_duplicate_router_rows():
+    w = syn.shrink(TINY, T=32, x_key=12)
+    c = host_case(w)
+    c.wr[9] = c.wr[2]
+    c.wr[12] = c.wr[2]
+    c.wr[7] = c.wr[4]
+    run_small(c, name="ties")
+
+
+def test_near_ties_one_ulp_apart():
+    """Router rows differing by one fp32 ulp in a single element: the fp32 logits cannot
+    separate them, the fp64 re-ranking must."""
+    w = syn.shrink(TINY, T=48, E=16, k=4, x_key=13)
+    c = host_case(w)
+    for a, b in ((1, 5), (3, 11), (0, 14)):
+        c.wr[b] = c.wr[a]
+        c.wr[b, 17] = np.nextafter(c.wr[a, 17], np.float32(np.inf))
+    run_small(c, name="near-ties")
+
+
+def test_zero_input_and_signed_zero_logits():
+    w = syn.shrink(TINY, T=4, x_key=14)
+    c = host_case(w)
+    c.x[:] = 0.0
+    c.x[1, 0] = -0.0
+    run_small(c, name="zeros")
+
+
+def test_T0_is_a_noop():
+    import torch
+    c = host_case(syn.shrink(TINY, T=1))
+    L = device_layer(c, max_tokens=4)
+    r = L.new_routing(0)
+    x = torch.empty((0, TINY.H), dtype=torch.float32, device="cuda")
+    L.route(x, r)
+    y = L.forward(x, r)
+    assert y.shape == (0, TINY.H)
+    dx = L.backward_input(x, x, r)
+    assert dx.shape == (0, TINY.H)
+
+
+def test_selection_experts_closed_form_on_gpu():
+    """Selection-matrix experts give y = 2^c silu(2^a x) 2^b x on the selected inputs; checks the
+    GPU dequantizer's nibble order and scale handling against the closed form directly."""
+    from test_oracle_pins import _selection_closed_form, _selection_mxfp4
+    H, I, E, k, T = 256, 128, 6, 3, 16
+    shifts, exps = (5, 77, 200), (1, -2, [0, 1, -1, 2, -3, 3])
+    codes, scales = _selection_mxfp4(H, I, E, shifts, exps)
+    w = syn.shrink(TINY, T=T, H=H, I=I, E=E, k=k, x_key=15)
+    c = host_case(w)
+    c.codes, c.scales = codes, scales
+    L, x, r, y = run_small(c, name="selection")
+    ids, p = _np(r.ids), _np(r.w).astype(np.float64)
+    for t in range(T):
+        want = sum(p[t, j] * _selection_closed_form(c.x64[t], H, I, shifts, exps, exps[2][ids[t, j]])
+                   for j in range(k))
+        assert rel_err(_np(y)[t], want) <= 1e-5
+
+
+def test_repeat_calls_are_bitwise_deterministic():
+    w = syn.shrink(TINY, T=40, E=12, k=3, x_dtype="bf16", with_dy=True, x_key=16)
+    c = host_case(w)
+    L, x, r, y = run_small(c, name="determinism")
+    dy = act_tensor(c.dy, "bf16")
+    hashes_y, hashes_dx = set(), set()
+    for _ in range(5):
+        r2 = L.route(x)
+        hashes_y.add(fnv1a32(_np(L.forward(x, r2))))
+        hashes_dx.add(fnv1a32(_np(L.backward_input(x, dy, r2))))
+    assert len(hashes_y) == 1 and len(hashes_dx) == 1

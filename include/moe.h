@@ -89,7 +89,7 @@ typedef struct {
  *   (E2M1: bit 3 sign, bits 2..1 exponent with bias 1, bit 0 mantissa);
  *   scales[m] is [E][out][in/32] E8M0 bytes, one per 32 consecutive `in`
  *   elements, value 2^(byte-127).  Element = E2M1(code) * 2^(scale-127).
- *   codes must be 16-byte aligned.  Scale bytes must lie in 1..254 (the
+ *   codes and scales must be 16-byte aligned.  Scale bytes must lie in 1..254 (the
  *   all-ones byte means NaN in the format and is not supported).
  * RVQ3 (wfmt = MOE_W_RVQ3): rvq_idx[m] is [E][3][out][in/8] bytes (stage-
  *   planar); rvq_cb[m] is [E][3][256][8] fp16 codewords.  Elements 8v..8v+7

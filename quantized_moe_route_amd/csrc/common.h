@@ -73,34 +73,109 @@ __device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c)
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Butterfly reductions over a 64-lane wave; every lane receives a result, and
-// lane 0's result is the one callers keep (the association order is fixed).
+// ---------------------------------------------------------------- wave reductions
+//
+// Reductions over the 64 lanes of a wave, built from DPP lane permutations within
+// each 16-lane row (quad xor 1, quad xor 2, half-row mirror, row mirror) and four
+// readlanes across the rows.  Each step combines a lane with its partner by a
+// commutative operation, so every lane of a row holds the same value, and the
+// cross-row combine runs on wave-uniform values: every lane receives the same
+// result, computed in a fixed association order.
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v)
+{
+    return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v)
+{
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint64_t lo = dpp_u32<CTRL>((uint32_t)u), hi = dpp_u32<CTRL>((uint32_t)(u >> 32));
+    return __builtin_bit_cast(double, lo | (hi << 32));
+}
+
+__device__ __forceinline__ float readlane_f32(float v, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l)); }
+
+__device__ __forceinline__ double readlane_f64(double v, int l)
+{
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+    return __builtin_bit_cast(double, lo | (hi << 32));
+}
+
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7-i within 8
+constexpr int kDppMirror = 0x140;     // lane i <-> 15-i within 16
+
 __device__ __forceinline__ float wave_sum_f32(float v)
 {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    v += dpp_f32<kDppXor1>(v);
+    v += dpp_f32<kDppXor2>(v);
+    v += dpp_f32<kDppHalfMirror>(v);
+    v += dpp_f32<kDppMirror>(v);
+    return (readlane_f32(v, 0) + readlane_f32(v, 16)) + (readlane_f32(v, 32) + readlane_f32(v, 48));
+}
+
+// Sum with a rigorous bound on its rounding error: on entry eb bounds this lane's
+// accumulated error (in units of the unit roundoff), on exit it bounds the result's.
+// Each add contributes at most u |result| (round to nearest), so the bound follows
+// the same tree: eb = eb_a + eb_b + |a + b|.
+__device__ __forceinline__ float wave_sum_f32_eb(float v, float &eb)
+{
+#define MOE_SUM_EB_STEP(C)                    \
+    {                                         \
+        const float pv = dpp_f32<C>(v);       \
+        const float pe = dpp_f32<C>(eb);      \
+        v += pv;                              \
+        eb = eb + pe + fabsf(v);              \
+    }
+    MOE_SUM_EB_STEP(kDppXor1)
+    MOE_SUM_EB_STEP(kDppXor2)
+    MOE_SUM_EB_STEP(kDppHalfMirror)
+    MOE_SUM_EB_STEP(kDppMirror)
+#undef MOE_SUM_EB_STEP
+    const float a = readlane_f32(v, 0), b = readlane_f32(v, 16), c = readlane_f32(v, 32), d = readlane_f32(v, 48);
+    const float ea = readlane_f32(eb, 0), eb1 = readlane_f32(eb, 16), ec = readlane_f32(eb, 32), ed = readlane_f32(eb, 48);
+    const float ab = a + b, cd = c + d, r = ab + cd;
+    eb = ((ea + eb1) + fabsf(ab)) + ((ec + ed) + fabsf(cd)) + fabsf(r);
+    return r;
 }
 
 __device__ __forceinline__ double wave_sum_f64(double v)
 {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-    return v;
+    v += dpp_f64<kDppXor1>(v);
+    v += dpp_f64<kDppXor2>(v);
+    v += dpp_f64<kDppHalfMirror>(v);
+    v += dpp_f64<kDppMirror>(v);
+    return (readlane_f64(v, 0) + readlane_f64(v, 16)) + (readlane_f64(v, 32) + readlane_f64(v, 48));
 }
 
 __device__ __forceinline__ float wave_min_f32(float v)
 {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fminf(v, __shfl_xor(v, o, 64));
-    return v;
+    v = fminf(v, dpp_f32<kDppXor1>(v));
+    v = fminf(v, dpp_f32<kDppXor2>(v));
+    v = fminf(v, dpp_f32<kDppHalfMirror>(v));
+    v = fminf(v, dpp_f32<kDppMirror>(v));
+    return fminf(fminf(readlane_f32(v, 0), readlane_f32(v, 16)), fminf(readlane_f32(v, 32), readlane_f32(v, 48)));
 }
 
 __device__ __forceinline__ float wave_max_f32(float v)
 {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-    return v;
+    v = fmaxf(v, dpp_f32<kDppXor1>(v));
+    v = fmaxf(v, dpp_f32<kDppXor2>(v));
+    v = fmaxf(v, dpp_f32<kDppHalfMirror>(v));
+    v = fmaxf(v, dpp_f32<kDppMirror>(v));
+    return fmaxf(fmaxf(readlane_f32(v, 0), readlane_f32(v, 16)), fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
 }
 
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }

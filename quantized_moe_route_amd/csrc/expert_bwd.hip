@@ -342,9 +342,11 @@ hipError_t launch_expert_backward(const ExpertBwdArgs &a0, hipStream_t s)
         f.active = a.active;
         f.n_active = a.n_active;
         f.w = a.w;
-        f.h = a.h;
+        f.h_hi = a.h_hi;
+        f.h_lo = a.h_lo;
         f.gu = a.gu_scratch;
         f.prof = a.prof;
+        set_lds_staging(f);
         hipError_t err = launch_gateup_only(f, s);
         if (err != hipSuccess) return err;
         a.gu = a.gu_scratch;

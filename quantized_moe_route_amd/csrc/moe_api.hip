@@ -199,7 +199,8 @@ moe_status moe_layer_create(const moe_desc *d, const moe_weights *w, void *works
     for (int m = 0; m < 3; m++) {
         if (d->wfmt == MOE_W_MXFP4) {
             if (!w->codes[m] || !w->scales[m]) return fail(MOE_ERR_INVALID_ARG, "%s codes/scales missing", names[m]);
-            if (!aligned(w->codes[m], 16)) return fail(MOE_ERR_INVALID_ARG, "%s codes must be 16-byte aligned", names[m]);
+            if (!aligned(w->codes[m], 16) || !aligned(w->scales[m], 16))
+                return fail(MOE_ERR_INVALID_ARG, "%s codes and scales must be 16-byte aligned", names[m]);
         } else {
             if (!w->rvq_idx[m] || !w->rvq_cb[m]) return fail(MOE_ERR_INVALID_ARG, "%s rvq_idx/rvq_cb missing", names[m]);
             if (!aligned(w->rvq_idx[m], 16) || !aligned(w->rvq_cb[m], 16))
@@ -292,11 +293,13 @@ moe_status moe_forward(moe_layer *L, const void *x, int32_t xt, int32_t T, const
     a.active = r->active;
     a.n_active = r->n_active;
     a.w = r->w;
-    a.h = (float *)(L->ws + L->lay.h);
+    a.h_hi = (uint16_t *)(L->ws + L->lay.h);
+    a.h_lo = a.h_hi + (size_t)T * a.k * a.I;
     a.gu = saved_gu;
     a.ybuf = (float *)(L->ws + L->lay.ybuf);
     a.y = y;
     a.prof = &L->prof;
+    moe::set_lds_staging(a);
     return device_status(moe::launch_expert_forward(a, (hipStream_t)stream), "forward");
 }
 
@@ -337,7 +340,8 @@ moe_status moe_backward_input(moe_layer *L, const void *x, int32_t xt, const voi
     a.w = r->w;
     a.wr = L->w.router_w;
     a.gu = saved_gu;
-    a.h = (float *)(L->ws + L->lay.h);
+    a.h_hi = (uint16_t *)(L->ws + L->lay.h);
+    a.h_lo = a.h_hi + (size_t)T * a.k * a.I;
     a.gu_scratch = (float *)(L->ws + L->lay.gu);
     a.dgdu = (float *)(L->ws + L->lay.dgdu);
     a.dp_part = (float *)(L->ws + L->lay.dp);

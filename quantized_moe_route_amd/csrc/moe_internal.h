@@ -80,10 +80,13 @@ struct ExpertFwdArgs {
     int T, H, I, E, k;
     const int32_t *offsets, *perm, *active, *n_active;
     const float *w;      // routing weights [T][k]
-    float *h;            // [S][I] grouped rows: silu(g) * u
+    uint16_t *h_hi;      // [S][I] grouped rows: h = silu(g) * u as bf16 hi ...
+    uint16_t *h_lo;      // ... + lo (h - hi rounded to bf16)
     float *gu;           // [S][2][I] grouped rows (g, u) or null
     float *ybuf;         // [S][H] slot rows: w * expert output
     float *y;            // [T][H]
+    int nl_x;            // experts with at most this many tokens stage their x rows in LDS
+    int nl_h;            // ... and their h rows (down product)
 };
 
 struct ExpertBwdArgs {
@@ -99,13 +102,25 @@ struct ExpertBwdArgs {
     const float *w;
     const float *wr;
     const float *gu;     // [S][2][I] grouped (g, u)
-    float *h;            // scratch for recomputation [S][I]
+    uint16_t *h_hi;      // scratch for recomputation [S][I] x 2
+    uint16_t *h_lo;
     float *gu_scratch;   // [S][2][I] when gu must be recomputed
     float *dgdu;         // [S][2][I] grouped (dg, du)
     float *dp_part;      // [S][ntile] partial <a, h>
     float *dxs;          // [S][H] slot rows
     float *dx;           // [T][H]
 };
+
+// Token rows staged in LDS by the few-token (decode) expert kernels: at most 16 rows
+// and at most 48 KB of LDS per block.
+inline void set_lds_staging(ExpertFwdArgs &a)
+{
+    const int tmax = a.T < 16 ? a.T : 16;
+    const int nx = (int)(48 * 1024 / ((size_t)(a.H + 8) * 2));
+    const int nh = (int)(48 * 1024 / ((size_t)(a.I + 8) * 4));
+    a.nl_x = tmax < nx ? tmax : nx;
+    a.nl_h = tmax < nh ? tmax : nh;
+}
 
 hipError_t launch_router(const RouteArgs &a, hipStream_t s);
 hipError_t launch_group(const GroupArgs &a, hipStream_t s);

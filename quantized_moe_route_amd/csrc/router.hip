@@ -5,15 +5,17 @@
 // (+ b[e]), the k largest are selected (equal logits rank the lower expert id
 // first) and the combining weights are the softmax over the k selected logits.
 //
-// Logits are formed in fp32.  Alongside each logit the kernel stores a bound
-// beta >= |l_fp32 - l_exact|: each lane's fp32 FMA chain plus the reduction
-// tree has depth m, so the error is at most gamma_m * sum|x_i w_i| (Higham,
-// Accuracy and Stability of Numerical Algorithms, sec. 3.1); beta uses
-// 2 (m+2) 2^-24 (sum|x_i w_i| + |b|), which also covers the rounding of the
-// bias add and of the computed absolute sum.  Tokens whose selection or rank
-// order is not decided by these intervals have their candidate logits
-// recomputed in fp64 (the products of fp32/bf16 inputs are exact in fp64) and
-// are re-ranked on those values.
+// Logits are formed in fp32 with fp32 FMA chains.  Alongside each logit the kernels
+// store a rigorous bound beta >= |l_fp32 - l_exact| computed a posteriori: with
+// round-to-nearest every FMA or add z -> fl(z) errs by at most u |fl(z)| (u = 2^-24,
+// Higham, Accuracy and Stability of Numerical Algorithms, sec. 2.2), and in a sum
+// the rounding errors add up exactly, so u times the sum of the absolute values of
+// all rounded intermediate results of the actual reduction tree bounds the error.
+// That sum is accumulated in fp32 beside the logit (its own relative error is far
+// below the 1e-3 margin applied).  Tokens whose selection or rank order is not
+// decided by the intervals [l - beta, l + beta] have their candidate logits
+// recomputed in fp64 (the products of fp32/bf16 inputs are exact in fp64) and are
+// re-ranked on those values.
 #include "common.h"
 #include "moe_internal.h"
 
@@ -38,46 +40,82 @@ __device__ __forceinline__ float load_x1(const void *x, int xt, size_t off)
     return xt == DT_BF16 ? bf16_bits_to_f32(((const uint16_t *)x)[off]) : ((const float *)x)[off];
 }
 
-// GEMV form for few tokens: grid (ceil(E/16), T), 4 waves per block, each wave
-// one (token, expert) pair at a time; lane i-stride 256, 4 consecutive inputs.
+constexpr float kU = 0x1p-24f;
+
+__device__ __forceinline__ float bound_of(float eb, float l)
+{
+    return 1.001f * kU * eb + kU * fabsf(l) + 1e-30f;
+}
+
+// GEMV form for up to 8 tokens: one wave per expert; the router row is read once
+// for all tokens.  Lane l owns inputs 4l + 256 m (m = 0, 1, ...), an FMA chain per
+// token, then the wave reduction.
+constexpr int kGemvMaxT = 8;
+
 __global__ __launch_bounds__(256) void k_router_gemv(const void *__restrict__ x, int xt, const float *__restrict__ wr,
-                                                     const float *__restrict__ bias, int H, int E,
+                                                     const float *__restrict__ bias, int T, int H, int E,
                                                      float *__restrict__ logits, float *__restrict__ beta)
 {
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int t = blockIdx.y;
-    const float depth = (float)(4 * ((H + 255) / 256) + 6 + 2);
-    for (int q = 0; q < 4; q++) {
-        const int e = blockIdx.x * 16 + wv * 4 + q;
-        if (e >= E) break;
-        float acc = 0.f, sab = 0.f;
-        for (int i = lane * 4; i < H; i += 256) {
-            float4 w4 = *(const float4 *)(wr + (size_t)e * H + i);
-            float x0, x1, x2, x3;
-            load_x4(x, xt, (size_t)t * H + i, x0, x1, x2, x3);
-            acc = fmaf(x0, w4.x, acc);
-            acc = fmaf(x1, w4.y, acc);
-            acc = fmaf(x2, w4.z, acc);
-            acc = fmaf(x3, w4.w, acc);
-            sab = fmaf(fabsf(x0), fabsf(w4.x), sab);
-            sab = fmaf(fabsf(x1), fabsf(w4.y), sab);
-            sab = fmaf(fabsf(x2), fabsf(w4.z), sab);
-            sab = fmaf(fabsf(x3), fabsf(w4.w), sab);
+    const int lane = threadIdx.x & 63;
+    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (e >= E) return;
+    float acc[kGemvMaxT], eb[kGemvMaxT];
+#pragma unroll
+    for (int t = 0; t < kGemvMaxT; t++) acc[t] = eb[t] = 0.f;
+    const float *wrow = wr + (size_t)e * H;
+    // up to 16 float4 of the router row per lane (H <= 4096) are in flight at once
+    for (int i0 = lane * 4; i0 < H; i0 += 256 * 16) {
+        float4 w4[16];
+#pragma unroll
+        for (int m = 0; m < 16; m++) {
+            const int i = i0 + 256 * m;
+            w4[m] = i < H ? *(const float4 *)(wrow + i) : float4{0.f, 0.f, 0.f, 0.f};
         }
-        acc = wave_sum_f32(acc);
-        sab = wave_sum_f32(sab);
+#pragma unroll
+        for (int t = 0; t < kGemvMaxT; t++) {
+            if (t >= T) break;
+            float xv[16][4];
+#pragma unroll
+            for (int m = 0; m < 16; m++) {
+                const int i = i0 + 256 * m;
+                if (i < H)
+                    load_x4(x, xt, (size_t)t * H + i, xv[m][0], xv[m][1], xv[m][2], xv[m][3]);
+                else
+                    xv[m][0] = xv[m][1] = xv[m][2] = xv[m][3] = 0.f;
+            }
+#pragma unroll
+            for (int m = 0; m < 16; m++) {
+                const int i = i0 + 256 * m;
+                if (i >= H) break;
+                const float x0 = xv[m][0], x1 = xv[m][1], x2 = xv[m][2], x3 = xv[m][3];
+                acc[t] = fmaf(x0, w4[m].x, acc[t]);
+                eb[t] += fabsf(acc[t]);
+                acc[t] = fmaf(x1, w4[m].y, acc[t]);
+                eb[t] += fabsf(acc[t]);
+                acc[t] = fmaf(x2, w4[m].z, acc[t]);
+                eb[t] += fabsf(acc[t]);
+                acc[t] = fmaf(x3, w4[m].w, acc[t]);
+                eb[t] += fabsf(acc[t]);
+            }
+        }
+    }
+    const float b = bias ? bias[e] : 0.f;
+#pragma unroll
+    for (int t = 0; t < kGemvMaxT; t++) {
+        if (t >= T) break;
+        float ebt = eb[t];
+        const float s = wave_sum_f32_eb(acc[t], ebt);
+        const float l = s + b;
         if (lane == 0) {
-            const float b = bias ? bias[e] : 0.f;
-            logits[(size_t)t * E + e] = acc + b;
-            beta[(size_t)t * E + e] = 2.f * depth * 0x1p-24f * (sab + fabsf(b));
+            logits[(size_t)t * E + e] = l;
+            beta[(size_t)t * E + e] = bound_of(ebt, l);
         }
     }
 }
 
 // Tiled form for many tokens: block = 32 tokens x 64 experts, K chunks of 32
 // staged in LDS; thread (ty, tx) owns tokens 2ty, 2ty+1 and experts tx+16q.
-// Each chunk is summed from zero (chain 32) and added to the running total
-// (chain ceil(H/32)), so the depth is 32 + ceil(H/32).
+// Each chunk is summed from zero and then added to the running total.
 __global__ __launch_bounds__(256) void k_router_tiled(const void *__restrict__ x, int xt, const float *__restrict__ wr,
                                                       const float *__restrict__ bias, int T, int H, int E,
                                                       float *__restrict__ logits, float *__restrict__ beta)
@@ -86,21 +124,19 @@ __global__ __launch_bounds__(256) void k_router_tiled(const void *__restrict__ x
     __shared__ float ws[64][33];
     const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
     const int t0 = blockIdx.y * 32, e0 = blockIdx.x * 64;
-    float acc[2][4], sab[2][4];
+    float acc[2][4], eb[2][4];
 #pragma unroll
     for (int a = 0; a < 2; a++)
 #pragma unroll
-        for (int q = 0; q < 4; q++) acc[a][q] = sab[a][q] = 0.f;
+        for (int q = 0; q < 4; q++) acc[a][q] = eb[a][q] = 0.f;
 
     for (int k0 = 0; k0 < H; k0 += 32) {
-        // x tile: 32 x 32 values, 4 per thread
 #pragma unroll
         for (int r = 0; r < 4; r++) {
             const int idx = tid + 256 * r, tt = idx >> 5, kk = idx & 31;
             const int t = t0 + tt, k = k0 + kk;
             xs[tt][kk] = (t < T && k < H) ? load_x1(x, xt, (size_t)t * H + k) : 0.f;
         }
-        // Wr tile: 64 x 32 values, 8 per thread
 #pragma unroll
         for (int r = 0; r < 8; r++) {
             const int idx = tid + 256 * r, ee = idx >> 5, kk = idx & 31;
@@ -108,11 +144,11 @@ __global__ __launch_bounds__(256) void k_router_tiled(const void *__restrict__ x
             ws[ee][kk] = (e < E && k < H) ? wr[(size_t)e * H + k] : 0.f;
         }
         __syncthreads();
-        float part[2][4], pab[2][4];
+        float part[2][4];
 #pragma unroll
         for (int a = 0; a < 2; a++)
 #pragma unroll
-            for (int q = 0; q < 4; q++) part[a][q] = pab[a][q] = 0.f;
+            for (int q = 0; q < 4; q++) part[a][q] = 0.f;
 #pragma unroll 8
         for (int kk = 0; kk < 32; kk++) {
             const float xa = xs[2 * ty][kk], xb = xs[2 * ty + 1][kk];
@@ -121,8 +157,8 @@ __global__ __launch_bounds__(256) void k_router_tiled(const void *__restrict__ x
                 const float wv = ws[tx + 16 * q][kk];
                 part[0][q] = fmaf(xa, wv, part[0][q]);
                 part[1][q] = fmaf(xb, wv, part[1][q]);
-                pab[0][q] = fmaf(fabsf(xa), fabsf(wv), pab[0][q]);
-                pab[1][q] = fmaf(fabsf(xb), fabsf(wv), pab[1][q]);
+                eb[0][q] += fabsf(part[0][q]);
+                eb[1][q] += fabsf(part[1][q]);
             }
         }
 #pragma unroll
@@ -130,11 +166,10 @@ __global__ __launch_bounds__(256) void k_router_tiled(const void *__restrict__ x
 #pragma unroll
             for (int q = 0; q < 4; q++) {
                 acc[a][q] += part[a][q];
-                sab[a][q] += pab[a][q];
+                eb[a][q] += fabsf(acc[a][q]);
             }
         __syncthreads();
     }
-    const float depth = (float)(32 + (H + 31) / 32 + 2);
 #pragma unroll
     for (int a = 0; a < 2; a++)
 #pragma unroll
@@ -142,23 +177,44 @@ __global__ __launch_bounds__(256) void k_router_tiled(const void *__restrict__ x
             const int t = t0 + 2 * ty + a, e = e0 + tx + 16 * q;
             if (t < T && e < E) {
                 const float b = bias ? bias[e] : 0.f;
-                logits[(size_t)t * E + e] = acc[a][q] + b;
-                beta[(size_t)t * E + e] = 2.f * depth * 0x1p-24f * (sab[a][q] + fabsf(b));
+                const float l = acc[a][q] + b;
+                logits[(size_t)t * E + e] = l;
+                beta[(size_t)t * E + e] = bound_of(eb[a][q], l);
             }
         }
 }
 
-// fp64 logit of expert c for token t: each lane sums its inputs i = lane + 64 m
-// sequentially (the fp32 x fp32 or bf16 x fp32 products are exact in fp64),
-// then a fixed butterfly; lane 0's value is broadcast.  The same code path for
-// every expert makes identical router rows give identical values.
+// fp64 logit of expert c for token t: lane l sums its inputs 4l + 256 m in order
+// (the fp32 x fp32 or bf16 x fp32 products are exact in fp64), then the fixed wave
+// reduction.  The same code path for every expert makes identical router rows give
+// identical values.  Called by a whole wave; every lane receives the result.
 __device__ double logit_f64(const void *x, int xt, const float *wr, const float *bias, int t, int c, int H, int lane)
 {
     double acc = 0.0;
-    for (int i = lane; i < H; i += 64)
-        acc = fma((double)load_x1(x, xt, (size_t)t * H + i), (double)wr[(size_t)c * H + i], acc);
+    const float *wrow = wr + (size_t)c * H;
+    for (int i0 = lane * 4; i0 < H; i0 += 256 * 8) {
+        float4 w4[8];
+        float xv[8][4];
+#pragma unroll
+        for (int m = 0; m < 8; m++) {
+            const int i = i0 + 256 * m;
+            if (i < H) {
+                w4[m] = *(const float4 *)(wrow + i);
+                load_x4(x, xt, (size_t)t * H + i, xv[m][0], xv[m][1], xv[m][2], xv[m][3]);
+            } else {
+                w4[m] = float4{0.f, 0.f, 0.f, 0.f};
+                xv[m][0] = xv[m][1] = xv[m][2] = xv[m][3] = 0.f;
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < 8; m++) {
+            acc = fma((double)xv[m][0], (double)w4[m].x, acc);
+            acc = fma((double)xv[m][1], (double)w4[m].y, acc);
+            acc = fma((double)xv[m][2], (double)w4[m].z, acc);
+            acc = fma((double)xv[m][3], (double)w4[m].w, acc);
+        }
+    }
     acc = wave_sum_f64(acc);
-    acc = __shfl(acc, 0, 64);
     if (bias) acc += (double)bias[c];
     return acc;
 }
@@ -170,18 +226,74 @@ __device__ __forceinline__ bool ahead(V va, int ia, V vb, int ib)
     return va > vb || (va == vb && ia < ib);
 }
 
+template <int C>
+__device__ __forceinline__ void argbest_step(float &v, int &id)
+{
+    const float pv = dpp_f32<C>(v);
+    const int pi = (int)dpp_u32<C>((uint32_t)id);
+    if (ahead(pv, pi, v, id)) { v = pv; id = pi; }
+}
+
+template <int C>
+__device__ __forceinline__ void argbest_step(double &v, int &id)
+{
+    const double pv = dpp_f64<C>(v);
+    const int pi = (int)dpp_u32<C>((uint32_t)id);
+    if (ahead(pv, pi, v, id)) { v = pv; id = pi; }
+}
+
+__device__ __forceinline__ float rl(float v, int l) { return readlane_f32(v, l); }
+__device__ __forceinline__ double rl(double v, int l) { return readlane_f64(v, l); }
+
+// Wave-wide best (value, id) under the (value desc, id asc) order; every lane gets it.
 template <typename V>
 __device__ __forceinline__ void wave_argbest(V &v, int &id)
 {
+    argbest_step<kDppXor1>(v, id);
+    argbest_step<kDppXor2>(v, id);
+    argbest_step<kDppHalfMirror>(v, id);
+    argbest_step<kDppMirror>(v, id);
+    V bv = rl(v, 0);
+    int bi = __builtin_amdgcn_readlane(id, 0);
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-        V ov = __shfl_xor(v, o, 64);
-        int oi = __shfl_xor(id, o, 64);
-        if (ahead(ov, oi, v, id)) { v = ov; id = oi; }
+    for (int r = 16; r < 64; r += 16) {
+        const V ov = rl(v, r);
+        const int oi = __builtin_amdgcn_readlane(id, r);
+        if (ahead(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+    v = bv;
+    id = bi;
+}
+
+// One wave per token.  PL = logits held per lane (E <= 64 PL).
+// Bitonic sort of one (value, id) pair per lane across the wave into rank order
+// (lane 0 = first under (value desc, id asc)).
+__device__ __forceinline__ void sort64(float &v, int &id)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int size = 2; size <= 64; size <<= 1) {
+        const bool desc = (lane & size) == 0 || size == 64;
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            const float pv = __shfl_xor(v, stride, 64);
+            const int pi = __shfl_xor(id, stride, 64);
+            const bool lower = (lane & stride) == 0;
+            const bool pa = ahead(pv, pi, v, id);
+            if (lower == desc ? pa : !pa) {
+                v = pv;
+                id = pi;
+            }
+        }
     }
 }
 
 // One wave per token.  PL = logits held per lane (E <= 64 PL).
+// Selection: every member of the top-k ranks at or above the k-th largest of the 64
+// per-lane maxima (those k maxima are k distinct elements), so only elements at or
+// above that threshold are candidates; when there are at most 64 of them (always,
+// short of massive ties) they are compacted and sorted in one pass.  Otherwise k
+// rounds of a wave-wide arg-best decide.
 template <int PL>
 __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, const float *__restrict__ beta,
                                               const void *__restrict__ x, int xt, const float *__restrict__ wr,
@@ -189,10 +301,14 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, 
                                               int32_t *__restrict__ ids, float *__restrict__ wts,
                                               int32_t *__restrict__ refined)
 {
+    __shared__ float cvs[4][64];
+    __shared__ int cis[4][64];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int t = blockIdx.x * 4 + wv;
-    if (t >= T) return;
+    const int t_raw = blockIdx.x * 4 + wv;
+    const bool live = t_raw < T;
+    const int t = live ? t_raw : T - 1;  // dead waves shadow the last token until the block barrier
     const float NEG = -__builtin_huge_valf();
+    const int BIG = 0x7FFFFFFF;
     float l[PL], b[PL];
     uint32_t sel = 0, cand = 0;  // bit q: logit q of this lane
     int rank_id = 0;             // lane j < k: expert ranked j-th
@@ -204,20 +320,60 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, 
         l[q] = lv != lv ? NEG : lv;
         b[q] = e < E ? beta[(size_t)t * E + e] : 0.f;
     }
-    // 1. fp32 selection, k rounds of a wave-wide arg-best
-    for (int j = 0; j < k; j++) {
-        float bv = NEG;
-        int bi = 0x7FFFFFFF;
+    // 1. fp32 selection
+    float mv = NEG;
+    int mi = BIG;
+#pragma unroll
+    for (int q = 0; q < PL; q++) {
+        const int e = lane + 64 * q;
+        if (e < E && ahead(l[q], e, mv, mi)) { mv = l[q]; mi = e; }
+    }
+    sort64(mv, mi);
+    const float thv = readlane_f32(mv, k - 1);
+    const int thi = __builtin_amdgcn_readlane(mi, k - 1);
+    int ncand = 0;
+    int pos[PL];
+#pragma unroll
+    for (int q = 0; q < PL; q++) {
+        const int e = lane + 64 * q;
+        const bool c = e < E && !ahead(thv, thi, l[q], e);
+        const unsigned long long m = __ballot(c);
+        pos[q] = ncand + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        ncand += __popcll(m);
+        if (c && pos[q] < 64) {
+            cvs[wv][pos[q]] = l[q];
+            cis[wv][pos[q]] = e;
+        }
+    }
+    __syncthreads();
+    if (!live) return;
+    if (ncand <= 64) {
+        float v = lane < ncand ? cvs[wv][lane] : NEG;
+        int id = lane < ncand ? cis[wv][lane] : BIG;
+        sort64(v, id);
+        rank_id = id;
+        const float kv = readlane_f32(v, k - 1);
+        const int ki = __builtin_amdgcn_readlane(id, k - 1);
 #pragma unroll
         for (int q = 0; q < PL; q++) {
             const int e = lane + 64 * q;
-            if (e < E && !((sel >> q) & 1u) && ahead(l[q], e, bv, bi)) { bv = l[q]; bi = e; }
+            if (e < E && !ahead(kv, ki, l[q], e)) sel |= 1u << q;
         }
-        wave_argbest(bv, bi);
+    } else {
+        for (int j = 0; j < k; j++) {
+            float bv = NEG;
+            int bi = BIG;
 #pragma unroll
-        for (int q = 0; q < PL; q++)
-            if (lane + 64 * q == bi) sel |= 1u << q;
-        if (lane == j) rank_id = bi;
+            for (int q = 0; q < PL; q++) {
+                const int e = lane + 64 * q;
+                if (e < E && !((sel >> q) & 1u) && ahead(l[q], e, bv, bi)) { bv = l[q]; bi = e; }
+            }
+            wave_argbest(bv, bi);
+#pragma unroll
+            for (int q = 0; q < PL; q++)
+                if (lane + 64 * q == bi) sel |= 1u << q;
+            if (lane == j) rank_id = bi;
+        }
     }
     // 2. is the ranking certain under the fp32 error intervals?
     float lo = __builtin_huge_valf();
@@ -225,7 +381,7 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, 
     for (int q = 0; q < PL; q++)
         if ((sel >> q) & 1u) lo = fminf(lo, l[q] - b[q]);
     lo = wave_min_f32(lo);
-    int ncand = 0;
+    ncand = 0;
 #pragma unroll
     for (int q = 0; q < PL; q++) {
         const int e = lane + 64 * q;
@@ -277,9 +433,9 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, 
     // 4. softmax over the selected fp32 logits, in rank order
     my_id = lane < k ? rank_id : 0;
     const float lj = lane < k ? logits[(size_t)t * E + my_id] : NEG;
-    const float mx = __shfl(wave_max_f32(lj), 0, 64);
+    const float mx = wave_max_f32(lj);
     const float ex = lane < k ? __expf(lj - mx) : 0.f;
-    const float den = __shfl(wave_sum_f32(ex), 0, 64);
+    const float den = wave_sum_f32(ex);
     if (lane < k) {
         ids[(size_t)t * k + lane] = my_id;
         wts[(size_t)t * k + lane] = ex / den;
@@ -300,8 +456,8 @@ hipError_t launch_router(const RouteArgs &a, hipStream_t s)
 {
     {
     ProfScope ps(a.prof, PK_ROUTER_LOGITS, s);
-    if (a.T <= 8) {
-        hipLaunchKernelGGL(k_router_gemv, dim3((a.E + 15) / 16, a.T), dim3(256), 0, s, a.x, a.xt, a.wr, a.bias, a.H,
+    if (a.T <= kGemvMaxT) {
+        hipLaunchKernelGGL(k_router_gemv, dim3((a.E + 3) / 4), dim3(256), 0, s, a.x, a.xt, a.wr, a.bias, a.T, a.H,
                            a.E, a.logits, a.beta);
     } else {
         hipLaunchKernelGGL(k_router_tiled, dim3((a.E + 63) / 64, (a.T + 31) / 32), dim3(256), 0, s, a.x, a.xt, a.wr,

@@ -73,7 +73,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="decode1", choices=["decode1", "decode64", "rvq16"])
+    ap.add_argument("--workload", default="decode1", choices=["decode1", "decode64", "rvq16", "train4096"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel family (stderr)")
@@ -93,7 +93,8 @@ def main():
     assert torch.cuda.is_available(), "no GPU visible"
     torch.cuda.set_device(0)
     w = syn.WORKLOADS[args.workload]
-    POOL = 64
+    POOL = 64 if w.T <= 64 else 2
+    train = w.with_dy and w.T > 64
     log(f"workload {w.name}: T={w.T} H={w.H} I={w.I} E={w.E} k={w.k} {w.wfmt}; generating weights")
     wr, bias = syn.router_weight(w), syn.router_bias(w)
     kw = dict(hidden=w.H, inter=w.I, n_experts=w.E, top_k=w.k, max_tokens=w.T, router_w=q.to_device(wr),
@@ -116,6 +117,10 @@ def main():
     x_pool = q.bf16_tensor(x_host.reshape(-1, w.H)).reshape(POOL, w.T, w.H)
     r = L.new_routing(w.T)
     y = torch.empty((w.T, w.H), dtype=torch.float32, device="cuda")
+    if train:
+        dy_pool = q.bf16_tensor(syn.upstream_grad(w, w.T * POOL)).reshape(POOL, w.T, w.H)
+        gu = L.new_saved_gu(w.T)
+        dx = torch.empty((w.T, w.H), dtype=torch.float32, device="cuda")
 
     # active experts per pool entry (device routing, read once before any timing)
     U = []
@@ -127,7 +132,11 @@ def main():
     def step(i):
         xi = x_pool[i % POOL]
         L.route(xi, r)
-        L.forward(xi, r, y=y)
+        if train:
+            L.forward(xi, r, y=y, saved_gu=gu)
+            L.backward_input(xi, dy_pool[i % POOL], r, saved_gu=gu, dx=dx)
+        else:
+            L.forward(xi, r, y=y)
 
     for i in range(args.warmup):
         step(i)
@@ -198,7 +207,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": f"{w.name}: K3-shaped routed-expert layer, {w.T} token(s) per step, H {w.H}, "
                                f"I {w.I}, {w.E} {w.wfmt} experts resident, top-{w.k}, bf16 activations, "
-                               "forward (route + group + experts + combine)",
+                               + ("forward + input gradient (route + group + experts + combine + dX)" if train
+                                  else "forward (route + group + experts + combine)"),
                    "T": w.T, "H": w.H, "I": w.I, "E": w.E, "k": w.k, "weights": w.wfmt},
         "roofline": {"bound": "hbm", "kernel": "k_gateup (dequant + gate/up + SwiGLU)", "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,

@@ -47,10 +47,11 @@ __device__ __forceinline__ float bound_of(float eb, float l)
     return 1.001f * kU * eb + kU * fabsf(l) + 1e-30f;
 }
 
-// GEMV form for up to 8 tokens: one wave per expert; the router row is read once
-// for all tokens.  Lane l owns inputs 4l + 256 m (m = 0, 1, ...), an FMA chain per
-// token, then the wave reduction.
-constexpr int kGemvMaxT = 8;
+// GEMV form for up to 64 tokens and H <= 4096: one wave per (expert, group of 8
+// tokens) holds the router row in registers (lane l owns inputs 4l + 256 m); per token
+// an FMA chain per lane, then the wave reduction.  Grid: (ceil(E/4), ceil(T/8)).
+constexpr int kGemvMaxT = 64;
+constexpr int kGemvMaxH = 4096;
 
 __global__ __launch_bounds__(256) void k_router_gemv(const void *__restrict__ x, int xt, const float *__restrict__ wr,
                                                      const float *__restrict__ bias, int T, int H, int E,
@@ -59,25 +60,27 @@ __global__ __launch_bounds__(256) void k_router_gemv(const void *__restrict__ x,
     const int lane = threadIdx.x & 63;
     const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
     if (e >= E) return;
-    float acc[kGemvMaxT], eb[kGemvMaxT];
-#pragma unroll
-    for (int t = 0; t < kGemvMaxT; t++) acc[t] = eb[t] = 0.f;
     const float *wrow = wr + (size_t)e * H;
-    // up to 16 float4 of the router row per lane (H <= 4096) are in flight at once
-    for (int i0 = lane * 4; i0 < H; i0 += 256 * 16) {
-        float4 w4[16];
+    float4 w4[16];
 #pragma unroll
-        for (int m = 0; m < 16; m++) {
-            const int i = i0 + 256 * m;
-            w4[m] = i < H ? *(const float4 *)(wrow + i) : float4{0.f, 0.f, 0.f, 0.f};
-        }
+    for (int m = 0; m < 16; m++) {
+        const int i = lane * 4 + 256 * m;
+        w4[m] = i < H ? *(const float4 *)(wrow + i) : float4{0.f, 0.f, 0.f, 0.f};
+    }
+    const float b = bias ? bias[e] : 0.f;
+    {
+        const int t0 = blockIdx.y * 8;
+        float acc[8], eb[8];
 #pragma unroll
-        for (int t = 0; t < kGemvMaxT; t++) {
+        for (int u = 0; u < 8; u++) acc[u] = eb[u] = 0.f;
+#pragma unroll
+        for (int u = 0; u < 8; u++) {
+            const int t = t0 + u;
             if (t >= T) break;
             float xv[16][4];
 #pragma unroll
             for (int m = 0; m < 16; m++) {
-                const int i = i0 + 256 * m;
+                const int i = lane * 4 + 256 * m;
                 if (i < H)
                     load_x4(x, xt, (size_t)t * H + i, xv[m][0], xv[m][1], xv[m][2], xv[m][3]);
                 else
@@ -85,30 +88,28 @@ __global__ __launch_bounds__(256) void k_router_gemv(const void *__restrict__ x,
             }
 #pragma unroll
             for (int m = 0; m < 16; m++) {
-                const int i = i0 + 256 * m;
-                if (i >= H) break;
-                const float x0 = xv[m][0], x1 = xv[m][1], x2 = xv[m][2], x3 = xv[m][3];
-                acc[t] = fmaf(x0, w4[m].x, acc[t]);
-                eb[t] += fabsf(acc[t]);
-                acc[t] = fmaf(x1, w4[m].y, acc[t]);
-                eb[t] += fabsf(acc[t]);
-                acc[t] = fmaf(x2, w4[m].z, acc[t]);
-                eb[t] += fabsf(acc[t]);
-                acc[t] = fmaf(x3, w4[m].w, acc[t]);
-                eb[t] += fabsf(acc[t]);
+                if (lane * 4 + 256 * m >= H) break;
+                acc[u] = fmaf(xv[m][0], w4[m].x, acc[u]);
+                eb[u] += fabsf(acc[u]);
+                acc[u] = fmaf(xv[m][1], w4[m].y, acc[u]);
+                eb[u] += fabsf(acc[u]);
+                acc[u] = fmaf(xv[m][2], w4[m].z, acc[u]);
+                eb[u] += fabsf(acc[u]);
+                acc[u] = fmaf(xv[m][3], w4[m].w, acc[u]);
+                eb[u] += fabsf(acc[u]);
             }
         }
-    }
-    const float b = bias ? bias[e] : 0.f;
 #pragma unroll
-    for (int t = 0; t < kGemvMaxT; t++) {
-        if (t >= T) break;
-        float ebt = eb[t];
-        const float s = wave_sum_f32_eb(acc[t], ebt);
-        const float l = s + b;
-        if (lane == 0) {
-            logits[(size_t)t * E + e] = l;
-            beta[(size_t)t * E + e] = bound_of(ebt, l);
+        for (int u = 0; u < 8; u++) {
+            const int t = t0 + u;
+            if (t >= T) break;
+            float ebt = eb[u];
+            const float sv = wave_sum_f32_eb(acc[u], ebt);
+            const float l = sv + b;
+            if (lane == 0) {
+                logits[(size_t)t * E + e] = l;
+                beta[(size_t)t * E + e] = bound_of(ebt, l);
+            }
         }
     }
 }
@@ -456,9 +457,9 @@ hipError_t launch_router(const RouteArgs &a, hipStream_t s)
 {
     {
     ProfScope ps(a.prof, PK_ROUTER_LOGITS, s);
-    if (a.T <= kGemvMaxT) {
-        hipLaunchKernelGGL(k_router_gemv, dim3((a.E + 3) / 4), dim3(256), 0, s, a.x, a.xt, a.wr, a.bias, a.T, a.H,
-                           a.E, a.logits, a.beta);
+    if (a.T <= kGemvMaxT && a.H <= kGemvMaxH) {
+        hipLaunchKernelGGL(k_router_gemv, dim3((a.E + 3) / 4, (a.T + 7) / 8), dim3(256), 0, s, a.x, a.xt, a.wr, a.bias,
+                           a.T, a.H, a.E, a.logits, a.beta);
     } else {
         hipLaunchKernelGGL(k_router_tiled, dim3((a.E + 63) / 64, (a.T + 31) / 32), dim3(256), 0, s, a.x, a.xt, a.wr,
                            a.bias, a.T, a.H, a.E, a.logits, a.beta);

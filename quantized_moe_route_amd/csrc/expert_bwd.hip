@@ -18,7 +18,6 @@
 
 namespace moe {
 
-hipError_t launch_gateup_only(const ExpertFwdArgs &a, hipStream_t s);
 
 constexpr int kTS = 72;  // LDS row stride (bf16) of a transposed 64x64 tile, padded
 

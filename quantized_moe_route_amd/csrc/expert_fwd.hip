@@ -324,6 +324,16 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ ybuf,
     }
 }
 
+static hipError_t launch_combine(const ExpertFwdArgs &a, hipStream_t s)
+{
+    const size_t n4 = (size_t)a.T * a.H / 4;
+    const size_t nb = (n4 + 255) / 256;
+    const int blocks = (int)(nb < 4096 ? nb : 4096);
+    ProfScope ps(a.prof, PK_COMBINE, s);
+    hipLaunchKernelGGL(k_combine, dim3(blocks), dim3(256), 0, s, a.ybuf, a.T, a.H, a.k, a.y);
+    return hipGetLastError();
+}
+
 template <int WFMT, int XT, int NTT, bool FULLG, bool FULLD>
 static hipError_t fwd_launch(const ExpertFwdArgs &a, hipStream_t s)
 {
@@ -340,14 +350,7 @@ static hipError_t fwd_launch(const ExpertFwdArgs &a, hipStream_t s)
         hipLaunchKernelGGL((k_down<WFMT, NTT, RT, FULLD>), dim3((a.H + 64 * RT - 1) / (64 * RT), maxU), dim3(256), lds,
                            s, a);
     }
-    const size_t n4 = (size_t)a.T * a.H / 4;
-    const size_t nb = (n4 + 255) / 256;
-    const int blocks = (int)(nb < 4096 ? nb : 4096);
-    {
-        ProfScope ps(a.prof, PK_COMBINE, s);
-        hipLaunchKernelGGL(k_combine, dim3(blocks), dim3(256), 0, s, a.ybuf, a.T, a.H, a.k, a.y);
-    }
-    return hipGetLastError();
+    return launch_combine(a, s);
 }
 
 template <int WFMT, int XT, int NTT>
@@ -391,6 +394,7 @@ static hipError_t gateup_only(const ExpertFwdArgs &a, hipStream_t s)
 // gate/up + SwiGLU only (the backward recomputes g and u when they were not saved)
 hipError_t launch_gateup_only(const ExpertFwdArgs &a, hipStream_t s)
 {
+    if (use_mm(a)) return launch_gateup_mm(a, s);
     if (a.wfmt == FMT_MXFP4)
         return a.xt == DT_BF16 ? gateup_only<FMT_MXFP4, DT_BF16>(a, s) : gateup_only<FMT_MXFP4, DT_F32>(a, s);
     return a.xt == DT_BF16 ? gateup_only<FMT_RVQ3, DT_BF16>(a, s) : gateup_only<FMT_RVQ3, DT_F32>(a, s);
@@ -398,6 +402,12 @@ hipError_t launch_gateup_only(const ExpertFwdArgs &a, hipStream_t s)
 
 hipError_t launch_expert_forward(const ExpertFwdArgs &a, hipStream_t s)
 {
+    if (use_mm(a)) {
+        hipError_t err = launch_gateup_mm(a, s);
+        if (err == hipSuccess) err = launch_down_mm(a, s);
+        if (err == hipSuccess) err = launch_combine(a, s);
+        return err;
+    }
     if (a.wfmt == FMT_MXFP4)
         return a.xt == DT_BF16 ? fwd_ntt<FMT_MXFP4, DT_BF16>(a, s) : fwd_ntt<FMT_MXFP4, DT_F32>(a, s);
     return a.xt == DT_BF16 ? fwd_ntt<FMT_RVQ3, DT_BF16>(a, s) : fwd_ntt<FMT_RVQ3, DT_F32>(a, s);

@@ -1,0 +1,403 @@
+// expert_mm.hip -- grouped-GEMM expert forward for experts holding many tokens (MXFP4).
+//
+// Same arithmetic as the few-token kernels of expert_fwd.hip (LazyLoRA README, "The
+// engine" / "Arithmetic": experts consumed in their packed format, fp32 accumulation;
+// "Measurement findings": one sweep over each expert's bytes amortised over all of the
+// expert's tokens), organised for experts with tens of tokens (prefill and training
+// batches):
+//
+//  - a block owns one expert, a column block of the output (128 I-columns of gate and
+//    up, or 256 rows of H for down) and all of the expert's tokens, up to 96 per pass in
+//    at most six tiles of 16 (the tile count is a template parameter chosen per pass, so
+//    the inner loop carries no per-tile branches);
+//  - the token operand of one K-step (gathered x rows, or the bf16 hi/lo planes of h)
+//    is staged in LDS, double-buffered and shared by the block's four waves; each wave
+//    applies every token fragment to its four 16-row weight tiles with
+//    v_mfma_f32_16x16x32_bf16;
+//  - weight codes and scale bytes stream from HBM into registers two K-steps ahead (three
+//    register stages, the K loop unrolled by three so that no stage is copied) and are
+//    dequantized exactly to bf16 (v_cvt_scalef32_pk_bf16_fp4) right before use;
+//  - blocks are spread over the XCDs expert by expert (xcd_split), so that the column
+//    blocks of one expert, which all read the same token rows, share one L2.
+//
+// LDS tile: [96 rows][16 chunks of 16 bytes]; chunk c of row r sits in slot c ^ (r & 15),
+// which spreads the 16 rows read by one MFMA operand load over all banks.
+#include <type_traits>
+
+#include "common.h"
+#include "moe_internal.h"
+
+namespace moe {
+
+constexpr int kMmTT = 6;            // token tiles of 16 per pass
+constexpr int kMmTok = 16 * kMmTT;  // tokens per pass
+
+template <int P>
+using Stage = std::integral_constant<int, P>;
+
+typedef u32x4 MmTile[kMmTok * 16];
+
+// XCD-aware work split.  The dispatcher hands block b to XCD b % 8; active expert ai
+// goes to XCD ai % 8, whose blocks walk their experts in order, nb blocks per expert.
+// The grid holds 8 * ceil(maxU / 8) * nb blocks.
+__device__ __forceinline__ void xcd_split(int nb, int &ai, int &cb)
+{
+    const int x = blockIdx.x & 7, j = blockIdx.x >> 3;
+    const int q = j / nb;
+    cb = j - q * nb;
+    ai = 8 * q + x;
+}
+
+static inline int xcd_grid(int maxU, int nb) { return 8 * ((maxU + 7) / 8) * nb; }
+
+__device__ __forceinline__ int lds_slot(int row, int chunk) { return row * 16 + (chunk ^ (row & 15)); }
+
+// 8 E2M1 codes (one dword) times a power-of-two scale -> 8 bf16, exact.
+__device__ __forceinline__ bf16x8 fp4x8_to_bf16(uint32_t w, float scale)
+{
+    const bf16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+    const bf16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
+    const bf16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2);
+    const bf16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3);
+    return as_bf16x8(__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1),
+                     __builtin_bit_cast(uint32_t, v2), __builtin_bit_cast(uint32_t, v3));
+}
+
+// Buffer resource over [p, p + bytes): raw (untyped) loads through it take a 32-bit lane
+// offset plus a wave-uniform offset, so an address costs one VGPR instead of two, and
+// offsets past `bytes` read zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ u32x4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
+}
+
+__device__ __forceinline__ u32x2 ld8(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b64(r, (int)voff, (int)soff, 0);
+}
+
+__device__ __forceinline__ uint32_t ld1(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff)
+{
+    return __builtin_amdgcn_raw_buffer_load_b8(r, (int)voff, (int)soff, 0);
+}
+
+// Runs step(Stage<st % 3>, st) for st = 0 .. n-1.  The loop body is three whole steps
+// with the remainder peeled after it, so the loop has a single back edge and the wait
+// counts the compiler derives at its head stay exact.
+template <typename F>
+__device__ __forceinline__ void k_loop3(int n, F &&step)
+{
+    int s0 = 0;
+    for (; s0 + 3 <= n; s0 += 3) {
+        step(Stage<0>(), s0);
+        step(Stage<1>(), s0 + 1);
+        step(Stage<2>(), s0 + 2);
+    }
+    if (s0 < n) step(Stage<0>(), s0);
+    if (s0 + 1 < n) step(Stage<1>(), s0 + 1);
+}
+
+// ---------------------------------------------------------------- gate/up + SwiGLU
+//
+// K-step 128: lane group g = lane / 16 owns reduction indices [32g, 32g + 32) of the
+// step, one MX scale block = 16 code bytes; sub-step s takes indices 32g + 8s + 0..7
+// on both operands.  Wave wv owns I-columns c0 = 128 cb + 32 wv .. +32 of gate
+// (tiles 0, 1) and of up (tiles 2, 3).
+
+struct GuBlock {
+    __amdgpu_buffer_rsrc_t code[2], scale[2];  // this expert's gate and up matrices
+    __amdgpu_buffer_rsrc_t x;                   // the token rows
+    uint32_t coff, soff;                        // this lane's code / scale byte offsets at K-step 0
+    int c0;                                     // first I-column of this wave
+};
+
+template <int NT>
+__device__ __forceinline__ void gateup_pass(const ExpertFwdArgs &a, const GuBlock &b, MmTile *xs, int r0, int tt0,
+                                            int nt)
+{
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
+    const int H = a.H, I = a.I, nsteps = H / 128;
+    const int xr = tid >> 4, xc = tid & 15;  // this thread's x-tile row (+16 i) and chunk
+    uint32_t xoff[NT];                       // byte offsets at K-step 0
+#pragma unroll
+    for (int i = 0; i < NT; i++) {
+        const int tok = a.perm[r0 + tt0 + min(xr + 16 * i, nt - 1)] / a.k;
+        xoff[i] = ((uint32_t)tok * H + 8 * xc) * 2;
+    }
+    f32x4 acc[4][NT];
+#pragma unroll
+    for (int t = 0; t < 4; t++)
+#pragma unroll
+        for (int tt = 0; tt < NT; tt++) acc[t][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4 q[3][4];
+    uint32_t sc[3][4];
+    auto load_w = [&](auto P, int st) {
+        constexpr int p = decltype(P)::value;
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+            q[p][t] = ld16(b.code[t >> 1], b.coff, (t & 1) * 8 * H + 64 * st);
+            sc[p][t] = ld1(b.scale[t >> 1], b.soff, (t & 1) * (H / 2) + 4 * st);
+        }
+    };
+    {
+        u32x4 xv[NT];
+#pragma unroll
+        for (int i = 0; i < NT; i++) xv[i] = ld16(b.x, xoff[i], 0);
+        load_w(Stage<0>(), 0);
+        load_w(Stage<1>(), min(1, nsteps - 1));
+#pragma unroll
+        for (int i = 0; i < NT; i++) xs[0][lds_slot(xr + 16 * i, xc)] = xv[i];
+    }
+    __syncthreads();
+
+    k_loop3(nsteps, [&](auto P, int st) {
+        constexpr int p = decltype(P)::value;
+        const int buf = st & 1;
+        u32x4 xv[NT];  // next step's x tile, issued before the weights so waiting for it
+        const int stn = min(st + 1, nsteps - 1);  // leaves the weight prefetch in flight
+#pragma unroll
+        for (int i = 0; i < NT; i++) xv[i] = ld16(b.x, xoff[i], 256 * stn);
+        load_w(Stage<(p + 2) % 3>(), min(st + 2, nsteps - 1));
+        __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the step's MFMAs
+        float scale[4];
+#pragma unroll
+        for (int t = 0; t < 4; t++) scale[t] = e8m0_to_f32(sc[p][t]);
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+            bf16x8 A[4], B[NT];
+#pragma unroll
+            for (int tt = 0; tt < NT; tt++) B[tt] = as_bf16x8(xs[buf][lds_slot(16 * tt + li, 4 * g + s)]);
+#pragma unroll
+            for (int t = 0; t < 4; t++) A[t] = fp4x8_to_bf16(q[p][t][s], scale[t]);
+#pragma unroll
+            for (int tt = 0; tt < NT; tt++)
+#pragma unroll
+                for (int t = 0; t < 4; t++) acc[t][tt] = mfma16(A[t], B[tt], acc[t][tt]);
+        }
+#pragma unroll
+        for (int i = 0; i < NT; i++) xs[buf ^ 1][lds_slot(xr + 16 * i, xc)] = xv[i];
+        __syncthreads();
+    });
+
+    // lane (g, li) holds I-columns c0 + 16 (t & 1) + 4 g + 0..3 of token 16 tt + li
+#pragma unroll
+    for (int tt = 0; tt < NT; tt++) {
+        const int j = 16 * tt + li;
+        if (j >= nt) continue;
+        const size_t rr = (size_t)(r0 + tt0 + j);
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+            const f32x4 gv = acc[t][tt], uv = acc[t + 2][tt];
+            uint32_t hh[4], hl[4];
+#pragma unroll
+            for (int r = 0; r < 4; r++) split_bf16(gv[r] * sigmoidf_(gv[r]) * uv[r], hh[r], hl[r]);
+            const int n = b.c0 + 16 * t + 4 * g;
+            *(u32x2 *)(a.h_hi + rr * I + n) = u32x2{pack2(hh[0], hh[1]), pack2(hh[2], hh[3])};
+            *(u32x2 *)(a.h_lo + rr * I + n) = u32x2{pack2(hl[0], hl[1]), pack2(hl[2], hl[3])};
+            if (a.gu) {
+                *(float4 *)(a.gu + (rr * 2 + 0) * I + n) = float4{gv[0], gv[1], gv[2], gv[3]};
+                *(float4 *)(a.gu + (rr * 2 + 1) * I + n) = float4{uv[0], uv[1], uv[2], uv[3]};
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(256, 2) void k_gateup_mm(const ExpertFwdArgs a)
+{
+    __shared__ MmTile xs[2];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
+    const int H = a.H, I = a.I;
+    int ai, cb;
+    xcd_split(I / 128, ai, cb);
+    if (ai >= *a.n_active) return;
+    const int e = a.active[ai];
+    const int r0 = a.offsets[e], ntok = a.offsets[e + 1] - r0;
+    GuBlock b;
+    const size_t eoc = (size_t)e * I * (H / 2), eos = (size_t)e * I * (H / 32);
+    b.code[0] = buf_rsrc(a.gate.codes + eoc, I * (H / 2));
+    b.code[1] = buf_rsrc(a.up.codes + eoc, I * (H / 2));
+    b.scale[0] = buf_rsrc(a.gate.scales + eos, I * (H / 32));
+    b.scale[1] = buf_rsrc(a.up.scales + eos, I * (H / 32));
+    b.x = buf_rsrc(a.x, (uint32_t)((size_t)a.T * H * 2));
+    b.c0 = cb * 128 + wv * 32;
+    b.coff = (uint32_t)(b.c0 + li) * (H / 2) + 16 * g;
+    b.soff = (uint32_t)(b.c0 + li) * (H / 32) + g;
+    for (int tt0 = 0; tt0 < ntok; tt0 += kMmTok) {
+        const int nt = min(kMmTok, ntok - tt0);
+        switch ((nt + 15) / 16) {
+        case 1: gateup_pass<1>(a, b, xs, r0, tt0, nt); break;
+        case 2: gateup_pass<2>(a, b, xs, r0, tt0, nt); break;
+        case 3: gateup_pass<3>(a, b, xs, r0, tt0, nt); break;
+        case 4: gateup_pass<4>(a, b, xs, r0, tt0, nt); break;
+        case 5: gateup_pass<5>(a, b, xs, r0, tt0, nt); break;
+        default: gateup_pass<6>(a, b, xs, r0, tt0, nt); break;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- down + routing weight
+//
+// K-step 64 over I: lane group g owns reduction indices [16g, 16g + 16) of the step
+// (half an MX scale block, 8 code bytes); sub-step s takes 16g + 8s + 0..7.  The LDS row
+// of a token holds the step's 64 bf16 of h_hi (chunks 0..7) then of h_lo (chunks 8..15);
+// h = h_hi + h_lo enters as two MFMAs per fragment.  Wave wv owns H-rows
+// m0 = 256 rb + 64 wv .. +64 (tiles 0..3).
+
+struct DnBlock {
+    __amdgpu_buffer_rsrc_t code, scale;  // this expert's down matrix
+    __amdgpu_buffer_rsrc_t h;            // h_hi then h_lo (contiguous planes)
+    uint32_t coff, soff;
+    int m0;
+};
+
+template <int NT>
+__device__ __forceinline__ void down_pass(const ExpertFwdArgs &a, const DnBlock &b, MmTile *hs, int r0, int tt0,
+                                          int nt)
+{
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
+    const int H = a.H, I = a.I, nsteps = I / 64;
+    const int xr = tid >> 4, xc = tid & 15;
+    const uint32_t plane = xc < 8 ? 0u : (uint32_t)(a.h_lo - a.h_hi) * 2;  // this thread's plane
+    uint32_t hoff[NT];                                                      // byte offsets at K-step 0
+#pragma unroll
+    for (int i = 0; i < NT; i++)
+        hoff[i] = plane + ((uint32_t)(r0 + tt0 + min(xr + 16 * i, nt - 1)) * I + 8 * (xc & 7)) * 2;
+    f32x4 acc[4][NT];
+#pragma unroll
+    for (int t = 0; t < 4; t++)
+#pragma unroll
+        for (int tt = 0; tt < NT; tt++) acc[t][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x2 q[3][4];
+    uint32_t sc[3][4];
+    auto load_w = [&](auto P, int st) {
+        constexpr int p = decltype(P)::value;
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+            q[p][t] = ld8(b.code, b.coff, t * 8 * I + 32 * st);
+            sc[p][t] = ld1(b.scale, b.soff, t * (I / 2) + 2 * st);
+        }
+    };
+    {
+        u32x4 hv[NT];
+#pragma unroll
+        for (int i = 0; i < NT; i++) hv[i] = ld16(b.h, hoff[i], 0);
+        load_w(Stage<0>(), 0);
+        load_w(Stage<1>(), min(1, nsteps - 1));
+#pragma unroll
+        for (int i = 0; i < NT; i++) hs[0][lds_slot(xr + 16 * i, xc)] = hv[i];
+    }
+    __syncthreads();
+
+    k_loop3(nsteps, [&](auto P, int st) {
+        constexpr int p = decltype(P)::value;
+        const int buf = st & 1;
+        u32x4 hv[NT];
+        const int stn = min(st + 1, nsteps - 1);
+#pragma unroll
+        for (int i = 0; i < NT; i++) hv[i] = ld16(b.h, hoff[i], 128 * stn);
+        load_w(Stage<(p + 2) % 3>(), min(st + 2, nsteps - 1));
+        __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the step's MFMAs
+        float scale[4];
+#pragma unroll
+        for (int t = 0; t < 4; t++) scale[t] = e8m0_to_f32(sc[p][t]);
+#pragma unroll
+        for (int s = 0; s < 2; s++) {
+            bf16x8 A[4], Bh[NT], Bl[NT];
+#pragma unroll
+            for (int tt = 0; tt < NT; tt++) {
+                Bh[tt] = as_bf16x8(hs[buf][lds_slot(16 * tt + li, 2 * g + s)]);
+                Bl[tt] = as_bf16x8(hs[buf][lds_slot(16 * tt + li, 8 + 2 * g + s)]);
+            }
+#pragma unroll
+            for (int t = 0; t < 4; t++) A[t] = fp4x8_to_bf16(q[p][t][s], scale[t]);
+#pragma unroll
+            for (int tt = 0; tt < NT; tt++)
+#pragma unroll
+                for (int t = 0; t < 4; t++) {
+                    acc[t][tt] = mfma16(A[t], Bh[tt], acc[t][tt]);
+                    acc[t][tt] = mfma16(A[t], Bl[tt], acc[t][tt]);
+                }
+        }
+#pragma unroll
+        for (int i = 0; i < NT; i++) hs[buf ^ 1][lds_slot(xr + 16 * i, xc)] = hv[i];
+        __syncthreads();
+    });
+
+    // lane (g, li) holds H-rows m0 + 16 t + 4 g + 0..3 of token 16 tt + li
+#pragma unroll
+    for (int tt = 0; tt < NT; tt++) {
+        const int j = 16 * tt + li;
+        if (j >= nt) continue;
+        const int slot = a.perm[r0 + tt0 + j];
+        const float p = a.w[slot];
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+            const f32x4 v = acc[t][tt];
+            *(float4 *)(a.ybuf + (size_t)slot * H + b.m0 + 16 * t + 4 * g) =
+                float4{p * v[0], p * v[1], p * v[2], p * v[3]};
+        }
+    }
+}
+
+__global__ __launch_bounds__(256, 2) void k_down_mm(const ExpertFwdArgs a)
+{
+    __shared__ MmTile hs[2];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
+    const int H = a.H, I = a.I;
+    int ai, rb;
+    xcd_split(H / 256, ai, rb);
+    if (ai >= *a.n_active) return;
+    const int e = a.active[ai];
+    const int r0 = a.offsets[e], ntok = a.offsets[e + 1] - r0;
+    DnBlock b;
+    b.code = buf_rsrc(a.down.codes + (size_t)e * H * (I / 2), H * (I / 2));
+    b.scale = buf_rsrc(a.down.scales + (size_t)e * H * (I / 32), H * (I / 32));
+    b.h = buf_rsrc(a.h_hi, (uint32_t)((size_t)a.T * a.k * I * 4));
+    b.m0 = rb * 256 + wv * 64;
+    b.coff = (uint32_t)(b.m0 + li) * (I / 2) + 8 * g;
+    b.soff = (uint32_t)(b.m0 + li) * (I / 32) + (g >> 1);
+    for (int tt0 = 0; tt0 < ntok; tt0 += kMmTok) {
+        const int nt = min(kMmTok, ntok - tt0);
+        switch ((nt + 15) / 16) {
+        case 1: down_pass<1>(a, b, hs, r0, tt0, nt); break;
+        case 2: down_pass<2>(a, b, hs, r0, tt0, nt); break;
+        case 3: down_pass<3>(a, b, hs, r0, tt0, nt); break;
+        case 4: down_pass<4>(a, b, hs, r0, tt0, nt); break;
+        case 5: down_pass<5>(a, b, hs, r0, tt0, nt); break;
+        default: down_pass<6>(a, b, hs, r0, tt0, nt); break;
+        }
+    }
+}
+
+// Buffer offsets are 32-bit: x, the two h planes and one expert matrix must each span
+// less than 4 GiB, and h_lo must follow h_hi directly.
+bool mm_supported(const ExpertFwdArgs &a)
+{
+    const size_t S = (size_t)a.T * a.k, lim = (size_t)1 << 32;
+    return a.wfmt == FMT_MXFP4 && a.xt == DT_BF16 && a.H % 512 == 0 && a.I % 512 == 0 &&
+           (size_t)a.T * a.H * 2 < lim && S * a.I * 4 < lim && (size_t)a.H * a.I < lim &&
+           a.h_lo == a.h_hi + S * a.I;
+}
+
+hipError_t launch_gateup_mm(const ExpertFwdArgs &a, hipStream_t s)
+{
+    const int maxU = min(a.E, a.T * a.k);
+    ProfScope ps(a.prof, PK_GATEUP, s);
+    hipLaunchKernelGGL(k_gateup_mm, dim3(xcd_grid(maxU, a.I / 128)), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_down_mm(const ExpertFwdArgs &a, hipStream_t s)
+{
+    const int maxU = min(a.E, a.T * a.k);
+    ProfScope ps(a.prof, PK_DOWN, s);
+    hipLaunchKernelGGL(k_down_mm, dim3(xcd_grid(maxU, a.H / 256)), dim3(256), 0, s, a);
+    return hipGetLastError();
+}
+
+}  // namespace moe

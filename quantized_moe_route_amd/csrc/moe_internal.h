@@ -125,6 +125,15 @@ inline void set_lds_staging(ExpertFwdArgs &a)
 hipError_t launch_router(const RouteArgs &a, hipStream_t s);
 hipError_t launch_group(const GroupArgs &a, hipStream_t s);
 hipError_t launch_expert_forward(const ExpertFwdArgs &a, hipStream_t s);
+hipError_t launch_gateup_only(const ExpertFwdArgs &a, hipStream_t s);
+
+// Grouped-GEMM forward kernels for experts holding many tokens (expert_mm.hip):
+// MXFP4 weights, bf16 tokens, H and I multiples of 512.
+bool mm_supported(const ExpertFwdArgs &a);
+hipError_t launch_gateup_mm(const ExpertFwdArgs &a, hipStream_t s);
+hipError_t launch_down_mm(const ExpertFwdArgs &a, hipStream_t s);
+// taken when the experts average at least 8 tokens each
+inline bool use_mm(const ExpertFwdArgs &a) { return (size_t)a.T * a.k >= (size_t)8 * a.E && mm_supported(a); }
 hipError_t launch_expert_backward(const ExpertBwdArgs &a, hipStream_t s);
 
 // number of I-column tiles whose partial <a, h> sums the backward stores per row

@@ -86,6 +86,23 @@ def test_many_tokens_per_expert_uses_multi_tile_path():
     run_small(host_case(w), name="multi-tile")
 
 
+def test_grouped_gemm_path_multi_pass():
+    # T * k >= 8 E with MXFP4, bf16 x and H, I multiples of 512 selects the grouped-GEMM
+    # kernels; ~100 tokens per expert puts some experts over one 96-token pass
+    w = syn.shrink(TINY, T=400, H=512, I=1024, E=8, k=2, x_dtype="bf16", x_key=15)
+    run_small(host_case(w), name="mm-multi-pass")
+
+
+def test_grouped_gemm_path_skew_and_idle_experts():
+    # one expert takes every token (four passes, the last a single partial tile); with
+    # E = 24 and k = 3 most experts see one or two tiles and some none
+    w = syn.shrink(TINY, T=300, H=1024, I=512, E=24, k=3, x_dtype="bf16", bias_sd=0.0, x_key=16)
+    c = host_case(w)
+    c.bias = np.zeros(w.E, np.float32)
+    c.bias[5] = 100.0
+    run_small(c, name="mm-skew")
+
+
 def test_rvq3_small():
     w = syn.shrink(syn.WORKLOADS["rvq16"], T=24, H=256, I=128, E=12, k=3, with_dy=True)
     run_small(host_case(w), name="rvq3-small")

@@ -350,6 +350,14 @@ hipError_t launch_expert_backward(const ExpertBwdArgs &a0, hipStream_t s)
         if (err != hipSuccess) return err;
         a.gu = a.gu_scratch;
     }
+    if ((size_t)a.T * a.k >= (size_t)8 * a.E && bwd_mm_supported(a)) {
+        hipError_t err = launch_bwd_down_mm(a, s);
+        if (err == hipSuccess) err = launch_bwd_gateup_mm(a, s);
+        if (err != hipSuccess) return err;
+        ProfScope ps(a.prof, PK_BWD_FINAL, s);
+        hipLaunchKernelGGL(k_bwd_final, dim3(a.T), dim3(256), 0, s, a);
+        return hipGetLastError();
+    }
     if (a.wfmt == FMT_MXFP4)
         return a.dyt == DT_BF16 ? bwd_ntt<FMT_MXFP4, DT_BF16>(a, s) : bwd_ntt<FMT_MXFP4, DT_F32>(a, s);
     return a.dyt == DT_BF16 ? bwd_ntt<FMT_RVQ3, DT_BF16>(a, s) : bwd_ntt<FMT_RVQ3, DT_F32>(a, s);

@@ -136,6 +136,12 @@ hipError_t launch_down_mm(const ExpertFwdArgs &a, hipStream_t s);
 inline bool use_mm(const ExpertFwdArgs &a) { return (size_t)a.T * a.k >= (size_t)8 * a.E && mm_supported(a); }
 hipError_t launch_expert_backward(const ExpertBwdArgs &a, hipStream_t s);
 
+// Grouped-GEMM backward kernels (expert_bwd_mm.hip): MXFP4, bf16 dy, H and I multiples
+// of 512.  They keep dg/du as bf16 hi + lo planes [2][S][2I] in the dgdu buffer.
+bool bwd_mm_supported(const ExpertBwdArgs &a);
+hipError_t launch_bwd_down_mm(const ExpertBwdArgs &a, hipStream_t s);
+hipError_t launch_bwd_gateup_mm(const ExpertBwdArgs &a, hipStream_t s);
+
 // number of I-column tiles whose partial <a, h> sums the backward stores per row
 __host__ __device__ inline int dp_tiles(int I) { return (I + 63) / 64; }
 

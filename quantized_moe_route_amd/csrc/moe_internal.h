@@ -132,6 +132,10 @@ hipError_t launch_gateup_only(const ExpertFwdArgs &a, hipStream_t s);
 bool mm_supported(const ExpertFwdArgs &a);
 hipError_t launch_gateup_mm(const ExpertFwdArgs &a, hipStream_t s);
 hipError_t launch_down_mm(const ExpertFwdArgs &a, hipStream_t s);
+// Few-token MXFP4 kernels (expert_dec.hip) for T <= nl_x, nl_h with bf16 tokens.
+bool dec_supported(const ExpertFwdArgs &a);
+hipError_t launch_gateup_dec(const ExpertFwdArgs &a, hipStream_t s);
+hipError_t launch_down_dec(const ExpertFwdArgs &a, hipStream_t s);
 // taken when the experts average at least 8 tokens each
 inline bool use_mm(const ExpertFwdArgs &a) { return (size_t)a.T * a.k >= (size_t)8 * a.E && mm_supported(a); }
 hipError_t launch_expert_backward(const ExpertBwdArgs &a, hipStream_t s);

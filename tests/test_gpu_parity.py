@@ -103,6 +103,18 @@ def test_grouped_gemm_path_skew_and_idle_experts():
     run_small(c, name="mm-skew")
 
 
+def test_decode_path_few_tokens():
+    # MXFP4, bf16 x, T <= 16 with every token row fitting the LDS stage selects the
+    # few-token stream kernels; I = 768 is not a multiple of the 4-step unroll
+    w = syn.shrink(TINY, T=6, H=512, I=768, E=12, k=3, x_dtype="bf16", x_key=17)
+    run_small(host_case(w), name="dec-few")
+
+
+def test_decode_path_single_token_full_tile():
+    w = syn.shrink(TINY, T=1, H=1024, I=256, E=16, k=8, x_dtype="bf16", x_key=18)
+    run_small(host_case(w), name="dec-T1")
+
+
 def test_rvq3_small():
     w = syn.shrink(syn.WORKLOADS["rvq16"], T=24, H=256, I=128, E=12, k=3, with_dy=True)
     run_small(host_case(w), name="rvq3-small")

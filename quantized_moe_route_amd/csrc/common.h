@@ -180,4 +180,23 @@ __device__ __forceinline__ float wave_max_f32(float v)
 
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
+// Exclusive scan of one int per thread over the block (scr: blockDim.x ints of LDS);
+// returns the total in *total.  Called by every thread of the block.
+__device__ __forceinline__ int block_exclusive_scan(int v, int *scr, int *total)
+{
+    const int tid = threadIdx.x, n = blockDim.x;
+    scr[tid] = v;
+    __syncthreads();
+    for (int off = 1; off < n; off <<= 1) {
+        const int add = tid >= off ? scr[tid - off] : 0;
+        __syncthreads();
+        scr[tid] += add;
+        __syncthreads();
+    }
+    const int incl = scr[tid];
+    *total = scr[n - 1];
+    __syncthreads();
+    return incl - v;
+}
+
 }  // namespace moe

@@ -22,24 +22,6 @@
 
 namespace moe {
 
-// Exclusive scan of one int per thread over the block; returns the total in *total.
-__device__ int block_exclusive_scan(int v, int *scr, int *total)
-{
-    const int tid = threadIdx.x, n = blockDim.x;
-    scr[tid] = v;
-    __syncthreads();
-    for (int off = 1; off < n; off <<= 1) {
-        const int add = tid >= off ? scr[tid - off] : 0;
-        __syncthreads();
-        scr[tid] += add;
-        __syncthreads();
-    }
-    const int incl = scr[tid];
-    *total = scr[n - 1];
-    __syncthreads();
-    return incl - v;
-}
-
 __global__ __launch_bounds__(1024) void k_group(const int32_t *__restrict__ ids, int T, int k, int E,
                                                 int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
                                                 int32_t *__restrict__ perm, int32_t *__restrict__ inv,

@@ -248,7 +248,6 @@ moe_status moe_route(moe_layer *L, const void *x, int32_t xt, int32_t T, const m
     a.w = r->w;
     a.refined = nullptr;
     a.prof = &L->prof;
-    if ((st = device_status(moe::launch_router(a, s), "router")) != MOE_OK) return st;
     moe::GroupArgs gq{};
     gq.ids = r->ids;
     gq.T = T;
@@ -261,6 +260,8 @@ moe_status moe_route(moe_layer *L, const void *x, int32_t xt, int32_t T, const m
     gq.active = r->active;
     gq.n_active = r->n_active;
     gq.prof = &L->prof;
+    if (moe::route_small_ok(a)) return device_status(moe::launch_route_small(a, gq, s), "route");
+    if ((st = device_status(moe::launch_router(a, s), "router")) != MOE_OK) return st;
     return device_status(moe::launch_group(gq, s), "group");
 }
 

@@ -123,6 +123,9 @@ inline void set_lds_staging(ExpertFwdArgs &a)
 }
 
 hipError_t launch_router(const RouteArgs &a, hipStream_t s);
+// Small batches (route_small_ok): router logits, then top-k and grouping in one launch.
+bool route_small_ok(const RouteArgs &a);
+hipError_t launch_route_small(const RouteArgs &a, const GroupArgs &g, hipStream_t s);
 hipError_t launch_group(const GroupArgs &a, hipStream_t s);
 hipError_t launch_expert_forward(const ExpertFwdArgs &a, hipStream_t s);
 hipError_t launch_gateup_only(const ExpertFwdArgs &a, hipStream_t s);

@@ -53,13 +53,11 @@ __device__ __forceinline__ float bound_of(float eb, float l)
 constexpr int kGemvMaxT = 64;
 constexpr int kGemvMaxH = 4096;
 
-__global__ __launch_bounds__(256) void k_router_gemv(const void *__restrict__ x, int xt, const float *__restrict__ wr,
-                                                     const float *__restrict__ bias, int T, int H, int E,
-                                                     float *__restrict__ logits, float *__restrict__ beta)
+__device__ __forceinline__ void gemv_wave(const void *__restrict__ x, int xt, const float *__restrict__ wr,
+                                          const float *__restrict__ bias, int T, int H, int E, int e, int t0,
+                                          float *__restrict__ logits, float *__restrict__ beta)
 {
     const int lane = threadIdx.x & 63;
-    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (e >= E) return;
     const float *wrow = wr + (size_t)e * H;
     float4 w4[16];
 #pragma unroll
@@ -68,50 +66,56 @@ __global__ __launch_bounds__(256) void k_router_gemv(const void *__restrict__ x,
         w4[m] = i < H ? *(const float4 *)(wrow + i) : float4{0.f, 0.f, 0.f, 0.f};
     }
     const float b = bias ? bias[e] : 0.f;
-    {
-        const int t0 = blockIdx.y * 8;
-        float acc[8], eb[8];
+    float acc[8], eb[8];
 #pragma unroll
-        for (int u = 0; u < 8; u++) acc[u] = eb[u] = 0.f;
+    for (int u = 0; u < 8; u++) acc[u] = eb[u] = 0.f;
 #pragma unroll
-        for (int u = 0; u < 8; u++) {
-            const int t = t0 + u;
-            if (t >= T) break;
-            float xv[16][4];
+    for (int u = 0; u < 8; u++) {
+        const int t = t0 + u;
+        if (t >= T) break;
+        float xv[16][4];
 #pragma unroll
-            for (int m = 0; m < 16; m++) {
-                const int i = lane * 4 + 256 * m;
-                if (i < H)
-                    load_x4(x, xt, (size_t)t * H + i, xv[m][0], xv[m][1], xv[m][2], xv[m][3]);
-                else
-                    xv[m][0] = xv[m][1] = xv[m][2] = xv[m][3] = 0.f;
-            }
-#pragma unroll
-            for (int m = 0; m < 16; m++) {
-                if (lane * 4 + 256 * m >= H) break;
-                acc[u] = fmaf(xv[m][0], w4[m].x, acc[u]);
-                eb[u] += fabsf(acc[u]);
-                acc[u] = fmaf(xv[m][1], w4[m].y, acc[u]);
-                eb[u] += fabsf(acc[u]);
-                acc[u] = fmaf(xv[m][2], w4[m].z, acc[u]);
-                eb[u] += fabsf(acc[u]);
-                acc[u] = fmaf(xv[m][3], w4[m].w, acc[u]);
-                eb[u] += fabsf(acc[u]);
-            }
+        for (int m = 0; m < 16; m++) {
+            const int i = lane * 4 + 256 * m;
+            if (i < H)
+                load_x4(x, xt, (size_t)t * H + i, xv[m][0], xv[m][1], xv[m][2], xv[m][3]);
+            else
+                xv[m][0] = xv[m][1] = xv[m][2] = xv[m][3] = 0.f;
         }
 #pragma unroll
-        for (int u = 0; u < 8; u++) {
-            const int t = t0 + u;
-            if (t >= T) break;
-            float ebt = eb[u];
-            const float sv = wave_sum_f32_eb(acc[u], ebt);
-            const float l = sv + b;
-            if (lane == 0) {
-                logits[(size_t)t * E + e] = l;
-                beta[(size_t)t * E + e] = bound_of(ebt, l);
-            }
+        for (int m = 0; m < 16; m++) {
+            if (lane * 4 + 256 * m >= H) break;
+            acc[u] = fmaf(xv[m][0], w4[m].x, acc[u]);
+            eb[u] += fabsf(acc[u]);
+            acc[u] = fmaf(xv[m][1], w4[m].y, acc[u]);
+            eb[u] += fabsf(acc[u]);
+            acc[u] = fmaf(xv[m][2], w4[m].z, acc[u]);
+            eb[u] += fabsf(acc[u]);
+            acc[u] = fmaf(xv[m][3], w4[m].w, acc[u]);
+            eb[u] += fabsf(acc[u]);
         }
     }
+#pragma unroll
+    for (int u = 0; u < 8; u++) {
+        const int t = t0 + u;
+        if (t >= T) break;
+        float ebt = eb[u];
+        const float sv = wave_sum_f32_eb(acc[u], ebt);
+        const float l = sv + b;
+        if (lane == 0) {
+            logits[(size_t)t * E + e] = l;
+            beta[(size_t)t * E + e] = bound_of(ebt, l);
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void k_router_gemv(const void *__restrict__ x, int xt, const float *__restrict__ wr,
+                                                     const float *__restrict__ bias, int T, int H, int E,
+                                                     float *__restrict__ logits, float *__restrict__ beta)
+{
+    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (e >= E) return;
+    gemv_wave(x, xt, wr, bias, T, H, E, e, blockIdx.y * 8, logits, beta);
 }
 
 // Tiled form for many tokens: block = 32 tokens x 64 experts, K chunks of 32
@@ -289,25 +293,22 @@ __device__ __forceinline__ void sort64(float &v, int &id)
     }
 }
 
-// One wave per token.  PL = logits held per lane (E <= 64 PL).
+// Top-k + softmax of token t by one wave.  PL = logits held per lane (E <= 64 PL);
+// cv/ci: 64-entry LDS scratch of this wave.  No block-level barrier inside, so waves
+// of one block may run it for different numbers of tokens.
 // Selection: every member of the top-k ranks at or above the k-th largest of the 64
 // per-lane maxima (those k maxima are k distinct elements), so only elements at or
 // above that threshold are candidates; when there are at most 64 of them (always,
 // short of massive ties) they are compacted and sorted in one pass.  Otherwise k
 // rounds of a wave-wide arg-best decide.
 template <int PL>
-__global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, const float *__restrict__ beta,
-                                              const void *__restrict__ x, int xt, const float *__restrict__ wr,
-                                              const float *__restrict__ bias, int T, int H, int E, int k,
-                                              int32_t *__restrict__ ids, float *__restrict__ wts,
-                                              int32_t *__restrict__ refined)
+__device__ __forceinline__ void topk_one(int t, const float *__restrict__ logits, const float *__restrict__ beta,
+                                         const void *__restrict__ x, int xt, const float *__restrict__ wr,
+                                         const float *__restrict__ bias, int H, int E, int k,
+                                         int32_t *__restrict__ ids, float *__restrict__ wts,
+                                         int32_t *__restrict__ refined, float *cv, int *ci)
 {
-    __shared__ float cvs[4][64];
-    __shared__ int cis[4][64];
-    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    const int t_raw = blockIdx.x * 4 + wv;
-    const bool live = t_raw < T;
-    const int t = live ? t_raw : T - 1;  // dead waves shadow the last token until the block barrier
+    const int lane = threadIdx.x & 63;
     const float NEG = -__builtin_huge_valf();
     const int BIG = 0x7FFFFFFF;
     float l[PL], b[PL];
@@ -342,15 +343,16 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, 
         pos[q] = ncand + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
         ncand += __popcll(m);
         if (c && pos[q] < 64) {
-            cvs[wv][pos[q]] = l[q];
-            cis[wv][pos[q]] = e;
+            cv[pos[q]] = l[q];
+            ci[pos[q]] = e;
         }
     }
-    __syncthreads();
-    if (!live) return;
+    // LDS accesses of one wave complete in order; the fence keeps the compiler from
+    // moving the reads above the writes
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     if (ncand <= 64) {
-        float v = lane < ncand ? cvs[wv][lane] : NEG;
-        int id = lane < ncand ? cis[wv][lane] : BIG;
+        float v = lane < ncand ? cv[lane] : NEG;
+        int id = lane < ncand ? ci[lane] : BIG;
         sort64(v, id);
         rank_id = id;
         const float kv = readlane_f32(v, k - 1);
@@ -441,6 +443,118 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, 
         ids[(size_t)t * k + lane] = my_id;
         wts[(size_t)t * k + lane] = ex / den;
     }
+}
+
+
+template <int PL>
+__global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, const float *__restrict__ beta,
+                                              const void *__restrict__ x, int xt, const float *__restrict__ wr,
+                                              const float *__restrict__ bias, int T, int H, int E, int k,
+                                              int32_t *__restrict__ ids, float *__restrict__ wts,
+                                              int32_t *__restrict__ refined)
+{
+    __shared__ float cvs[4][64];
+    __shared__ int cis[4][64];
+    const int wv = threadIdx.x >> 6;
+    const int t = blockIdx.x * 4 + wv;
+    if (t >= T) return;
+    topk_one<PL>(t, logits, beta, x, xt, wr, bias, H, E, k, ids, wts, refined, cvs[wv], cis[wv]);
+}
+
+// Small batches (T <= 16, T k <= 256): top-k of every token and the grouping of the
+// T k slots in one single-block launch (the logits come from k_router_gemv, whose
+// kernel boundary makes them visible).  Wave w ranks tokens w, w + 4, ...; then the
+// block groups the slots: counts by LDS atomics, offsets and the active list by block
+// scans, and each slot's place from the number of earlier slots routed to the same
+// expert, i.e. slots ordered by (expert, token).
+constexpr int kSmallT = 16;
+constexpr int kSmallS = 256;
+constexpr int kSmallE = 2048;
+
+template <int PL>
+__global__ __launch_bounds__(256) void k_topk_group(const RouteArgs a, const GroupArgs gq)
+{
+    __shared__ float cvs[4][64];
+    __shared__ int cis[4][64];
+    __shared__ int cnt[kSmallE];
+    __shared__ int sids[kSmallS];
+    __shared__ int scr[256];
+    const int tid = threadIdx.x, wv = tid >> 6;
+    for (int t = wv; t < a.T; t += 4)
+        topk_one<PL>(t, a.logits, a.beta, a.x, a.xt, a.wr, a.bias, a.H, a.E, a.k, a.ids, a.w, a.refined, cvs[wv],
+                     cis[wv]);
+    __syncthreads();
+
+    const int S = a.T * a.k, E = a.E;
+    for (int i = tid; i < E; i += 256) cnt[i] = 0;
+    if (tid < S) sids[tid] = a.ids[tid];
+    __syncthreads();
+    if (tid < S) atomicAdd(&cnt[sids[tid]], 1);
+    __syncthreads();
+    const int per = (E + 255) / 256;
+    const int ea = min(E, tid * per), eb = min(E, ea + per);
+    int my = 0, myact = 0;
+    for (int q = ea; q < eb; q++) {
+        my += cnt[q];
+        myact += cnt[q] > 0;
+    }
+    int total, atot;
+    const int base = block_exclusive_scan(my, scr, &total);
+    const int abase = block_exclusive_scan(myact, scr, &atot);
+    int run = base, arun = abase;
+    for (int q = ea; q < eb; q++) {
+        const int c = cnt[q];
+        gq.counts[q] = c;
+        gq.offsets[q] = run;
+        if (c > 0) gq.active[arun++] = q;
+        cnt[q] = run;  // from here on: first grouped row of expert q
+        run += c;
+    }
+    if (tid == 0) {
+        gq.offsets[E] = total;
+        *gq.n_active = atot;
+    }
+    __syncthreads();
+    if (tid < S) {
+        const int q = sids[tid];
+        int rank = 0;
+        for (int s2 = 0; s2 < tid; s2++) rank += sids[s2] == q;
+        const int pos = cnt[q] + rank;
+        gq.perm[pos] = tid;
+        gq.inv[tid] = pos;
+    }
+}
+
+bool route_small_ok(const RouteArgs &a)
+{
+    return a.T <= kSmallT && a.T * a.k <= kSmallS && a.E <= kSmallE && a.H <= kGemvMaxH;
+}
+
+template <int PL>
+static hipError_t launch_small_pl(const RouteArgs &a, const GroupArgs &g, hipStream_t s)
+{
+    {
+        ProfScope ps(a.prof, PK_ROUTER_LOGITS, s);
+        hipLaunchKernelGGL(k_router_gemv, dim3((a.E + 3) / 4, (a.T + 7) / 8), dim3(256), 0, s, a.x, a.xt, a.wr,
+                           a.bias, a.T, a.H, a.E, a.logits, a.beta);
+    }
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    ProfScope ps(a.prof, PK_ROUTER_TOPK, s);
+    hipLaunchKernelGGL(k_topk_group<PL>, dim3(1), dim3(256), 0, s, a, g);
+    return hipGetLastError();
+}
+
+hipError_t launch_route_small(const RouteArgs &a, const GroupArgs &g, hipStream_t s)
+{
+    const int pl = (a.E + 63) / 64;
+    if (pl <= 1) return launch_small_pl<1>(a, g, s);
+    if (pl <= 2) return launch_small_pl<2>(a, g, s);
+    if (pl <= 4) return launch_small_pl<4>(a, g, s);
+    if (pl <= 8) return launch_small_pl<8>(a, g, s);
+    if (pl <= 14) return launch_small_pl<14>(a, g, s);
+    if (pl <= 16) return launch_small_pl<16>(a, g, s);
+    return launch_small_pl<32>(a, g, s);
 }
 
 template <int PL>

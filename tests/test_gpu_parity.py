@@ -153,6 +153,20 @@ def test_near_ties_one_ulp_apart():
     run_small(c, name="near-ties")
 
 
+def test_small_batch_fused_routing_ties():
+    """T <= 16 routes through the single-launch router (logits, top-k and grouping in one
+    kernel); exact duplicate router rows and one-ulp near-ties must resolve there as
+    they do in the separate kernels."""
+    w = syn.shrink(TINY, T=12, E=16, k=4, x_key=19)
+    c = host_case(w)
+    c.wr[9] = c.wr[2]
+    c.wr[12] = c.wr[2]
+    c.wr[3] = c.wr[6]
+    c.wr[11] = c.wr[6]
+    c.wr[11, 40] = np.nextafter(c.wr[6, 40], np.float32(np.inf))
+    run_small(c, name="fused-ties")
+
+
 def test_zero_input_and_signed_zero_logits():
     w = syn.shrink(TINY, T=4, x_key=14)
     c = host_case(w)

@@ -133,11 +133,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 {
     extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
+    // The weight prefetch needs only e: the active-list entry is read together with the
+    // list length (entries past it are stale but name a valid expert) and the first code
+    // loads go out before the block learns whether it has work.
     const int ai = blockIdx.y;
-    if (ai >= *a.n_active) return;
-    const int e = a.active[ai];
+    const int nact = *a.n_active;
+    const int e = min(max(a.active[ai], 0), a.E - 1);
     const int H = a.H, I = a.I;
-    const int r0 = a.offsets[e], ntok = a.offsets[e + 1] - r0;
     const int row0 = blockIdx.x * 64 + wv * 16;
     const int nsteps = H / 256, spr = H / 32;
     const size_t eoc = (size_t)e * I * (H / 2), eos = (size_t)e * I * spr;
@@ -155,6 +157,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     TileScales tg, tu;
     get_scales(tg, buf_rsrc(a.gate.scales + eos, I * spr), (uint32_t)row0 * spr, lane);
     get_scales(tu, buf_rsrc(a.up.scales + eos, I * spr), (uint32_t)row0 * spr, lane);
+    if (ai >= nact) return;
+    const int r0 = a.offsets[e], ntok = a.offsets[e + 1] - r0;
     // token rows to LDS while the first weight bytes are in flight
     __shared__ uint32_t xrow[16];
     if (threadIdx.x < ntok) xrow[threadIdx.x] = (uint32_t)(a.perm[r0 + threadIdx.x] / a.k);
@@ -204,10 +208,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     extern __shared__ __attribute__((aligned(16))) uint16_t hs[];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
     const int ai = blockIdx.y;
-    if (ai >= *a.n_active) return;
-    const int e = a.active[ai];
+    const int nact = *a.n_active;
+    const int e = min(max(a.active[ai], 0), a.E - 1);  // as in k_gateup_dec
     const int H = a.H, I = a.I;
-    const int r0 = a.offsets[e], ntok = a.offsets[e + 1] - r0;
     const int m0 = blockIdx.x * 128 + wv * 32;
     const int nsteps = I / 256, spr = I / 32;
     const __amdgpu_buffer_rsrc_t cd = buf_rsrc(a.down.codes + (size_t)e * H * (I / 2), H * (I / 2));
@@ -223,6 +226,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     TileScales t0, t1;
     get_scales(t0, sd, (uint32_t)m0 * spr, lane);
     get_scales(t1, sd, (uint32_t)(m0 + 16) * spr, lane);
+    if (ai >= nact) return;
+    const int r0 = a.offsets[e], ntok = a.offsets[e + 1] - r0;
     const size_t lo = (size_t)a.nl_h * (I + 8);
     stage_rows(hs, a.h_hi, [&](int r) { return (size_t)(r0 + r) * I; }, ntok, I);
     stage_rows(hs + lo, a.h_lo, [&](int r) { return (size_t)(r0 + r) * I; }, ntok, I);

@@ -30,9 +30,18 @@ def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-def kernel_source_hash() -> str:
+# The kernel whose roofline each workload reports, and the sources that define it.
+ROOF_KERNEL = {
+    "decode1": ("k_gateup_dec", ("expert_dec.hip",)),
+    "decode64": ("k_gateup", ("expert_fwd.hip", "expert_frag.h")),
+    "rvq16": ("k_gateup", ("expert_fwd.hip", "expert_frag.h")),
+    "train4096": ("k_gateup_mm", ("expert_mm.hip",)),
+}
+
+
+def kernel_source_hash(workload: str) -> str:
     h = hashlib.sha256()
-    for f in ("expert_fwd.hip", "expert_frag.h", "common.h"):
+    for f in ROOF_KERNEL[workload][1] + ("common.h", "moe_internal.h"):
         h.update(open(os.path.join(ROOT, "quantized_moe_route_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -44,7 +53,7 @@ def traffic_record(workload: str):
     if not os.path.exists(p):
         return None
     rec = json.load(open(p))
-    if rec.get("kernel_source_hash") != kernel_source_hash():
+    if rec.get("kernel_source_hash") != kernel_source_hash(workload):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -77,11 +86,19 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel family (stderr)")
+    ap.add_argument("--calib-copy-mb", type=int, default=0,
+                    help="after the run, copy a buffer of this many MB three times (a kernel of known "
+                         "traffic for calibrating hardware byte counters)")
+    ap.add_argument("--print-hash", action="store_true", help="print the roofline kernel's source hash and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (every box here has one GPU, "
               "and the layer's multi-GPU sharding is a design, not a build)", file=sys.stderr)
         sys.exit(2)
+
+    if args.print_hash:
+        print(kernel_source_hash(args.workload))
+        return
 
     import numpy as np
     import torch
@@ -155,13 +172,12 @@ def main():
     gu_ms, gu_n = L.prof_read(C.PROF_GATEUP)
     L.prof_enable([])
     assert gu_n == args.steps
-
     steps_U = [U[(args.warmup + i) % POOL] for i in range(args.steps)]
     S = w.T * w.k
     x_bytes = w.T * w.H * 2
     gu_alg = [u * gateup_bytes_per_expert + x_bytes + S * w.I * 4 for u in steps_U]
     gu_bytes = sum(gu_alg) / len(gu_alg)
-    gu_avg_s = gu_ms / gu_n / 1e3
+    gu_avg_s = gu_ms / gu_n / 1e3  # events stamped at the kernel's own start and end
     achieved = gu_bytes / gu_avg_s / 1e9
     step_bytes = [u * expert_bytes + wr.nbytes + x_bytes + w.T * w.H * 4 for u in steps_U]
     step_s = ms / 1e3 / args.steps
@@ -173,7 +189,7 @@ def main():
     detail = {"step_hbm_GBps": sum(step_bytes) / len(step_bytes) / step_s / 1e9,
               "step_alg_bytes": sum(step_bytes) / len(step_bytes),
               "active_experts_mean": sum(steps_U) / len(steps_U),
-              "gateup_us": gu_avg_s * 1e6}
+              "gateup_us": gu_avg_s * 1e6, "gateup_alg_bytes": gu_bytes}
     if args.breakdown:
         fams = list(range(len(C.PROF_NAMES)))
         L.prof_enable(fams, max_launches=args.steps)
@@ -210,13 +226,22 @@ def main():
                                + ("forward + input gradient (route + group + experts + combine + dX)" if train
                                   else "forward (route + group + experts + combine)"),
                    "T": w.T, "H": w.H, "I": w.I, "E": w.E, "k": w.k, "weights": w.wfmt},
-        "roofline": {"bound": "hbm", "kernel": "k_gateup (dequant + gate/up + SwiGLU)", "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": ROOF_KERNEL[w.name][0] + " (dequant + gate/up + SwiGLU)",
+                     "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                      "traffic": traffic},
         "cpu_baseline": base,
         "detail": detail,
     }
     print(json.dumps(out), flush=True)
+    if args.calib_copy_mb:
+        n = args.calib_copy_mb * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copies: 3 x {n * 4} bytes read and written")
     L.close()
 
 

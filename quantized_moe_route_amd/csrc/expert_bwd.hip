@@ -301,15 +301,15 @@ static hipError_t bwd_launch(const ExpertBwdArgs &a, hipStream_t s)
     const int maxU = min(a.E, a.T * a.k);
     {
         ProfScope ps(a.prof, PK_BWD_DOWN, s);
-        hipLaunchKernelGGL((k_bwd_down<WFMT, DYT, NTT>), dim3((a.I + 63) / 64, maxU), dim3(256), 0, s, a);
+        ps.launch((k_bwd_down<WFMT, DYT, NTT>), dim3((a.I + 63) / 64, maxU), dim3(256), 0, a);
     }
     {
         ProfScope ps(a.prof, PK_BWD_GATEUP, s);
-        hipLaunchKernelGGL((k_bwd_gateup<WFMT, NTT>), dim3((a.H + 63) / 64, maxU), dim3(256), 0, s, a);
+        ps.launch((k_bwd_gateup<WFMT, NTT>), dim3((a.H + 63) / 64, maxU), dim3(256), 0, a);
     }
     {
         ProfScope ps(a.prof, PK_BWD_FINAL, s);
-        hipLaunchKernelGGL(k_bwd_final, dim3(a.T), dim3(256), 0, s, a);
+        ps.launch(k_bwd_final, dim3(a.T), dim3(256), 0, a);
     }
     return hipGetLastError();
 }
@@ -355,7 +355,7 @@ hipError_t launch_expert_backward(const ExpertBwdArgs &a0, hipStream_t s)
         if (err == hipSuccess) err = launch_bwd_gateup_mm(a, s);
         if (err != hipSuccess) return err;
         ProfScope ps(a.prof, PK_BWD_FINAL, s);
-        hipLaunchKernelGGL(k_bwd_final, dim3(a.T), dim3(256), 0, s, a);
+        ps.launch(k_bwd_final, dim3(a.T), dim3(256), 0, a);
         return hipGetLastError();
     }
     if (a.wfmt == FMT_MXFP4)

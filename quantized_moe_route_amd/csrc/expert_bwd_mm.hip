@@ -361,7 +361,7 @@ hipError_t launch_bwd_down_mm(const ExpertBwdArgs &a, hipStream_t s)
 {
     const int maxU = min(a.E, a.T * a.k);
     ProfScope ps(a.prof, PK_BWD_DOWN, s);
-    hipLaunchKernelGGL(k_bwdt_mm<false>, dim3(xcd_grid(maxU, a.I / 256)), dim3(256), 0, s, a);
+    ps.launch(k_bwdt_mm<false>, dim3(xcd_grid(maxU, a.I / 256)), dim3(256), 0, a);
     return hipGetLastError();
 }
 
@@ -369,7 +369,7 @@ hipError_t launch_bwd_gateup_mm(const ExpertBwdArgs &a, hipStream_t s)
 {
     const int maxU = min(a.E, a.T * a.k);
     ProfScope ps(a.prof, PK_BWD_GATEUP, s);
-    hipLaunchKernelGGL(k_bwdt_mm<true>, dim3(xcd_grid(maxU, a.H / 256)), dim3(256), 0, s, a);
+    ps.launch(k_bwdt_mm<true>, dim3(xcd_grid(maxU, a.H / 256)), dim3(256), 0, a);
     return hipGetLastError();
 }
 

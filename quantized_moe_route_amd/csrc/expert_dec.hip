@@ -279,7 +279,7 @@ hipError_t launch_gateup_dec(const ExpertFwdArgs &a, hipStream_t s)
     const int maxU = min(a.E, a.T * a.k);
     ProfScope ps(a.prof, PK_GATEUP, s);
     const size_t lds = (size_t)a.nl_x * (a.H + 8) * 2 + 16384;
-    hipLaunchKernelGGL(k_gateup_dec, dim3(a.I / 64, maxU), dim3(256), lds, s, a);
+    ps.launch(k_gateup_dec, dim3(a.I / 64, maxU), dim3(256), lds, a);
     return hipGetLastError();
 }
 
@@ -288,7 +288,7 @@ hipError_t launch_down_dec(const ExpertFwdArgs &a, hipStream_t s)
     const int maxU = min(a.E, a.T * a.k);
     ProfScope ps(a.prof, PK_DOWN, s);
     const size_t lds = (size_t)a.nl_h * (a.I + 8) * 2 * 2 + 16384;
-    hipLaunchKernelGGL(k_down_dec, dim3(a.H / 128, maxU), dim3(256), lds, s, a);
+    ps.launch(k_down_dec, dim3(a.H / 128, maxU), dim3(256), lds, a);
     return hipGetLastError();
 }
 

@@ -330,7 +330,7 @@ static hipError_t launch_combine(const ExpertFwdArgs &a, hipStream_t s)
     const size_t nb = (n4 + 255) / 256;
     const int blocks = (int)(nb < 4096 ? nb : 4096);
     ProfScope ps(a.prof, PK_COMBINE, s);
-    hipLaunchKernelGGL(k_combine, dim3(blocks), dim3(256), 0, s, a.ybuf, a.T, a.H, a.k, a.y);
+    ps.launch(k_combine, dim3(blocks), dim3(256), 0, a.ybuf, a.T, a.H, a.k, a.y);
     return hipGetLastError();
 }
 
@@ -341,14 +341,13 @@ static hipError_t fwd_launch(const ExpertFwdArgs &a, hipStream_t s)
     {
         ProfScope ps(a.prof, PK_GATEUP, s);
         const size_t lds = NTT == 1 && XT == DT_BF16 ? (size_t)a.nl_x * (a.H + 8) * 2 : 0;
-        hipLaunchKernelGGL((k_gateup<WFMT, XT, NTT, FULLG>), dim3((a.I + 63) / 64, maxU), dim3(256), lds, s, a);
+        ps.launch((k_gateup<WFMT, XT, NTT, FULLG>), dim3((a.I + 63) / 64, maxU), dim3(256), lds, a);
     }
     {
         ProfScope ps(a.prof, PK_DOWN, s);
         constexpr int RT = NTT == 1 ? 2 : 1;
         const size_t lds = NTT == 1 ? (size_t)a.nl_h * (a.I + 8) * 2 * 2 : 0;
-        hipLaunchKernelGGL((k_down<WFMT, NTT, RT, FULLD>), dim3((a.H + 64 * RT - 1) / (64 * RT), maxU), dim3(256), lds,
-                           s, a);
+        ps.launch((k_down<WFMT, NTT, RT, FULLD>), dim3((a.H + 64 * RT - 1) / (64 * RT), maxU), dim3(256), lds, a);
     }
     return launch_combine(a, s);
 }
@@ -379,14 +378,14 @@ static hipError_t gateup_only(const ExpertFwdArgs &a, hipStream_t s)
     const bool f = a.H % 256 == 0 && a.H <= 32 * kMaxScaleRow;
     if (a.T <= 64) {
         if (f)
-            hipLaunchKernelGGL((k_gateup<WFMT, XT, 1, true>), grid, dim3(256), lds, s, a);
+            ps.launch((k_gateup<WFMT, XT, 1, true>), grid, dim3(256), lds, a);
         else
-            hipLaunchKernelGGL((k_gateup<WFMT, XT, 1, false>), grid, dim3(256), lds, s, a);
+            ps.launch((k_gateup<WFMT, XT, 1, false>), grid, dim3(256), lds, a);
     } else {
         if (f)
-            hipLaunchKernelGGL((k_gateup<WFMT, XT, 4, true>), grid, dim3(256), 0, s, a);
+            ps.launch((k_gateup<WFMT, XT, 4, true>), grid, dim3(256), 0, a);
         else
-            hipLaunchKernelGGL((k_gateup<WFMT, XT, 4, false>), grid, dim3(256), 0, s, a);
+            ps.launch((k_gateup<WFMT, XT, 4, false>), grid, dim3(256), 0, a);
     }
     return hipGetLastError();
 }

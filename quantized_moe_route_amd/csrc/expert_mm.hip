@@ -388,7 +388,7 @@ hipError_t launch_gateup_mm(const ExpertFwdArgs &a, hipStream_t s)
 {
     const int maxU = min(a.E, a.T * a.k);
     ProfScope ps(a.prof, PK_GATEUP, s);
-    hipLaunchKernelGGL(k_gateup_mm, dim3(xcd_grid(maxU, a.I / 128)), dim3(256), 0, s, a);
+    ps.launch(k_gateup_mm, dim3(xcd_grid(maxU, a.I / 128)), dim3(256), 0, a);
     return hipGetLastError();
 }
 
@@ -396,7 +396,7 @@ hipError_t launch_down_mm(const ExpertFwdArgs &a, hipStream_t s)
 {
     const int maxU = min(a.E, a.T * a.k);
     ProfScope ps(a.prof, PK_DOWN, s);
-    hipLaunchKernelGGL(k_down_mm, dim3(xcd_grid(maxU, a.H / 256)), dim3(256), 0, s, a);
+    ps.launch(k_down_mm, dim3(xcd_grid(maxU, a.H / 256)), dim3(256), 0, a);
     return hipGetLastError();
 }
 

@@ -101,7 +101,7 @@ hipError_t launch_group(const GroupArgs &a, hipStream_t s)
     while (nw > 1 && (size_t)nw * a.E * 4 + (size_t)nw * 64 * 4 > 64 * 1024) nw >>= 1;
     const size_t lds = ((size_t)nw * a.E + (size_t)nw * 64) * sizeof(int);
     ProfScope ps(a.prof, PK_GROUP, s);
-    hipLaunchKernelGGL(k_group, dim3(1), dim3(nw * 64), lds, s, a.ids, a.T, a.k, a.E, a.counts, a.offsets, a.perm,
+    ps.launch(k_group, dim3(1), dim3(nw * 64), lds, a.ids, a.T, a.k, a.E, a.counts, a.offsets, a.perm,
                        a.inv, a.active, a.n_active);
     return hipGetLastError();
 }

@@ -2,6 +2,7 @@
 // kernel files.  Host-side only declarations; no torch, no oracle.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -20,18 +21,25 @@ struct Prof {
     int n[PK_N] = {};
 };
 
+// Launches one kernel; when timing of its family is on, through hipExtLaunchKernelGGL
+// with the family's next event pair, which the runtime stamps at the kernel's start and
+// end (not at the queue position before and after it).
 class ProfScope {
   public:
     ProfScope(Prof *p, int kid, hipStream_t s) : p_(p), kid_(kid), s_(s)
     {
         on_ = p_ && ((p_->mask >> kid_) & 1u) && p_->n[kid_] < p_->cap;
-        if (on_) hipEventRecord(p_->ev[kid_][2 * p_->n[kid_]], s_);
     }
-    ~ProfScope()
+    template <typename K, typename... Args>
+    void launch(K kernel, dim3 grid, dim3 block, size_t shmem, Args... args)
     {
         if (on_) {
-            hipEventRecord(p_->ev[kid_][2 * p_->n[kid_] + 1], s_);
-            p_->n[kid_]++;
+            const int n = p_->n[kid_]++;
+            hipExtLaunchKernelGGL(kernel, grid, block, (uint32_t)shmem, s_, p_->ev[kid_][2 * n],
+                                  p_->ev[kid_][2 * n + 1], 0, args...);
+            on_ = false;
+        } else {
+            hipLaunchKernelGGL(kernel, grid, block, shmem, s_, args...);
         }
     }
 

@@ -535,13 +535,13 @@ static hipError_t launch_small_pl(const RouteArgs &a, const GroupArgs &g, hipStr
 {
     {
         ProfScope ps(a.prof, PK_ROUTER_LOGITS, s);
-        hipLaunchKernelGGL(k_router_gemv, dim3((a.E + 3) / 4, (a.T + 7) / 8), dim3(256), 0, s, a.x, a.xt, a.wr,
+        ps.launch(k_router_gemv, dim3((a.E + 3) / 4, (a.T + 7) / 8), dim3(256), 0, a.x, a.xt, a.wr,
                            a.bias, a.T, a.H, a.E, a.logits, a.beta);
     }
     const hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     ProfScope ps(a.prof, PK_ROUTER_TOPK, s);
-    hipLaunchKernelGGL(k_topk_group<PL>, dim3(1), dim3(256), 0, s, a, g);
+    ps.launch(k_topk_group<PL>, dim3(1), dim3(256), 0, a, g);
     return hipGetLastError();
 }
 
@@ -562,7 +562,7 @@ static hipError_t launch_topk_pl(const RouteArgs &a, hipStream_t s)
 {
     const dim3 grid((a.T + 3) / 4);
     ProfScope ps(a.prof, PK_ROUTER_TOPK, s);
-    hipLaunchKernelGGL(k_topk<PL>, grid, dim3(256), 0, s, a.logits, a.beta, a.x, a.xt, a.wr, a.bias, a.T, a.H, a.E,
+    ps.launch(k_topk<PL>, grid, dim3(256), 0, a.logits, a.beta, a.x, a.xt, a.wr, a.bias, a.T, a.H, a.E,
                        a.k, a.ids, a.w, a.refined);
     return hipGetLastError();
 }
@@ -572,10 +572,10 @@ hipError_t launch_router(const RouteArgs &a, hipStream_t s)
     {
     ProfScope ps(a.prof, PK_ROUTER_LOGITS, s);
     if (a.T <= kGemvMaxT && a.H <= kGemvMaxH) {
-        hipLaunchKernelGGL(k_router_gemv, dim3((a.E + 3) / 4, (a.T + 7) / 8), dim3(256), 0, s, a.x, a.xt, a.wr, a.bias,
+        ps.launch(k_router_gemv, dim3((a.E + 3) / 4, (a.T + 7) / 8), dim3(256), 0, a.x, a.xt, a.wr, a.bias,
                            a.T, a.H, a.E, a.logits, a.beta);
     } else {
-        hipLaunchKernelGGL(k_router_tiled, dim3((a.E + 63) / 64, (a.T + 31) / 32), dim3(256), 0, s, a.x, a.xt, a.wr,
+        ps.launch(k_router_tiled, dim3((a.E + 63) / 64, (a.T + 31) / 32), dim3(256), 0, a.x, a.xt, a.wr,
                            a.bias, a.T, a.H, a.E, a.logits, a.beta);
     }
     }

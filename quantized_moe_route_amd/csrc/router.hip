@@ -47,44 +47,46 @@ __device__ __forceinline__ float bound_of(float eb, float l)
     return 1.001f * kU * eb + kU * fabsf(l) + 1e-30f;
 }
 
-// GEMV form for up to 64 tokens and H <= 4096: one wave per (expert, group of 8
-// tokens) holds the router row in registers (lane l owns inputs 4l + 256 m); per token
-// an FMA chain per lane, then the wave reduction.  Grid: (ceil(E/4), ceil(T/8)).
+// GEMV form for up to 64 tokens and H <= 4096: one block per (expert, group of 8
+// tokens).  Thread tid owns the float4 chunks tid + 256 m of the router row (held in
+// registers) and runs one FMA chain per token over them; the 64 lanes of a wave are
+// summed by the DPP tree and the four wave sums in a fixed order.  Grid: (E, ceil(T/8)).
 constexpr int kGemvMaxT = 64;
 constexpr int kGemvMaxH = 4096;
 
-__device__ __forceinline__ void gemv_wave(const void *__restrict__ x, int xt, const float *__restrict__ wr,
-                                          const float *__restrict__ bias, int T, int H, int E, int e, int t0,
-                                          float *__restrict__ logits, float *__restrict__ beta)
+__global__ __launch_bounds__(256) void k_router_gemv(const void *__restrict__ x, int xt, const float *__restrict__ wr,
+                                                     const float *__restrict__ bias, int T, int H, int E,
+                                                     float *__restrict__ logits, float *__restrict__ beta)
 {
-    const int lane = threadIdx.x & 63;
+    __shared__ float ps[4][8], pe[4][8];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int e = blockIdx.x, t0 = blockIdx.y * 8;
+    const int n4 = H / 4;
     const float *wrow = wr + (size_t)e * H;
-    float4 w4[16];
+    float4 w4[4];
 #pragma unroll
-    for (int m = 0; m < 16; m++) {
-        const int i = lane * 4 + 256 * m;
-        w4[m] = i < H ? *(const float4 *)(wrow + i) : float4{0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < 4; m++) {
+        const int c = tid + 256 * m;
+        w4[m] = c < n4 ? *(const float4 *)(wrow + 4 * c) : float4{0.f, 0.f, 0.f, 0.f};
     }
-    const float b = bias ? bias[e] : 0.f;
     float acc[8], eb[8];
 #pragma unroll
-    for (int u = 0; u < 8; u++) acc[u] = eb[u] = 0.f;
-#pragma unroll
     for (int u = 0; u < 8; u++) {
+        acc[u] = eb[u] = 0.f;
         const int t = t0 + u;
-        if (t >= T) break;
-        float xv[16][4];
+        if (t >= T) continue;
+        float xv[4][4];
 #pragma unroll
-        for (int m = 0; m < 16; m++) {
-            const int i = lane * 4 + 256 * m;
-            if (i < H)
-                load_x4(x, xt, (size_t)t * H + i, xv[m][0], xv[m][1], xv[m][2], xv[m][3]);
+        for (int m = 0; m < 4; m++) {
+            const int c = tid + 256 * m;
+            if (c < n4)
+                load_x4(x, xt, (size_t)t * H + 4 * c, xv[m][0], xv[m][1], xv[m][2], xv[m][3]);
             else
                 xv[m][0] = xv[m][1] = xv[m][2] = xv[m][3] = 0.f;
         }
 #pragma unroll
-        for (int m = 0; m < 16; m++) {
-            if (lane * 4 + 256 * m >= H) break;
+        for (int m = 0; m < 4; m++) {
+            if (tid + 256 * m >= n4) break;
             acc[u] = fmaf(xv[m][0], w4[m].x, acc[u]);
             eb[u] += fabsf(acc[u]);
             acc[u] = fmaf(xv[m][1], w4[m].y, acc[u]);
@@ -97,25 +99,23 @@ __device__ __forceinline__ void gemv_wave(const void *__restrict__ x, int xt, co
     }
 #pragma unroll
     for (int u = 0; u < 8; u++) {
-        const int t = t0 + u;
-        if (t >= T) break;
+        if (t0 + u >= T) break;
         float ebt = eb[u];
         const float sv = wave_sum_f32_eb(acc[u], ebt);
-        const float l = sv + b;
         if (lane == 0) {
-            logits[(size_t)t * E + e] = l;
-            beta[(size_t)t * E + e] = bound_of(ebt, l);
+            ps[wv][u] = sv;
+            pe[wv][u] = ebt;
         }
     }
-}
-
-__global__ __launch_bounds__(256) void k_router_gemv(const void *__restrict__ x, int xt, const float *__restrict__ wr,
-                                                     const float *__restrict__ bias, int T, int H, int E,
-                                                     float *__restrict__ logits, float *__restrict__ beta)
-{
-    const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (e >= E) return;
-    gemv_wave(x, xt, wr, bias, T, H, E, e, blockIdx.y * 8, logits, beta);
+    __syncthreads();
+    if (tid < 8 && t0 + tid < T) {
+        const int u = tid, t = t0 + u;
+        const float s01 = ps[0][u] + ps[1][u], s23 = ps[2][u] + ps[3][u], r = s01 + s23;
+        const float ebt = ((pe[0][u] + pe[1][u]) + fabsf(s01)) + ((pe[2][u] + pe[3][u]) + fabsf(s23)) + fabsf(r);
+        const float l = r + (bias ? bias[e] : 0.f);
+        logits[(size_t)t * E + e] = l;
+        beta[(size_t)t * E + e] = bound_of(ebt, l);
+    }
 }
 
 // Tiled form for many tokens: block = 32 tokens x 64 experts, K chunks of 32
@@ -273,6 +273,22 @@ __device__ __forceinline__ void wave_argbest(V &v, int &id)
 // One wave per token.  PL = logits held per lane (E <= 64 PL).
 // Bitonic sort of one (value, id) pair per lane across the wave into rank order
 // (lane 0 = first under (value desc, id asc)).
+// Value of lane ^ stride.  Within a 16-lane row: xor 1 and xor 2 are quad permutations,
+// xor 4 is the quad reversal of the 8-lane mirror, xor 8 the 8-lane mirror of the 16-lane
+// mirror; xor 16 and xor 32 cross rows and go through ds_bpermute.
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v, int stride)
+{
+    switch (stride) {
+    case 1: return dpp_u32<kDppXor1>(v);
+    case 2: return dpp_u32<kDppXor2>(v);
+    case 4: return dpp_u32<0x1B>(dpp_u32<kDppHalfMirror>(v));
+    case 8: return dpp_u32<kDppHalfMirror>(dpp_u32<kDppMirror>(v));
+    default: return (uint32_t)__shfl_xor((int)v, stride, 64);
+    }
+}
+
+// Bitonic sort of one (value, id) pair per lane across the wave into rank order
+// (lane 0 = first under (value desc, id asc)).
 __device__ __forceinline__ void sort64(float &v, int &id)
 {
     const int lane = threadIdx.x & 63;
@@ -281,8 +297,8 @@ __device__ __forceinline__ void sort64(float &v, int &id)
         const bool desc = (lane & size) == 0 || size == 64;
 #pragma unroll
         for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            const float pv = __shfl_xor(v, stride, 64);
-            const int pi = __shfl_xor(id, stride, 64);
+            const float pv = __uint_as_float(lane_xor(__float_as_uint(v), stride));
+            const int pi = (int)lane_xor((uint32_t)id, stride);
             const bool lower = (lane & stride) == 0;
             const bool pa = ahead(pv, pi, v, id);
             if (lower == desc ? pa : !pa) {
@@ -306,7 +322,7 @@ __device__ __forceinline__ void topk_one(int t, const float *__restrict__ logits
                                          const void *__restrict__ x, int xt, const float *__restrict__ wr,
                                          const float *__restrict__ bias, int H, int E, int k,
                                          int32_t *__restrict__ ids, float *__restrict__ wts,
-                                         int32_t *__restrict__ refined, float *cv, int *ci)
+                                         int32_t *__restrict__ refined, float *cv, int *ci, float *cb)
 {
     const int lane = threadIdx.x & 63;
     const float NEG = -__builtin_huge_valf();
@@ -344,19 +360,26 @@ __device__ __forceinline__ void topk_one(int t, const float *__restrict__ logits
         ncand += __popcll(m);
         if (c && pos[q] < 64) {
             cv[pos[q]] = l[q];
-            ci[pos[q]] = e;
+            ci[pos[q]] = (e << 6) | pos[q];  // the expert id orders ties; the LDS slot rides along
+            cb[pos[q]] = b[q];
         }
     }
     // LDS accesses of one wave complete in order; the fence keeps the compiler from
     // moving the reads above the writes
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    if (ncand <= 64) {
+    // lane j < k: fp32 logit and error bound of the expert ranked j-th (when have_rank)
+    float rank_l = NEG, rank_b = 0.f;
+    const bool have_rank = ncand <= 64;
+    if (have_rank) {
         float v = lane < ncand ? cv[lane] : NEG;
         int id = lane < ncand ? ci[lane] : BIG;
         sort64(v, id);
-        rank_id = id;
+        const bool real = id != BIG;
+        rank_id = real ? id >> 6 : BIG;
+        rank_l = v;
+        rank_b = real ? cb[id & 63] : 0.f;
         const float kv = readlane_f32(v, k - 1);
-        const int ki = __builtin_amdgcn_readlane(id, k - 1);
+        const int ki = __builtin_amdgcn_readlane(rank_id, k - 1);
 #pragma unroll
         for (int q = 0; q < PL; q++) {
             const int e = lane + 64 * q;
@@ -393,14 +416,20 @@ __device__ __forceinline__ void topk_one(int t, const float *__restrict__ logits
         ncand += __popcll(__ballot(c));
     }
     bool overlap = false;
-    const int next_id = __shfl(rank_id, (lane + 1) & 63, 64);
-    if (lane < k - 1) {
-        const int ea = rank_id, eb = next_id;
-        const float la = logits[(size_t)t * E + ea], lb = logits[(size_t)t * E + eb];
-        const float ba = beta[(size_t)t * E + ea], bb = beta[(size_t)t * E + eb];
-        overlap = la - ba <= lb + bb;
+    if (have_rank) {
+        const float nl = __shfl(rank_l, (lane + 1) & 63, 64), nb = __shfl(rank_b, (lane + 1) & 63, 64);
+        overlap = lane < k - 1 && rank_l - rank_b <= nl + nb;
+    } else {
+        const int next_id = __shfl(rank_id, (lane + 1) & 63, 64);
+        if (lane < k - 1) {
+            const int ea = rank_id, eb = next_id;
+            const float la = logits[(size_t)t * E + ea], lb = logits[(size_t)t * E + eb];
+            const float ba = beta[(size_t)t * E + ea], bb = beta[(size_t)t * E + eb];
+            overlap = la - ba <= lb + bb;
+        }
     }
     overlap = __ballot(overlap) != 0;
+    bool reranked = false;
     int my_id;
     if (ncand > k || overlap) {
         // 3. re-rank every candidate on fp64 logits
@@ -432,10 +461,11 @@ __device__ __forceinline__ void topk_one(int t, const float *__restrict__ logits
             if (lane == j) rank_id = bi;
         }
         if (lane == 0 && refined) atomicAdd(refined, 1);
+        reranked = true;
     }
     // 4. softmax over the selected fp32 logits, in rank order
     my_id = lane < k ? rank_id : 0;
-    const float lj = lane < k ? logits[(size_t)t * E + my_id] : NEG;
+    const float lj = lane >= k ? NEG : have_rank && !reranked ? rank_l : logits[(size_t)t * E + my_id];
     const float mx = wave_max_f32(lj);
     const float ex = lane < k ? __expf(lj - mx) : 0.f;
     const float den = wave_sum_f32(ex);
@@ -455,10 +485,11 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, 
 {
     __shared__ float cvs[4][64];
     __shared__ int cis[4][64];
+    __shared__ float cbs[4][64];
     const int wv = threadIdx.x >> 6;
     const int t = blockIdx.x * 4 + wv;
     if (t >= T) return;
-    topk_one<PL>(t, logits, beta, x, xt, wr, bias, H, E, k, ids, wts, refined, cvs[wv], cis[wv]);
+    topk_one<PL>(t, logits, beta, x, xt, wr, bias, H, E, k, ids, wts, refined, cvs[wv], cis[wv], cbs[wv]);
 }
 
 // Small batches (T <= 16, T k <= 256): top-k of every token and the grouping of the
@@ -476,13 +507,14 @@ __global__ __launch_bounds__(256) void k_topk_group(const RouteArgs a, const Gro
 {
     __shared__ float cvs[4][64];
     __shared__ int cis[4][64];
+    __shared__ float cbs[4][64];
     __shared__ int cnt[kSmallE];
     __shared__ int sids[kSmallS];
     __shared__ int scr[256];
     const int tid = threadIdx.x, wv = tid >> 6;
     for (int t = wv; t < a.T; t += 4)
         topk_one<PL>(t, a.logits, a.beta, a.x, a.xt, a.wr, a.bias, a.H, a.E, a.k, a.ids, a.w, a.refined, cvs[wv],
-                     cis[wv]);
+                     cis[wv], cbs[wv]);
     __syncthreads();
 
     const int S = a.T * a.k, E = a.E;
@@ -535,7 +567,7 @@ static hipError_t launch_small_pl(const RouteArgs &a, const GroupArgs &g, hipStr
 {
     {
         ProfScope ps(a.prof, PK_ROUTER_LOGITS, s);
-        ps.launch(k_router_gemv, dim3((a.E + 3) / 4, (a.T + 7) / 8), dim3(256), 0, a.x, a.xt, a.wr,
+        ps.launch(k_router_gemv, dim3(a.E, (a.T + 7) / 8), dim3(256), 0, a.x, a.xt, a.wr,
                            a.bias, a.T, a.H, a.E, a.logits, a.beta);
     }
     const hipError_t err = hipGetLastError();
@@ -572,7 +604,7 @@ hipError_t launch_router(const RouteArgs &a, hipStream_t s)
     {
     ProfScope ps(a.prof, PK_ROUTER_LOGITS, s);
     if (a.T <= kGemvMaxT && a.H <= kGemvMaxH) {
-        ps.launch(k_router_gemv, dim3((a.E + 3) / 4, (a.T + 7) / 8), dim3(256), 0, a.x, a.xt, a.wr, a.bias,
+        ps.launch(k_router_gemv, dim3(a.E, (a.T + 7) / 8), dim3(256), 0, a.x, a.xt, a.wr, a.bias,
                            a.T, a.H, a.E, a.logits, a.beta);
     } else {
         ps.launch(k_router_tiled, dim3((a.E + 63) / 64, (a.T + 31) / 32), dim3(256), 0, a.x, a.xt, a.wr,

@@ -309,6 +309,24 @@ __device__ __forceinline__ void sort64(float &v, int &id)
     }
 }
 
+// Ascending bitonic sort of one 32-bit key per lane across the wave.
+__device__ __forceinline__ uint32_t sort64_asc(uint32_t v)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int size = 2; size <= 64; size <<= 1) {
+        const bool asc = (lane & size) == 0 || size == 64;
+#pragma unroll
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            const uint32_t pv = lane_xor(v, stride);
+            const bool lower = (lane & stride) == 0;
+            v = lower == asc ? min(v, pv) : max(v, pv);
+        }
+    }
+    return v;
+}
+
+
 // Top-k + softmax of token t by one wave.  PL = logits held per lane (E <= 64 PL);
 // cv/ci: 64-entry LDS scratch of this wave.  No block-level barrier inside, so waves
 // of one block may run it for different numbers of tokens.
@@ -322,7 +340,8 @@ __device__ __forceinline__ void topk_one(int t, const float *__restrict__ logits
                                          const void *__restrict__ x, int xt, const float *__restrict__ wr,
                                          const float *__restrict__ bias, int H, int E, int k,
                                          int32_t *__restrict__ ids, float *__restrict__ wts,
-                                         int32_t *__restrict__ refined, float *cv, int *ci, float *cb)
+                                         int32_t *__restrict__ refined, float *cv, int *ci, float *cb,
+                                         int *lds_ids = nullptr)
 {
     const int lane = threadIdx.x & 63;
     const float NEG = -__builtin_huge_valf();
@@ -472,6 +491,7 @@ __device__ __forceinline__ void topk_one(int t, const float *__restrict__ logits
     if (lane < k) {
         ids[(size_t)t * k + lane] = my_id;
         wts[(size_t)t * k + lane] = ex / den;
+        if (lds_ids) lds_ids[t * k + lane] = my_id;
     }
 }
 
@@ -511,15 +531,57 @@ __global__ __launch_bounds__(256) void k_topk_group(const RouteArgs a, const Gro
     __shared__ int cnt[kSmallE];
     __shared__ int sids[kSmallS];
     __shared__ int scr[256];
-    const int tid = threadIdx.x, wv = tid >> 6;
+    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
     for (int t = wv; t < a.T; t += 4)
         topk_one<PL>(t, a.logits, a.beta, a.x, a.xt, a.wr, a.bias, a.H, a.E, a.k, a.ids, a.w, a.refined, cvs[wv],
-                     cis[wv], cbs[wv]);
+                     cis[wv], cbs[wv], sids);
     __syncthreads();
 
     const int S = a.T * a.k, E = a.E;
+    if (S <= 64) {
+        // Up to 64 slots: one wave sorts the keys (expert << 10 | slot); rank p of the
+        // sorted order is the slot's grouped row.  Offsets and counts of every expert are
+        // then binary searches in the sorted expert list.
+        int *se = cnt;  // sorted experts
+        if (wv == 0) {
+            const uint32_t key = lane < S ? ((uint32_t)sids[lane] << 10) | (uint32_t)lane : 0xFFFFFFFFu;
+            const uint32_t sk = sort64_asc(key);
+            const int e = (int)(sk >> 10), slot = (int)(sk & 1023u);
+            const bool real = lane < S;
+            if (real) {
+                gq.perm[lane] = slot;
+                gq.inv[slot] = lane;
+                se[lane] = e;
+            }
+            const int prev = __shfl_up(e, 1, 64);
+            const bool first = real && (lane == 0 || prev != e);
+            const unsigned long long m = __ballot(first);
+            const int apos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            if (first) gq.active[apos] = e;
+            if (lane == 0) {
+                *gq.n_active = (int)__popcll(m);
+                gq.offsets[E] = S;
+            }
+        }
+        __syncthreads();
+        for (int q = tid; q < E; q += 256) {
+            int lo = 0, hi = S;  // first sorted entry >= q
+            while (lo < hi) {
+                const int mid = (lo + hi) >> 1;
+                if (se[mid] < q) lo = mid + 1; else hi = mid;
+            }
+            int lo2 = lo, hi2 = S;  // first sorted entry > q
+            while (lo2 < hi2) {
+                const int mid = (lo2 + hi2) >> 1;
+                if (se[mid] <= q) lo2 = mid + 1; else hi2 = mid;
+            }
+            gq.offsets[q] = lo;
+            gq.counts[q] = lo2 - lo;
+        }
+        return;
+    }
+
     for (int i = tid; i < E; i += 256) cnt[i] = 0;
-    if (tid < S) sids[tid] = a.ids[tid];
     __syncthreads();
     if (tid < S) atomicAdd(&cnt[sids[tid]], 1);
     __syncthreads();

@@ -201,8 +201,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     }
 }
 
-// down + routing weight.  Block = 4 waves x 2 tiles x 16 rows = 128 H-rows of one
+// down + routing weight.  Block = 4 waves x RT tiles x 16 rows = 64 RT H-rows of one
 // active expert; h (hi and lo planes) of its tokens (<= nl_h) staged in LDS.
+// PACK (at most 8 tokens): MFMA column 2j carries token j's h_hi and column 2j + 1 its
+// h_lo, so one MFMA per sub-step covers both planes and the two columns are added in the
+// epilogue; otherwise column j is token j and each plane takes its own MFMA.
+template <int RT, bool PACK>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_down_dec(const ExpertFwdArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint16_t hs[];
@@ -211,57 +215,78 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     const int nact = *a.n_active;
     const int e = min(max(a.active[ai], 0), a.E - 1);  // as in k_gateup_dec
     const int H = a.H, I = a.I;
-    const int m0 = blockIdx.x * 128 + wv * 32;
+    const int m0 = blockIdx.x * (64 * RT) + wv * (16 * RT);
     const int nsteps = I / 256, spr = I / 32;
     const __amdgpu_buffer_rsrc_t cd = buf_rsrc(a.down.codes + (size_t)e * H * (I / 2), H * (I / 2));
     const __amdgpu_buffer_rsrc_t sd = buf_rsrc(a.down.scales + (size_t)e * H * spr, H * spr);
-    const uint32_t coff0 = (uint32_t)(m0 + li) * (I / 2) + 32 * g, coff1 = coff0 + 16 * (I / 2);
-
-    Raw r0_[4], r1_[4];
+    uint32_t coff[RT];
 #pragma unroll
-    for (int s = 0; s < 3; s++) {
-        fetch(r0_[s], cd, coff0, min(s, nsteps - 1));
-        fetch(r1_[s], cd, coff1, min(s, nsteps - 1));
-    }
-    TileScales t0, t1;
-    get_scales(t0, sd, (uint32_t)m0 * spr, lane);
-    get_scales(t1, sd, (uint32_t)(m0 + 16) * spr, lane);
+    for (int t = 0; t < RT; t++) coff[t] = (uint32_t)(m0 + 16 * t + li) * (I / 2) + 32 * g;
+
+    Raw rr[4][RT];
+#pragma unroll
+    for (int s = 0; s < 3; s++)
+#pragma unroll
+        for (int t = 0; t < RT; t++) fetch(rr[s][t], cd, coff[t], min(s, nsteps - 1));
+    TileScales ts[RT];
+#pragma unroll
+    for (int t = 0; t < RT; t++) get_scales(ts[t], sd, (uint32_t)(m0 + 16 * t) * spr, lane);
     if (ai >= nact) return;
     const int r0 = a.offsets[e], ntok = a.offsets[e + 1] - r0;
     const size_t lo = (size_t)a.nl_h * (I + 8);
     stage_rows(hs, a.h_hi, [&](int r) { return (size_t)(r0 + r) * I; }, ntok, I);
     stage_rows(hs + lo, a.h_lo, [&](int r) { return (size_t)(r0 + r) * I; }, ntok, I);
-    uint8_t *sreg = (uint8_t *)(hs + 2 * lo) + 4096 * wv;
-    put_scales(sreg, t0, lane);
-    put_scales(sreg + 2048, t1, lane);
+    uint8_t *sreg = (uint8_t *)(hs + 2 * lo) + 2048 * RT * wv;
+#pragma unroll
+    for (int t = 0; t < RT; t++) put_scales(sreg + 2048 * t, ts[t], lane);
     __syncthreads();
 
-    const uint16_t *hl = hs + (size_t)min(li, ntok - 1) * (I + 8) + 64 * g;
-    const uint16_t *sl0 = (const uint16_t *)(sreg + li * spr + 2 * g);
-    const uint16_t *sl1 = (const uint16_t *)(sreg + 2048 + li * spr + 2 * g);
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    // B row of this lane: PACK -> plane li & 1 of token li >> 1, else token li (hi; lo at + lo)
+    const int tok = PACK ? min(li >> 1, ntok - 1) : min(li, ntok - 1);
+    const uint16_t *hl = hs + (PACK && (li & 1) ? lo : 0) + (size_t)tok * (I + 8) + 64 * g;
+    const uint16_t *sl = (const uint16_t *)(sreg + li * spr + 2 * g);
+    f32x4 acc[RT];
+#pragma unroll
+    for (int t = 0; t < RT; t++) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
     k_loop4(nsteps, [&](auto P, int st) {
         constexpr int p = decltype(P)::value;
         const int sn = min(st + 3, nsteps - 1);
-        fetch(r0_[(p + 3) % 4], cd, coff0, sn);
-        fetch(r1_[(p + 3) % 4], cd, coff1, sn);
+#pragma unroll
+        for (int t = 0; t < RT; t++) fetch(rr[(p + 3) % 4][t], cd, coff[t], sn);
         __builtin_amdgcn_sched_barrier(0);
-        const uint32_t s0 = sl0[4 * st], s1 = sl1[4 * st];
-        bf16x8 B[8];
+        bf16x8 B[8], Bl[8];
         lds_row8(B, hl + 256 * st);
-        mma_raw(acc0, r0_[p], s0, B);
-        mma_raw(acc1, r1_[p], s1, B);
-        lds_row8(B, hl + lo + 256 * st);
-        mma_raw(acc0, r0_[p], s0, B);
-        mma_raw(acc1, r1_[p], s1, B);
+        if constexpr (!PACK) lds_row8(Bl, hl + lo + 256 * st);
+#pragma unroll
+        for (int t = 0; t < RT; t++) {
+            const uint32_t sc = sl[1024 * t + 4 * st];
+            uint32_t d[32];
+            decode_fp4x32(rr[p][t].c0, e8m0_to_f32(sc & 0xFFu), d);
+            decode_fp4x32(rr[p][t].c1, e8m0_to_f32(sc >> 8), d + 16);
+#pragma unroll
+            for (int s = 0; s < 8; s++) {
+                const bf16x8 A = as_bf16x8(d[4 * s], d[4 * s + 1], d[4 * s + 2], d[4 * s + 3]);
+                acc[t] = mfma16(A, B[s], acc[t]);
+                if constexpr (!PACK) acc[t] = mfma16(A, Bl[s], acc[t]);
+            }
+        }
     });
 
-    if (li < ntok) {
-        const int slot = a.perm[r0 + li];
+    if constexpr (PACK) {
+        // column 2j + 1 (h_lo part) onto column 2j
+#pragma unroll
+        for (int t = 0; t < RT; t++)
+#pragma unroll
+            for (int r = 0; r < 4; r++) acc[t][r] += dpp_f32<kDppXor1>(acc[t][r]);
+    }
+    const int j = PACK ? li >> 1 : li;
+    if (j < ntok && (!PACK || (li & 1) == 0)) {
+        const int slot = a.perm[r0 + j];
         const float pw = a.w[slot];
         float *yb = a.ybuf + (size_t)slot * H + m0 + 4 * g;
-        *(float4 *)yb = float4{pw * acc0[0], pw * acc0[1], pw * acc0[2], pw * acc0[3]};
-        *(float4 *)(yb + 16) = float4{pw * acc1[0], pw * acc1[1], pw * acc1[2], pw * acc1[3]};
+#pragma unroll
+        for (int t = 0; t < RT; t++)
+            *(float4 *)(yb + 16 * t) = float4{pw * acc[t][0], pw * acc[t][1], pw * acc[t][2], pw * acc[t][3]};
     }
 }
 
@@ -285,10 +310,15 @@ hipError_t launch_gateup_dec(const ExpertFwdArgs &a, hipStream_t s)
 
 hipError_t launch_down_dec(const ExpertFwdArgs &a, hipStream_t s)
 {
+    constexpr int RT = 1;  // one 16-row tile per wave: 4x as many waves as H / 16 rows per expert
     const int maxU = min(a.E, a.T * a.k);
     ProfScope ps(a.prof, PK_DOWN, s);
-    const size_t lds = (size_t)a.nl_h * (a.I + 8) * 2 * 2 + 16384;
-    ps.launch(k_down_dec, dim3(a.H / 128, maxU), dim3(256), lds, a);
+    const size_t lds = (size_t)a.nl_h * (a.I + 8) * 2 * 2 + 4 * 2048 * RT;
+    const dim3 grid(a.H / (64 * RT), maxU);
+    if (a.T <= 8)
+        ps.launch(k_down_dec<RT, true>, grid, dim3(256), lds, a);
+    else
+        ps.launch(k_down_dec<RT, false>, grid, dim3(256), lds, a);
     return hipGetLastError();
 }
 

@@ -115,6 +115,12 @@ def test_decode_path_single_token_full_tile():
     run_small(host_case(w), name="dec-T1")
 
 
+def test_decode_path_unpacked_planes():
+    # 9..16 tokens: the few-token down kernel gives each plane of h its own MFMA
+    w = syn.shrink(TINY, T=12, H=512, I=512, E=8, k=2, x_dtype="bf16", x_key=20)
+    run_small(host_case(w), name="dec-unpacked")
+
+
 def test_rvq3_small():
     w = syn.shrink(syn.WORKLOADS["rvq16"], T=24, H=256, I=128, E=12, k=3, with_dy=True)
     run_small(host_case(w), name="rvq3-small")

@@ -395,6 +395,7 @@ hipError_t launch_gateup_only(const ExpertFwdArgs &a, hipStream_t s)
 {
     if (use_mm(a)) return launch_gateup_mm(a, s);
     if (dec_supported(a)) return launch_gateup_dec(a, s);
+    if (rvq_dec_supported(a)) return launch_gateup_rvq(a, s);
     if (a.wfmt == FMT_MXFP4)
         return a.xt == DT_BF16 ? gateup_only<FMT_MXFP4, DT_BF16>(a, s) : gateup_only<FMT_MXFP4, DT_F32>(a, s);
     return a.xt == DT_BF16 ? gateup_only<FMT_RVQ3, DT_BF16>(a, s) : gateup_only<FMT_RVQ3, DT_F32>(a, s);
@@ -411,6 +412,12 @@ hipError_t launch_expert_forward(const ExpertFwdArgs &a, hipStream_t s)
     if (dec_supported(a)) {
         hipError_t err = launch_gateup_dec(a, s);
         if (err == hipSuccess) err = launch_down_dec(a, s);
+        if (err == hipSuccess) err = launch_combine(a, s);
+        return err;
+    }
+    if (rvq_dec_supported(a)) {
+        hipError_t err = launch_gateup_rvq(a, s);
+        if (err == hipSuccess) err = launch_down_rvq(a, s);
         if (err == hipSuccess) err = launch_combine(a, s);
         return err;
     }

@@ -147,6 +147,10 @@ hipError_t launch_down_mm(const ExpertFwdArgs &a, hipStream_t s);
 bool dec_supported(const ExpertFwdArgs &a);
 hipError_t launch_gateup_dec(const ExpertFwdArgs &a, hipStream_t s);
 hipError_t launch_down_dec(const ExpertFwdArgs &a, hipStream_t s);
+// Few-token RVQ3 kernels (expert_rvq.hip): codeword gathers as fp16 MFMA operands.
+bool rvq_dec_supported(const ExpertFwdArgs &a);
+hipError_t launch_gateup_rvq(const ExpertFwdArgs &a, hipStream_t s);
+hipError_t launch_down_rvq(const ExpertFwdArgs &a, hipStream_t s);
 // taken when the experts average at least 8 tokens each
 inline bool use_mm(const ExpertFwdArgs &a) { return (size_t)a.T * a.k >= (size_t)8 * a.E && mm_supported(a); }
 hipError_t launch_expert_backward(const ExpertBwdArgs &a, hipStream_t s);

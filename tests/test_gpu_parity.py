@@ -126,6 +126,18 @@ def test_rvq3_small():
     run_small(host_case(w), name="rvq3-small")
 
 
+def test_rvq3_fp16_gather_path():
+    # bf16 x, H and I multiples of 256, T <= 64: codewords gathered as fp16 MFMA operands
+    w = syn.shrink(syn.WORKLOADS["rvq16"], T=10, H=512, I=768, E=12, k=3, with_dy=True, x_key=21)
+    run_small(host_case(w), name="rvq3-gather")
+
+
+def test_rvq3_fp16_gather_multi_pass():
+    # ~13 tokens per expert: four passes of up to 4 tokens, the weights re-read per pass
+    w = syn.shrink(syn.WORKLOADS["rvq16"], T=40, H=256, I=512, E=6, k=2, with_dy=True, x_key=22)
+    run_small(host_case(w), name="rvq3-gather-passes")
+
+
 def test_single_token_and_k1():
     w = syn.shrink(TINY, T=1, k=1, x_key=10)
     run_small(host_case(w), name="T1-k1")

@@ -512,13 +512,13 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, 
     topk_one<PL>(t, logits, beta, x, xt, wr, bias, H, E, k, ids, wts, refined, cvs[wv], cis[wv], cbs[wv]);
 }
 
-// Small batches (T <= 16, T k <= 256): top-k of every token and the grouping of the
+// Small batches (T <= 4, T k <= 256): top-k of every token and the grouping of the
 // T k slots in one single-block launch (the logits come from k_router_gemv, whose
-// kernel boundary makes them visible).  Wave w ranks tokens w, w + 4, ...; then the
+// kernel boundary makes them visible).  Wave w ranks token w; then the
 // block groups the slots: counts by LDS atomics, offsets and the active list by block
 // scans, and each slot's place from the number of earlier slots routed to the same
 // expert, i.e. slots ordered by (expert, token).
-constexpr int kSmallT = 16;
+constexpr int kSmallT = 4;  // one wave per token; more tokens run k_topk over several blocks
 constexpr int kSmallS = 256;
 constexpr int kSmallE = 2048;
 

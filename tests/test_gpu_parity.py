@@ -172,10 +172,9 @@ def test_near_ties_one_ulp_apart():
 
 
 def test_small_batch_fused_routing_ties():
-    """T <= 16 routes through the single-launch router (logits, top-k and grouping in one
-    kernel); exact duplicate router rows and one-ulp near-ties must resolve there as
-    they do in the separate kernels."""
-    w = syn.shrink(TINY, T=12, E=16, k=4, x_key=19)
+    """T <= 4 routes through the combined top-k + grouping kernel; exact duplicate router
+    rows and one-ulp near-ties must resolve there as they do in the separate kernels."""
+    w = syn.shrink(TINY, T=4, E=16, k=4, x_key=19)
     c = host_case(w)
     c.wr[9] = c.wr[2]
     c.wr[12] = c.wr[2]

@@ -270,222 +270,242 @@ __device__ __forceinline__ void wave_argbest(V &v, int &id)
     id = bi;
 }
 
-// One wave per token.  PL = logits held per lane (E <= 64 PL).
-// Bitonic sort of one (value, id) pair per lane across the wave into rank order
-// (lane 0 = first under (value desc, id asc)).
-// Value of lane ^ stride.  Within a 16-lane row: xor 1 and xor 2 are quad permutations,
-// xor 4 is the quad reversal of the 8-lane mirror, xor 8 the 8-lane mirror of the 16-lane
-// mirror; xor 16 and xor 32 cross rows and go through ds_bpermute.
-__device__ __forceinline__ uint32_t lane_xor(uint32_t v, int stride)
+// Sortable key of (logit, expert): under unsigned comparison a larger key ranks
+// first in the (value desc, id asc) order.  High word: the float's bits mapped
+// monotonically (-0 taken as +0, so equal values compare equal); low word: ~expert.
+// Key 0 lies below every real key and marks "no element".
+__device__ __forceinline__ uint64_t make_key(float v, int e)
 {
-    switch (stride) {
-    case 1: return dpp_u32<kDppXor1>(v);
-    case 2: return dpp_u32<kDppXor2>(v);
-    case 4: return dpp_u32<0x1B>(dpp_u32<kDppHalfMirror>(v));
-    case 8: return dpp_u32<kDppHalfMirror>(dpp_u32<kDppMirror>(v));
-    default: return (uint32_t)__shfl_xor((int)v, stride, 64);
-    }
+    uint32_t u = __float_as_uint(v + 0.0f);  // -0 + 0 = +0
+    u ^= (uint32_t)((int32_t)u >> 31) | 0x80000000u;
+    return ((uint64_t)u << 32) | (uint32_t)~(uint32_t)e;
 }
 
-// Bitonic sort of one (value, id) pair per lane across the wave into rank order
-// (lane 0 = first under (value desc, id asc)).
-__device__ __forceinline__ void sort64(float &v, int &id)
+__device__ __forceinline__ float key_logit(uint64_t k)
 {
-    const int lane = threadIdx.x & 63;
-#pragma unroll
-    for (int size = 2; size <= 64; size <<= 1) {
-        const bool desc = (lane & size) == 0 || size == 64;
-#pragma unroll
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            const float pv = __uint_as_float(lane_xor(__float_as_uint(v), stride));
-            const int pi = (int)lane_xor((uint32_t)id, stride);
-            const bool lower = (lane & stride) == 0;
-            const bool pa = ahead(pv, pi, v, id);
-            if (lower == desc ? pa : !pa) {
-                v = pv;
-                id = pi;
-            }
-        }
-    }
+    const uint32_t u = (uint32_t)(k >> 32);
+    return __uint_as_float((u & 0x80000000u) ? (u & 0x7FFFFFFFu) : ~u);
 }
 
-// Ascending bitonic sort of one 32-bit key per lane across the wave.
-__device__ __forceinline__ uint32_t sort64_asc(uint32_t v)
+__device__ __forceinline__ int key_expert(uint64_t k) { return (int)~(uint32_t)k; }
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int l)
 {
-    const int lane = threadIdx.x & 63;
+    const uint64_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, l);
+    const uint64_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), l);
+    return lo | (hi << 32);
+}
+
+// Wave-wide maximum of a 64-bit key; every lane gets it.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t v)
+{
 #pragma unroll
-    for (int size = 2; size <= 64; size <<= 1) {
-        const bool asc = (lane & size) == 0 || size == 64;
-#pragma unroll
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            const uint32_t pv = lane_xor(v, stride);
-            const bool lower = (lane & stride) == 0;
-            v = lower == asc ? min(v, pv) : max(v, pv);
-        }
+    for (int s = 1; s < 64; s <<= 1) {
+        const uint64_t lo = (uint32_t)__shfl_xor((int)(uint32_t)v, s, 64);
+        const uint64_t hi = (uint32_t)__shfl_xor((int)(uint32_t)(v >> 32), s, 64);
+        const uint64_t p = lo | (hi << 32);
+        v = p > v ? p : v;
     }
     return v;
 }
 
+// Number of the 64 keys s[0, 64) larger than `mine`.  The LDS reads are wave-uniform
+// (broadcasts) and all issued before the first comparison.
+__device__ __forceinline__ int count_above64(const uint64_t *s, uint64_t mine)
+{
+    u32x4 v[32];
+#pragma unroll
+    for (int i = 0; i < 32; i++) v[i] = ((const u32x4 *)s)[i];
+#pragma unroll
+    for (int i = 0; i < 32; i++) asm volatile("" : "+v"(v[i]));
+    int r = 0;
+#pragma unroll
+    for (int i = 0; i < 32; i++) {
+        const uint64_t a = v[i][0] | ((uint64_t)v[i][1] << 32), b = v[i][2] | ((uint64_t)v[i][3] << 32);
+        r += (int)(a > mine) + (int)(b > mine);
+    }
+    return r;
+}
 
-// Top-k + softmax of token t by one wave.  PL = logits held per lane (E <= 64 PL);
-// cv/ci: 64-entry LDS scratch of this wave.  No block-level barrier inside, so waves
-// of one block may run it for different numbers of tokens.
+template <int N>
+__device__ __forceinline__ uint64_t tree_max(const uint64_t *k)
+{
+    if constexpr (N == 1) {
+        return k[0];
+    } else {
+        const uint64_t a = tree_max<N / 2>(k), b = tree_max<N - N / 2>(k + N / 2);
+        return a > b ? a : b;
+    }
+}
+
+// Per-wave LDS scratch of the top-k.  Entries 64.. of ckey/cb/rkey/rb take the
+// writes of lanes that have nothing to store, so that no store needs a branch.
+struct TopkScratch {
+    uint64_t mkey[64];   // lane maxima
+    uint64_t ckey[128];  // candidates
+    uint64_t rkey[128];  // candidates in rank order
+    float cb[128];       // error bounds of the candidates
+    float rb[128];       // ... in rank order
+};
+
+// fp64 re-ranking of the candidate set `cand` (bit q: expert lane + 64 q) of token t;
+// returns, on lane j < k, the expert ranked j-th (other lanes: rank_id unchanged).
+// Called by a whole wave.
+template <int PL>
+__device__ __noinline__ int rerank_f64(int t, const void *__restrict__ x, int xt, const float *__restrict__ wr,
+                                       const float *__restrict__ bias, int H, int k, uint32_t cand, int rank_id)
+{
+    const int lane = threadIdx.x & 63;
+    double dkey[PL];
+#pragma unroll
+    for (int q = 0; q < PL; q++) {
+        dkey[q] = -__builtin_huge_val();
+        unsigned long long m = __ballot((cand >> q) & 1u);
+        while (m) {
+            const int owner = __ffsll((long long)m) - 1;
+            m &= m - 1;
+            const double v = logit_f64(x, xt, wr, bias, t, owner + 64 * q, H, lane);
+            if (lane == owner) dkey[q] = v != v ? -__builtin_huge_val() : v;
+        }
+    }
+    uint32_t taken = 0;
+    for (int j = 0; j < k; j++) {
+        double bv = -__builtin_huge_val();
+        int bi = 0x7FFFFFFF;
+#pragma unroll
+        for (int q = 0; q < PL; q++) {
+            const int e = lane + 64 * q;
+            if (((cand >> q) & 1u) && !((taken >> q) & 1u) && ahead(dkey[q], e, bv, bi)) { bv = dkey[q]; bi = e; }
+        }
+        wave_argbest(bv, bi);
+#pragma unroll
+        for (int q = 0; q < PL; q++)
+            if (lane + 64 * q == bi) taken |= 1u << q;
+        if (lane == j) rank_id = bi;
+    }
+    return rank_id;
+}
+
+// Top-k + softmax of token t by one wave.  PL = logits held per lane (E <= 64 PL).
+// No block-level barrier inside, so waves of one block may run it for different
+// numbers of tokens.
 // Selection: every member of the top-k ranks at or above the k-th largest of the 64
 // per-lane maxima (those k maxima are k distinct elements), so only elements at or
-// above that threshold are candidates; when there are at most 64 of them (always,
-// short of massive ties) they are compacted and sorted in one pass.  Otherwise k
-// rounds of a wave-wide arg-best decide.
+// above that threshold are candidates.  Ranks are counted, not sorted: each lane
+// holds one key and counts the keys above it, reading them from LDS as broadcasts,
+// first among the 64 lane maxima (the threshold is the one with k-1 above it), then
+// among the candidates when there are at most 64 of them (always, short of massive
+// ties); a candidate with r keys above it takes rank r.  Otherwise k rounds of a
+// wave-wide maximum decide.
 template <int PL>
 __device__ __forceinline__ void topk_one(int t, const float *__restrict__ logits, const float *__restrict__ beta,
                                          const void *__restrict__ x, int xt, const float *__restrict__ wr,
                                          const float *__restrict__ bias, int H, int E, int k,
                                          int32_t *__restrict__ ids, float *__restrict__ wts,
-                                         int32_t *__restrict__ refined, float *cv, int *ci, float *cb,
-                                         int *lds_ids = nullptr)
+                                         int32_t *__restrict__ refined, TopkScratch &sc, int *lds_ids = nullptr)
 {
     const int lane = threadIdx.x & 63;
     const float NEG = -__builtin_huge_valf();
-    const int BIG = 0x7FFFFFFF;
+    uint64_t key[PL];
     float l[PL], b[PL];
-    uint32_t sel = 0, cand = 0;  // bit q: logit q of this lane
-    int rank_id = 0;             // lane j < k: expert ranked j-th
+#pragma unroll
+    for (int q = 0; q < PL; q++) {
+        const int ec = min(lane + 64 * q, E - 1);  // clamped, so that every load is issued up front
+        l[q] = logits[(size_t)t * E + ec];
+        b[q] = beta[(size_t)t * E + ec];
+    }
+#pragma unroll
+    for (int q = 0; q < PL; q++) asm volatile("" : "+v"(l[q]), "+v"(b[q]));
 #pragma unroll
     for (int q = 0; q < PL; q++) {
         const int e = lane + 64 * q;
         // a NaN logit (non-finite input) ranks last, so every rank still names a valid expert
-        const float lv = e < E ? logits[(size_t)t * E + e] : NEG;
-        l[q] = lv != lv ? NEG : lv;
-        b[q] = e < E ? beta[(size_t)t * E + e] : 0.f;
+        key[q] = e < E ? make_key(l[q] != l[q] ? NEG : l[q], e) : 0;
+        b[q] = e < E ? b[q] : 0.f;
     }
-    // 1. fp32 selection
-    float mv = NEG;
-    int mi = BIG;
-#pragma unroll
-    for (int q = 0; q < PL; q++) {
-        const int e = lane + 64 * q;
-        if (e < E && ahead(l[q], e, mv, mi)) { mv = l[q]; mi = e; }
-    }
-    sort64(mv, mi);
-    const float thv = readlane_f32(mv, k - 1);
-    const int thi = __builtin_amdgcn_readlane(mi, k - 1);
-    int ncand = 0;
-    int pos[PL];
-#pragma unroll
-    for (int q = 0; q < PL; q++) {
-        const int e = lane + 64 * q;
-        const bool c = e < E && !ahead(thv, thi, l[q], e);
-        const unsigned long long m = __ballot(c);
-        pos[q] = ncand + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-        ncand += __popcll(m);
-        if (c && pos[q] < 64) {
-            cv[pos[q]] = l[q];
-            ci[pos[q]] = (e << 6) | pos[q];  // the expert id orders ties; the LDS slot rides along
-            cb[pos[q]] = b[q];
-        }
-    }
+    // 1. threshold: the k-th largest lane maximum (lanes with an element outnumber k)
+    const uint64_t mk = tree_max<PL>(key);
+    sc.mkey[lane] = mk;
     // LDS accesses of one wave complete in order; the fence keeps the compiler from
     // moving the reads above the writes
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    // lane j < k: fp32 logit and error bound of the expert ranked j-th (when have_rank)
-    float rank_l = NEG, rank_b = 0.f;
-    const bool have_rank = ncand <= 64;
-    if (have_rank) {
-        float v = lane < ncand ? cv[lane] : NEG;
-        int id = lane < ncand ? ci[lane] : BIG;
-        sort64(v, id);
-        const bool real = id != BIG;
-        rank_id = real ? id >> 6 : BIG;
-        rank_l = v;
-        rank_b = real ? cb[id & 63] : 0.f;
-        const float kv = readlane_f32(v, k - 1);
-        const int ki = __builtin_amdgcn_readlane(rank_id, k - 1);
-#pragma unroll
-        for (int q = 0; q < PL; q++) {
-            const int e = lane + 64 * q;
-            if (e < E && !ahead(kv, ki, l[q], e)) sel |= 1u << q;
-        }
-    } else {
-        for (int j = 0; j < k; j++) {
-            float bv = NEG;
-            int bi = BIG;
-#pragma unroll
-            for (int q = 0; q < PL; q++) {
-                const int e = lane + 64 * q;
-                if (e < E && !((sel >> q) & 1u) && ahead(l[q], e, bv, bi)) { bv = l[q]; bi = e; }
-            }
-            wave_argbest(bv, bi);
-#pragma unroll
-            for (int q = 0; q < PL; q++)
-                if (lane + 64 * q == bi) sel |= 1u << q;
-            if (lane == j) rank_id = bi;
-        }
-    }
-    // 2. is the ranking certain under the fp32 error intervals?
-    float lo = __builtin_huge_valf();
-#pragma unroll
-    for (int q = 0; q < PL; q++)
-        if ((sel >> q) & 1u) lo = fminf(lo, l[q] - b[q]);
-    lo = wave_min_f32(lo);
-    ncand = 0;
+    const int mr = count_above64(sc.mkey, mk);
+    const int tl = __ffsll((long long)__ballot(mr == k - 1)) - 1;
+    const uint64_t thr = readlane_u64(mk, tl);
+    // 2. candidates (key >= thr), compacted into LDS
+    int ncand = 0;
 #pragma unroll
     for (int q = 0; q < PL; q++) {
-        const int e = lane + 64 * q;
-        const bool c = e < E && (((sel >> q) & 1u) || l[q] + b[q] >= lo);
-        if (c) cand |= 1u << q;
-        ncand += __popcll(__ballot(c));
+        const bool c = key[q] >= thr;
+        const unsigned long long m = __ballot(c);
+        const int pos = ncand + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        ncand += __popcll(m);
+        const int slot = c && pos < 64 ? pos : 64 + lane;
+        sc.ckey[slot] = key[q];
+        sc.cb[slot] = b[q];
     }
-    bool overlap = false;
-    if (have_rank) {
-        const float nl = __shfl(rank_l, (lane + 1) & 63, 64), nb = __shfl(rank_b, (lane + 1) & 63, 64);
-        overlap = lane < k - 1 && rank_l - rank_b <= nl + nb;
+    // lane j < k: key and error bound of the expert ranked j-th
+    uint64_t rank_key = 0;
+    float rank_b = 0.f;
+    if (ncand <= 64) {
+        sc.ckey[lane >= ncand ? lane : 64 + lane] = 0;
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        const uint64_t ck = sc.ckey[lane];
+        const float cbl = sc.cb[lane];
+        const int cr = count_above64(sc.ckey, ck);
+        const int rs = lane < ncand && cr < k ? cr : 64 + lane;
+        sc.rkey[rs] = ck;
+        sc.rb[rs] = cbl;
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+        rank_key = lane < k ? sc.rkey[lane] : 0;
+        rank_b = lane < k ? sc.rb[lane] : 0.f;
     } else {
-        const int next_id = __shfl(rank_id, (lane + 1) & 63, 64);
-        if (lane < k - 1) {
-            const int ea = rank_id, eb = next_id;
-            const float la = logits[(size_t)t * E + ea], lb = logits[(size_t)t * E + eb];
-            const float ba = beta[(size_t)t * E + ea], bb = beta[(size_t)t * E + eb];
-            overlap = la - ba <= lb + bb;
-        }
-    }
-    overlap = __ballot(overlap) != 0;
-    bool reranked = false;
-    int my_id;
-    if (ncand > k || overlap) {
-        // 3. re-rank every candidate on fp64 logits
-        double key[PL];
-#pragma unroll
-        for (int q = 0; q < PL; q++) {
-            key[q] = -__builtin_huge_val();
-            unsigned long long m = __ballot((cand >> q) & 1u);
-            while (m) {
-                const int owner = __ffsll((long long)m) - 1;
-                m &= m - 1;
-                const double v = logit_f64(x, xt, wr, bias, t, owner + 64 * q, H, lane);
-                if (lane == owner) key[q] = v != v ? -__builtin_huge_val() : v;
-            }
-        }
-        uint32_t taken = 0;
+        uint32_t taken = 0;  // bit q: key q already ranked
         for (int j = 0; j < k; j++) {
-            double bv = -__builtin_huge_val();
-            int bi = 0x7FFFFFFF;
-#pragma unroll
-            for (int q = 0; q < PL; q++) {
-                const int e = lane + 64 * q;
-                if (((cand >> q) & 1u) && !((taken >> q) & 1u) && ahead(key[q], e, bv, bi)) { bv = key[q]; bi = e; }
-            }
-            wave_argbest(bv, bi);
+            uint64_t bv = 0;
 #pragma unroll
             for (int q = 0; q < PL; q++)
-                if (lane + 64 * q == bi) taken |= 1u << q;
-            if (lane == j) rank_id = bi;
+                if (!((taken >> q) & 1u) && key[q] > bv) bv = key[q];
+            bv = wave_max_key(bv);
+#pragma unroll
+            for (int q = 0; q < PL; q++)
+                if (key[q] == bv) taken |= 1u << q;
+            if (lane == j) rank_key = bv;
         }
+        if (lane < k) rank_b = beta[(size_t)t * E + key_expert(rank_key)];
+        sc.rkey[lane] = rank_key;
+        sc.rb[lane] = rank_b;
+        __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    }
+    const uint64_t kth = readlane_u64(rank_key, k - 1);
+    const float rank_l = key_logit(rank_key);
+    // 3. is the ranking certain under the fp32 error intervals?  Every selected logit's
+    // interval must lie above every other logit's, and consecutive ranks must not overlap.
+    const float lo = wave_min_f32(lane < k ? rank_l - rank_b : __builtin_huge_valf());
+    uint32_t cand = 0;  // bit q: selected, or not separable from the selection
+    int ncand2 = 0;
+#pragma unroll
+    for (int q = 0; q < PL; q++) {
+        const bool c = key[q] != 0 && (key[q] >= kth || key_logit(key[q]) + b[q] >= lo);
+        if (c) cand |= 1u << q;
+        ncand2 += __popcll(__ballot(c));
+    }
+    bool overlap = false;
+    if (lane < k - 1) overlap = rank_l - rank_b <= key_logit(sc.rkey[lane + 1]) + sc.rb[lane + 1];
+    overlap = __ballot(overlap) != 0;
+    int rank_id = key_expert(rank_key);
+    bool reranked = false;
+    if (ncand2 > k || overlap) {
+        // 4. re-rank every candidate on fp64 logits (rare: kept out of line)
+        rank_id = rerank_f64<PL>(t, x, xt, wr, bias, H, k, cand, rank_id);
         if (lane == 0 && refined) atomicAdd(refined, 1);
         reranked = true;
     }
-    // 4. softmax over the selected fp32 logits, in rank order
-    my_id = lane < k ? rank_id : 0;
-    const float lj = lane >= k ? NEG : have_rank && !reranked ? rank_l : logits[(size_t)t * E + my_id];
-    const float mx = wave_max_f32(lj);
+    // 5. softmax over the selected fp32 logits, in rank order (rank 0 holds the
+    // largest unless the fp64 ranking reordered them)
+    const int my_id = lane < k ? rank_id : 0;
+    const float lj = lane >= k ? NEG : !reranked ? rank_l : logits[(size_t)t * E + my_id];
+    const float mx = reranked ? wave_max_f32(lj) : readlane_f32(lj, 0);
     const float ex = lane < k ? __expf(lj - mx) : 0.f;
     const float den = wave_sum_f32(ex);
     if (lane < k) {
@@ -503,21 +523,28 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, 
                                               int32_t *__restrict__ ids, float *__restrict__ wts,
                                               int32_t *__restrict__ refined)
 {
-    __shared__ float cvs[4][64];
-    __shared__ int cis[4][64];
-    __shared__ float cbs[4][64];
+    __shared__ TopkScratch scs[4];
     const int wv = threadIdx.x >> 6;
     const int t = blockIdx.x * 4 + wv;
     if (t >= T) return;
-    topk_one<PL>(t, logits, beta, x, xt, wr, bias, H, E, k, ids, wts, refined, cvs[wv], cis[wv], cbs[wv]);
+    topk_one<PL>(t, logits, beta, x, xt, wr, bias, H, E, k, ids, wts, refined, scs[wv]);
+}
+
+// Position of q among the sorted s[0, 128) (entries past the slot count hold INT_MAX):
+// the number of entries below q.  Fixed steps and no branch, so that the searches of
+// one thread interleave.
+__device__ __forceinline__ int lower_bound128(const int *s, int q)
+{
+    int pos = 0;
+#pragma unroll
+    for (int step = 64; step > 0; step >>= 1) pos += s[pos + step - 1] < q ? step : 0;
+    return pos;
 }
 
 // Small batches (T <= 4, T k <= 256): top-k of every token and the grouping of the
 // T k slots in one single-block launch (the logits come from k_router_gemv, whose
-// kernel boundary makes them visible).  Wave w ranks token w; then the
-// block groups the slots: counts by LDS atomics, offsets and the active list by block
-// scans, and each slot's place from the number of earlier slots routed to the same
-// expert, i.e. slots ordered by (expert, token).
+// kernel boundary makes them visible).  Wave w ranks token w; then the block groups
+// the slots, ordered by (expert, slot).
 constexpr int kSmallT = 4;  // one wave per token; more tokens run k_topk over several blocks
 constexpr int kSmallS = 256;
 constexpr int kSmallE = 2048;
@@ -525,58 +552,62 @@ constexpr int kSmallE = 2048;
 template <int PL>
 __global__ __launch_bounds__(256) void k_topk_group(const RouteArgs a, const GroupArgs gq)
 {
-    __shared__ float cvs[4][64];
-    __shared__ int cis[4][64];
-    __shared__ float cbs[4][64];
+    __shared__ TopkScratch scs[4];
     __shared__ int cnt[kSmallE];
     __shared__ int sids[kSmallS];
     __shared__ int scr[256];
     const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
-    for (int t = wv; t < a.T; t += 4)
-        topk_one<PL>(t, a.logits, a.beta, a.x, a.xt, a.wr, a.bias, a.H, a.E, a.k, a.ids, a.w, a.refined, cvs[wv],
-                     cis[wv], cbs[wv], sids);
+    if (wv < a.T)  // T <= 4
+        topk_one<PL>(wv, a.logits, a.beta, a.x, a.xt, a.wr, a.bias, a.H, a.E, a.k, a.ids, a.w, a.refined, scs[wv],
+                     sids);
     __syncthreads();
 
     const int S = a.T * a.k, E = a.E;
     if (S <= 64) {
-        // Up to 64 slots: one wave sorts the keys (expert << 10 | slot); rank p of the
-        // sorted order is the slot's grouped row.  Offsets and counts of every expert are
-        // then binary searches in the sorted expert list.
+        // Up to 64 slots: slot s's grouped row is the number of slots ordered before it
+        // (counted by wave 0 against the broadcast slot list); offsets and counts of
+        // every expert are then searches in the sorted expert list.
         int *se = cnt;  // sorted experts
         if (wv == 0) {
-            const uint32_t key = lane < S ? ((uint32_t)sids[lane] << 10) | (uint32_t)lane : 0xFFFFFFFFu;
-            const uint32_t sk = sort64_asc(key);
-            const int e = (int)(sk >> 10), slot = (int)(sk & 1023u);
-            const bool real = lane < S;
-            if (real) {
-                gq.perm[lane] = slot;
-                gq.inv[slot] = lane;
-                se[lane] = e;
+            const int e = lane < S ? sids[lane] : 0x7FFFFFFF;
+            const uint32_t mine = ((uint32_t)e << 10) | (uint32_t)lane;
+            int p = 0;
+            for (int i = 0; i < S; i++) p += (((uint32_t)sids[i] << 10) | (uint32_t)i) < mine;
+            if (lane < S) {
+                gq.perm[p] = lane;
+                gq.inv[lane] = p;
             }
-            const int prev = __shfl_up(e, 1, 64);
-            const bool first = real && (lane == 0 || prev != e);
+            se[lane < S ? p : lane] = e;  // slots past S: INT_MAX
+            se[64 + lane] = 0x7FFFFFFF;
+            __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+            const bool real = lane < S;
+            const int ep = real ? se[lane] : 0;
+            const bool first = real && (lane == 0 || se[max(lane - 1, 0)] != ep);
             const unsigned long long m = __ballot(first);
             const int apos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-            if (first) gq.active[apos] = e;
+            if (first) gq.active[apos] = ep;
             if (lane == 0) {
                 *gq.n_active = (int)__popcll(m);
                 gq.offsets[E] = S;
             }
         }
         __syncthreads();
-        for (int q = tid; q < E; q += 256) {
-            int lo = 0, hi = S;  // first sorted entry >= q
-            while (lo < hi) {
-                const int mid = (lo + hi) >> 1;
-                if (se[mid] < q) lo = mid + 1; else hi = mid;
+        for (int q0 = 0; q0 < E; q0 += 1024) {
+            int lo[4], hi[4];
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int q = q0 + tid + 256 * r;
+                lo[r] = lower_bound128(se, q);
+                hi[r] = lower_bound128(se, q + 1);
             }
-            int lo2 = lo, hi2 = S;  // first sorted entry > q
-            while (lo2 < hi2) {
-                const int mid = (lo2 + hi2) >> 1;
-                if (se[mid] <= q) lo2 = mid + 1; else hi2 = mid;
+#pragma unroll
+            for (int r = 0; r < 4; r++) {
+                const int q = q0 + tid + 256 * r;
+                if (q < E) {
+                    gq.offsets[q] = lo[r];
+                    gq.counts[q] = hi[r] - lo[r];
+                }
             }
-            gq.offsets[q] = lo;
-            gq.counts[q] = lo2 - lo;
         }
         return;
     }

@@ -184,6 +184,20 @@ def test_small_batch_fused_routing_ties():
     run_small(c, name="fused-ties")
 
 
+def test_massive_ties_beyond_64_candidates():
+    """Logits equal to the bias and tied across each lane's experts (e, e + 64, ...): more
+    than 64 experts pass the lane-maximum threshold, so the top-k takes k rounds of
+    wave-wide maxima, and the equal values send every token through the fp64 re-ranking.
+    T = 4 runs the single-block top-k + grouping, T = 8 the multi-block top-k."""
+    for T in (4, 8):
+        w = syn.shrink(TINY, T=T, E=896, k=16, x_key=20 + T)
+        c = host_case(w)
+        c.wr[:] = 0.0
+        e = np.arange(w.E)
+        c.bias = np.where(e % 64 < 16, 10.0 - 0.001 * (e % 64), 0.0).astype(np.float32)
+        run_small(c, name=f"massive-ties-T{T}")
+
+
 def test_zero_input_and_signed_zero_logits():
     w = syn.shrink(TINY, T=4, x_key=14)
     c = host_case(w)

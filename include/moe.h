@@ -63,7 +63,12 @@ typedef enum { MOE_ACT_SWIGLU = 0 } moe_act;
 
 /* flags */
 enum {
-    MOE_F_DETERMINISTIC = 1u  /* combine and gradient reductions in a fixed order (always on in this build) */
+    MOE_F_DETERMINISTIC = 1u, /* combine and gradient reductions in a fixed order (always on in this build) */
+    MOE_F_MX_GATEUP = 2u      /* grouped-GEMM gate/up (MXFP4, bf16 x, many tokens per expert) on the
+                                 gfx950 block-scaled MFMA: weights enter as FP4 codes with their E8M0
+                                 scales and x as two E4M3 terms with per-32 scales (exact to about
+                                 2^-20 of each block's maximum); more workspace (3H + H/16 bytes per
+                                 token).  Off: exact bf16 dequantization and bf16 MFMA. */
 };
 
 /* Layer description.  moe_desc_init() fills the K3 defaults. */

@@ -32,7 +32,8 @@ typedef enum {
     MOE_PROF_BWD_DOWN = 6,       /* transposed down product + SwiGLU backward */
     MOE_PROF_BWD_GATEUP = 7,     /* transposed gate/up products */
     MOE_PROF_BWD_FINAL = 8,      /* slot reduction + router term */
-    MOE_PROF_NKERNELS = 9
+    MOE_PROF_XTERMS = 9,         /* x as two E4M3 terms for the block-scaled gate/up */
+    MOE_PROF_NKERNELS = 10
 } moe_prof_kernel;
 
 /* Enable timing of the families whose bit (1u << family) is set in mask, for

@@ -11,6 +11,7 @@ MOE_DT_F32, MOE_DT_BF16 = 0, 1
 MOE_W_MXFP4, MOE_W_RVQ3 = 0, 1
 MOE_ACT_SWIGLU = 0
 MOE_F_DETERMINISTIC = 1
+MOE_F_MX_GATEUP = 2
 
 EXPORTED = (
     "moe_desc_init", "moe_workspace_size", "moe_layer_create", "moe_route", "moe_forward",
@@ -20,9 +21,9 @@ EXPORTED = (
 
 # kernel families of include/moe_prof.h
 PROF_ROUTER_LOGITS, PROF_ROUTER_TOPK, PROF_GROUP, PROF_GATEUP, PROF_DOWN, PROF_COMBINE, PROF_BWD_DOWN, \
-    PROF_BWD_GATEUP, PROF_BWD_FINAL = range(9)
+    PROF_BWD_GATEUP, PROF_BWD_FINAL, PROF_XTERMS = range(10)
 PROF_NAMES = ("router_logits", "router_topk", "group", "gateup", "down", "combine", "bwd_down", "bwd_gateup",
-              "bwd_final")
+              "bwd_final", "xterms")
 
 
 class MoeDesc(ctypes.Structure):

@@ -344,6 +344,8 @@ hipError_t launch_expert_backward(const ExpertBwdArgs &a0, hipStream_t s)
         f.h_hi = a.h_hi;
         f.h_lo = a.h_lo;
         f.gu = a.gu_scratch;
+        f.xq = a.xq;
+        f.xq_s = a.xq_s;
         f.prof = a.prof;
         set_lds_staging(f);
         hipError_t err = launch_gateup_only(f, s);

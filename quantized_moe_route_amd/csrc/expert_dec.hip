@@ -8,9 +8,9 @@
 //  - a wave owns 16 rows of the gate and of the up matrix (or two 16-row tiles of down)
 //    and walks K in steps of 256: per step and tile each lane loads 32 contiguous code
 //    bytes and the two scale bytes of its 64 reduction indices;
-//  - code bytes go through four register stages (three steps of prefetch); the K loop
-//    is unrolled by four so that no stage is ever copied, and the prefetch loads are
-//    issued ahead of the step's math;
+//  - code bytes go through kGuStages / kDnStages register stages (one fewer steps of
+//    prefetch); the K loop is unrolled by the stage count so that no stage is ever
+//    copied, and the prefetch loads are issued ahead of the step's math;
 //  - each wave copies the scale bytes of its 16-row tiles (contiguous) into its own LDS
 //    region with two 16-byte loads per lane, issued behind the first code prefetches;
 //  - the expert's token rows (x, or the bf16 hi/lo planes of h) are staged in LDS once
@@ -39,21 +39,41 @@ __device__ __forceinline__ u32x4 ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0);
 }
 
-// Runs step(Stage<st % 4>, st) for st = 0 .. n-1 with a single loop back edge.
-template <typename F>
-__device__ __forceinline__ void k_loop4(int n, F &&step)
+template <int I, int N>
+struct Unroll {
+    template <typename F>
+    __device__ __forceinline__ static void run(int s0, F &step)
+    {
+        step(Stage<I>(), s0 + I);
+        Unroll<I + 1, N>::run(s0, step);
+    }
+    template <typename F>
+    __device__ __forceinline__ static void tail(int s0, int n, F &step)
+    {
+        if (s0 + I < n) step(Stage<I>(), s0 + I);
+        Unroll<I + 1, N>::tail(s0, n, step);
+    }
+};
+template <int N>
+struct Unroll<N, N> {
+    template <typename F>
+    __device__ __forceinline__ static void run(int, F &) {}
+    template <typename F>
+    __device__ __forceinline__ static void tail(int, int, F &) {}
+};
+
+// Runs step(Stage<st % NS>, st) for st = 0 .. n-1: the loop body is NS whole steps (so a
+// register stage is never copied) with the remainder peeled after it, a single back edge.
+template <int NS, typename F>
+__device__ __forceinline__ void k_loop(int n, F &&step)
 {
     int s0 = 0;
-    for (; s0 + 4 <= n; s0 += 4) {
-        step(Stage<0>(), s0);
-        step(Stage<1>(), s0 + 1);
-        step(Stage<2>(), s0 + 2);
-        step(Stage<3>(), s0 + 3);
-    }
-    if (s0 < n) step(Stage<0>(), s0);
-    if (s0 + 1 < n) step(Stage<1>(), s0 + 1);
-    if (s0 + 2 < n) step(Stage<2>(), s0 + 2);
+    for (; s0 + NS <= n; s0 += NS) Unroll<0, NS>::run(s0, step);
+    Unroll<0, NS - 1>::tail(s0, n, step);
 }
+
+constexpr int kGuStages = 4;  // register stages of the weight stream (prefetch distance + 1)
+constexpr int kDnStages = 4;
 
 // One tile's raw code bytes for one K-step (32 per lane).
 struct Raw {
@@ -147,13 +167,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     const __amdgpu_buffer_rsrc_t cu = buf_rsrc(a.up.codes + eoc, I * (H / 2));
     const uint32_t coff = (uint32_t)(row0 + li) * (H / 2) + 32 * g;
 
-    Raw rg[4], ru[4];
-    fetch(rg[0], cg, coff, 0);
-    fetch(ru[0], cu, coff, 0);
-    fetch(rg[1], cg, coff, min(1, nsteps - 1));
-    fetch(ru[1], cu, coff, min(1, nsteps - 1));
-    fetch(rg[2], cg, coff, min(2, nsteps - 1));
-    fetch(ru[2], cu, coff, min(2, nsteps - 1));
+    Raw rg[kGuStages], ru[kGuStages];
+#pragma unroll
+    for (int s = 0; s < kGuStages - 1; s++) {
+        fetch(rg[s], cg, coff, min(s, nsteps - 1));
+        fetch(ru[s], cu, coff, min(s, nsteps - 1));
+    }
     TileScales tg, tu;
     get_scales(tg, buf_rsrc(a.gate.scales + eos, I * spr), (uint32_t)row0 * spr, lane);
     get_scales(tu, buf_rsrc(a.up.scales + eos, I * spr), (uint32_t)row0 * spr, lane);
@@ -173,11 +192,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     const uint16_t *slg = (const uint16_t *)(sreg + li * spr + 2 * g);
     const uint16_t *slu = (const uint16_t *)(sreg + 2048 + li * spr + 2 * g);
     f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-    k_loop4(nsteps, [&](auto P, int st) {
+    k_loop<kGuStages>(nsteps, [&](auto P, int st) {
         constexpr int p = decltype(P)::value;
-        const int sn = min(st + 3, nsteps - 1);
-        fetch(rg[(p + 3) % 4], cg, coff, sn);
-        fetch(ru[(p + 3) % 4], cu, coff, sn);
+        const int sn = min(st + kGuStages - 1, nsteps - 1);
+        fetch(rg[(p + kGuStages - 1) % kGuStages], cg, coff, sn);
+        fetch(ru[(p + kGuStages - 1) % kGuStages], cu, coff, sn);
         __builtin_amdgcn_sched_barrier(0);
         bf16x8 B[8];
         lds_row8(B, xl + 256 * st);
@@ -223,9 +242,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 #pragma unroll
     for (int t = 0; t < RT; t++) coff[t] = (uint32_t)(m0 + 16 * t + li) * (I / 2) + 32 * g;
 
-    Raw rr[4][RT];
+    Raw rr[kDnStages][RT];
 #pragma unroll
-    for (int s = 0; s < 3; s++)
+    for (int s = 0; s < kDnStages - 1; s++)
 #pragma unroll
         for (int t = 0; t < RT; t++) fetch(rr[s][t], cd, coff[t], min(s, nsteps - 1));
     TileScales ts[RT];
@@ -248,11 +267,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     f32x4 acc[RT];
 #pragma unroll
     for (int t = 0; t < RT; t++) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    k_loop4(nsteps, [&](auto P, int st) {
+    k_loop<kDnStages>(nsteps, [&](auto P, int st) {
         constexpr int p = decltype(P)::value;
-        const int sn = min(st + 3, nsteps - 1);
+        const int sn = min(st + kDnStages - 1, nsteps - 1);
 #pragma unroll
-        for (int t = 0; t < RT; t++) fetch(rr[(p + 3) % 4][t], cd, coff[t], sn);
+        for (int t = 0; t < RT; t++) fetch(rr[(p + kDnStages - 1) % kDnStages][t], cd, coff[t], sn);
         __builtin_amdgcn_sched_barrier(0);
         bf16x8 B[8], Bl[8];
         lds_row8(B, hl + 256 * st);

@@ -102,6 +102,87 @@ __device__ __forceinline__ void k_loop3(int n, F &&step)
     if (s0 + 1 < n) step(Stage<1>(), s0 + 1);
 }
 
+// Runs step(Stage<st % 2>, st) for st = 0 .. n-1: two register stages.
+template <typename F>
+__device__ __forceinline__ void k_loop2(int n, F &&step)
+{
+    int s0 = 0;
+    for (; s0 + 2 <= n; s0 += 2) {
+        step(Stage<0>(), s0);
+        step(Stage<1>(), s0 + 1);
+    }
+    if (s0 < n) step(Stage<0>(), s0);
+}
+
+// ---------------------------------------------------------------- x as two E4M3 terms
+//
+// For the block-scaled gate/up, each 32-element block of a token row is written as
+// x = 2^e1 q1 + 2^e2 q2 (+ a remainder below 2^-20 of the block maximum), q1, q2 E4M3
+// (OCP, round to nearest even), e1 = exponent of the block maximum - 7 (so |x| 2^-e1 <
+// 256 < 448) and e2 likewise for the remainder x - 2^e1 q1 (exact in fp32).  A bf16 value
+// has 8 significant bits and each term carries 4, so only elements more than 2^6 below
+// the block maximum can leave a remainder.
+// Layout: per token, per K-step of 128 elements, the 128 q1 bytes then the 128 q2 bytes
+// (a token row is 2H bytes, like the bf16 row); scales [T][H/32][2] (e1 + 127, e2 + 127).
+
+__device__ __forceinline__ int block_exp(float m)  // exponent of m's leading bit - 7, in E8M0 range
+{
+    const int e = (int)((__float_as_uint(m) >> 23) & 0xFF) - 127 - 7;
+    return e < -127 ? -127 : e;
+}
+
+__device__ __forceinline__ float pow2f(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }  // -126..127
+
+__global__ __launch_bounds__(256) void k_x_terms(const uint16_t *__restrict__ x, int T, int H, uint8_t *__restrict__ xq,
+                                                 uint8_t *__restrict__ xs)
+{
+    const int nb = H / 32;
+    const size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (size_t)T * nb) return;
+    const size_t t = i / nb;
+    const int q = (int)(i - t * nb);
+    float v[32];
+    const u32x4 *src = (const u32x4 *)(x + t * H + 32 * q);
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+        const u32x4 w = src[c];
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            v[8 * c + 2 * j] = __uint_as_float(w[j] << 16);
+            v[8 * c + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+        }
+    }
+    uint8_t *dst = xq + t * (size_t)(2 * H) + (size_t)(q >> 2) * 256 + 32 * (q & 3);
+    int eb[2];
+#pragma unroll
+    for (int p = 0; p < 2; p++) {
+        float m = 0.f;
+#pragma unroll
+        for (int j = 0; j < 32; j++) m = fmaxf(m, fabsf(v[j]));
+        const int e = block_exp(m);
+        eb[p] = e + 127;
+        // 2^-e in two factors, so that e = -127 stays in range
+        const float inv_hi = pow2f(-(e >> 1)), inv_lo = pow2f(-(e - (e >> 1)));
+        u32x4 out[2];
+#pragma unroll
+        for (int j = 0; j < 16; j++) {
+            const float a0 = v[2 * j] * inv_hi * inv_lo, a1 = v[2 * j + 1] * inv_hi * inv_lo;
+            const uint32_t pk = (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(a0, a1, 0, false) & 0xFFFFu;
+            const uint32_t sh = 16 * (j & 1);
+            if ((j & 1) == 0) out[j >> 3][(j >> 1) & 3] = pk;
+            else out[j >> 3][(j >> 1) & 3] |= pk << sh;
+            // remainder for the next term: x - 2^e q (q decoded back from the byte)
+            const float d0 = __builtin_amdgcn_cvt_f32_fp8((int)pk, 0), d1 = __builtin_amdgcn_cvt_f32_fp8((int)pk, 1);
+            const float sc_hi = pow2f(e >> 1), sc_lo = pow2f(e - (e >> 1));
+            v[2 * j] -= d0 * sc_hi * sc_lo;
+            v[2 * j + 1] -= d1 * sc_hi * sc_lo;
+        }
+        *(u32x4 *)(dst + 128 * p) = out[0];
+        *(u32x4 *)(dst + 128 * p + 16) = out[1];
+    }
+    *(uint16_t *)(xs + 2 * i) = (uint16_t)(eb[0] | (eb[1] << 8));
+}
+
 // ---------------------------------------------------------------- gate/up + SwiGLU
 //
 // K-step 128: lane group g = lane / 16 owns reduction indices [32g, 32g + 32) of the
@@ -236,6 +317,169 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mm(const ExpertFwdArgs a)
         case 4: gateup_pass<4>(a, b, xs, r0, tt0, nt); break;
         case 5: gateup_pass<5>(a, b, xs, r0, tt0, nt); break;
         default: gateup_pass<6>(a, b, xs, r0, tt0, nt); break;
+        }
+    }
+}
+
+// ---------------------------------------------------------------- block-scaled gate/up + SwiGLU
+//
+// Same blocking as k_gateup_mm, on v_mfma_scale_f32_16x16x128_f8f6f4: the weight tile
+// enters as its FP4 codes with their E8M0 scale (A operand; lane group g holds the
+// step's reduction indices 32g .. 32g+31, one MX block, exactly the 16 bytes and the
+// scale byte the lane loads), the token tile as the two E4M3 terms of x with their
+// block scales (B operand; lane group g holds indices 16g .. 16g+15 and 64+16g ..
+// 64+16g+15; the scale of block q of a row or column comes from lane group q).  One
+// MFMA per term and 16 x 16 tile covers a K-step of 128, with no dequantization.
+// The LDS row of a token holds the step's q1 bytes (chunks 0..7) then q2 (8..15);
+// the terms' scales go to a separate 8-byte-per-token array.
+
+template <int PB>
+__device__ __forceinline__ f32x4 mfma_mx(u32x4 a, u32x4 b0, u32x4 b1, f32x4 c, uint32_t sa, uint32_t sb)
+{
+    typedef __attribute__((ext_vector_type(8))) int i32x8;
+    typedef __attribute__((ext_vector_type(4))) int i32x4;
+    const i32x4 a4 = __builtin_bit_cast(i32x4, a);
+    // an FP4 operand occupies the low four registers only; the upper half is left undefined
+    const i32x8 A = __builtin_shufflevector(a4, a4, 0, 1, 2, 3, -1, -1, -1, -1);
+    const i32x8 B = __builtin_shufflevector(__builtin_bit_cast(i32x4, b0), __builtin_bit_cast(i32x4, b1), 0, 1, 2, 3, 4,
+                                            5, 6, 7);
+    // A: FP4 (format 4), scale byte 0 of sa; B: E4M3 (format 0), scale byte PB of sb
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, c, 4, 0, 0, (int)sa, PB, (int)sb);
+}
+
+typedef u32x2 MmScl[kMmTok];
+
+template <int NT>
+__device__ __forceinline__ void gateup_pass_mx(const ExpertFwdArgs &a, const GuBlock &b, MmTile *xs, MmScl *xsc,
+                                               int r0, int tt0, int nt)
+{
+    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
+    const int H = a.H, I = a.I, nsteps = H / 128;
+    const int xr = tid >> 4, xc = tid & 15;  // this thread's x-tile row (+16 i) and chunk
+    const __amdgpu_buffer_rsrc_t xsr = buf_rsrc(a.xq_s, (uint32_t)((size_t)a.T * (H / 16)));
+    uint32_t xoff[NT];                       // byte offsets at K-step 0
+#pragma unroll
+    for (int i = 0; i < NT; i++) {
+        const int tok = a.perm[r0 + tt0 + min(xr + 16 * i, nt - 1)] / a.k;
+        xoff[i] = (uint32_t)tok * (2 * H) + 16 * xc;
+    }
+    // scales: thread tid < 16 NT stages token row tid's 8 bytes per step
+    const bool sthr = tid < 16 * NT;
+    const uint32_t soffx = (uint32_t)(a.perm[r0 + tt0 + min(tid, nt - 1)] / a.k) * (H / 16);
+    f32x4 acc[4][NT];
+#pragma unroll
+    for (int t = 0; t < 4; t++)
+#pragma unroll
+        for (int tt = 0; tt < NT; tt++) acc[t][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    u32x4 q[2][4];
+    uint32_t sc[2][4];
+    auto load_w = [&](auto P, int st) {
+        constexpr int p = decltype(P)::value;
+#pragma unroll
+        for (int t = 0; t < 4; t++) {
+            q[p][t] = ld16(b.code[t >> 1], b.coff, (t & 1) * 8 * H + 64 * st);
+            sc[p][t] = ld1(b.scale[t >> 1], b.soff, (t & 1) * (H / 2) + 4 * st);
+        }
+    };
+    {
+        u32x4 xv[NT];
+#pragma unroll
+        for (int i = 0; i < NT; i++) xv[i] = ld16(b.x, xoff[i], 0);
+        const u32x2 sv = ld8(xsr, soffx, 0);
+        load_w(Stage<0>(), 0);
+#pragma unroll
+        for (int i = 0; i < NT; i++) xs[0][lds_slot(xr + 16 * i, xc)] = xv[i];
+        if (sthr) xsc[0][tid] = sv;
+    }
+    __syncthreads();
+
+    k_loop2(nsteps, [&](auto P, int st) {
+        constexpr int p = decltype(P)::value;
+        const int buf = st & 1;
+        u32x4 xv[NT];  // next step's x tile, issued before the weights so waiting for it
+        const int stn = min(st + 1, nsteps - 1);  // leaves the weight prefetch in flight
+#pragma unroll
+        for (int i = 0; i < NT; i++) xv[i] = ld16(b.x, xoff[i], 256 * stn);
+        const u32x2 sv = ld8(xsr, soffx, 8 * stn);
+        load_w(Stage<p ^ 1>(), stn);
+        __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the step's MFMAs
+#pragma unroll
+        for (int tt = 0; tt < NT; tt++) {
+            const int row = 16 * tt + li;
+            const u32x4 b00 = xs[buf][lds_slot(row, g)], b01 = xs[buf][lds_slot(row, 4 + g)];
+            const u32x4 b10 = xs[buf][lds_slot(row, 8 + g)], b11 = xs[buf][lds_slot(row, 12 + g)];
+            const uint32_t sw = ((const uint16_t *)&xsc[buf][row])[g];
+            // term 0 on the four weight tiles, then term 1: dependent MFMAs four apart
+#pragma unroll
+            for (int t = 0; t < 4; t++) acc[t][tt] = mfma_mx<0>(q[p][t], b00, b01, acc[t][tt], sc[p][t], sw);
+#pragma unroll
+            for (int t = 0; t < 4; t++) acc[t][tt] = mfma_mx<1>(q[p][t], b10, b11, acc[t][tt], sc[p][t], sw);
+        }
+        // the accumulators are pinned here: without it the compiler sinks the step's
+        // MFMAs (pure operations) below the later steps and keeps all their operands live
+#pragma unroll
+        for (int t = 0; t < 4; t++)
+#pragma unroll
+            for (int tt = 0; tt < NT; tt++) asm volatile("" : "+v"(acc[t][tt]));
+#pragma unroll
+        for (int i = 0; i < NT; i++) xs[buf ^ 1][lds_slot(xr + 16 * i, xc)] = xv[i];
+        if (sthr) xsc[buf ^ 1][tid] = sv;
+        __syncthreads();
+    });
+
+    // lane (g, li) holds I-columns c0 + 16 (t & 1) + 4 g + 0..3 of token 16 tt + li
+#pragma unroll
+    for (int tt = 0; tt < NT; tt++) {
+        const int j = 16 * tt + li;
+        if (j >= nt) continue;
+        const size_t rr = (size_t)(r0 + tt0 + j);
+#pragma unroll
+        for (int t = 0; t < 2; t++) {
+            const f32x4 gv = acc[t][tt], uv = acc[t + 2][tt];
+            uint32_t hh[4], hl[4];
+#pragma unroll
+            for (int r = 0; r < 4; r++) split_bf16(gv[r] * sigmoidf_(gv[r]) * uv[r], hh[r], hl[r]);
+            const int n = b.c0 + 16 * t + 4 * g;
+            *(u32x2 *)(a.h_hi + rr * I + n) = u32x2{pack2(hh[0], hh[1]), pack2(hh[2], hh[3])};
+            *(u32x2 *)(a.h_lo + rr * I + n) = u32x2{pack2(hl[0], hl[1]), pack2(hl[2], hl[3])};
+            if (a.gu) {
+                *(float4 *)(a.gu + (rr * 2 + 0) * I + n) = float4{gv[0], gv[1], gv[2], gv[3]};
+                *(float4 *)(a.gu + (rr * 2 + 1) * I + n) = float4{uv[0], uv[1], uv[2], uv[3]};
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(256, 2) void k_gateup_mx(const ExpertFwdArgs a)
+{
+    __shared__ MmTile xs[2];
+    __shared__ MmScl xsc[2];
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
+    const int H = a.H, I = a.I;
+    int ai, cb;
+    xcd_split(I / 128, ai, cb);
+    if (ai >= *a.n_active) return;
+    const int e = a.active[ai];
+    const int r0 = a.offsets[e], ntok = a.offsets[e + 1] - r0;
+    GuBlock b;
+    const size_t eoc = (size_t)e * I * (H / 2), eos = (size_t)e * I * (H / 32);
+    b.code[0] = buf_rsrc(a.gate.codes + eoc, I * (H / 2));
+    b.code[1] = buf_rsrc(a.up.codes + eoc, I * (H / 2));
+    b.scale[0] = buf_rsrc(a.gate.scales + eos, I * (H / 32));
+    b.scale[1] = buf_rsrc(a.up.scales + eos, I * (H / 32));
+    b.x = buf_rsrc(a.xq, (uint32_t)((size_t)a.T * H * 2));
+    b.c0 = cb * 128 + wv * 32;
+    b.coff = (uint32_t)(b.c0 + li) * (H / 2) + 16 * g;
+    b.soff = (uint32_t)(b.c0 + li) * (H / 32) + g;
+    for (int tt0 = 0; tt0 < ntok; tt0 += kMmTok) {
+        const int nt = min(kMmTok, ntok - tt0);
+        switch ((nt + 15) / 16) {
+        case 1: gateup_pass_mx<1>(a, b, xs, xsc, r0, tt0, nt); break;
+        case 2: gateup_pass_mx<2>(a, b, xs, xsc, r0, tt0, nt); break;
+        case 3: gateup_pass_mx<3>(a, b, xs, xsc, r0, tt0, nt); break;
+        case 4: gateup_pass_mx<4>(a, b, xs, xsc, r0, tt0, nt); break;
+        case 5: gateup_pass_mx<5>(a, b, xs, xsc, r0, tt0, nt); break;
+        default: gateup_pass_mx<6>(a, b, xs, xsc, r0, tt0, nt); break;
         }
     }
 }
@@ -381,14 +625,27 @@ bool mm_supported(const ExpertFwdArgs &a)
     const size_t S = (size_t)a.T * a.k, lim = (size_t)1 << 32;
     return a.wfmt == FMT_MXFP4 && a.xt == DT_BF16 && a.H % 512 == 0 && a.I % 512 == 0 &&
            (size_t)a.T * a.H * 2 < lim && S * a.I * 4 < lim && (size_t)a.H * a.I < lim &&
-           a.h_lo == a.h_hi + S * a.I;
+           a.h_lo == a.h_hi + S * a.I && (!a.xq || a.xq_s);
 }
 
 hipError_t launch_gateup_mm(const ExpertFwdArgs &a, hipStream_t s)
 {
     const int maxU = min(a.E, a.T * a.k);
+    if (!a.xq) {
+        ProfScope ps(a.prof, PK_GATEUP, s);
+        ps.launch(k_gateup_mm, dim3(xcd_grid(maxU, a.I / 128)), dim3(256), 0, a);
+        return hipGetLastError();
+    }
+    {
+        ProfScope ps(a.prof, PK_XTERMS, s);
+        const size_t n = (size_t)a.T * (a.H / 32);
+        ps.launch(k_x_terms, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, (const uint16_t *)a.x, a.T, a.H, a.xq,
+                  a.xq_s);
+    }
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
     ProfScope ps(a.prof, PK_GATEUP, s);
-    ps.launch(k_gateup_mm, dim3(xcd_grid(maxU, a.I / 128)), dim3(256), 0, a);
+    ps.launch(k_gateup_mx, dim3(xcd_grid(maxU, a.I / 128)), dim3(256), 0, a);
     return hipGetLastError();
 }
 

@@ -37,7 +37,7 @@ constexpr int kMaxTopK = 64;
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-    size_t logits, beta, h, ybuf, gu, dgdu, dp, total;
+    size_t logits, beta, h, ybuf, gu, dgdu, dp, xq, xqs, total;
 };
 
 Layout layout_of(const moe_desc &d)
@@ -58,6 +58,9 @@ Layout layout_of(const moe_desc &d)
     L.gu = take(S * 2 * I * 4);
     L.dgdu = take(S * 2 * I * 4);
     L.dp = take(S * (size_t)moe::dp_tiles((int)I) * 4);
+    const bool mx = (d.flags & MOE_F_MX_GATEUP) != 0;
+    L.xq = take(mx ? T * H * 2 : 0);
+    L.xqs = take(mx ? T * (H / 32) * 2 : 0);
     L.total = off;
     return L;
 }
@@ -299,6 +302,10 @@ moe_status moe_forward(moe_layer *L, const void *x, int32_t xt, int32_t T, const
     a.gu = saved_gu;
     a.ybuf = (float *)(L->ws + L->lay.ybuf);
     a.y = y;
+    if (L->d.flags & MOE_F_MX_GATEUP) {
+        a.xq = (uint8_t *)(L->ws + L->lay.xq);
+        a.xq_s = (uint8_t *)(L->ws + L->lay.xqs);
+    }
     a.prof = &L->prof;
     moe::set_lds_staging(a);
     return device_status(moe::launch_expert_forward(a, (hipStream_t)stream), "forward");
@@ -348,6 +355,10 @@ moe_status moe_backward_input(moe_layer *L, const void *x, int32_t xt, const voi
     a.dp_part = (float *)(L->ws + L->lay.dp);
     a.dxs = (float *)(L->ws + L->lay.ybuf);
     a.dx = dx;
+    if (L->d.flags & MOE_F_MX_GATEUP) {
+        a.xq = (uint8_t *)(L->ws + L->lay.xq);
+        a.xq_s = (uint8_t *)(L->ws + L->lay.xqs);
+    }
     a.prof = &L->prof;
     return device_status(moe::launch_expert_backward(a, (hipStream_t)stream), "backward_input");
 }

@@ -12,7 +12,7 @@ namespace moe {
 
 // Optional per-kernel timing (include/moe_prof.h): two events per launch on the launch stream.
 enum { PK_ROUTER_LOGITS = 0, PK_ROUTER_TOPK, PK_GROUP, PK_GATEUP, PK_DOWN, PK_COMBINE, PK_BWD_DOWN, PK_BWD_GATEUP,
-       PK_BWD_FINAL, PK_N };
+       PK_BWD_FINAL, PK_XTERMS, PK_N };
 
 struct Prof {
     uint32_t mask = 0;
@@ -93,6 +93,8 @@ struct ExpertFwdArgs {
     float *gu;           // [S][2][I] grouped rows (g, u) or null
     float *ybuf;         // [S][H] slot rows: w * expert output
     float *y;            // [T][H]
+    uint8_t *xq;         // [T][2H] x as two E4M3 terms for the block-scaled gate/up (grouped-GEMM
+    uint8_t *xq_s;       // path; null: bf16 path) and [T][H/32][2] their E8M0 block scales
     int nl_x;            // experts with at most this many tokens stage their x rows in LDS
     int nl_h;            // ... and their h rows (down product)
 };
@@ -117,6 +119,7 @@ struct ExpertBwdArgs {
     float *dp_part;      // [S][ntile] partial <a, h>
     float *dxs;          // [S][H] slot rows
     float *dx;           // [T][H]
+    uint8_t *xq, *xq_s;  // x terms for the gate/up recomputation (as in ExpertFwdArgs)
 };
 
 // Token rows staged in LDS by the few-token (decode) expert kernels: at most 16 rows

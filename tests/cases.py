@@ -59,11 +59,11 @@ def act_tensor(a: np.ndarray, dtype: str):
     return q.bf16_tensor(a) if dtype == "bf16" else q.to_device(np.asarray(a, np.float32))
 
 
-def device_layer(c: HostCase, max_tokens: int):
+def device_layer(c: HostCase, max_tokens: int, flags: int = 0):
     import quantized_moe_route_amd as q
     w = c.w
     kw = dict(hidden=w.H, inter=w.I, n_experts=w.E, top_k=w.k, max_tokens=max_tokens,
-              router_w=q.to_device(c.wr), router_b=None if c.bias is None else q.to_device(c.bias))
+              router_w=q.to_device(c.wr), router_b=None if c.bias is None else q.to_device(c.bias), flags=flags)
     if c.codes is not None:
         kw["codes"] = [q.to_device(a) for a in c.codes]
         kw["scales"] = [q.to_device(a) for a in c.scales]

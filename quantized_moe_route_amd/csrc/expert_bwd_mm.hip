@@ -61,8 +61,15 @@ __device__ __forceinline__ uint32_t ld1(__amdgpu_buffer_rsrc_t r, uint32_t voff,
 }
 
 // Element offset of W-tile entry (row, m).  Rows 8..15 and 24..31 are stored with m
-// flipped by 64, so the 16 rows one transposed read touches fall into distinct banks.
-__device__ __forceinline__ int wt_pos(int row, int m) { return row * kWRow + (m ^ (((row >> 3) & 1) << 6)); }
+// flipped by 64, so the 16 rows one transposed read touches fall into distinct banks; the
+// upper half of a row (m >= 128) sits 8 elements further on, so the 16-byte stores of a
+// quarter wave (two rows, m = 32 j + 8 v for j = 0..7) fall into 16 distinct bank groups
+// instead of pairing j with j + 4.  A transposed read stays within one half.
+__device__ __forceinline__ int wt_pos(int row, int m)
+{
+    const int mm = m ^ (((row >> 3) & 1) << 6);
+    return row * kWRow + mm + ((mm >> 7) << 3);
+}
 
 // B tile: [96 rows][16 chunks of 16 bytes], chunk c of row r in slot c ^ (r & 15).
 __device__ __forceinline__ int bt_slot(int row, int c) { return row * 16 + (c ^ (row & 15)); }

@@ -118,75 +118,123 @@ __global__ __launch_bounds__(256) void k_router_gemv(const void *__restrict__ x,
     }
 }
 
-// Tiled form for many tokens: block = 32 tokens x 64 experts, K chunks of 32
-// staged in LDS; thread (ty, tx) owns tokens 2ty, 2ty+1 and experts tx+16q.
-// Each chunk is summed from zero and then added to the running total.
-__global__ __launch_bounds__(256) void k_router_tiled(const void *__restrict__ x, int xt, const float *__restrict__ wr,
-                                                      const float *__restrict__ bias, int T, int H, int E,
-                                                      float *__restrict__ logits, float *__restrict__ beta)
+// Many tokens: logits on the fp64 matrix cores (v_mfma_f64_16x16x4_f64).  The fp32 (or
+// bf16) inputs are exact in fp64 and so are their products; only the fp64 additions
+// round, so |l64 - l| <= gamma_H sum_i |x_i w_i| <= gamma_H ||x|| ||w|| (Higham, sec. 3.1,
+// any summation order, each add erring by at most u = 2^-53 of its result; Cauchy-Schwarz
+// for the sum), taken twice over as a margin for the unit's internal order.  The logit is
+// returned in fp32 with beta = that bound + |l64 - l32| + the bias add's rounding, rounded
+// upwards, so the top-k certifies on the same intervals as for the fp32 kernels; only
+// logits within ~1e-7 of each other call for the fp64 re-ranking.
+// Block = 64 tokens x 64 experts, four waves of 32 x 32 (2 x 2 MFMA tiles); K in chunks of
+// 32 staged in LDS as fp32 (row stride 36: the 64 single-element fragment reads of an
+// MFMA operand hit 64 distinct banks).  Operand layouts: A lane l = (row l % 16, k l / 16),
+// B lane l = (k l / 16, column l % 16); result value i of lane l = (row 4 i + l / 16,
+// column l % 16).
+typedef __attribute__((ext_vector_type(4))) double f64x4;
+constexpr int kRfTile = 64, kRfK = 32, kRfStride = 36;
+
+__global__ __launch_bounds__(256, 2) void k_router_f64(const void *__restrict__ x, int xt, const float *__restrict__ wr,
+                                                       const float *__restrict__ bias, int T, int H, int E,
+                                                       float *__restrict__ logits, float *__restrict__ beta)
 {
-    __shared__ float xs[32][33];
-    __shared__ float ws[64][33];
-    const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
-    const int t0 = blockIdx.y * 32, e0 = blockIdx.x * 64;
-    float acc[2][4], eb[2][4];
+    __shared__ __attribute__((aligned(16))) float xs[2][kRfTile * kRfStride];
+    __shared__ __attribute__((aligned(16))) float ws[2][kRfTile * kRfStride];
+    __shared__ double nx[kRfTile], nw[kRfTile];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int t0 = blockIdx.y * kRfTile, e0 = blockIdx.x * kRfTile;
+    // staging: thread tid moves 8 consecutive k of row tid / 4 of both tiles
+    const int sr = tid >> 2, sk = 8 * (tid & 3);
+    const int st_t = min(t0 + sr, T - 1), st_e = min(e0 + sr, E - 1);
+    const bool tok_ok = t0 + sr < T, exp_ok = e0 + sr < E;
+    double sx = 0.0, sw = 0.0;  // sums of squares of this thread's staged values
+    float xv[8], wv8[8];
+    auto load = [&](int k0) {
+        if (xt == DT_BF16) {
+            const u32x4 v = *(const u32x4 *)((const uint16_t *)x + (size_t)st_t * H + k0 + sk);
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                xv[2 * j] = __uint_as_float(v[j] << 16);
+                xv[2 * j + 1] = __uint_as_float(v[j] & 0xFFFF0000u);
+            }
+        } else {
+            const float4 a = *(const float4 *)((const float *)x + (size_t)st_t * H + k0 + sk);
+            const float4 b = *(const float4 *)((const float *)x + (size_t)st_t * H + k0 + sk + 4);
+            xv[0] = a.x; xv[1] = a.y; xv[2] = a.z; xv[3] = a.w; xv[4] = b.x; xv[5] = b.y; xv[6] = b.z; xv[7] = b.w;
+        }
+        const float4 a = *(const float4 *)(wr + (size_t)st_e * H + k0 + sk);
+        const float4 b = *(const float4 *)(wr + (size_t)st_e * H + k0 + sk + 4);
+        wv8[0] = a.x; wv8[1] = a.y; wv8[2] = a.z; wv8[3] = a.w; wv8[4] = b.x; wv8[5] = b.y; wv8[6] = b.z; wv8[7] = b.w;
+    };
+    auto store = [&](int buf) {
+        float4 *xd = (float4 *)&xs[buf][sr * kRfStride + sk], *wd = (float4 *)&ws[buf][sr * kRfStride + sk];
+        const float m = tok_ok ? 1.f : 0.f, n = exp_ok ? 1.f : 0.f;  // rows past T or E are zero
+        xd[0] = float4{m * xv[0], m * xv[1], m * xv[2], m * xv[3]};
+        xd[1] = float4{m * xv[4], m * xv[5], m * xv[6], m * xv[7]};
+        wd[0] = float4{n * wv8[0], n * wv8[1], n * wv8[2], n * wv8[3]};
+        wd[1] = float4{n * wv8[4], n * wv8[5], n * wv8[6], n * wv8[7]};
+#pragma unroll
+        for (int j = 0; j < 8; j++) {
+            sx = fma((double)xv[j], (double)xv[j], sx);
+            sw = fma((double)wv8[j], (double)wv8[j], sw);
+        }
+    };
+    f64x4 acc[2][2];
 #pragma unroll
     for (int a = 0; a < 2; a++)
 #pragma unroll
-        for (int q = 0; q < 4; q++) acc[a][q] = eb[a][q] = 0.f;
-
-    for (int k0 = 0; k0 < H; k0 += 32) {
+        for (int b = 0; b < 2; b++) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
+    const int mr = 32 * (wv & 1), mc = 32 * (wv >> 1);  // this wave's tokens / experts in the tile
+    const int fr = lane & 15, fk = lane >> 4;           // fragment row (or column) and k
+    const int nchunks = H / kRfK;
+    load(0);
+    store(0);
+    __syncthreads();
+    for (int c = 0; c < nchunks; c++) {
+        const int buf = c & 1;
+        if (c + 1 < nchunks) load((c + 1) * kRfK);
 #pragma unroll
-        for (int r = 0; r < 4; r++) {
-            const int idx = tid + 256 * r, tt = idx >> 5, kk = idx & 31;
-            const int t = t0 + tt, k = k0 + kk;
-            xs[tt][kk] = (t < T && k < H) ? load_x1(x, xt, (size_t)t * H + k) : 0.f;
-        }
+        for (int ks = 0; ks < kRfK / 4; ks++) {
+            double A[2], B[2];
 #pragma unroll
-        for (int r = 0; r < 8; r++) {
-            const int idx = tid + 256 * r, ee = idx >> 5, kk = idx & 31;
-            const int e = e0 + ee, k = k0 + kk;
-            ws[ee][kk] = (e < E && k < H) ? wr[(size_t)e * H + k] : 0.f;
-        }
-        __syncthreads();
-        float part[2][4];
-#pragma unroll
-        for (int a = 0; a < 2; a++)
-#pragma unroll
-            for (int q = 0; q < 4; q++) part[a][q] = 0.f;
-#pragma unroll 8
-        for (int kk = 0; kk < 32; kk++) {
-            const float xa = xs[2 * ty][kk], xb = xs[2 * ty + 1][kk];
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                const float wv = ws[tx + 16 * q][kk];
-                part[0][q] = fmaf(xa, wv, part[0][q]);
-                part[1][q] = fmaf(xb, wv, part[1][q]);
-                eb[0][q] += fabsf(part[0][q]);
-                eb[1][q] += fabsf(part[1][q]);
+            for (int u = 0; u < 2; u++) {
+                A[u] = (double)xs[buf][(mr + 16 * u + fr) * kRfStride + 4 * ks + fk];
+                B[u] = (double)ws[buf][(mc + 16 * u + fr) * kRfStride + 4 * ks + fk];
             }
+#pragma unroll
+            for (int a = 0; a < 2; a++)
+#pragma unroll
+                for (int b = 0; b < 2; b++) acc[a][b] = __builtin_amdgcn_mfma_f64_16x16x4f64(A[a], B[b], acc[a][b], 0, 0, 0);
         }
-#pragma unroll
-        for (int a = 0; a < 2; a++)
-#pragma unroll
-            for (int q = 0; q < 4; q++) {
-                acc[a][q] += part[a][q];
-                eb[a][q] += fabsf(acc[a][q]);
-            }
+        if (c + 1 < nchunks) store(buf ^ 1);
         __syncthreads();
     }
+    // norms: the four threads of a staged row are adjacent lanes
+    sx += __shfl_xor(sx, 1, 64);
+    sx += __shfl_xor(sx, 2, 64);
+    sw += __shfl_xor(sw, 1, 64);
+    sw += __shfl_xor(sw, 2, 64);
+    if ((tid & 3) == 0) {
+        nx[sr] = sqrt(sx);
+        nw[sr] = sqrt(sw);
+    }
+    __syncthreads();
+    const double g2 = 2.0 * (double)(H + 1) * 0x1p-53 * (1.0 + 0x1p-20);  // 2 gamma_{H+1}, rounded up
 #pragma unroll
     for (int a = 0; a < 2; a++)
 #pragma unroll
-        for (int q = 0; q < 4; q++) {
-            const int t = t0 + 2 * ty + a, e = e0 + tx + 16 * q;
-            if (t < T && e < E) {
-                const float b = bias ? bias[e] : 0.f;
-                const float l = acc[a][q] + b;
-                logits[(size_t)t * E + e] = l;
-                beta[(size_t)t * E + e] = bound_of(eb[a][q], l);
+        for (int b = 0; b < 2; b++)
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const int tr = mr + 16 * a + 4 * i + fk, ec = mc + 16 * b + fr;
+                const int t = t0 + tr, e = e0 + ec;
+                if (t >= T || e >= E) continue;
+                const double l64 = acc[a][b][i] + (bias ? (double)bias[e] : 0.0);
+                const float l32 = (float)l64;
+                const double bd = g2 * nx[tr] * nw[ec] + fabs(l64 - (double)l32) + 0x1p-52 * fabs(l64);
+                logits[(size_t)t * E + e] = l32;
+                beta[(size_t)t * E + e] = (float)(bd * (1.0 + 0x1p-20)) + 1e-30f;
             }
-        }
 }
 
 // fp64 logit of expert c for token t: lane l sums its inputs 4l + 256 m in order
@@ -700,8 +748,8 @@ hipError_t launch_router(const RouteArgs &a, hipStream_t s)
         ps.launch(k_router_gemv, dim3(a.E, (a.T + 7) / 8), dim3(256), 0, a.x, a.xt, a.wr, a.bias,
                            a.T, a.H, a.E, a.logits, a.beta);
     } else {
-        ps.launch(k_router_tiled, dim3((a.E + 63) / 64, (a.T + 31) / 32), dim3(256), 0, a.x, a.xt, a.wr,
-                           a.bias, a.T, a.H, a.E, a.logits, a.beta);
+        ps.launch(k_router_f64, dim3((a.E + kRfTile - 1) / kRfTile, (a.T + kRfTile - 1) / kRfTile), dim3(256), 0,
+                  a.x, a.xt, a.wr, a.bias, a.T, a.H, a.E, a.logits, a.beta);
     }
     }
     hipError_t err = hipGetLastError();

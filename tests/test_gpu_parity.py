@@ -221,6 +221,19 @@ def test_near_ties_one_ulp_apart():
     run_small(c, name="near-ties")
 
 
+def test_many_token_router_ties_and_near_ties():
+    """T > 64 takes the fp64 matrix-core logits: exact duplicate router rows must tie (lower
+    id first) and one-ulp near-ties must be ordered by the fp64 re-ranking."""
+    w = syn.shrink(TINY, T=150, E=16, k=4, x_key=28)
+    c = host_case(w)
+    c.wr[9] = c.wr[2]
+    c.wr[12] = c.wr[2]
+    for a, b in ((1, 5), (3, 11)):
+        c.wr[b] = c.wr[a]
+        c.wr[b, 17] = np.nextafter(c.wr[a, 17], np.float32(np.inf))
+    run_small(c, name="f64-router-ties")
+
+
 def test_small_batch_fused_routing_ties():
     """T <= 4 routes through the combined top-k + grouping kernel; exact duplicate router
     rows and one-ulp near-ties must resolve there as they do in the separate kernels."""

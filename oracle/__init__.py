@@ -40,7 +40,10 @@ class _Weights(ctypes.Structure):
                 ("codes", ctypes.c_void_p * 3),
                 ("scales", ctypes.c_void_p * 3),
                 ("rvq_idx", ctypes.c_void_p * 3),
-                ("rvq_cb", ctypes.c_void_p * 3)]
+                ("rvq_cb", ctypes.c_void_p * 3),
+                ("act", ctypes.c_int)]
+
+ACT_SWIGLU, ACT_SITU = 0, 1
 
 
 def lib():
@@ -91,10 +94,11 @@ class Weights:
     m = 0 gate, 1 up (rows = I, cols = H), 2 down (rows = H, cols = I).
     """
 
-    def __init__(self, H: int, I: int, codes=None, scales=None, idx=None, cb=None):
+    def __init__(self, H: int, I: int, codes=None, scales=None, idx=None, cb=None, act: int = 0):
         self.H, self.I = H, I
         self._keep = []
         s = _Weights()
+        s.act = act  # ACT_SWIGLU or ACT_SITU
         if codes is not None:
             s.fmt = FMT_MXFP4
             for m in range(3):

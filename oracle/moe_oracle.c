@@ -21,6 +21,8 @@
  *     expert weight: residual VQ with 3 stages of 256-entry codebooks over
  *     8-dimensional vectors.
  *   - OCP Microscaling Formats (MX) v1.0: the E2M1 element and E8M0 scale.
+ *   LazyLoRA README, "File map": K3's SiTU expert activation,
+ *     4 tanh(g/4) sigmoid(g) x 25 tanh(u/25) (the optional second activation).
  * Readings where the pages are silent (SwiGLU with the gate as the SiLU
  * branch, softmax over the selected logits, ties to the lower expert id,
  * nibble order, block direction, RVQ vector orientation) are the ones listed
@@ -246,8 +248,34 @@ void oracle_group(int T, int k, int E, const int32_t *ids, int32_t *counts, int3
 
 static double sigmoid(double z) { return 1.0 / (1.0 + exp(-z)); }
 
-/* One expert on one token: g = Wg x, u = Wu x, h = silu(g) * u with
- * silu(g) = g * sigmoid(g), o = Wd h.  Any output pointer may be NULL. */
+/* The gated activation h = act(g, u) and its partial derivatives.
+ *   SwiGLU (the reading for the configs): h = g sigmoid(g) u.
+ *   SiTU (LazyLoRA README, "File map", the K3 expert activation):
+ *     h = A(g) B(u),  A(g) = 4 tanh(g / 4) sigmoid(g),  B(u) = 25 tanh(u / 25);
+ *     dA/dg = sech^2(g / 4) sigmoid(g) + 4 tanh(g / 4) sigmoid(g) (1 - sigmoid(g)),
+ *     dB/du = sech^2(u / 25). */
+static double act_h(int act, double g, double u)
+{
+    if (act == ORACLE_ACT_SITU) return 4.0 * tanh(g / 4.0) * sigmoid(g) * (25.0 * tanh(u / 25.0));
+    return g * sigmoid(g) * u;
+}
+
+static void act_grad(int act, double g, double u, double *dhdg, double *dhdu)
+{
+    double s = sigmoid(g);
+    if (act == ORACLE_ACT_SITU) {
+        double tg = tanh(g / 4.0), tu = tanh(u / 25.0);
+        *dhdg = ((1.0 - tg * tg) * s + 4.0 * tg * s * (1.0 - s)) * (25.0 * tu);
+        *dhdu = 4.0 * tg * s * (1.0 - tu * tu);
+        return;
+    }
+    *dhdg = u * s * (1.0 + g * (1.0 - s));
+    *dhdu = g * s;
+}
+
+/* One expert on one token: g = Wg x, u = Wu x, h = act(g, u) (SwiGLU:
+ * silu(g) u with silu(g) = g sigmoid(g)), o = Wd h.  Any output pointer may
+ * be NULL. */
 void oracle_expert_forward(const oracle_weights *W, int e, int H, int I, const double *x, double *g_out,
                            double *u_out, double *h_out, double *o_out)
 {
@@ -260,7 +288,7 @@ void oracle_expert_forward(const oracle_weights *W, int e, int H, int I, const d
         for (int i = 0; i < H; i++) g += row[i] * x[i];
         oracle_decode_row(W, ORACLE_MAT_UP, e, H, I, n, row);
         for (int i = 0; i < H; i++) u += row[i] * x[i];
-        h[n] = g * sigmoid(g) * u;
+        h[n] = act_h(W->act, g, u);
         if (g_out) g_out[n] = g;
         if (u_out) u_out[n] = u;
     }
@@ -315,7 +343,8 @@ void oracle_forward(int T, int H, int I, int k, const double *x, const int32_t *
  *   a  = Wd^T dy                (reduces over the down matrix's rows)
  *   dp = <a, h>                 (= <dy, o>, the gradient w.r.t. the weight p)
  *   dh = p a
- *   dg = dh * u * s * (1 + g (1 - s)),  du = dh * g * s,   s = sigmoid(g)
+ *   dg = dh dh/dg,  du = dh dh/du   (SwiGLU: dg = dh u s (1 + g (1 - s)),
+ *                                    du = dh g s, s = sigmoid(g); SiTU: act_grad)
  *   dx = Wg^T dg + Wu^T du      (reduces over the gate/up rows). */
 static void bwd_slot(void *vctx, long s)
 {
@@ -341,10 +370,11 @@ static void bwd_slot(void *vctx, long s)
     c->dp[s] = dp;
     for (int i = 0; i < H; i++) dx[i] = 0.0;
     for (int n = 0; n < I; n++) {
-        double sg = sigmoid(g[n]);
+        double dhdg, dhdu;
+        act_grad(c->W->act, g[n], u[n], &dhdg, &dhdu);
         double dh = p * a[n];
-        double dg = dh * u[n] * sg * (1.0 + g[n] * (1.0 - sg));
-        double du = dh * g[n] * sg;
+        double dg = dh * dhdg;
+        double du = dh * dhdu;
         oracle_decode_row(c->W, ORACLE_MAT_GATE, e, H, I, n, row);
         for (int i = 0; i < H; i++) dx[i] += row[i] * dg;
         oracle_decode_row(c->W, ORACLE_MAT_UP, e, H, I, n, row);

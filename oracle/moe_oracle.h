@@ -15,7 +15,10 @@ typedef struct {
     const uint8_t *scales[3];    /* MXFP4: [E][rows][cols/32] */
     const uint8_t *rvq_idx[3];   /* RVQ3:  [E][3][rows][cols/8] */
     const uint16_t *rvq_cb[3];   /* RVQ3:  [E][3][256][8] fp16 bits */
+    int act;                     /* expert activation: ORACLE_ACT_SWIGLU or ORACLE_ACT_SITU */
 } oracle_weights;
+
+enum { ORACLE_ACT_SWIGLU = 0, ORACLE_ACT_SITU = 1 };
 
 double oracle_e2m1(unsigned code);
 double oracle_e8m0(unsigned b);

@@ -333,7 +333,7 @@ def test_rvq3_residual_sum_of_random_codebooks():
                 assert np.array_equal(D[r, 8 * v: 8 * v + 8], want)
 
 
-def _tiny_layer(E=16, identical=False, seed_family=syn.FAMILY_TINY):
+def _tiny_layer(E=16, identical=False, seed_family=syn.FAMILY_TINY, act=oracle.ACT_SWIGLU):
     w = syn.WORKLOADS["tiny"]
     w = syn.shrink(w, E=E)
     if identical:
@@ -342,7 +342,45 @@ def _tiny_layer(E=16, identical=False, seed_family=syn.FAMILY_TINY):
         scales = [np.repeat(s, E, 0) for s in one_s]
     else:
         codes, scales = syn.mxfp4_layer(w)
-    return w, oracle.Weights(w.H, w.I, codes=codes, scales=scales)
+    return w, oracle.Weights(w.H, w.I, codes=codes, scales=scales, act=act)
+
+
+def _act_probe(act):
+    """h = act(g, u) of the oracle's expert at chosen (g, u): a one-expert selection layer
+    with g_n = x_n and u_n = x_{n+128} (shifts 0 and 128, unit scales), read back as h."""
+    H, I = 256, 128
+    codes, scales = _selection_mxfp4(H, I, 1, (0, 128, 0), (0, 0, [0]))
+    W = oracle.Weights(H, I, codes=codes, scales=scales, act=act)
+
+    def h_of(pairs):
+        x = np.zeros(H)
+        for n, (gv, uv) in enumerate(pairs):
+            x[n], x[n + 128] = gv, uv
+        g, u, h, _ = oracle.expert_forward(W, 0, x)
+        assert np.array_equal(g[: len(pairs)], [p[0] for p in pairs])  # the probe reaches g, u exactly
+        assert np.array_equal(u[: len(pairs)], [p[1] for p in pairs])
+        return h[: len(pairs)]
+    return h_of
+
+
+def test_situ_activation_limits():
+    """SiTU (LazyLoRA README, "File map"): h = A(g) B(u), A(g) = 4 tanh(g/4) sigmoid(g),
+    B(u) = 25 tanh(u/25).  Pinned by limits the definition fixes, not by its formula: zeros;
+    saturation at A = 4 and B = 25 (the outer factors); slopes A(g)/g -> 1/2 and B(u)/u -> 1
+    at 0 (with the saturations they fix the inner scales 1/4 and 1/25); A(g) / (-4 e^g) -> 1
+    as g -> -inf (the sigmoid factor); B odd."""
+    h = _act_probe(oracle.ACT_SITU)
+    v = h([(0.0, 3.0), (2.0, 0.0), (400.0, 4000.0), (1e-6, 4000.0), (400.0, 1e-6), (-40.0, 4000.0),
+           (1.5, 2.5), (1.5, -2.5)])
+    assert v[0] == 0.0 and v[1] == 0.0
+    assert v[2] == 100.0
+    assert abs(v[3] / (25 * 1e-6) - 0.5) < 1e-6
+    assert abs(v[4] / (4 * 1e-6) - 1.0) < 1e-9
+    assert abs(v[5] / (25 * -4 * math.exp(-40.0)) - 1.0) < 1e-8
+    assert v[6] == -v[7] and v[6] > 0
+    # SwiGLU through the same probe: g sigmoid(g) u at a point, and its slope 1/2 at g = 0
+    s = _act_probe(oracle.ACT_SWIGLU)([(1e-6, 1.0), (400.0, 2.0)])
+    assert abs(s[0] / 1e-6 - 0.5) < 1e-6 and s[1] == 800.0
 
 
 def test_k1_single_expert_is_textbook_swiglu_mlp():
@@ -387,12 +425,13 @@ def _loss(x, dy, wr, bias, k, W):
     return float(np.sum(dy * y)), ids
 
 
-@pytest.mark.parametrize("with_bias", [False, True])
-def test_backward_matches_central_finite_differences(with_bias):
+@pytest.mark.parametrize("with_bias,act", [(False, 0), (True, 0), (False, 1)])
+def test_backward_matches_central_finite_differences(with_bias, act):
     """Directional derivatives of L(x) = sum_t <dY_t, y_t(x)> by central differences in fp64,
     with a step relative to the tensor norm and routing-flip detection (a direction whose
-    perturbation changes any token's expert set is retried with half the step)."""
-    w, W = _tiny_layer()
+    perturbation changes any token's expert set is retried with half the step); SwiGLU and
+    SiTU experts."""
+    w, W = _tiny_layer(act=act)
     x = oracle.to_f64(syn.activations(w), "f32")
     wr = syn.router_weight(w)
     bias = np.linspace(-0.3, 0.3, w.E).astype(np.float32) if with_bias else None

@@ -265,8 +265,9 @@ static void act_grad(int act, double g, double u, double *dhdg, double *dhdu)
     double s = sigmoid(g);
     if (act == ORACLE_ACT_SITU) {
         double tg = tanh(g / 4.0), tu = tanh(u / 25.0);
-        *dhdg = ((1.0 - tg * tg) * s + 4.0 * tg * s * (1.0 - s)) * (25.0 * tu);
-        *dhdu = 4.0 * tg * s * (1.0 - tu * tu);
+        double cg = cosh(g / 4.0), cu = cosh(u / 25.0);  /* sech^2 = 1 / cosh^2 */
+        *dhdg = (s / (cg * cg) + 4.0 * tg * s * (1.0 - s)) * (25.0 * tu);
+        *dhdu = 4.0 * tg * s / (cu * cu);
         return;
     }
     *dhdg = u * s * (1.0 + g * (1.0 - s));

@@ -59,7 +59,11 @@ typedef enum {
 
 typedef enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1 } moe_dtype;
 typedef enum { MOE_W_MXFP4 = 0, MOE_W_RVQ3 = 1 } moe_wfmt;
-typedef enum { MOE_ACT_SWIGLU = 0 } moe_act;
+typedef enum {
+    MOE_ACT_SWIGLU = 0,  /* h = silu(g) * u = g sigmoid(g) u (the configs' activation) */
+    MOE_ACT_SITU = 1     /* h = 4 tanh(g/4) sigmoid(g) * 25 tanh(u/25): K3's SiTU (LazyLoRA README,
+                            "File map", core/situ_activation.py) */
+} moe_act;
 
 /* flags */
 enum {
@@ -79,7 +83,7 @@ typedef struct {
     int32_t top_k;       /* k: experts per token (K3: 16); 1..min(E, 64) */
     int32_t max_tokens;  /* largest T any call on this layer will pass; sizes the workspace */
     int32_t wfmt;        /* moe_wfmt */
-    int32_t act;         /* moe_act (SwiGLU: h = silu(gate) * up) */
+    int32_t act;         /* moe_act: the gated activation h = act(gate, up) */
     int32_t bias_mode;   /* 0: no router bias; 1: bias added to the logits (selection and weights) */
     uint32_t flags;
 } moe_desc;

@@ -88,7 +88,8 @@ class MoELayer:
 
     def __init__(self, *, hidden: int, inter: int, n_experts: int, top_k: int, max_tokens: int, router_w,
                  router_b=None, codes: Optional[Sequence] = None, scales: Optional[Sequence] = None,
-                 rvq_idx: Optional[Sequence] = None, rvq_cb: Optional[Sequence] = None, flags: int = 0):
+                 rvq_idx: Optional[Sequence] = None, rvq_cb: Optional[Sequence] = None, flags: int = 0,
+                 act: int = 0):
         torch = _torch()
         L = C.lib()
         d = C.MoeDesc()
@@ -97,6 +98,7 @@ class MoELayer:
         d.wfmt = C.MOE_W_MXFP4 if codes is not None else C.MOE_W_RVQ3
         d.bias_mode = 1 if router_b is not None else 0
         d.flags |= flags
+        d.act = act
         self.desc = d
         self.H, self.I, self.E, self.k, self.max_tokens = hidden, inter, n_experts, top_k, max_tokens
         self.device = router_w.device

@@ -11,6 +11,7 @@ MOE_DT_F32, MOE_DT_BF16 = 0, 1
 MOE_W_MXFP4, MOE_W_RVQ3 = 0, 1
 MOE_ACT_SWIGLU = 0
 MOE_F_DETERMINISTIC = 1
+MOE_ACT_SWIGLU, MOE_ACT_SITU = 0, 1
 MOE_F_MX_GATEUP = 2
 
 EXPORTED = (

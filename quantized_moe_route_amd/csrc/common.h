@@ -180,6 +180,46 @@ __device__ __forceinline__ float wave_max_f32(float v)
 
 __device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
 
+// The gated activation of the experts, h = act(g, u) (values match the API's moe_act):
+//   SwiGLU: h = g sigmoid(g) u;
+//   SiTU (LazyLoRA README, "File map"): h = A(g) B(u), A(g) = 4 tanh(g/4) sigmoid(g),
+//   B(u) = 25 tanh(u/25).
+enum { ACT_SWIGLU = 0, ACT_SITU = 1 };
+
+__device__ __forceinline__ float act_h(int act, float g, float u)
+{
+    if (act == ACT_SITU) return 4.f * tanhf(0.25f * g) * sigmoidf_(g) * (25.f * tanhf(u * (1.f / 25.f)));
+    return g * sigmoidf_(g) * u;
+}
+
+// sech^2(z) = 4 e / (1 + e)^2 with e = exp(-2 |z|): no cancellation where tanh(z) nears 1
+// (1 - tanh^2 in fp32 would lose ~eps / sech^2 relative accuracy there).
+__device__ __forceinline__ float sech2f_(float z)
+{
+    const float e = __expf(-2.f * fabsf(z)), d = 1.f + e;
+    return 4.f * e / (d * d);
+}
+
+// h and its partial derivatives: SwiGLU dh/dg = u s (1 + g (1 - s)), dh/du = g s (s = sigmoid(g));
+// SiTU dh/dg = (sech^2(g/4) s + 4 tanh(g/4) s (1 - s)) B(u), dh/du = A(g) sech^2(u/25).
+__device__ __forceinline__ void act_grad(int act, float g, float u, float &h, float &dhdg, float &dhdu)
+{
+    const float s = sigmoidf_(g);
+    if (act == ACT_SITU) {
+        const float zg = 0.25f * g, zu = u * (1.f / 25.f);
+        const float tg = tanhf(zg), tu = tanhf(zu);
+        const float A = 4.f * tg * s, B = 25.f * tu;
+        h = A * B;
+        dhdg = (sech2f_(zg) * s + 4.f * tg * s * (1.f - s)) * B;
+        dhdu = A * sech2f_(zu);
+        return;
+    }
+    const float silu = g * s;
+    h = silu * u;
+    dhdg = u * s * (1.f + g * (1.f - s));
+    dhdu = silu;
+}
+
 // Exclusive scan of one int per thread over the block (scr: blockDim.x ints of LDS);
 // returns the total in *total.  Called by every thread of the block.
 __device__ __forceinline__ int block_exclusive_scan(int v, int *scr, int *total)

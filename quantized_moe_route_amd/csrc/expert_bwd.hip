@@ -7,7 +7,7 @@
 // the transposed product needed for it).  Per slot (t, j, e) with weight p:
 //   a  = Wd^T dy_t                  (reduction over the down matrix's rows)
 //   dp = <a, h>                     (gradient of the combine w.r.t. p)
-//   dh = p a,  dg = dh u s (1 + g (1 - s)),  du = dh g s,   s = sigmoid(g)
+//   dh = p a,  dg = dh dact/dg,  du = dh dact/du   (act_grad: SwiGLU or SiTU)
 //   dx_tj = Wg^T dg + Wu^T du       (reduction over the gate/up rows)
 //   dX_t = sum_j dx_tj + sum_j p_tj (dp_tj - sum_j' p_tj' dp_tj') Wr[e_j]
 // The block scales of the stored matrices run along the forward reduction
@@ -129,7 +129,7 @@ __device__ __forceinline__ void tile_mma(f32x4 (&acc)[NTT], const uint16_t *wt_h
     }
 }
 
-// a = Wd^T dy for the block's 64 columns of I, then the SwiGLU backward.
+// a = Wd^T dy for the block's 64 columns of I, then the activation backward.
 template <int WFMT, int DYT, int NTT>
 __global__ __launch_bounds__(256) void k_bwd_down(const ExpertBwdArgs a)
 {
@@ -176,12 +176,13 @@ __global__ __launch_bounds__(256) void k_bwd_down(const ExpertBwdArgs a)
                     const int c = c0 + cw + 4 * g + r;
                     if (c < I) {
                         const float gv = a.gu[(rr * 2) * I + c], uv = a.gu[(rr * 2 + 1) * I + c];
-                        const float sg = sigmoidf_(gv), silu = gv * sg;
+                        float hv, dhdg, dhdu;
+                        act_grad(a.act, gv, uv, hv, dhdg, dhdu);
                         const float av = acc[tt][r];
-                        dpp += av * (silu * uv);
+                        dpp += av * hv;
                         const float dh = p * av;
-                        a.dgdu[(rr * 2) * I + c] = dh * uv * sg * (1.f + gv * (1.f - sg));
-                        a.dgdu[(rr * 2 + 1) * I + c] = dh * silu;
+                        a.dgdu[(rr * 2) * I + c] = dh * dhdg;
+                        a.dgdu[(rr * 2 + 1) * I + c] = dh * dhdu;
                     }
                 }
             }
@@ -344,6 +345,7 @@ hipError_t launch_expert_backward(const ExpertBwdArgs &a0, hipStream_t s)
         f.h_hi = a.h_hi;
         f.h_lo = a.h_lo;
         f.gu = a.gu_scratch;
+        f.act = a.act;
         f.xq = a.xq;
         f.xq_s = a.xq_s;
         f.prof = a.prof;

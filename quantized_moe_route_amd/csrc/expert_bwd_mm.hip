@@ -3,7 +3,7 @@
 // The two transposed products of the expert backward (LazyLoRA README, "Routed experts":
 // the experts are streamed again in the backward to form the gradient with respect to
 // the latent input; "File map": the native kernel supplies the transposed product):
-//   k_bwd_down_mm    a = Wd^T dy per slot, then the SwiGLU backward;
+//   k_bwd_down_mm    a = Wd^T dy per slot, then the activation backward;
 //   k_bwd_gateup_mm  dxs = Wg^T dg + Wu^T du per slot.
 // Both have the form out[m][token] = sum_k W[k][m] B[token][k] with the stored matrix
 // W [K rows][M cols] packed along M, so the MX block scales run along M and the reduction
@@ -253,11 +253,12 @@ __device__ __forceinline__ void bwd_down_pass(const ExpertBwdArgs &a, const BtBl
 #pragma unroll
             for (int r = 0; r < 4; r++) {
                 const float av = acc[t][tt][r];
-                const float sg = sigmoidf_(gg[r]), silu = gg[r] * sg;
-                dpp += av * (silu * uu[r]);
+                float hv, dhdg, dhdu;
+                act_grad(a.act, gg[r], uu[r], hv, dhdg, dhdu);
+                dpp += av * hv;
                 const float dh = p * av;
-                split_bf16(dh * uu[r] * sg * (1.f + gg[r] * (1.f - sg)), dh_[r], dl_[r]);
-                split_bf16(dh * silu, uh_[r], ul_[r]);
+                split_bf16(dh * dhdg, dh_[r], dl_[r]);
+                split_bf16(dh * dhdu, uh_[r], ul_[r]);
             }
             if (ok) {
                 const size_t o = rr * 2 * I + m;

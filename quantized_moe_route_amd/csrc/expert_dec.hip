@@ -146,7 +146,7 @@ __device__ __forceinline__ void stage_rows(uint16_t *dst, const uint16_t *src, O
 
 }  // namespace
 
-// gate/up + SwiGLU.  Block = 4 waves x 16 rows = 64 I-columns of one active expert
+// gate/up + activation.  Block = 4 waves x 16 rows = 64 I-columns of one active expert
 // (blockIdx.y indexes the active list); all of the expert's tokens (<= nl_x) in one
 // 16-column MFMA tile.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_gateup_dec(const ExpertFwdArgs a)
@@ -210,7 +210,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         const int n = row0 + 4 * g;
         uint32_t hh[4], hl[4];
 #pragma unroll
-        for (int r = 0; r < 4; r++) split_bf16(accg[r] * sigmoidf_(accg[r]) * accu[r], hh[r], hl[r]);
+        for (int r = 0; r < 4; r++) split_bf16(act_h(a.act, accg[r], accu[r]), hh[r], hl[r]);
         *(u32x2 *)(a.h_hi + rr * I + n) = u32x2{pack2(hh[0], hh[1]), pack2(hh[2], hh[3])};
         *(u32x2 *)(a.h_lo + rr * I + n) = u32x2{pack2(hl[0], hl[1]), pack2(hl[2], hl[3])};
         if (a.gu) {

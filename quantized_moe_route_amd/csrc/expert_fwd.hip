@@ -1,10 +1,11 @@
-// expert_fwd.hip -- routed-expert forward: fused dequant + gate/up + SwiGLU,
+// expert_fwd.hip -- routed-expert forward: fused dequant + gate/up + gated activation,
 // down projection with the routing weight, and a fixed-order combine.
 //
 // Per routed slot (t, j) with expert e and weight p (LazyLoRA README, "The
 // engine" / "Arithmetic": MXFP4 experts consumed packed, fused decode-and-dot,
 // fp32 accumulation; "File map": the combine uses the routing weights):
-//   g = Wg x_t,  u = Wu x_t,  h = silu(g) * u,  o = Wd h,  y_t = sum_j p_tj o_tj.
+//   g = Wg x_t,  u = Wu x_t,  h = act(g, u),  o = Wd h,  y_t = sum_j p_tj o_tj,
+//   act = SwiGLU silu(g) u, or SiTU (act_h).
 // The quantized weights are dequantized in registers straight from HBM (each
 // active expert's bytes are read once per token tile) and fed to bf16 MFMA
 // with fp32 accumulation.  MXFP4 dequantizes exactly to bf16; bf16 tokens are
@@ -145,7 +146,7 @@ void k_gateup(const ExpertFwdArgs a)
 #pragma unroll
             for (int r = 0; r < 4; r++) {
                 const float gv = accg[tt][r], uv = accu[tt][r];
-                split_bf16(gv * sigmoidf_(gv) * uv, hh[r], hl[r]);
+                split_bf16(act_h(a.act, gv, uv), hh[r], hl[r]);
             }
             const size_t o = rr * I + n0 + 4 * g;
             *(u32x2 *)(a.h_hi + o) = u32x2{pack2(hh[0], hh[1]), pack2(hh[2], hh[3])};
@@ -390,7 +391,7 @@ static hipError_t gateup_only(const ExpertFwdArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
-// gate/up + SwiGLU only (the backward recomputes g and u when they were not saved)
+// gate/up + activation only (the backward recomputes g and u when they were not saved)
 hipError_t launch_gateup_only(const ExpertFwdArgs &a, hipStream_t s)
 {
     if (use_mm(a)) return launch_gateup_mm(a, s);

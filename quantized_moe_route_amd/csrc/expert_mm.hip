@@ -183,7 +183,7 @@ __global__ __launch_bounds__(256) void k_x_terms(const uint16_t *__restrict__ x,
     *(uint16_t *)(xs + 2 * i) = (uint16_t)(eb[0] | (eb[1] << 8));
 }
 
-// ---------------------------------------------------------------- gate/up + SwiGLU
+// ---------------------------------------------------------------- gate/up + activation
 //
 // K-step 128: lane group g = lane / 16 owns reduction indices [32g, 32g + 32) of the
 // step, one MX scale block = 16 code bytes; sub-step s takes indices 32g + 8s + 0..7
@@ -276,7 +276,7 @@ __device__ __forceinline__ void gateup_pass(const ExpertFwdArgs &a, const GuBloc
             const f32x4 gv = acc[t][tt], uv = acc[t + 2][tt];
             uint32_t hh[4], hl[4];
 #pragma unroll
-            for (int r = 0; r < 4; r++) split_bf16(gv[r] * sigmoidf_(gv[r]) * uv[r], hh[r], hl[r]);
+            for (int r = 0; r < 4; r++) split_bf16(act_h(a.act, gv[r], uv[r]), hh[r], hl[r]);
             const int n = b.c0 + 16 * t + 4 * g;
             *(u32x2 *)(a.h_hi + rr * I + n) = u32x2{pack2(hh[0], hh[1]), pack2(hh[2], hh[3])};
             *(u32x2 *)(a.h_lo + rr * I + n) = u32x2{pack2(hl[0], hl[1]), pack2(hl[2], hl[3])};
@@ -321,7 +321,7 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mm(const ExpertFwdArgs a)
     }
 }
 
-// ---------------------------------------------------------------- block-scaled gate/up + SwiGLU
+// ---------------------------------------------------------------- block-scaled gate/up + activation
 //
 // Same blocking as k_gateup_mm, on v_mfma_scale_f32_16x16x128_f8f6f4: the weight tile
 // enters as its FP4 codes with their E8M0 scale (A operand; lane group g holds the
@@ -438,7 +438,7 @@ __device__ __forceinline__ void gateup_pass_mx(const ExpertFwdArgs &a, const GuB
             const f32x4 gv = acc[t][tt], uv = acc[t + 2][tt];
             uint32_t hh[4], hl[4];
 #pragma unroll
-            for (int r = 0; r < 4; r++) split_bf16(gv[r] * sigmoidf_(gv[r]) * uv[r], hh[r], hl[r]);
+            for (int r = 0; r < 4; r++) split_bf16(act_h(a.act, gv[r], uv[r]), hh[r], hl[r]);
             const int n = b.c0 + 16 * t + 4 * g;
             *(u32x2 *)(a.h_hi + rr * I + n) = u32x2{pack2(hh[0], hh[1]), pack2(hh[2], hh[3])};
             *(u32x2 *)(a.h_lo + rr * I + n) = u32x2{pack2(hl[0], hl[1]), pack2(hl[2], hl[3])};

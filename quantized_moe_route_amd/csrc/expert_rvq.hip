@@ -105,7 +105,7 @@ __device__ __forceinline__ void token_max(float (&m)[kRvqTok], float *red, float
 
 }  // namespace
 
-// gate/up + SwiGLU.  Block = 4 waves x 16 rows = 64 I-columns of one active expert, gate
+// gate/up + activation.  Block = 4 waves x 16 rows = 64 I-columns of one active expert, gate
 // and up tiles per wave.  Dynamic LDS: codebooks (2 x 12 KB), x rows [4][H + 8] fp16.
 __global__ __launch_bounds__(256) void k_gateup_rvq(const ExpertFwdArgs a)
 {
@@ -211,7 +211,7 @@ __global__ __launch_bounds__(256) void k_gateup_rvq(const ExpertFwdArgs a)
             for (int r = 0; r < 4; r++) {
                 gv[r] = ldexpf(accg[r], se);
                 uv[r] = ldexpf(accu[r], se);
-                split_bf16(gv[r] * sigmoidf_(gv[r]) * uv[r], hh[r], hl[r]);
+                split_bf16(act_h(a.act, gv[r], uv[r]), hh[r], hl[r]);
             }
             *(u32x2 *)(a.h_hi + rr * I + n) = u32x2{pack2(hh[0], hh[1]), pack2(hh[2], hh[3])};
             *(u32x2 *)(a.h_lo + rr * I + n) = u32x2{pack2(hl[0], hl[1]), pack2(hl[2], hl[3])};

@@ -78,7 +78,8 @@ moe_status check_desc(const moe_desc *d)
     if ((long long)d->max_tokens * d->top_k > (1LL << 30))
         return fail(MOE_ERR_INVALID_ARG, "max_tokens*top_k exceeds 2^30");
     if (d->wfmt != MOE_W_MXFP4 && d->wfmt != MOE_W_RVQ3) return fail(MOE_ERR_INVALID_ARG, "unknown wfmt %d", d->wfmt);
-    if (d->act != MOE_ACT_SWIGLU) return fail(MOE_ERR_UNSUPPORTED, "activation %d is not implemented", d->act);
+    if (d->act != MOE_ACT_SWIGLU && d->act != MOE_ACT_SITU)
+        return fail(MOE_ERR_UNSUPPORTED, "activation %d is not implemented", d->act);
     if (d->bias_mode != 0 && d->bias_mode != 1)
         return fail(MOE_ERR_UNSUPPORTED, "bias_mode %d is not implemented", d->bias_mode);
     return MOE_OK;
@@ -302,6 +303,7 @@ moe_status moe_forward(moe_layer *L, const void *x, int32_t xt, int32_t T, const
     a.gu = saved_gu;
     a.ybuf = (float *)(L->ws + L->lay.ybuf);
     a.y = y;
+    a.act = L->d.act;
     if (L->d.flags & MOE_F_MX_GATEUP) {
         a.xq = (uint8_t *)(L->ws + L->lay.xq);
         a.xq_s = (uint8_t *)(L->ws + L->lay.xqs);
@@ -355,6 +357,7 @@ moe_status moe_backward_input(moe_layer *L, const void *x, int32_t xt, const voi
     a.dp_part = (float *)(L->ws + L->lay.dp);
     a.dxs = (float *)(L->ws + L->lay.ybuf);
     a.dx = dx;
+    a.act = L->d.act;
     if (L->d.flags & MOE_F_MX_GATEUP) {
         a.xq = (uint8_t *)(L->ws + L->lay.xq);
         a.xq_s = (uint8_t *)(L->ws + L->lay.xqs);

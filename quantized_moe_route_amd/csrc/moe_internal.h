@@ -88,11 +88,12 @@ struct ExpertFwdArgs {
     int T, H, I, E, k;
     const int32_t *offsets, *perm, *active, *n_active;
     const float *w;      // routing weights [T][k]
-    uint16_t *h_hi;      // [S][I] grouped rows: h = silu(g) * u as bf16 hi ...
+    uint16_t *h_hi;      // [S][I] grouped rows: h = act(g, u) as bf16 hi ...
     uint16_t *h_lo;      // ... + lo (h - hi rounded to bf16)
     float *gu;           // [S][2][I] grouped rows (g, u) or null
     float *ybuf;         // [S][H] slot rows: w * expert output
     float *y;            // [T][H]
+    int act;             // ACT_SWIGLU or ACT_SITU
     uint8_t *xq;         // [T][2H] x as two E4M3 terms for the block-scaled gate/up (grouped-GEMM
     uint8_t *xq_s;       // path; null: bf16 path) and [T][H/32][2] their E8M0 block scales
     int nl_x;            // experts with at most this many tokens stage their x rows in LDS
@@ -120,6 +121,7 @@ struct ExpertBwdArgs {
     float *dxs;          // [S][H] slot rows
     float *dx;           // [T][H]
     uint8_t *xq, *xq_s;  // x terms for the gate/up recomputation (as in ExpertFwdArgs)
+    int act;             // ACT_SWIGLU or ACT_SITU
 };
 
 // Token rows staged in LDS by the few-token (decode) expert kernels: at most 16 rows

@@ -28,6 +28,7 @@ class HostCase:
     scales: Optional[List[np.ndarray]] = None
     idx: Optional[List[np.ndarray]] = None
     cb: Optional[List[np.ndarray]] = None
+    act: int = 0  # 0 SwiGLU, 1 SiTU
 
     @property
     def x64(self):
@@ -39,8 +40,8 @@ class HostCase:
 
     def oracle_weights(self):
         if self.codes is not None:
-            return oracle.Weights(self.w.H, self.w.I, codes=self.codes, scales=self.scales)
-        return oracle.Weights(self.w.H, self.w.I, idx=self.idx, cb=self.cb)
+            return oracle.Weights(self.w.H, self.w.I, codes=self.codes, scales=self.scales, act=self.act)
+        return oracle.Weights(self.w.H, self.w.I, idx=self.idx, cb=self.cb, act=self.act)
 
 
 def host_case(w: syn.Workload, T: Optional[int] = None, with_dy: Optional[bool] = None) -> HostCase:
@@ -63,7 +64,8 @@ def device_layer(c: HostCase, max_tokens: int, flags: int = 0):
     import quantized_moe_route_amd as q
     w = c.w
     kw = dict(hidden=w.H, inter=w.I, n_experts=w.E, top_k=w.k, max_tokens=max_tokens,
-              router_w=q.to_device(c.wr), router_b=None if c.bias is None else q.to_device(c.bias), flags=flags)
+              router_w=q.to_device(c.wr), router_b=None if c.bias is None else q.to_device(c.bias), flags=flags,
+              act=c.act)
     if c.codes is not None:
         kw["codes"] = [q.to_device(a) for a in c.codes]
         kw["scales"] = [q.to_device(a) for a in c.scales]

@@ -53,7 +53,10 @@ def test_workspace_size_and_desc_validation():
     assert L.moe_workspace_size(ctypes.byref(_desc(max_tokens=64)), ctypes.byref(n)) == C.MOE_OK
     assert n.value > small
     bad = [dict(hidden=100), dict(inter=0), dict(n_experts=0), dict(n_experts=5000), dict(top_k=0),
-           dict(top_k=65), dict(n_experts=8, top_k=9), dict(max_tokens=-1), dict(wfmt=7), dict(bias_mode=3)]
+           dict(top_k=65), dict(n_experts=8, top_k=9), dict(max_tokens=-1), dict(wfmt=7), dict(bias_mode=3),
+           dict(act=2), dict(act=-1)]
+    for act in (C.MOE_ACT_SWIGLU, C.MOE_ACT_SITU):
+        assert L.moe_workspace_size(ctypes.byref(_desc(act=act)), ctypes.byref(n)) == C.MOE_OK
     for kw in bad:
         st = L.moe_workspace_size(ctypes.byref(_desc(**kw)), ctypes.byref(n))
         assert st in (C.MOE_ERR_INVALID_ARG, C.MOE_ERR_UNSUPPORTED), kw

@@ -153,6 +153,52 @@ def test_block_scaled_gateup_wide_x_range_deviation():
     assert max(errs["mx"]) < 1e-2
 
 
+def _scale_x(c, e):
+    """Multiply every activation by 2^e (exact for bf16 bits and fp32)."""
+    if c.w.x_dtype == "bf16":
+        f = (c.x.astype(np.uint32) << 16).view(np.float32) * np.float32(2.0**e)
+        c.x = (f.view(np.uint32) >> 16).astype(np.uint16)
+    else:
+        c.x = (c.x * np.float32(2.0**e)).astype(np.float32)
+
+
+SITU_CASES = {
+    # name: (workload overrides, x scale exponent, flags): the generic kernels (fp32 x), the
+    # single-token and few-token stream kernels, the grouped GEMMs with their backward, the
+    # block-scaled gate/up, the RVQ3 gather kernels; x scaled so that g/4 and u/25 reach the
+    # bent parts of both tanh branches.  The SiTU derivatives sech^2(g/4) and s (1 - s) change
+    # by a relative amount of the order of the ABSOLUTE error of g, so dX's relative error
+    # grows like max|g| times the precision x enters the products with: exact for bf16 x on
+    # the bf16 paths, about 2^-17 for fp32 x (two bf16 terms) and for the two E4M3 terms of
+    # the block-scaled gate/up.  Those two paths take 2^3 (max|g| about 75 to 110, dX error about
+    # 3e-5); at 2^5 (max|g| about 255 to 390) they reach 1.1e-4 to 1.3e-4.
+    "generic": (dict(T=37, with_dy=True), 3, 0),
+    "dec-T1": (dict(T=1, H=1024, I=256, E=16, k=8, x_dtype="bf16"), 5, 0),
+    "dec-few": (dict(T=6, H=512, I=768, E=12, k=3, x_dtype="bf16", with_dy=True), 5, 0),
+    "mm": (dict(T=400, H=512, I=1024, E=8, k=2, x_dtype="bf16", with_dy=True), 5, 0),
+    "mm-mx": (dict(T=400, H=512, I=1024, E=8, k=2, x_dtype="bf16"), 3, 2),
+}
+
+
+@pytest.mark.parametrize("case", sorted(SITU_CASES))
+def test_situ_activation_paths(case):
+    """SiTU experts (MOE_ACT_SITU) through every forward and backward kernel family."""
+    over, e, flags = SITU_CASES[case]
+    w = syn.shrink(TINY, x_key=30, **over)
+    c = host_case(w)
+    c.act = 1
+    _scale_x(c, e)
+    run_small(c, name=f"situ-{case}", flags=flags)
+
+
+def test_situ_activation_rvq3():
+    w = syn.shrink(syn.WORKLOADS["rvq16"], T=24, H=256, I=128, E=12, k=3, with_dy=True, x_key=31)
+    c = host_case(w)
+    c.act = 1
+    _scale_x(c, 6)
+    run_small(c, name="situ-rvq3")
+
+
 def test_decode_path_few_tokens():
     # MXFP4, bf16 x, T <= 16 with every token row fitting the LDS stage selects the
     # few-token stream kernels; I = 768 is not a multiple of the 4-step unroll

@@ -28,6 +28,7 @@ ENTROPY = 20260909
 _T_X, _T_WR, _T_BIAS, _T_DY = 1, 2, 3, 4
 _T_CODES, _T_SCALES = 10, 20          # + matrix index (0 gate, 1 up, 2 down)
 _T_RVQ_IDX, _T_RVQ_CB = 30, 40        # + matrix index
+_T_LORA_A, _T_LORA_B = 50, 60         # + matrix index
 
 # family ids: the K3-shaped MXFP4 layer is shared by the three MXFP4 K3 workloads
 FAMILY_TINY, FAMILY_K3_MXFP4, FAMILY_K3_RVQ = 1, 2, 4
@@ -167,6 +168,22 @@ def rvq3_layer(w: Workload, experts=None):
         idxs.append(ia)
         cbs.append(ca)
     return idxs, cbs
+
+
+def lora_adapter(w: Workload, r: int = 16, b_sd: float = 0.05):
+    """The layer's shared low-rank adapter as fp32 arrays: A[m] [r][in] ~ N(0, 1/in) (the
+    scale of a freshly initialised A, so A z has unit-order entries for unit-order z) and
+    B[m] [out][r] ~ N(0, b_sd^2) (nonzero, as after some training steps; a fresh B is 0),
+    for m = gate, up, down (in = H, H, I; out = I, I, H).  Rank 16 is the LazyLoRA
+    README's ("LoRA")."""
+    A, B = [], []
+    for mat in range(3):
+        rows, cols = matrix_shape(mat, w.H, w.I)
+        A.append((_rng(w.family, _T_LORA_A + mat, r).standard_normal((r, cols), dtype=np.float32)
+                  * np.float32(1.0 / np.sqrt(cols))).astype(np.float32))
+        B.append((_rng(w.family, _T_LORA_B + mat, r).standard_normal((rows, r), dtype=np.float32)
+                  * np.float32(b_sd)).astype(np.float32))
+    return A, B
 
 
 def shrink(w: Workload, **kw) -> Workload:

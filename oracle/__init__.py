@@ -35,13 +35,21 @@ def build() -> str:
     return _LIB_PATH
 
 
+class _Lora(ctypes.Structure):
+    _fields_ = [("r", ctypes.c_int),
+                ("scale", ctypes.c_double),
+                ("A", ctypes.c_void_p * 3),
+                ("B", ctypes.c_void_p * 3)]
+
+
 class _Weights(ctypes.Structure):
     _fields_ = [("fmt", ctypes.c_int),
                 ("codes", ctypes.c_void_p * 3),
                 ("scales", ctypes.c_void_p * 3),
                 ("rvq_idx", ctypes.c_void_p * 3),
                 ("rvq_cb", ctypes.c_void_p * 3),
-                ("act", ctypes.c_int)]
+                ("act", ctypes.c_int),
+                ("lora", ctypes.POINTER(_Lora))]
 
 ACT_SWIGLU, ACT_SITU = 0, 1
 
@@ -67,6 +75,7 @@ def lib():
         L.oracle_expert_forward.argtypes = [vp, i, i, i, vp, vp, vp, vp, vp]
         L.oracle_forward.argtypes = [i, i, i, i, vp, vp, vp, vp, vp, i]
         L.oracle_backward_input.argtypes = [i, i, i, i, vp, vp, vp, vp, vp, vp, vp, i]
+        L.oracle_lora_grads.argtypes = [i, i, i, i, vp, vp, vp, vp, vp, vp * 3, vp * 3, i]
         _lib = L
     return _lib
 
@@ -94,11 +103,32 @@ class Weights:
     m = 0 gate, 1 up (rows = I, cols = H), 2 down (rows = H, cols = I).
     """
 
-    def __init__(self, H: int, I: int, codes=None, scales=None, idx=None, cb=None, act: int = 0):
+    def __init__(self, H: int, I: int, codes=None, scales=None, idx=None, cb=None, act: int = 0, lora=None):
         self.H, self.I = H, I
         self._keep = []
         s = _Weights()
         s.act = act  # ACT_SWIGLU or ACT_SITU
+        self.lora = None
+        if lora is not None:
+            # lora = (A [gate, up, down], B [gate, up, down], scale); A[m] is [r][in],
+            # B[m] is [out][r]; values widened exactly to float64
+            A, B, scale = lora
+            r = np.asarray(A[0]).shape[0]
+            assert 1 <= r <= 64
+            shapes_a = [(r, H), (r, H), (r, I)]
+            shapes_b = [(I, r), (I, r), (H, r)]
+            ls = _Lora()
+            ls.r, ls.scale = r, float(scale)
+            for m in range(3):
+                a64 = np.ascontiguousarray(np.asarray(A[m], np.float64))
+                b64 = np.ascontiguousarray(np.asarray(B[m], np.float64))
+                assert a64.shape == shapes_a[m] and b64.shape == shapes_b[m], (m, a64.shape, b64.shape)
+                self._keep += [a64, b64]
+                ls.A[m] = a64.ctypes.data
+                ls.B[m] = b64.ctypes.data
+            self._lora_struct = ls
+            s.lora = ctypes.pointer(ls)
+            self.lora = (r, float(scale))
         if codes is not None:
             s.fmt = FMT_MXFP4
             for m in range(3):
@@ -219,6 +249,24 @@ def backward_input(x64, dy64, ids, w, wr, W: Weights, nthreads=None) -> np.ndarr
     lib().oracle_backward_input(T, W.H, W.I, k, _p(x64), _p(dy64), _p(ids), _p(w), _p(wr64), W.ref(),
                                 _p(dx), nthreads or default_threads())
     return dx
+
+
+def lora_grads(x64, dy64, ids, w, W: Weights, nthreads=None):
+    """Adapter gradients (dA [gate, up, down], dB [gate, up, down]) of sum_t <dy[t], y[t]>."""
+    assert W.lora is not None
+    r = W.lora[0]
+    x64 = np.ascontiguousarray(x64, np.float64)
+    dy64 = np.ascontiguousarray(dy64, np.float64)
+    ids = np.ascontiguousarray(ids, np.int32)
+    w = np.ascontiguousarray(w, np.float64)
+    T, k = ids.shape
+    dA = [np.empty((r, W.H)), np.empty((r, W.H)), np.empty((r, W.I))]
+    dB = [np.empty((W.I, r)), np.empty((W.I, r)), np.empty((W.H, r))]
+    vp3 = ctypes.c_void_p * 3
+    lib().oracle_lora_grads(T, W.H, W.I, k, _p(x64), _p(dy64), _p(ids), _p(w), W.ref(),
+                            vp3(*[a.ctypes.data for a in dA]), vp3(*[b.ctypes.data for b in dB]),
+                            nthreads or default_threads())
+    return dA, dB
 
 
 def layer_forward(x64, wr, bias, k, W: Weights, nthreads=None):

@@ -274,33 +274,72 @@ static void act_grad(int act, double g, double u, double *dhdg, double *dhdu)
     *dhdu = g * s;
 }
 
+/* Low-rank adapter (LazyLoRA README, "LoRA": rank 16, alpha 32, one adapter
+ * per layer in the latent space shared by all routed experts, on the expert
+ * gate, up and down projections).  The adapted matrix is W + scale B A with
+ * A [r][in], B [out][r]; the README gives rank and alpha, and the scale is
+ * the usual LoRA alpha / r.  Applied to a vector z it adds scale B (A z),
+ * which is what these two helpers compute. */
+
+/* v = M z for M [r][n] (v has r entries). */
+static void lr_in(int r, int n, const double *M, const double *z, double *v)
+{
+    for (int q = 0; q < r; q++) {
+        double acc = 0.0;
+        for (int i = 0; i < n; i++) acc += M[(size_t)q * n + i] * z[i];
+        v[q] = acc;
+    }
+}
+
+/* Row m of scale B v for B [rows][r]. */
+static double lr_out(int r, double scale, const double *B, int m, const double *v)
+{
+    double acc = 0.0;
+    for (int q = 0; q < r; q++) acc += B[(size_t)m * r + q] * v[q];
+    return scale * acc;
+}
+
 /* One expert on one token: g = Wg x, u = Wu x, h = act(g, u) (SwiGLU:
- * silu(g) u with silu(g) = g sigmoid(g)), o = Wd h.  Any output pointer may
- * be NULL. */
+ * silu(g) u with silu(g) = g sigmoid(g)), o = Wd h; with an adapter each
+ * product W z becomes (W + scale B A) z = W z + scale B (A z).  Any output
+ * pointer may be NULL. */
 void oracle_expert_forward(const oracle_weights *W, int e, int H, int I, const double *x, double *g_out,
                            double *u_out, double *h_out, double *o_out)
 {
+    const oracle_lora *L = W->lora;
     int wmax = H > I ? H : I;
     double *row = (double *)malloc(sizeof(double) * (size_t)wmax);
     double *h = (double *)malloc(sizeof(double) * (size_t)I);
+    double va[64], vu[64], vd[64];
+    if (L) {
+        lr_in(L->r, H, L->A[ORACLE_MAT_GATE], x, va);
+        lr_in(L->r, H, L->A[ORACLE_MAT_UP], x, vu);
+    }
     for (int n = 0; n < I; n++) {
         double g = 0.0, u = 0.0;
         oracle_decode_row(W, ORACLE_MAT_GATE, e, H, I, n, row);
         for (int i = 0; i < H; i++) g += row[i] * x[i];
         oracle_decode_row(W, ORACLE_MAT_UP, e, H, I, n, row);
         for (int i = 0; i < H; i++) u += row[i] * x[i];
+        if (L) {
+            g += lr_out(L->r, L->scale, L->B[ORACLE_MAT_GATE], n, va);
+            u += lr_out(L->r, L->scale, L->B[ORACLE_MAT_UP], n, vu);
+        }
         h[n] = act_h(W->act, g, u);
         if (g_out) g_out[n] = g;
         if (u_out) u_out[n] = u;
     }
     if (h_out) memcpy(h_out, h, sizeof(double) * (size_t)I);
-    if (o_out)
+    if (o_out) {
+        if (L) lr_in(L->r, I, L->A[ORACLE_MAT_DOWN], h, vd);
         for (int m = 0; m < H; m++) {
             double o = 0.0;
             oracle_decode_row(W, ORACLE_MAT_DOWN, e, H, I, m, row);
             for (int n = 0; n < I; n++) o += row[n] * h[n];
+            if (L) o += lr_out(L->r, L->scale, L->B[ORACLE_MAT_DOWN], m, vd);
             o_out[m] = o;
         }
+    }
     free(h);
     free(row);
 }
@@ -313,6 +352,7 @@ typedef struct {
     double *o;      /* [slots][H] forward expert outputs */
     double *dxs;    /* [slots][H] backward per-slot input gradient */
     double *dp;     /* [slots] */
+    double *keep;   /* [slots][3][I]: dL/dg, dL/du and h of each slot, or NULL */
 } slot_ctx;
 
 static void fwd_slot(void *vctx, long s)
@@ -329,7 +369,7 @@ void oracle_forward(int T, int H, int I, int k, const double *x, const int32_t *
 {
     long S = (long)T * k;
     double *o = (double *)malloc(sizeof(double) * (size_t)S * H);
-    slot_ctx c = { W, H, I, k, x, NULL, NULL, w, ids, o, NULL, NULL };
+    slot_ctx c = { W, H, I, k, x, NULL, NULL, w, ids, o, NULL, NULL, NULL };
     parallel_for(S, nthreads, fwd_slot, &c);
     for (int t = 0; t < T; t++)
         for (int m = 0; m < H; m++) {
@@ -346,10 +386,13 @@ void oracle_forward(int T, int H, int I, int k, const double *x, const int32_t *
  *   dh = p a
  *   dg = dh dh/dg,  du = dh dh/du   (SwiGLU: dg = dh u s (1 + g (1 - s)),
  *                                    du = dh g s, s = sigmoid(g); SiTU: act_grad)
- *   dx = Wg^T dg + Wu^T du      (reduces over the gate/up rows). */
+ *   dx = Wg^T dg + Wu^T du      (reduces over the gate/up rows).
+ * With an adapter every W above is W + scale B A, so Wd^T dy gains
+ * scale A_d^T (B_d^T dy) and Wg^T dg gains scale A_g^T (B_g^T dg) (up alike). */
 static void bwd_slot(void *vctx, long s)
 {
     slot_ctx *c = (slot_ctx *)vctx;
+    const oracle_lora *L = c->W->lora;
     int H = c->H, I = c->I, e = c->ids[s];
     long t = s / c->k;
     double p = c->w[s];
@@ -359,12 +402,29 @@ static void bwd_slot(void *vctx, long s)
     double *u = (double *)malloc(sizeof(double) * (size_t)I);
     double *h = (double *)malloc(sizeof(double) * (size_t)I);
     double *a = (double *)calloc((size_t)I, sizeof(double));
+    double *dgv = (double *)malloc(sizeof(double) * (size_t)I);
+    double *duv = (double *)malloc(sizeof(double) * (size_t)I);
     double *row = (double *)malloc(sizeof(double) * (size_t)wmax);
     double *dx = c->dxs + (size_t)s * H;
     oracle_expert_forward(c->W, e, H, I, x, g, u, h, NULL);
     for (int m = 0; m < H; m++) {
         oracle_decode_row(c->W, ORACLE_MAT_DOWN, e, H, I, m, row);
         for (int n = 0; n < I; n++) a[n] += row[n] * dy[m];
+    }
+    if (L) {
+        /* a += scale A_d^T (B_d^T dy) */
+        double bd[64];
+        const double *Bd = L->B[ORACLE_MAT_DOWN], *Ad = L->A[ORACLE_MAT_DOWN];
+        for (int q = 0; q < L->r; q++) {
+            double acc = 0.0;
+            for (int m = 0; m < H; m++) acc += Bd[(size_t)m * L->r + q] * dy[m];
+            bd[q] = acc;
+        }
+        for (int n = 0; n < I; n++) {
+            double acc = 0.0;
+            for (int q = 0; q < L->r; q++) acc += Ad[(size_t)q * I + n] * bd[q];
+            a[n] += L->scale * acc;
+        }
     }
     double dp = 0.0;
     for (int n = 0; n < I; n++) dp += a[n] * h[n];
@@ -376,12 +436,31 @@ static void bwd_slot(void *vctx, long s)
         double dh = p * a[n];
         double dg = dh * dhdg;
         double du = dh * dhdu;
+        dgv[n] = dg;
+        duv[n] = du;
         oracle_decode_row(c->W, ORACLE_MAT_GATE, e, H, I, n, row);
         for (int i = 0; i < H; i++) dx[i] += row[i] * dg;
         oracle_decode_row(c->W, ORACLE_MAT_UP, e, H, I, n, row);
         for (int i = 0; i < H; i++) dx[i] += row[i] * du;
     }
-    free(g); free(u); free(h); free(a); free(row);
+    if (L) {
+        /* dx += scale A_g^T (B_g^T dg) + scale A_u^T (B_u^T du) */
+        for (int mat = ORACLE_MAT_GATE; mat <= ORACLE_MAT_UP; mat++) {
+            const double *B = L->B[mat], *A = L->A[mat], *d = mat == ORACLE_MAT_GATE ? dgv : duv;
+            for (int q = 0; q < L->r; q++) {
+                double m = 0.0;
+                for (int n = 0; n < I; n++) m += B[(size_t)n * L->r + q] * d[n];
+                for (int i = 0; i < H; i++) dx[i] += L->scale * A[(size_t)q * H + i] * m;
+            }
+        }
+    }
+    if (c->keep) {
+        double *kp = c->keep + (size_t)s * 3 * I;
+        memcpy(kp, dgv, sizeof(double) * (size_t)I);
+        memcpy(kp + I, duv, sizeof(double) * (size_t)I);
+        memcpy(kp + 2 * (size_t)I, h, sizeof(double) * (size_t)I);
+    }
+    free(g); free(u); free(h); free(a); free(dgv); free(duv); free(row);
 }
 
 /* dX[t] = sum_j dx_tj + sum_j dl_tj * Wr[e_j], with the router term
@@ -394,7 +473,7 @@ void oracle_backward_input(int T, int H, int I, int k, const double *x, const do
     long S = (long)T * k;
     double *dxs = (double *)malloc(sizeof(double) * (size_t)S * H);
     double *dp = (double *)malloc(sizeof(double) * (size_t)S);
-    slot_ctx c = { W, H, I, k, x, dy, wr, w, ids, NULL, dxs, dp };
+    slot_ctx c = { W, H, I, k, x, dy, wr, w, ids, NULL, dxs, dp, NULL };
     parallel_for(S, nthreads, bwd_slot, &c);
     for (int t = 0; t < T; t++) {
         double pdp = 0.0;
@@ -411,4 +490,71 @@ void oracle_backward_input(int T, int H, int I, int k, const double *x, const do
     }
     free(dxs);
     free(dp);
+}
+
+/* Adapter gradients of L = sum_t <dy[t], y[t]>, y[t] = sum_j p_tj o_tj, routing
+ * held fixed.  Per slot s = (t, j) with dL/dg = dg_s, dL/du = du_s and h_s from
+ * the slot backward:
+ *   g_s = Wg x_t + scale B_g (A_g x_t)  =>  dB_g += scale dg_s (A_g x_t)^T,
+ *                                           dA_g += scale (B_g^T dg_s) x_t^T   (up alike);
+ *   o_s = Wd h_s + scale B_d (A_d h_s) and dL/do_s = p_s dy_t
+ *                                       =>  dB_d += scale p_s dy_t (A_d h_s)^T,
+ *                                           dA_d += scale (B_d^T p_s dy_t) h_s^T.
+ * Slots are summed in slot order. */
+void oracle_lora_grads(int T, int H, int I, int k, const double *x, const double *dy, const int32_t *ids,
+                       const double *w, const oracle_weights *W, double *dA[3], double *dB[3], int nthreads)
+{
+    const oracle_lora *L = W->lora;
+    int r = L->r;
+    double sc = L->scale;
+    long S = (long)T * k;
+    double *dxs = (double *)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1) * H);
+    double *dp = (double *)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1));
+    double *keep = (double *)malloc(sizeof(double) * (size_t)(S > 0 ? S : 1) * 3 * I);
+    slot_ctx c = { W, H, I, k, x, dy, NULL, w, ids, NULL, dxs, dp, keep };
+    parallel_for(S, nthreads, bwd_slot, &c);
+    memset(dA[ORACLE_MAT_GATE], 0, sizeof(double) * (size_t)r * H);
+    memset(dA[ORACLE_MAT_UP], 0, sizeof(double) * (size_t)r * H);
+    memset(dA[ORACLE_MAT_DOWN], 0, sizeof(double) * (size_t)r * I);
+    memset(dB[ORACLE_MAT_GATE], 0, sizeof(double) * (size_t)I * r);
+    memset(dB[ORACLE_MAT_UP], 0, sizeof(double) * (size_t)I * r);
+    memset(dB[ORACLE_MAT_DOWN], 0, sizeof(double) * (size_t)H * r);
+    double v[64], m[64];
+    for (long s = 0; s < S; s++) {
+        long t = s / k;
+        double p = w[s];
+        const double *xt = x + (size_t)t * H, *dyt = dy + (size_t)t * H;
+        const double *ks = keep + (size_t)s * 3 * I;
+        for (int mat = ORACLE_MAT_GATE; mat <= ORACLE_MAT_UP; mat++) {
+            const double *d = ks + (mat == ORACLE_MAT_GATE ? 0 : I);
+            const double *A = L->A[mat], *B = L->B[mat];
+            lr_in(r, H, A, xt, v);                          /* A x_t */
+            for (int q = 0; q < r; q++) {                   /* B^T d */
+                double acc = 0.0;
+                for (int n = 0; n < I; n++) acc += B[(size_t)n * r + q] * d[n];
+                m[q] = acc;
+            }
+            for (int n = 0; n < I; n++)
+                for (int q = 0; q < r; q++) dB[mat][(size_t)n * r + q] += sc * d[n] * v[q];
+            for (int q = 0; q < r; q++)
+                for (int i = 0; i < H; i++) dA[mat][(size_t)q * H + i] += sc * m[q] * xt[i];
+        }
+        {
+            const double *h = ks + 2 * (size_t)I;
+            const double *A = L->A[ORACLE_MAT_DOWN], *B = L->B[ORACLE_MAT_DOWN];
+            lr_in(r, I, A, h, v);                           /* A_d h_s */
+            for (int q = 0; q < r; q++) {                   /* B_d^T (p dy_t) */
+                double acc = 0.0;
+                for (int mm = 0; mm < H; mm++) acc += B[(size_t)mm * r + q] * p * dyt[mm];
+                m[q] = acc;
+            }
+            for (int mm = 0; mm < H; mm++)
+                for (int q = 0; q < r; q++) dB[ORACLE_MAT_DOWN][(size_t)mm * r + q] += sc * p * dyt[mm] * v[q];
+            for (int q = 0; q < r; q++)
+                for (int n = 0; n < I; n++) dA[ORACLE_MAT_DOWN][(size_t)q * I + n] += sc * m[q] * h[n];
+        }
+    }
+    free(dxs);
+    free(dp);
+    free(keep);
 }

@@ -9,6 +9,17 @@
 enum { ORACLE_FMT_MXFP4 = 0, ORACLE_FMT_RVQ3 = 1 };
 enum { ORACLE_MAT_GATE = 0, ORACLE_MAT_UP = 1, ORACLE_MAT_DOWN = 2 };
 
+/* Low-rank adapter shared by every routed expert of the layer (LazyLoRA
+ * README, "LoRA"): each of gate, up and down gets W + scale * B A.
+ * A[gate], A[up]: [r][H]; A[down]: [r][I]; B[gate], B[up]: [I][r];
+ * B[down]: [H][r]; row-major fp64. */
+typedef struct {
+    int r;
+    double scale;
+    const double *A[3];
+    const double *B[3];
+} oracle_lora;
+
 typedef struct {
     int fmt;
     const uint8_t *codes[3];     /* MXFP4: [E][rows][cols/2]  */
@@ -16,6 +27,7 @@ typedef struct {
     const uint8_t *rvq_idx[3];   /* RVQ3:  [E][3][rows][cols/8] */
     const uint16_t *rvq_cb[3];   /* RVQ3:  [E][3][256][8] fp16 bits */
     int act;                     /* expert activation: ORACLE_ACT_SWIGLU or ORACLE_ACT_SITU */
+    const oracle_lora *lora;     /* shared adapter, or NULL */
 } oracle_weights;
 
 enum { ORACLE_ACT_SWIGLU = 0, ORACLE_ACT_SITU = 1 };
@@ -36,4 +48,8 @@ void oracle_forward(int T, int H, int I, int k, const double *x, const int32_t *
                     const oracle_weights *W, double *y, int nthreads);
 void oracle_backward_input(int T, int H, int I, int k, const double *x, const double *dy, const int32_t *ids,
                            const double *w, const double *wr, const oracle_weights *W, double *dx, int nthreads);
+/* Gradients of sum_t <dy[t], y[t]> with respect to the adapter's A and B
+ * (same layouts as oracle_lora), routing held fixed.  W->lora must be set. */
+void oracle_lora_grads(int T, int H, int I, int k, const double *x, const double *dy, const int32_t *ids,
+                       const double *w, const oracle_weights *W, double *dA[3], double *dB[3], int nthreads);
 #endif

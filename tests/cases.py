@@ -29,6 +29,7 @@ class HostCase:
     idx: Optional[List[np.ndarray]] = None
     cb: Optional[List[np.ndarray]] = None
     act: int = 0  # 0 SwiGLU, 1 SiTU
+    lora: Optional[tuple] = None  # (A [3], B [3], scale) fp32 arrays: the shared adapter
 
     @property
     def x64(self):
@@ -40,8 +41,9 @@ class HostCase:
 
     def oracle_weights(self):
         if self.codes is not None:
-            return oracle.Weights(self.w.H, self.w.I, codes=self.codes, scales=self.scales, act=self.act)
-        return oracle.Weights(self.w.H, self.w.I, idx=self.idx, cb=self.cb, act=self.act)
+            return oracle.Weights(self.w.H, self.w.I, codes=self.codes, scales=self.scales, act=self.act,
+                                  lora=self.lora)
+        return oracle.Weights(self.w.H, self.w.I, idx=self.idx, cb=self.cb, act=self.act, lora=self.lora)
 
 
 def host_case(w: syn.Workload, T: Optional[int] = None, with_dy: Optional[bool] = None) -> HostCase:

@@ -333,7 +333,7 @@ def test_rvq3_residual_sum_of_random_codebooks():
                 assert np.array_equal(D[r, 8 * v: 8 * v + 8], want)
 
 
-def _tiny_layer(E=16, identical=False, seed_family=syn.FAMILY_TINY, act=oracle.ACT_SWIGLU):
+def _tiny_layer(E=16, identical=False, seed_family=syn.FAMILY_TINY, act=oracle.ACT_SWIGLU, lora=None):
     w = syn.WORKLOADS["tiny"]
     w = syn.shrink(w, E=E)
     if identical:
@@ -342,7 +342,12 @@ def _tiny_layer(E=16, identical=False, seed_family=syn.FAMILY_TINY, act=oracle.A
         scales = [np.repeat(s, E, 0) for s in one_s]
     else:
         codes, scales = syn.mxfp4_layer(w)
-    return w, oracle.Weights(w.H, w.I, codes=codes, scales=scales, act=act)
+    return w, oracle.Weights(w.H, w.I, codes=codes, scales=scales, act=act, lora=lora)
+
+
+def _tiny_lora(w, r=16, scale=2.0):
+    A, B = syn.lora_adapter(w, r)
+    return (A, B, scale)
 
 
 def _act_probe(act):
@@ -425,13 +430,15 @@ def _loss(x, dy, wr, bias, k, W):
     return float(np.sum(dy * y)), ids
 
 
-@pytest.mark.parametrize("with_bias,act", [(False, 0), (True, 0), (False, 1)])
-def test_backward_matches_central_finite_differences(with_bias, act):
+@pytest.mark.parametrize("with_bias,act,lora", [(False, 0, False), (True, 0, False), (False, 1, False),
+                                                (False, 0, True), (True, 1, True)])
+def test_backward_matches_central_finite_differences(with_bias, act, lora):
     """Directional derivatives of L(x) = sum_t <dY_t, y_t(x)> by central differences in fp64,
     with a step relative to the tensor norm and routing-flip detection (a direction whose
     perturbation changes any token's expert set is retried with half the step); SwiGLU and
-    SiTU experts."""
-    w, W = _tiny_layer(act=act)
+    SiTU experts, with and without the shared adapter."""
+    w0 = syn.WORKLOADS["tiny"]
+    w, W = _tiny_layer(act=act, lora=_tiny_lora(w0) if lora else None)
     x = oracle.to_f64(syn.activations(w), "f32")
     wr = syn.router_weight(w)
     bias = np.linspace(-0.3, 0.3, w.E).astype(np.float32) if with_bias else None
@@ -484,3 +491,104 @@ def test_backward_router_term_by_finite_differences_on_router_logits():
         fd = (lp - lm) / (2 * eps)
         an = float(np.sum(dx * v))
         assert abs(an) > 1e-6 and abs(fd - an) <= 1e-7 * abs(an)
+
+
+# ---------------------------------------------------------------- shared low-rank adapter
+
+
+def _merged_forward(x, ids, p, W, lora, act):
+    """y from dense merged matrices W_e + scale B A (the identity a LoRA adapter merges by),
+    one numpy matmul chain per slot -- a different association from the oracle's
+    W z + scale B (A z)."""
+    A, B, sc = lora
+    T, k = ids.shape
+    y = np.zeros((T, W.H))
+    for t in range(T):
+        for j in range(k):
+            e = ids[t, j]
+            Wg, Wu, Wd = (oracle.decode_matrix(W, m, e) + sc * (B[m].astype(np.float64) @ A[m].astype(np.float64))
+                          for m in range(3))
+            g, u = Wg @ x[t], Wu @ x[t]
+            if act == oracle.ACT_SITU:
+                h = 4 * np.tanh(g / 4) * scipy.special.expit(g) * 25 * np.tanh(u / 25)
+            else:
+                h = g * scipy.special.expit(g) * u
+            y[t] += p[t, j] * (Wd @ h)
+    return y
+
+
+@pytest.mark.parametrize("act", [oracle.ACT_SWIGLU, oracle.ACT_SITU])
+def test_lora_forward_equals_merged_weights(act):
+    w0 = syn.WORKLOADS["tiny"]
+    lora = _tiny_lora(w0)
+    w, W = _tiny_layer(act=act, lora=lora)
+    x = oracle.to_f64(syn.activations(w), "f32")
+    wr = syn.router_weight(w)
+    ids, p, _ = oracle.route(x, wr, None, w.k)
+    y = oracle.forward(x, ids, p, W)
+    ref = _merged_forward(x, ids, p, W, lora, act)
+    assert np.allclose(y, ref, rtol=1e-11, atol=1e-12 * np.abs(ref).max())
+    # the adapter moves the output by much more than the tolerance
+    _, W0 = _tiny_layer(act=act)
+    assert np.abs(oracle.forward(x, ids, p, W0) - y).max() > 1e-2 * np.abs(y).max()
+
+
+def test_lora_with_zero_B_is_the_plain_layer():
+    w0 = syn.WORKLOADS["tiny"]
+    A, B, sc = _tiny_lora(w0)
+    w, W = _tiny_layer(lora=(A, [np.zeros_like(b) for b in B], sc))
+    _, W0 = _tiny_layer()
+    x = oracle.to_f64(syn.activations(w), "f32")
+    dy = oracle.to_f64(syn.upstream_grad(w), "f32")
+    wr = syn.router_weight(w)
+    ids, p, _ = oracle.route(x, wr, None, w.k)
+    assert np.array_equal(oracle.forward(x, ids, p, W), oracle.forward(x, ids, p, W0))
+    assert np.array_equal(oracle.backward_input(x, dy, ids, p, wr, W), oracle.backward_input(x, dy, ids, p, wr, W0))
+    # with B = 0 only dB can be nonzero; dA vanishes identically
+    dA, dB = oracle.lora_grads(x, dy, ids, p, W)
+    assert all(np.all(a == 0) for a in dA) and all(np.abs(b).max() > 0 for b in dB)
+
+
+@pytest.mark.parametrize("act", [oracle.ACT_SWIGLU, oracle.ACT_SITU])
+def test_lora_grads_match_central_finite_differences(act):
+    """Directional derivatives of L = sum_t <dY_t, y_t> with respect to each of the six adapter
+    matrices, routing held fixed (it does not depend on the adapter), by central differences
+    in fp64 on the forward; random directions and single entries."""
+    w0 = syn.shrink(syn.WORKLOADS["tiny"], T=12)
+    A, B, sc = _tiny_lora(w0, r=4)
+    A = [a.astype(np.float64) for a in A]
+    B = [b.astype(np.float64) for b in B]
+    w, W = _tiny_layer(act=act, lora=(A, B, sc))
+    w = syn.shrink(w, T=12)
+    x = oracle.to_f64(syn.activations(w), "f32")
+    dy = oracle.to_f64(syn.upstream_grad(w), "f32") * 100.0
+    wr = syn.router_weight(w)
+    ids, p, _ = oracle.route(x, wr, None, w.k)
+    dA, dB = oracle.lora_grads(x, dy, ids, p, W)
+    codes, scales = syn.mxfp4_layer(w)
+
+    def loss(A_, B_):
+        Wl = oracle.Weights(w.H, w.I, codes=codes, scales=scales, act=act, lora=(A_, B_, sc))
+        return float(np.sum(dy * oracle.forward(x, ids, p, Wl, nthreads=1)))
+
+    rng = np.random.default_rng(5)
+    for which in ("A", "B"):
+        for m in range(3):
+            P = A if which == "A" else B
+            G = (dA if which == "A" else dB)[m]
+            dirs = [rng.standard_normal(P[m].shape) for _ in range(2)]
+            v = np.zeros(P[m].shape)
+            v[-1, 1] = 1.0
+            dirs.append(v)
+            for v in dirs:
+                eps = 1e-5 * np.linalg.norm(P[m]) / np.linalg.norm(v)
+                Pp = [q.copy() for q in P]
+                Pm = [q.copy() for q in P]
+                Pp[m] = P[m] + eps * v
+                Pm[m] = P[m] - eps * v
+                lp = loss(Pp, B) if which == "A" else loss(A, Pp)
+                lm = loss(Pm, B) if which == "A" else loss(A, Pm)
+                fd = (lp - lm) / (2 * eps)
+                an = float(np.sum(G * v))
+                assert abs(fd - an) <= 1e-6 * max(abs(an), 1e-3 * np.linalg.norm(G) * np.linalg.norm(v)), \
+                    (which, m, fd, an)

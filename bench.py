@@ -96,6 +96,8 @@ def main():
     ap.add_argument("--workload", default="decode1", choices=["decode1", "decode64", "rvq16", "train4096"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-plain-read", action="store_true",
+                    help="skip the reference stream (a plain read of the roofline kernel's byte count)")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel family (stderr)")
     ap.add_argument("--calib-copy-mb", type=int, default=0,
                     help="after the run, copy a buffer of this many MB three times (a kernel of known "
@@ -218,6 +220,26 @@ def main():
         roofline = {"bound": "hbm", "kernel": ROOF_KERNEL[w.name][0] + " (dequant + gate/up + SwiGLU)",
                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                     "traffic": traffic}
+    if not train and not args.no_plain_read:
+        # the practical read rate for the roofline kernel's byte count: a plain coalesced
+        # read kernel over the same number of bytes, cold (a different buffer each time)
+        import ctypes
+        nb = (int(gu_bytes) + 15) // 16 * 16
+        bufs = torch.empty((8, nb), dtype=torch.uint8, device="cuda")
+        bufs.fill_(1)
+        torch.cuda.synchronize()
+        t = []
+        for i in range(24):
+            ms_ = ctypes.c_double()
+            C.check(C.lib().moe_prof_hbm_read(bufs[i % 8].data_ptr(), nb, ctypes.c_void_p(
+                torch.cuda.current_stream().cuda_stream), ctypes.byref(ms_)), "moe_prof_hbm_read")
+            t.append(ms_.value)
+        del bufs
+        t_plain = sorted(t[8:])[len(t[8:]) // 2] / 1e3
+        roofline["plain_read"] = {"bytes": nb, "GBps": nb / t_plain / 1e9, "us": t_plain * 1e6,
+                                  "frac": achieved / (nb / t_plain / 1e9)}
+        log(f"plain read of {nb} bytes: {t_plain * 1e6:.1f} us = {nb / t_plain / 1e9:.0f} GB/s; the gate/up kernel "
+            f"reaches {roofline['plain_read']['frac']:.3f} of it")
     if args.breakdown:
         fams = list(range(len(C.PROF_NAMES)))
         L.prof_enable(fams, max_launches=args.steps)

@@ -48,6 +48,15 @@ moe_status moe_prof_enable(moe_layer *L, uint32_t mask, int32_t max_launches);
  * last enable.  Waits for the recorded events (a host synchronization). */
 moe_status moe_prof_read(moe_layer *L, int32_t family, double *total_ms, int32_t *launches);
 
+/* Reference stream: reads `bytes` of the device buffer buf once with a plain coalesced
+ * kernel (16 bytes per lane, 2048 blocks of 256 threads), enqueued on stream, and
+ * returns that kernel's own duration in *ms (waits for it: a host synchronization).  It
+ * gives the practical HBM read rate for a transfer of that size (launch ramp and tail
+ * included), beside the 8 TB/s peak, for judging the expert stream kernels.  buf must
+ * be 16-byte aligned and bytes a nonzero multiple of 16 (else MOE_ERR_INVALID_ARG);
+ * nothing is written.  MOE_ERR_DEVICE if the launch or the events fail. */
+moe_status moe_prof_hbm_read(const void *buf, size_t bytes, void *stream, double *ms);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,7 +17,7 @@ MOE_F_MX_GATEUP = 2
 EXPORTED = (
     "moe_desc_init", "moe_workspace_size", "moe_layer_create", "moe_route", "moe_forward",
     "moe_backward_input", "moe_destroy", "moe_status_string", "moe_last_error",
-    "moe_prof_enable", "moe_prof_read",
+    "moe_prof_enable", "moe_prof_read", "moe_prof_hbm_read",
 )
 
 # kernel families of include/moe_prof.h
@@ -83,6 +83,8 @@ def lib() -> ctypes.CDLL:
         L.moe_prof_enable.restype = st
         L.moe_prof_read.argtypes = [vp, i32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(i32)]
         L.moe_prof_read.restype = st
+        L.moe_prof_hbm_read.argtypes = [vp, ctypes.c_size_t, vp, ctypes.POINTER(ctypes.c_double)]
+        L.moe_prof_hbm_read.restype = st
         _lib = L
     return _lib
 

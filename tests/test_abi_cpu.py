@@ -158,6 +158,11 @@ def test_prof_argument_checks():
     assert L.moe_prof_read(h, 99, ctypes.byref(ms), ctypes.byref(n)) == C.MOE_ERR_INVALID_ARG
     assert L.moe_prof_read(h, 3, ctypes.byref(ms), ctypes.byref(n)) == C.MOE_OK and n.value == 0
     L.moe_destroy(h)
+    # the reference stream checks its buffer before launching anything
+    assert L.moe_prof_hbm_read(None, 1024, None, ctypes.byref(ms)) == C.MOE_ERR_INVALID_ARG
+    assert L.moe_prof_hbm_read(0x1000, 1000, None, ctypes.byref(ms)) == C.MOE_ERR_INVALID_ARG  # not 16-byte sized
+    assert L.moe_prof_hbm_read(0x1008, 1024, None, ctypes.byref(ms)) == C.MOE_ERR_INVALID_ARG  # misaligned
+    assert L.moe_prof_hbm_read(0x1000, 1024, None, None) == C.MOE_ERR_INVALID_ARG
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):

@@ -217,6 +217,22 @@ def test_decode_path_unpacked_planes():
     run_small(host_case(w), name="dec-unpacked")
 
 
+def test_decode_path_single_token_ten_steps():
+    # one token, 16 of 24 experts, ten K-steps per row (not a multiple of the four-step
+    # unroll); with dY the backward recomputes g and u on the few-token kernel
+    w = syn.shrink(TINY, T=1, H=2560, I=2560, E=24, k=16, x_dtype="bf16", with_dy=True, x_key=40)
+    run_small(host_case(w), name="dec-T1-10steps")
+
+
+@pytest.mark.parametrize("T,k,E,bias_sd", [(2, 16, 40, 1.0), (3, 8, 24, 0.0), (4, 8, 32, 0.5)])
+def test_decode_few_tokens_shared_experts(T, k, E, bias_sd):
+    # 2..4 tokens sharing experts (each expert holds 1..T of them), I = 4096: the few-token
+    # kernels while the h rows fit their LDS stage (T = 2), the generic kernels beyond
+    w = syn.shrink(TINY, T=T, H=1024, I=4096, E=E, k=k, x_dtype="bf16", bias_sd=bias_sd, with_dy=True,
+                   x_key=41 + T)
+    run_small(host_case(w), name=f"dec-T{T}-shared")
+
+
 def test_rvq3_small():
     w = syn.shrink(syn.WORKLOADS["rvq16"], T=24, H=256, I=128, E=12, k=3, with_dy=True)
     run_small(host_case(w), name="rvq3-small")

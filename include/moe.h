@@ -68,11 +68,12 @@ typedef enum {
 /* flags */
 enum {
     MOE_F_DETERMINISTIC = 1u, /* combine and gradient reductions in a fixed order (always on in this build) */
-    MOE_F_MX_GATEUP = 2u      /* grouped-GEMM gate/up (MXFP4, bf16 x, many tokens per expert) on the
+    MOE_F_MX_GATEUP = 2u,     /* grouped-GEMM gate/up (MXFP4, bf16 x, many tokens per expert) on the
                                  gfx950 block-scaled MFMA: weights enter as FP4 codes with their E8M0
                                  scales and x as two E4M3 terms with per-32 scales (exact to about
                                  2^-20 of each block's maximum); more workspace (3H + H/16 bytes per
                                  token).  Off: exact bf16 dequantization and bf16 MFMA. */
+    MOE_F_LORA = 4u           /* workspace for a shared low-rank adapter (moe_set_lora) */
 };
 
 /* Layer description.  moe_desc_init() fills the K3 defaults. */
@@ -175,6 +176,39 @@ moe_status moe_forward(moe_layer *L, const void *x, int32_t xt, int32_t T, const
  * inputs, or NULL to recompute it. */
 moe_status moe_backward_input(moe_layer *L, const void *x, int32_t xt, const void *dy, int32_t dyt, int32_t T,
                               const moe_routing *r, const float *saved_gu, float *dx, void *stream);
+
+/* Shared low-rank adapter on the routed experts (LazyLoRA README, "LoRA": one
+ * adapter per MoE layer in the latent space, shared by every routed expert, on
+ * the gate, up and down projections; rank 16 there).  While attached, every
+ * expert product W z of moe_forward, moe_backward_input and moe_backward_lora
+ * becomes (W + scale B A) z = W z + scale B (A z).  BORROWED fp32 device
+ * pointers, 16-byte aligned, kept alive and unchanged while attached:
+ *   A[0], A[1] [rank][H] and B[0], B[1] [I][rank]  (gate, up)
+ *   A[2] [rank][I] and B[2] [H][rank]              (down)
+ * scale is typically alpha / rank. */
+typedef struct {
+    int32_t rank;  /* 1..64 */
+    float scale;
+    const float *A[3];
+    const float *B[3];
+} moe_lora;
+
+/* Attach the adapter (lora != NULL) or detach it (NULL).  The layer must have
+ * been created with MOE_F_LORA in desc->flags (its workspace holds the
+ * adapter's buffers); otherwise, or for a rank outside 1..64, a non-finite
+ * scale or a NULL or misaligned pointer: MOE_ERR_INVALID_ARG and nothing
+ * changes.  Copies *lora; enqueues nothing. */
+moe_status moe_set_lora(moe_layer *L, const moe_lora *lora);
+
+/* moe_backward_input() plus the adapter gradients of sum_t <dy[t], y[t]>
+ * (routing held fixed): dA[m] and dB[m] receive fp32 arrays shaped like A[m]
+ * and B[m] (overwritten; caller-owned device buffers, 16-byte aligned).  The
+ * sums over tokens and slots run in a fixed order, so repeated calls give the
+ * same bits.  Requires an attached adapter (else MOE_ERR_INVALID_ARG).  T = 0
+ * writes zero gradients. */
+moe_status moe_backward_lora(moe_layer *L, const void *x, int32_t xt, const void *dy, int32_t dyt, int32_t T,
+                             const moe_routing *r, const float *saved_gu, float *dx, float *const dA[3],
+                             float *const dB[3], void *stream);
 
 /* Release the handle (NULL is a no-op).  Borrowed memory is not freed. */
 void moe_destroy(moe_layer *L);

@@ -103,6 +103,7 @@ class MoELayer:
         self.H, self.I, self.E, self.k, self.max_tokens = hidden, inter, n_experts, top_k, max_tokens
         self.device = router_w.device
         self._keep = [router_w, router_b, codes, scales, rvq_idx, rvq_cb]
+        self._lora = None
         w = C.MoeWeights()
         w.router_w = router_w.data_ptr()
         w.router_b = _ptr(router_b)
@@ -161,6 +162,39 @@ class MoELayer:
                                            T, ctypes.byref(rs), _ptr(saved_gu), dx.data_ptr(), _stream()),
                 "moe_backward_input")
         return dx
+
+    def set_lora(self, A=None, B=None, scale: float = 1.0):
+        """Attach the shared low-rank adapter (A = [gate, up, down] fp32 [r][in] device tensors,
+        B = [gate, up, down] fp32 [out][r]), or detach it with no arguments.  The layer must
+        have been created with flags including MOE_F_LORA."""
+        L = C.lib()
+        if A is None:
+            C.check(L.moe_set_lora(self._h, None), "moe_set_lora")
+            self._lora = None
+            return
+        s = C.MoeLora()
+        s.rank, s.scale = int(A[0].shape[0]), float(scale)
+        for m in range(3):
+            s.A[m], s.B[m] = A[m].data_ptr(), B[m].data_ptr()
+        C.check(L.moe_set_lora(self._h, ctypes.byref(s)), "moe_set_lora")
+        self._lora = (list(A), list(B), s.rank)
+
+    def backward_lora(self, x, dy, routing: Routing, saved_gu=None, dx=None):
+        """Input gradient and the adapter gradients: (dx, dA [3], dB [3])."""
+        torch = _torch()
+        A, B, r = self._lora
+        T = x.shape[0]
+        if dx is None:
+            dx = torch.empty((T, self.H), dtype=torch.float32, device=self.device)
+        dA = [torch.empty_like(a) for a in A]
+        dB = [torch.empty_like(b) for b in B]
+        rs = routing.c_struct()
+        vp3 = ctypes.c_void_p * 3
+        C.check(C.lib().moe_backward_lora(self._h, x.data_ptr(), _dtype_code(x), dy.data_ptr(), _dtype_code(dy), T,
+                                          ctypes.byref(rs), _ptr(saved_gu), dx.data_ptr(),
+                                          vp3(*[a.data_ptr() for a in dA]), vp3(*[b.data_ptr() for b in dB]),
+                                          _stream()), "moe_backward_lora")
+        return dx, dA, dB
 
     def new_saved_gu(self, T: int):
         torch = _torch()

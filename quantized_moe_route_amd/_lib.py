@@ -13,11 +13,12 @@ MOE_ACT_SWIGLU = 0
 MOE_F_DETERMINISTIC = 1
 MOE_ACT_SWIGLU, MOE_ACT_SITU = 0, 1
 MOE_F_MX_GATEUP = 2
+MOE_F_LORA = 4
 
 EXPORTED = (
     "moe_desc_init", "moe_workspace_size", "moe_layer_create", "moe_route", "moe_forward",
     "moe_backward_input", "moe_destroy", "moe_status_string", "moe_last_error",
-    "moe_prof_enable", "moe_prof_read", "moe_prof_hbm_read",
+    "moe_set_lora", "moe_backward_lora", "moe_prof_enable", "moe_prof_read", "moe_prof_hbm_read",
 )
 
 # kernel families of include/moe_prof.h
@@ -37,6 +38,11 @@ class MoeWeights(ctypes.Structure):
     _fields_ = [("router_w", ctypes.c_void_p), ("router_b", ctypes.c_void_p),
                 ("codes", ctypes.c_void_p * 3), ("scales", ctypes.c_void_p * 3),
                 ("rvq_idx", ctypes.c_void_p * 3), ("rvq_cb", ctypes.c_void_p * 3)]
+
+
+class MoeLora(ctypes.Structure):
+    _fields_ = [("rank", ctypes.c_int32), ("scale", ctypes.c_float), ("A", ctypes.c_void_p * 3),
+                ("B", ctypes.c_void_p * 3)]
 
 
 class MoeRouting(ctypes.Structure):
@@ -73,6 +79,11 @@ def lib() -> ctypes.CDLL:
         L.moe_forward.restype = st
         L.moe_backward_input.argtypes = [vp, vp, i32, vp, i32, i32, ctypes.POINTER(MoeRouting), vp, vp, vp]
         L.moe_backward_input.restype = st
+        L.moe_set_lora.argtypes = [vp, ctypes.POINTER(MoeLora)]
+        L.moe_set_lora.restype = st
+        L.moe_backward_lora.argtypes = [vp, vp, i32, vp, i32, i32, ctypes.POINTER(MoeRouting), vp, vp,
+                                        ctypes.POINTER(vp), ctypes.POINTER(vp), vp]
+        L.moe_backward_lora.restype = st
         L.moe_destroy.argtypes = [vp]
         L.moe_destroy.restype = None
         L.moe_status_string.argtypes = [st]

@@ -220,6 +220,18 @@ __device__ __forceinline__ void act_grad(int act, float g, float u, float &h, fl
     dhdu = silu;
 }
 
+// The adapter's per-token gate/up terms (lgu [T][2I], or null) for I-columns n..n+3 of
+// the token of grouped row rr, added to g and u before the activation.
+__device__ __forceinline__ void add_lora_gu(const float *lgu, const int32_t *perm, int k, size_t rr, int I, int n, f32x4 &g,
+                                            f32x4 &u)
+{
+    if (!lgu) return;
+    const float *p = lgu + (size_t)(perm[rr] / k) * 2 * I + n;
+    const float4 dg = *(const float4 *)p, du = *(const float4 *)(p + I);
+    g += f32x4{dg.x, dg.y, dg.z, dg.w};
+    u += f32x4{du.x, du.y, du.z, du.w};
+}
+
 // Exclusive scan of one int per thread over the block (scr: blockDim.x ints of LDS);
 // returns the total in *total.  Called by every thread of the block.
 __device__ __forceinline__ int block_exclusive_scan(int v, int *scr, int *total)

@@ -178,7 +178,8 @@ __global__ __launch_bounds__(256) void k_bwd_down(const ExpertBwdArgs a)
                         const float gv = a.gu[(rr * 2) * I + c], uv = a.gu[(rr * 2 + 1) * I + c];
                         float hv, dhdg, dhdu;
                         act_grad(a.act, gv, uv, hv, dhdg, dhdu);
-                        const float av = acc[tt][r];
+                        // the shared adapter's per-token term of Wd^T dy
+                        const float av = acc[tt][r] + (a.lora_c ? a.lora_c[(size_t)(a.perm[rr] / a.k) * I + c] : 0.f);
                         dpp += av * hv;
                         const float dh = p * av;
                         a.dgdu[(rr * 2) * I + c] = dh * dhdg;
@@ -348,13 +349,14 @@ hipError_t launch_expert_backward(const ExpertBwdArgs &a0, hipStream_t s)
         f.act = a.act;
         f.xq = a.xq;
         f.xq_s = a.xq_s;
+        f.lora_gu = a.lora_gu;
         f.prof = a.prof;
         set_lds_staging(f);
         hipError_t err = launch_gateup_only(f, s);
         if (err != hipSuccess) return err;
         a.gu = a.gu_scratch;
     }
-    if ((size_t)a.T * a.k >= (size_t)8 * a.E && bwd_mm_supported(a)) {
+    if (bwd_uses_mm(a)) {
         hipError_t err = launch_bwd_down_mm(a, s);
         if (err == hipSuccess) err = launch_bwd_gateup_mm(a, s);
         if (err != hipSuccess) return err;

@@ -242,6 +242,8 @@ __device__ __forceinline__ void bwd_down_pass(const ExpertBwdArgs &a, const BtBl
         const bool ok = j < nt;
         const size_t rr = (size_t)(r0 + tt0 + min(j, nt - 1));
         const float p = a.w[a.perm[rr]];
+        // the shared adapter's per-token term of Wd^T dy (null: none)
+        const float *lc = a.lora_c ? a.lora_c + (size_t)(a.perm[rr] / a.k) * I : nullptr;
         float dpp = 0.f;
 #pragma unroll
         for (int t = 0; t < 4; t++) {
@@ -250,9 +252,11 @@ __device__ __forceinline__ void bwd_down_pass(const ExpertBwdArgs &a, const BtBl
             const float4 uv = *(const float4 *)(a.gu + (rr * 2 + 1) * I + m);
             const float gg[4] = {gv.x, gv.y, gv.z, gv.w}, uu[4] = {uv.x, uv.y, uv.z, uv.w};
             uint32_t dh_[4], dl_[4], uh_[4], ul_[4];
+            const float4 cv = lc ? *(const float4 *)(lc + m) : float4{0.f, 0.f, 0.f, 0.f};
+            const float cc[4] = {cv.x, cv.y, cv.z, cv.w};
 #pragma unroll
             for (int r = 0; r < 4; r++) {
-                const float av = acc[t][tt][r];
+                const float av = acc[t][tt][r] + cc[r];
                 float hv, dhdg, dhdu;
                 act_grad(a.act, gg[r], uu[r], hv, dhdg, dhdu);
                 dpp += av * hv;

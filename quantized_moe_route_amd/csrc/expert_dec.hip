@@ -208,6 +208,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     if (li < ntok) {
         const size_t rr = (size_t)(r0 + li);
         const int n = row0 + 4 * g;
+        add_lora_gu(a.lora_gu, a.perm, a.k, rr, I, n, accg, accu);
         uint32_t hh[4], hl[4];
 #pragma unroll
         for (int r = 0; r < 4; r++) split_bf16(act_h(a.act, accg[r], accu[r]), hh[r], hl[r]);

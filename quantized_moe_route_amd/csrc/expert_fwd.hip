@@ -142,6 +142,7 @@ void k_gateup(const ExpertFwdArgs a)
             const int j = tt0 + 16 * tt + li;
             if (j >= ntok) continue;
             const size_t rr = (size_t)(r0 + j);
+            add_lora_gu(a.lora_gu, a.perm, a.k, rr, I, n0 + 4 * g, accg[tt], accu[tt]);
             uint32_t hh[4], hl[4];
 #pragma unroll
             for (int r = 0; r < 4; r++) {

@@ -273,11 +273,12 @@ __device__ __forceinline__ void gateup_pass(const ExpertFwdArgs &a, const GuBloc
         const size_t rr = (size_t)(r0 + tt0 + j);
 #pragma unroll
         for (int t = 0; t < 2; t++) {
-            const f32x4 gv = acc[t][tt], uv = acc[t + 2][tt];
+            f32x4 gv = acc[t][tt], uv = acc[t + 2][tt];
+            const int n = b.c0 + 16 * t + 4 * g;
+            add_lora_gu(a.lora_gu, a.perm, a.k, rr, I, n, gv, uv);
             uint32_t hh[4], hl[4];
 #pragma unroll
             for (int r = 0; r < 4; r++) split_bf16(act_h(a.act, gv[r], uv[r]), hh[r], hl[r]);
-            const int n = b.c0 + 16 * t + 4 * g;
             *(u32x2 *)(a.h_hi + rr * I + n) = u32x2{pack2(hh[0], hh[1]), pack2(hh[2], hh[3])};
             *(u32x2 *)(a.h_lo + rr * I + n) = u32x2{pack2(hl[0], hl[1]), pack2(hl[2], hl[3])};
             if (a.gu) {
@@ -435,11 +436,12 @@ __device__ __forceinline__ void gateup_pass_mx(const ExpertFwdArgs &a, const GuB
         const size_t rr = (size_t)(r0 + tt0 + j);
 #pragma unroll
         for (int t = 0; t < 2; t++) {
-            const f32x4 gv = acc[t][tt], uv = acc[t + 2][tt];
+            f32x4 gv = acc[t][tt], uv = acc[t + 2][tt];
+            const int n = b.c0 + 16 * t + 4 * g;
+            add_lora_gu(a.lora_gu, a.perm, a.k, rr, I, n, gv, uv);
             uint32_t hh[4], hl[4];
 #pragma unroll
             for (int r = 0; r < 4; r++) split_bf16(act_h(a.act, gv[r], uv[r]), hh[r], hl[r]);
-            const int n = b.c0 + 16 * t + 4 * g;
             *(u32x2 *)(a.h_hi + rr * I + n) = u32x2{pack2(hh[0], hh[1]), pack2(hh[2], hh[3])};
             *(u32x2 *)(a.h_lo + rr * I + n) = u32x2{pack2(hl[0], hl[1]), pack2(hl[2], hl[3])};
             if (a.gu) {

@@ -205,14 +205,16 @@ __global__ __launch_bounds__(256) void k_gateup_rvq(const ExpertFwdArgs a)
         if (li < nt) {
             const size_t rr = (size_t)(r0 + tt0 + li);
             const int n = row0 + 4 * g, se = sexp[li];
-            float gv[4], uv[4];
+            f32x4 gv, uv;
             uint32_t hh[4], hl[4];
 #pragma unroll
             for (int r = 0; r < 4; r++) {
                 gv[r] = ldexpf(accg[r], se);
                 uv[r] = ldexpf(accu[r], se);
-                split_bf16(act_h(a.act, gv[r], uv[r]), hh[r], hl[r]);
             }
+            add_lora_gu(a.lora_gu, a.perm, a.k, rr, I, n, gv, uv);
+#pragma unroll
+            for (int r = 0; r < 4; r++) split_bf16(act_h(a.act, gv[r], uv[r]), hh[r], hl[r]);
             *(u32x2 *)(a.h_hi + rr * I + n) = u32x2{pack2(hh[0], hh[1]), pack2(hh[2], hh[3])};
             *(u32x2 *)(a.h_lo + rr * I + n) = u32x2{pack2(hl[0], hl[1]), pack2(hl[2], hl[3])};
             if (a.gu) {

@@ -6,6 +6,7 @@
 // status and fills an out-handle, and a destroy call.  A missing input is an
 // error, never replaced (LazyLoRA README, "Three rules the engine is built
 // around").
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -37,8 +38,13 @@ constexpr int kMaxTopK = 64;
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
-    size_t logits, beta, h, ybuf, gu, dgdu, dp, xq, xqs, total;
+    size_t logits, beta, h, ybuf, gu, dgdu, dp, xq, xqs;
+    size_t l_vx, l_gu, l_zs, l_z, l_wd, l_c, l_dgu, l_m, l_u, l_part;  // adapter (MOE_F_LORA)
+    size_t total;
 };
+
+constexpr int kMaxLoraRank = 64;
+constexpr size_t kLoraPartFloats = (size_t)4 << 20;  // split-K partial sums of the adapter GEMMs
 
 Layout layout_of(const moe_desc &d)
 {
@@ -61,6 +67,18 @@ Layout layout_of(const moe_desc &d)
     const bool mx = (d.flags & MOE_F_MX_GATEUP) != 0;
     L.xq = take(mx ? T * H * 2 : 0);
     L.xqs = take(mx ? T * (H / 32) * 2 : 0);
+    const bool lo = (d.flags & MOE_F_LORA) != 0;
+    const size_t R = lo ? kMaxLoraRank : 0, Tl = lo ? T : 0, Sl = lo ? S : 0;
+    L.l_vx = take(Tl * 2 * R * 4);
+    L.l_gu = take(Tl * 2 * I * 4);
+    L.l_zs = take(Sl * R * 4);
+    L.l_z = take(Tl * R * 4);
+    L.l_wd = take(Tl * R * 4);
+    L.l_c = take(Tl * I * 4);
+    L.l_dgu = take(Tl * 2 * I * 4);
+    L.l_m = take(Tl * 2 * R * 4);
+    L.l_u = take(Sl * R * 4);
+    L.l_part = take(lo ? kLoraPartFloats * 4 : 0);
     L.total = off;
     return L;
 }
@@ -108,6 +126,8 @@ struct moe_layer {
     size_t ws_bytes;
     Layout lay;
     moe::Prof prof;
+    bool has_lora = false;
+    moe::LoraW lora{};
 };
 
 namespace {
@@ -127,6 +147,24 @@ void prof_release(moe::Prof &p)
 }  // namespace
 
 namespace {
+
+moe::LoraWs lora_ws(const moe_layer *L)
+{
+    moe::LoraWs w{};
+    char *b = L->ws;
+    w.vx = (float *)(b + L->lay.l_vx);
+    w.gu = (float *)(b + L->lay.l_gu);
+    w.zs = (float *)(b + L->lay.l_zs);
+    w.z = (float *)(b + L->lay.l_z);
+    w.wd = (float *)(b + L->lay.l_wd);
+    w.c = (float *)(b + L->lay.l_c);
+    w.dgu = (float *)(b + L->lay.l_dgu);
+    w.m = (float *)(b + L->lay.l_m);
+    w.u = (float *)(b + L->lay.l_u);
+    w.part = (float *)(b + L->lay.l_part);
+    w.part_cap = kLoraPartFloats;
+    return w;
+}
 
 moe_status check_layer(const moe_layer *L)
 {
@@ -310,13 +348,23 @@ moe_status moe_forward(moe_layer *L, const void *x, int32_t xt, int32_t T, const
     }
     a.prof = &L->prof;
     moe::set_lds_staging(a);
-    return device_status(moe::launch_expert_forward(a, (hipStream_t)stream), "forward");
+    const hipStream_t hs = (hipStream_t)stream;
+    if (!L->has_lora) return device_status(moe::launch_expert_forward(a, hs), "forward");
+    const moe::LoraWs lw = lora_ws(L);
+    if ((st = device_status(moe::lora_forward_pre(L->lora, lw, x, xt, T, a.H, a.I, hs), "adapter (gate/up terms)")) != MOE_OK)
+        return st;
+    a.lora_gu = lw.gu;
+    if ((st = device_status(moe::launch_expert_forward(a, hs), "forward")) != MOE_OK) return st;
+    return device_status(moe::lora_forward_post(L->lora, lw, a, r->inv, hs), "adapter (down term)");
 }
 
-moe_status moe_backward_input(moe_layer *L, const void *x, int32_t xt, const void *dy, int32_t dyt, int32_t T,
-                              const moe_routing *r, const float *saved_gu, float *dx, void *stream)
+namespace {
+
+// Input gradient, and the adapter gradients when dA is not NULL.
+moe_status backward_impl(moe_layer *L, const void *x, int32_t xt, const void *dy, int32_t dyt, int32_t T,
+                         const moe_routing *r, const float *saved_gu, float *dx, float *const *dA, float *const *dB,
+                         void *stream)
 {
-    g_last_error.clear();
     moe_status st;
     if ((st = check_layer(L)) != MOE_OK || (st = check_tokens(L, T)) != MOE_OK || (st = check_dtype(xt, "x")) != MOE_OK ||
         (st = check_dtype(dyt, "dy")) != MOE_OK)
@@ -363,8 +411,95 @@ moe_status moe_backward_input(moe_layer *L, const void *x, int32_t xt, const voi
         a.xq_s = (uint8_t *)(L->ws + L->lay.xqs);
     }
     a.prof = &L->prof;
-    return device_status(moe::launch_expert_backward(a, (hipStream_t)stream), "backward_input");
+    const hipStream_t hs = (hipStream_t)stream;
+    if (!L->has_lora) return device_status(moe::launch_expert_backward(a, hs), "backward_input");
+    const moe::LoraWs lw = lora_ws(L);
+    const bool grads = dA != nullptr;
+    if (!saved_gu || grads) {  // the gate/up terms: for recomputing g, u and for dB_g, dB_u
+        if ((st = device_status(moe::lora_forward_pre(L->lora, lw, x, xt, T, a.H, a.I, hs), "adapter (gate/up terms)")) != MOE_OK)
+            return st;
+        a.lora_gu = lw.gu;
+    }
+    if ((st = device_status(moe::lora_backward_pre(L->lora, lw, dy, dyt, T, a.H, a.I, hs), "adapter (down term)")) != MOE_OK)
+        return st;
+    a.lora_c = lw.c;
+    if ((st = device_status(moe::launch_expert_backward(a, hs), "backward_input")) != MOE_OK) return st;
+    if ((st = device_status(moe::lora_backward_post(L->lora, lw, a, moe::bwd_uses_mm(a), hs), "adapter (input gradient)")) !=
+        MOE_OK)
+        return st;
+    if (!grads) return MOE_OK;
+    if (saved_gu && (st = device_status(moe::launch_h_from_gu(a, hs), "adapter (h from saved g, u)")) != MOE_OK) return st;
+    return device_status(moe::lora_grads(L->lora, lw, a, dA, dB, hs), "adapter (gradients)");
 }
+
+}  // namespace
+
+moe_status moe_backward_input(moe_layer *L, const void *x, int32_t xt, const void *dy, int32_t dyt, int32_t T,
+                              const moe_routing *r, const float *saved_gu, float *dx, void *stream)
+{
+    g_last_error.clear();
+    return backward_impl(L, x, xt, dy, dyt, T, r, saved_gu, dx, nullptr, nullptr, stream);
+}
+
+moe_status moe_backward_lora(moe_layer *L, const void *x, int32_t xt, const void *dy, int32_t dyt, int32_t T,
+                             const moe_routing *r, const float *saved_gu, float *dx, float *const dA[3], float *const dB[3],
+                             void *stream)
+{
+    g_last_error.clear();
+    moe_status st;
+    if ((st = check_layer(L)) != MOE_OK) return st;
+    if (!L->has_lora) return fail(MOE_ERR_INVALID_ARG, "no adapter is attached (moe_set_lora)");
+    if (!dA || !dB) return fail(MOE_ERR_INVALID_ARG, "dA or dB is NULL");
+    for (int m = 0; m < 3; m++)
+        if (!dA[m] || !dB[m] || !aligned(dA[m], 16) || !aligned(dB[m], 16))
+            return fail(MOE_ERR_INVALID_ARG, "dA[%d] and dB[%d] must be non-NULL and 16-byte aligned", m, m);
+    if (T == 0) {
+        // no tokens: the adapter gradients are zero
+        const moe_desc &d = L->d;
+        const size_t na[3] = {(size_t)L->lora.r * d.hidden, (size_t)L->lora.r * d.hidden, (size_t)L->lora.r * d.inter};
+        const size_t nb[3] = {(size_t)d.inter * L->lora.r, (size_t)d.inter * L->lora.r, (size_t)d.hidden * L->lora.r};
+        if ((st = check_tokens(L, T)) != MOE_OK) return st;
+        for (int m = 0; m < 3; m++) {
+            hipError_t e = moe::fill_zero(dA[m], na[m], (hipStream_t)stream);
+            if (e == hipSuccess) e = moe::fill_zero(dB[m], nb[m], (hipStream_t)stream);
+            if (e != hipSuccess) return device_status(e, "zero adapter gradients");
+        }
+        return MOE_OK;
+    }
+    return backward_impl(L, x, xt, dy, dyt, T, r, saved_gu, dx, dA, dB, stream);
+}
+
+moe_status moe_set_lora(moe_layer *L, const moe_lora *lora)
+{
+    g_last_error.clear();
+    moe_status st;
+    if ((st = check_layer(L)) != MOE_OK) return st;
+    if (!lora) {
+        L->has_lora = false;
+        L->lora = moe::LoraW{};
+        return MOE_OK;
+    }
+    if (!(L->d.flags & MOE_F_LORA))
+        return fail(MOE_ERR_INVALID_ARG, "the layer's workspace was sized without MOE_F_LORA");
+    if (lora->rank < 1 || lora->rank > kMaxLoraRank)
+        return fail(MOE_ERR_INVALID_ARG, "rank=%d must be in 1..%d", lora->rank, kMaxLoraRank);
+    if (!std::isfinite(lora->scale)) return fail(MOE_ERR_INVALID_ARG, "scale is not finite");
+    for (int m = 0; m < 3; m++)
+        if (!lora->A[m] || !lora->B[m] || !aligned(lora->A[m], 16) || !aligned(lora->B[m], 16))
+            return fail(MOE_ERR_INVALID_ARG, "A[%d] and B[%d] must be non-NULL and 16-byte aligned", m, m);
+    moe::LoraW w{};
+    w.r = lora->rank;
+    w.scale = lora->scale;
+    for (int m = 0; m < 3; m++) {
+        w.A[m] = lora->A[m];
+        w.B[m] = lora->B[m];
+    }
+    L->lora = w;
+    L->has_lora = true;
+    return MOE_OK;
+}
+
+
 
 void moe_destroy(moe_layer *L)
 {

@@ -98,6 +98,7 @@ struct ExpertFwdArgs {
     uint8_t *xq_s;       // path; null: bf16 path) and [T][H/32][2] their E8M0 block scales
     int nl_x;            // experts with at most this many tokens stage their x rows in LDS
     int nl_h;            // ... and their h rows (down product)
+    const float *lora_gu;  // [T][2I] per-token adapter terms added to g | u, or null
 };
 
 struct ExpertBwdArgs {
@@ -122,6 +123,8 @@ struct ExpertBwdArgs {
     float *dx;           // [T][H]
     uint8_t *xq, *xq_s;  // x terms for the gate/up recomputation (as in ExpertFwdArgs)
     int act;             // ACT_SWIGLU or ACT_SITU
+    const float *lora_gu;  // [T][2I] adapter terms of g | u for the recomputation, or null
+    const float *lora_c;   // [T][I] adapter term added to a = Wd^T dy per token, or null
 };
 
 // Token rows staged in LDS by the few-token (decode) expert kernels: at most 16 rows
@@ -165,6 +168,39 @@ hipError_t launch_expert_backward(const ExpertBwdArgs &a, hipStream_t s);
 bool bwd_mm_supported(const ExpertBwdArgs &a);
 hipError_t launch_bwd_down_mm(const ExpertBwdArgs &a, hipStream_t s);
 hipError_t launch_bwd_gateup_mm(const ExpertBwdArgs &a, hipStream_t s);
+
+// The grouped-GEMM backward runs when the experts average at least 8 tokens each; its
+// dg/du rows are bf16 hi + lo planes, the generic backward's fp32.
+inline bool bwd_uses_mm(const ExpertBwdArgs &a) { return (size_t)a.T * a.k >= (size_t)8 * a.E && bwd_mm_supported(a); }
+
+// Shared low-rank adapter (lora.hip): weights (borrowed, fp32) and workspace.
+struct LoraW {
+    int r;
+    float scale;
+    const float *A[3];  // [r][in]
+    const float *B[3];  // [out][r]
+};
+struct LoraWs {
+    float *vx;    // [T][2r]  A_g x | A_u x
+    float *gu;    // [T][2I]  s B_g A_g x | s B_u A_u x
+    float *zs;    // [S][r]   A_d h per grouped row
+    float *z;     // [T][r]   sum_j p A_d h
+    float *wd;    // [T][r]   B_d^T dy
+    float *c;     // [T][I]   s A_d^T B_d^T dy
+    float *dgu;   // [T][2I]  per-token sums of dL/dg | dL/du
+    float *m;     // [T][2r]  B_g^T dgu_g | B_u^T dgu_u
+    float *u;     // [S][r]   p_s wd[t(s)]
+    float *part;  // split-K partial sums
+    size_t part_cap;  // floats
+};
+hipError_t lora_forward_pre(const LoraW &L, const LoraWs &w, const void *x, int xt, int T, int H, int I, hipStream_t s);
+hipError_t lora_forward_post(const LoraW &L, const LoraWs &w, const ExpertFwdArgs &a, const int32_t *inv, hipStream_t s);
+hipError_t lora_backward_pre(const LoraW &L, const LoraWs &w, const void *dy, int dyt, int T, int H, int I, hipStream_t s);
+hipError_t lora_backward_post(const LoraW &L, const LoraWs &w, const ExpertBwdArgs &a, bool pair, hipStream_t s);
+hipError_t lora_grads(const LoraW &L, const LoraWs &w, const ExpertBwdArgs &a, float *const dA[3], float *const dB[3],
+                      hipStream_t s);
+hipError_t launch_h_from_gu(const ExpertBwdArgs &a, hipStream_t s);
+hipError_t fill_zero(float *p, size_t n, hipStream_t s);
 
 // number of I-column tiles whose partial <a, h> sums the backward stores per row
 __host__ __device__ inline int dp_tiles(int I) { return (I + 63) / 64; }

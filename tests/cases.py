@@ -97,3 +97,65 @@ def fnv1a32(a: np.ndarray) -> int:
     for b in np.ascontiguousarray(a).view(np.uint8).tobytes():
         h = ((h ^ b) * 0x01000193) & 0xFFFFFFFF
     return h
+
+
+def lora_parity(c: HostCase, L, name: str, rank: int = 16, scale: float = 2.0, saved=(True, False)) -> None:
+    """Attach a seeded rank-`rank` adapter to the device layer L (created with MOE_F_LORA
+    over c's weights), then compare forward, dX and the adapter gradients with the oracle
+    on c's tokens; also: backward_input equals backward_lora's dX bit for bit, repeated
+    gradients are bitwise equal, and detaching restores the plain layer."""
+    import torch
+
+    import quantized_moe_route_amd as q
+
+    def np_(t):
+        return t.detach().cpu().numpy()
+
+    w = c.w
+    A, B = syn.lora_adapter(w, rank)
+    c.lora = (A, B, scale)
+    log(f"case {name}: T={w.T} H={w.H} I={w.I} E={w.E} k={w.k} fmt={w.wfmt} x={w.x_dtype} act={c.act} rank={rank}")
+    L.set_lora([q.to_device(a) for a in A], [q.to_device(b) for b in B], scale)
+    x = act_tensor(c.x, w.x_dtype)
+    dy = act_tensor(c.dy, w.x_dtype)
+    r = L.route(x)
+    ids, p, _ = oracle.route(c.x64, c.wr, c.bias, w.k)
+    torch.cuda.synchronize()
+    assert np.array_equal(np_(r.ids), ids), f"{name}: routing ids"
+    W = c.oracle_weights()
+    y_ref = oracle.forward(c.x64, ids, p, W)
+    dx_ref = oracle.backward_input(c.x64, c.dy64, ids, p, c.wr, W)
+    dA_ref, dB_ref = oracle.lora_grads(c.x64, c.dy64, ids, p, W)
+    gu = L.new_saved_gu(w.T)
+    y = L.forward(x, r, saved_gu=gu)
+    torch.cuda.synchronize()
+    e = rel_err(np_(y), y_ref)
+    log(f"  y rel err {e:.3e}")
+    assert e <= TOL, f"{name}: y {e}"
+    first = None
+    for sv in saved:
+        g = gu if sv else None
+        dx, dA, dB = L.backward_lora(x, dy, r, saved_gu=g)
+        dx_only = L.backward_input(x, dy, r, saved_gu=g)
+        torch.cuda.synchronize()
+        e = rel_err(np_(dx), dx_ref)
+        log(f"  dX rel err {e:.3e} (saved g/u: {sv})")
+        assert e <= TOL, f"{name}: dX {e}"
+        assert np.array_equal(np_(dx_only), np_(dx)), f"{name}: backward_input and backward_lora disagree on dX"
+        for m, nm in enumerate(("gate", "up", "down")):
+            ea, eb = rel_err(np_(dA[m]), dA_ref[m]), rel_err(np_(dB[m]), dB_ref[m])
+            log(f"  dA[{nm}] {ea:.3e}  dB[{nm}] {eb:.3e}")
+            assert ea <= TOL and eb <= TOL, f"{name}: adapter gradient {nm}: dA {ea} dB {eb}"
+        if first is None:
+            first = (g, dA, dB)
+    # the sums run in a fixed order: the same bits again
+    _, dA2, dB2 = L.backward_lora(x, dy, r, saved_gu=first[0])
+    torch.cuda.synchronize()
+    for m in range(3):
+        assert np.array_equal(np_(dA2[m]), np_(first[1][m])) and np.array_equal(np_(dB2[m]), np_(first[2][m]))
+    # detached: the plain layer again
+    L.set_lora()
+    y0 = L.forward(x, r)
+    torch.cuda.synchronize()
+    c.lora = None
+    assert rel_err(np_(y0), oracle.forward(c.x64, ids, p, c.oracle_weights())) <= TOL, f"{name}: detached forward"

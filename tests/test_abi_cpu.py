@@ -170,3 +170,49 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(C, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(RuntimeError, match="missing"):
         C.lib()
+
+
+def _fake_lora(rank=16, scale=2.0, align=256):
+    s = C.MoeLora()
+    s.rank, s.scale = rank, scale
+    for m in range(3):
+        s.A[m] = 0x40000 + m * align
+        s.B[m] = 0x50000 + m * align
+    return s
+
+
+def test_lora_argument_checks():
+    L = C.lib()
+    n0, n1 = ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.moe_workspace_size(ctypes.byref(_desc(max_tokens=8)), ctypes.byref(n0)) == C.MOE_OK
+    assert L.moe_workspace_size(ctypes.byref(_desc(max_tokens=8, flags=C.MOE_F_LORA)), ctypes.byref(n1)) == C.MOE_OK
+    assert n1.value > n0.value  # the adapter's buffers
+    # a layer sized without MOE_F_LORA refuses an adapter
+    st, h = _create(_desc(max_tokens=8), _fake_weights())
+    assert st == C.MOE_OK
+    assert L.moe_set_lora(h, ctypes.byref(_fake_lora())) == C.MOE_ERR_INVALID_ARG
+    assert L.moe_set_lora(h, None) == C.MOE_OK  # detaching is always allowed
+    # moe_backward_lora needs an attached adapter (checked before anything else is touched)
+    vp3 = ctypes.c_void_p * 3
+    r = C.MoeRouting()
+    dA, dB = vp3(0x1000, 0x2000, 0x3000), vp3(0x4000, 0x5000, 0x6000)
+    assert L.moe_backward_lora(h, 0x1000, C.MOE_DT_BF16, 0x1000, C.MOE_DT_BF16, 1, ctypes.byref(r), None, 0x1000, dA, dB,
+                               None) == C.MOE_ERR_INVALID_ARG
+    L.moe_destroy(h)
+    st, h = _create(_desc(max_tokens=8, flags=C.MOE_F_LORA), _fake_weights())
+    assert st == C.MOE_OK
+    assert L.moe_set_lora(None, ctypes.byref(_fake_lora())) == C.MOE_ERR_INVALID_ARG
+    for bad in (_fake_lora(rank=0), _fake_lora(rank=65), _fake_lora(scale=float("inf")), _fake_lora(scale=float("nan")),
+                _fake_lora(align=8)):
+        assert L.moe_set_lora(h, ctypes.byref(bad)) == C.MOE_ERR_INVALID_ARG
+    nul = _fake_lora()
+    nul.B[2] = None
+    assert L.moe_set_lora(h, ctypes.byref(nul)) == C.MOE_ERR_INVALID_ARG
+    assert L.moe_set_lora(h, ctypes.byref(_fake_lora())) == C.MOE_OK
+    assert L.moe_set_lora(h, ctypes.byref(_fake_lora(rank=64))) == C.MOE_OK
+    # with an adapter: NULL or misaligned gradient buffers are refused
+    assert L.moe_backward_lora(h, 0x1000, C.MOE_DT_BF16, 0x1000, C.MOE_DT_BF16, 1, ctypes.byref(r), None, 0x1000, None, dB,
+                               None) == C.MOE_ERR_INVALID_ARG
+    assert L.moe_backward_lora(h, 0x1000, C.MOE_DT_BF16, 0x1000, C.MOE_DT_BF16, 1, ctypes.byref(r), None, 0x1000,
+                               vp3(0x1000, 0x2008, 0x3000), dB, None) == C.MOE_ERR_INVALID_ARG
+    L.moe_destroy(h)

@@ -6,7 +6,7 @@ import pytest
 
 import moe_synth as syn
 import oracle
-from cases import TOL, act_tensor, device_layer, host_case, log, rel_err
+from cases import TOL, act_tensor, device_layer, host_case, log, lora_parity, rel_err
 
 pytestmark = pytest.mark.gpu
 
@@ -126,3 +126,18 @@ def test_rvq16_full_size():
     log(f"rvq16: y rel err {e:.3e}")
     assert e <= TOL
     L.close()
+
+
+def test_lora_k3_two_tokens(k3_mxfp4):
+    """The K3 layer with a rank-16 shared adapter (LazyLoRA README, "LoRA") on two tokens:
+    y, dX and all six adapter gradients in full against the oracle."""
+    import quantized_moe_route_amd as q
+    from quantized_moe_route_amd import _lib as C
+    c, L = k3_mxfp4
+    w = syn.shrink(c.w, T=2, x_key=57)
+    cc = type(c)(w, syn.activations(w, 2), c.wr, None, syn.upstream_grad(w, 2), codes=c.codes, scales=c.scales)
+    router_w, _, codes, scales = L._keep[:4]
+    La = q.MoELayer(hidden=w.H, inter=w.I, n_experts=w.E, top_k=w.k, max_tokens=2, router_w=router_w, codes=codes,
+                    scales=scales, flags=C.MOE_F_LORA)
+    lora_parity(cc, La, "lora-k3-T2", saved=(True,))
+    La.close()

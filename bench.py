@@ -59,13 +59,13 @@ def traffic_record(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, x_pool, wr, bias, codes, scales, budget_s: float, dy_pool=None):
+def cpu_baseline(w, x_pool, wr, bias, codes, scales, budget_s: float, dy_pool=None, lora=None):
     """The fp64 oracle as it stands, timed on a bounded sample of the same pool: consecutive
     chunks of at most 16 tokens (route + group + forward, and the input gradient when dy_pool
     is given), until budget_s of CPU work; tokens/s over the tokens processed."""
     import oracle
     nthreads = oracle.default_threads()
-    W = oracle.Weights(w.H, w.I, codes=codes, scales=scales)
+    W = oracle.Weights(w.H, w.I, codes=codes, scales=scales, lora=lora)
     flat = x_pool.reshape(-1, w.H)
     dflat = None if dy_pool is None else dy_pool.reshape(-1, w.H)
     chunk = min(w.T, 16)
@@ -77,12 +77,17 @@ def cpu_baseline(w, x_pool, wr, bias, codes, scales, budget_s: float, dy_pool=No
         else:
             ids, p, _ = oracle.route(xb, wr, bias, w.k, nthreads=nthreads)
             oracle.forward(xb, ids, p, W, nthreads=nthreads)
-            oracle.backward_input(xb, oracle.to_f64(dflat[n:n + chunk], "bf16"), ids, p, wr, W, nthreads=nthreads)
+            dyb = oracle.to_f64(dflat[n:n + chunk], "bf16")
+            oracle.backward_input(xb, dyb, ids, p, wr, W, nthreads=nthreads)
+            if lora is not None:
+                oracle.lora_grads(xb, dyb, ids, p, W, nthreads=nthreads)
         n += chunk
         el = time.perf_counter() - t0
         if el >= budget_s or n + chunk > flat.shape[0]:
             break
     what = "route + group + forward" + (" + input gradient" if dflat is not None else "")
+    if lora is not None:
+        what += " with the adapter" + (" and its gradients" if dflat is not None else "")
     return {"value": n / el, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
             "sample": f"{n} tokens of the timed pool in chunks of {chunk} ({what} with {w.k} experts per "
                       f"token), {el:.1f} s of fp64 CPU work"}
@@ -96,6 +101,9 @@ def main():
     ap.add_argument("--workload", default="decode1", choices=["decode1", "decode64", "rvq16", "train4096"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--lora", type=int, default=0, metavar="RANK",
+                    help="attach a shared low-rank adapter of this rank (LazyLoRA's is 16); the training pass then "
+                         "also computes the adapter gradients")
     ap.add_argument("--no-plain-read", action="store_true",
                     help="skip the reference stream (a plain read of the roofline kernel's byte count)")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel family (stderr)")
@@ -142,7 +150,12 @@ def main():
         kw["rvq_cb"] = [q.to_device(a) for a in cb]
         expert_bytes = sum(a[0].nbytes for a in idx) + sum(a[0].nbytes for a in cb)
         gateup_bytes_per_expert = sum(a[0].nbytes for a in idx[:2]) + sum(a[0].nbytes for a in cb[:2])
+    if args.lora:
+        kw["flags"] = C.MOE_F_LORA
     L = q.MoELayer(**kw)
+    if args.lora:
+        A_h, B_h = syn.lora_adapter(w, args.lora)
+        L.set_lora([q.to_device(a) for a in A_h], [q.to_device(b_) for b_ in B_h], 32.0 / args.lora)
     x_host = syn.activations(w, w.T * POOL).reshape(POOL, w.T, w.H)
     x_pool = q.bf16_tensor(x_host.reshape(-1, w.H)).reshape(POOL, w.T, w.H)
     r = L.new_routing(w.T)
@@ -164,7 +177,10 @@ def main():
         L.route(xi, r)
         if train:
             L.forward(xi, r, y=y, saved_gu=gu)
-            L.backward_input(xi, dy_pool[i % POOL], r, saved_gu=gu, dx=dx)
+            if args.lora:
+                L.backward_lora(xi, dy_pool[i % POOL], r, saved_gu=gu, dx=dx)
+            else:
+                L.backward_input(xi, dy_pool[i % POOL], r, saved_gu=gu, dx=dx)
         else:
             L.forward(xi, r, y=y)
 
@@ -257,7 +273,8 @@ def main():
     if not args.no_cpu_baseline:
         log("CPU baseline: fp64 oracle")
         dy_host = syn.upstream_grad(w, w.T * POOL).reshape(POOL, w.T, w.H) if train else None
-        base = (cpu_baseline(w, x_host, wr, bias, codes, scales, args.cpu_seconds, dy_host)
+        base = (cpu_baseline(w, x_host, wr, bias, codes, scales, args.cpu_seconds, dy_host,
+                             lora=(A_h, B_h, 32.0 / args.lora) if args.lora else None)
                 if codes is not None else None)
 
     out = {
@@ -276,8 +293,10 @@ def main():
         "config": {"workload": f"{w.name}: K3-shaped routed-expert layer, {w.T} token(s) per step, H {w.H}, "
                                f"I {w.I}, {w.E} {w.wfmt} experts resident, top-{w.k}, bf16 activations, "
                                + ("forward + input gradient (route + group + experts + combine + dX)" if train
-                                  else "forward (route + group + experts + combine)"),
-                   "T": w.T, "H": w.H, "I": w.I, "E": w.E, "k": w.k, "weights": w.wfmt},
+                                  else "forward (route + group + experts + combine)")
+                               + (f", shared rank-{args.lora} adapter" + (" with its gradients" if train else "")
+                                  if args.lora else ""),
+                   "T": w.T, "H": w.H, "I": w.I, "E": w.E, "k": w.k, "weights": w.wfmt, "lora_rank": args.lora},
         "roofline": roofline,
         "cpu_baseline": base,
         "detail": detail,

@@ -6,7 +6,8 @@
 // s the adapter scale.  Because the adapter is the same for every expert:
 //  - the gate/up terms s B_g (A_g x_t), s B_u (A_u x_t) are per TOKEN ([T][2I]), formed
 //    once before the expert kernels and added in their epilogues before the activation;
-//  - the down term of a token is s B_d z_t with z_t = sum_j p_tj A_d h_tj, added to y
+//  - the down term of a token is s B_d z_t with z_t = sum_j p_tj A_d h_tj = A_d hbar_t,
+//    hbar_t = sum_j p_tj h_tj (one gather-sum over the token's slot rows), added to y
 //    after the combine;
 //  - in the backward, the term s A_d^T (B_d^T dy_t) of W_d^T dy is again per token and is
 //    added in the backward down epilogue; the gate/up input gradient gains
@@ -14,7 +15,8 @@
 //    slots of dL/dg, dL/du;
 //  - the adapter gradients are sums of outer products over tokens (or slots):
 //    dB_g = s sum_t DG_t (A_g x_t)^T, dA_g = s sum_t (B_g^T DG_t) x_t^T (up alike),
-//    dB_d = s sum_t dy_t z_t^T, dA_d = s sum_s p_s (B_d^T dy_t(s)) h_s^T.
+//    dB_d = s sum_t dy_t z_t^T, dA_d = s sum_s p_s (B_d^T dy_t(s)) h_s^T
+//    = s sum_t (B_d^T dy_t) hbar_t^T.
 // Everything here is skinny fp32 GEMMs (one dimension is the rank) with fp32 accumulation
 // in a fixed order (split-K partial sums reduced in chunk order), plus three gathers over
 // the grouped slot rows.
@@ -203,16 +205,38 @@ Opnd op(const void *p, long s0, long s1, const void *p2 = nullptr) { return Opnd
 
 int od(int dt) { return dt == DT_BF16 ? OD_BF16 : OD_F32; }
 
-// z[t][q] = sum_j w[t][j] zs[inv[t k + j]][q], j in rank order.
-__global__ __launch_bounds__(256) void k_lora_z(const float *__restrict__ zs, const int32_t *__restrict__ inv,
-                                                const float *__restrict__ w, int T, int k, int r, float *__restrict__ z)
+// hbar[t][n] = sum_j w[t][j] h(grouped row inv[t k + j], n), j in rank order; h read from
+// its bf16 hi + lo planes [S][I] (GU = false) or formed from the pre-activations g, u
+// [S][2][I] (GU = true).  Four columns per thread.
+template <bool GU>
+__global__ __launch_bounds__(256) void k_lora_hbar(const uint16_t *__restrict__ h_hi, const uint16_t *__restrict__ h_lo,
+                                                   const float *__restrict__ gu, int act, const int32_t *__restrict__ inv,
+                                                   const float *__restrict__ w, int k, int I, float *__restrict__ hbar)
 {
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= T * r) return;
-    const int t = i / r, q = i - t * r;
-    float s = 0.f;
-    for (int j = 0; j < k; j++) s += w[t * k + j] * zs[(size_t)inv[t * k + j] * r + q];
-    z[i] = s;
+    const int t = blockIdx.y, n = 4 * (blockIdx.x * blockDim.x + threadIdx.x);
+    if (n >= I) return;
+    float s[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; j++) {
+        const size_t row = (size_t)inv[t * k + j];
+        const float p = w[t * k + j];
+        float h[4];
+        if constexpr (GU) {
+            const float4 g = *(const float4 *)(gu + (2 * row) * I + n), u = *(const float4 *)(gu + (2 * row + 1) * I + n);
+            h[0] = act_h(act, g.x, u.x);
+            h[1] = act_h(act, g.y, u.y);
+            h[2] = act_h(act, g.z, u.z);
+            h[3] = act_h(act, g.w, u.w);
+        } else {
+            const u32x2 hi = *(const u32x2 *)(h_hi + row * I + n), lo = *(const u32x2 *)(h_lo + row * I + n);
+            h[0] = bf16_bits_to_f32(hi[0] & 0xFFFFu) + bf16_bits_to_f32(lo[0] & 0xFFFFu);
+            h[1] = bf16_bits_to_f32(hi[0] >> 16) + bf16_bits_to_f32(lo[0] >> 16);
+            h[2] = bf16_bits_to_f32(hi[1] & 0xFFFFu) + bf16_bits_to_f32(lo[1] & 0xFFFFu);
+            h[3] = bf16_bits_to_f32(hi[1] >> 16) + bf16_bits_to_f32(lo[1] >> 16);
+        }
+#pragma unroll
+        for (int c = 0; c < 4; c++) s[c] += p * h[c];
+    }
+    *(float4 *)(hbar + (size_t)t * I + n) = float4{s[0], s[1], s[2], s[3]};
 }
 
 // dgu[t][c] = sum_j (dL/dg | dL/du)(grouped row inv[t k + j], c) for c < 2I, j in rank
@@ -234,30 +258,6 @@ __global__ __launch_bounds__(256) void k_lora_dgu(const void *__restrict__ dgdu,
             }
         }
         dgu[(size_t)t * row + c] = s;
-    }
-}
-
-// u[s][q] = p_slot wd[token][q] for grouped row s (slot perm[s]).
-__global__ __launch_bounds__(256) void k_lora_u(const float *__restrict__ wd, const int32_t *__restrict__ perm,
-                                                const float *__restrict__ w, int S, int k, int r, float *__restrict__ u)
-{
-    const int i = blockIdx.x * blockDim.x + threadIdx.x;
-    if (i >= S * r) return;
-    const int s = i / r, q = i - s * r, slot = perm[s];
-    u[i] = w[slot] * wd[(size_t)(slot / k) * r + q];
-}
-
-// h = act(g, u) as bf16 hi + lo planes from saved pre-activations [S][2][I].
-__global__ __launch_bounds__(256) void k_h_from_gu(const float *__restrict__ gu, int S, int I, int act,
-                                                   uint16_t *__restrict__ h_hi, uint16_t *__restrict__ h_lo)
-{
-    const size_t n = (size_t)S * I;
-    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) {
-        const size_t s = i / I, c = i - s * I;
-        uint32_t hh, hl;
-        split_bf16(act_h(act, gu[(2 * s) * I + c], gu[(2 * s + 1) * I + c]), hh, hl);
-        h_hi[i] = (uint16_t)hh;
-        h_lo[i] = (uint16_t)hl;
     }
 }
 
@@ -290,21 +290,24 @@ hipError_t lora_forward_pre(const LoraW &L, const LoraWs &w, const void *x, int 
     return hipSuccess;
 }
 
-hipError_t lora_down_z(const LoraW &L, const LoraWs &w, const uint16_t *h_hi, const uint16_t *h_lo, const int32_t *inv,
-                       const float *pw, int T, int k, int I, hipStream_t s)
+// hbar and z = hbar A_d^T  [T][r]; h from its planes (gu == nullptr) or from g, u.
+hipError_t lora_down_z(const LoraW &L, const LoraWs &w, const uint16_t *h_hi, const uint16_t *h_lo, const float *gu, int act,
+                       const int32_t *inv, const float *pw, int T, int k, int I, hipStream_t s)
 {
-    const int r = L.r, S = T * k;
-    // zs = h A_d^T  [S][r] (grouped rows), z = sum_j p zs  [T][r]
-    hipError_t e = gemm(OD_PAIR, OD_F32, gargs(op(h_hi, I, 1, h_lo), op(L.A[2], 1, I), w.zs, r, 1, S, r, I, 1.f, false), w.part,
-                        w.part_cap, s);
+    const dim3 grid((I / 4 + 255) / 256, T);
+    if (gu)
+        hipLaunchKernelGGL(k_lora_hbar<true>, grid, dim3(256), 0, s, h_hi, h_lo, gu, act, inv, pw, k, I, w.hbar);
+    else
+        hipLaunchKernelGGL(k_lora_hbar<false>, grid, dim3(256), 0, s, h_hi, h_lo, gu, act, inv, pw, k, I, w.hbar);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_lora_z, dim3((T * r + 255) / 256), dim3(256), 0, s, w.zs, inv, pw, T, k, r, w.z);
-    return hipGetLastError();
+    return gemm(OD_F32, OD_F32, gargs(op(w.hbar, I, 1), op(L.A[2], 1, I), w.z, L.r, 1, T, L.r, I, 1.f, false), w.part, w.part_cap,
+                s);
 }
 
 hipError_t lora_forward_post(const LoraW &L, const LoraWs &w, const ExpertFwdArgs &a, const int32_t *inv, hipStream_t s)
 {
-    hipError_t e = lora_down_z(L, w, a.h_hi, a.h_lo, inv, a.w, a.T, a.k, a.I, s);
+    hipError_t e = lora_down_z(L, w, a.h_hi, a.h_lo, nullptr, a.act, inv, a.w, a.T, a.k, a.I, s);
     if (e != hipSuccess) return e;
     // y += s z B_d^T
     return gemm(OD_F32, OD_F32, gargs(op(w.z, L.r, 1), op(L.B[2], 1, L.r), a.y, a.H, 1, a.T, a.H, L.r, L.scale, true), w.part,
@@ -342,8 +345,8 @@ hipError_t lora_backward_post(const LoraW &L, const LoraWs &w, const ExpertBwdAr
 hipError_t lora_grads(const LoraW &L, const LoraWs &w, const ExpertBwdArgs &a, float *const dA[3], float *const dB[3],
                       hipStream_t s)
 {
-    const int r = L.r, T = a.T, H = a.H, I = a.I, S = a.T * a.k;
-    hipError_t e = lora_down_z(L, w, a.h_hi, a.h_lo, a.inv, a.w, T, a.k, I, s);
+    const int r = L.r, T = a.T, H = a.H, I = a.I;
+    hipError_t e = lora_down_z(L, w, a.h_hi, a.h_lo, a.gu, a.act, a.inv, a.w, T, a.k, I, s);
     for (int m = 0; m < 2 && e == hipSuccess; m++) {
         // dB = s dgu^T vx  [I][r];  dA = s m^T x  [r][H]
         e = gemm(OD_F32, OD_F32, gargs(op(w.dgu + (size_t)m * I, 1, 2 * I), op(w.vx + m * r, 2 * r, 1), dB[m], r, 1, I, r, T, L.scale,
@@ -356,22 +359,11 @@ hipError_t lora_grads(const LoraW &L, const LoraWs &w, const ExpertBwdArgs &a, f
     // dB_d = s dy^T z  [H][r]
     if (e == hipSuccess)
         e = gemm(od(a.dyt), OD_F32, gargs(op(a.dy, 1, H), op(w.z, r, 1), dB[2], r, 1, H, r, T, L.scale, false), w.part, w.part_cap, s);
-    // dA_d = s u^T h  [r][I], u[s] = p_s wd[t(s)]
-    if (e == hipSuccess) {
-        hipLaunchKernelGGL(k_lora_u, dim3((S * r + 255) / 256), dim3(256), 0, s, w.wd, a.perm, a.w, S, a.k, r, w.u);
-        e = hipGetLastError();
-    }
+    // dA_d = s wd^T hbar  [r][I]
     if (e == hipSuccess)
-        e = gemm(OD_F32, OD_PAIR, gargs(op(w.u, 1, r), op(a.h_hi, I, 1, a.h_lo), dA[2], I, 1, r, I, S, L.scale, false), w.part,
-                 w.part_cap, s);
+        e = gemm(OD_F32, OD_F32, gargs(op(w.wd, 1, r), op(w.hbar, I, 1), dA[2], I, 1, r, I, T, L.scale, false), w.part, w.part_cap,
+                 s);
     return e;
-}
-
-hipError_t launch_h_from_gu(const ExpertBwdArgs &a, hipStream_t s)
-{
-    const size_t n = (size_t)a.T * a.k * a.I;
-    hipLaunchKernelGGL(k_h_from_gu, dim3(blocks_for(n)), dim3(256), 0, s, a.gu, a.T * a.k, a.I, a.act, a.h_hi, a.h_lo);
-    return hipGetLastError();
 }
 
 hipError_t fill_zero(float *p, size_t n, hipStream_t s)

@@ -39,7 +39,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Layout {
     size_t logits, beta, h, ybuf, gu, dgdu, dp, xq, xqs;
-    size_t l_vx, l_gu, l_zs, l_z, l_wd, l_c, l_dgu, l_m, l_u, l_part;  // adapter (MOE_F_LORA)
+    size_t l_vx, l_gu, l_hbar, l_z, l_wd, l_c, l_dgu, l_m, l_part;  // adapter (MOE_F_LORA)
     size_t total;
 };
 
@@ -68,16 +68,15 @@ Layout layout_of(const moe_desc &d)
     L.xq = take(mx ? T * H * 2 : 0);
     L.xqs = take(mx ? T * (H / 32) * 2 : 0);
     const bool lo = (d.flags & MOE_F_LORA) != 0;
-    const size_t R = lo ? kMaxLoraRank : 0, Tl = lo ? T : 0, Sl = lo ? S : 0;
+    const size_t R = lo ? kMaxLoraRank : 0, Tl = lo ? T : 0;
     L.l_vx = take(Tl * 2 * R * 4);
     L.l_gu = take(Tl * 2 * I * 4);
-    L.l_zs = take(Sl * R * 4);
+    L.l_hbar = take(Tl * I * 4);
     L.l_z = take(Tl * R * 4);
     L.l_wd = take(Tl * R * 4);
     L.l_c = take(Tl * I * 4);
     L.l_dgu = take(Tl * 2 * I * 4);
     L.l_m = take(Tl * 2 * R * 4);
-    L.l_u = take(Sl * R * 4);
     L.l_part = take(lo ? kLoraPartFloats * 4 : 0);
     L.total = off;
     return L;
@@ -154,13 +153,12 @@ moe::LoraWs lora_ws(const moe_layer *L)
     char *b = L->ws;
     w.vx = (float *)(b + L->lay.l_vx);
     w.gu = (float *)(b + L->lay.l_gu);
-    w.zs = (float *)(b + L->lay.l_zs);
+    w.hbar = (float *)(b + L->lay.l_hbar);
     w.z = (float *)(b + L->lay.l_z);
     w.wd = (float *)(b + L->lay.l_wd);
     w.c = (float *)(b + L->lay.l_c);
     w.dgu = (float *)(b + L->lay.l_dgu);
     w.m = (float *)(b + L->lay.l_m);
-    w.u = (float *)(b + L->lay.l_u);
     w.part = (float *)(b + L->lay.l_part);
     w.part_cap = kLoraPartFloats;
     return w;
@@ -428,7 +426,7 @@ moe_status backward_impl(moe_layer *L, const void *x, int32_t xt, const void *dy
         MOE_OK)
         return st;
     if (!grads) return MOE_OK;
-    if (saved_gu && (st = device_status(moe::launch_h_from_gu(a, hs), "adapter (h from saved g, u)")) != MOE_OK) return st;
+    if (!a.gu) a.gu = a.gu_scratch;  // recomputed by the backward above
     return device_status(moe::lora_grads(L->lora, lw, a, dA, dB, hs), "adapter (gradients)");
 }
 

@@ -183,13 +183,12 @@ struct LoraW {
 struct LoraWs {
     float *vx;    // [T][2r]  A_g x | A_u x
     float *gu;    // [T][2I]  s B_g A_g x | s B_u A_u x
-    float *zs;    // [S][r]   A_d h per grouped row
+    float *hbar;  // [T][I]   sum_j p h over the token's slots
     float *z;     // [T][r]   sum_j p A_d h
     float *wd;    // [T][r]   B_d^T dy
     float *c;     // [T][I]   s A_d^T B_d^T dy
     float *dgu;   // [T][2I]  per-token sums of dL/dg | dL/du
     float *m;     // [T][2r]  B_g^T dgu_g | B_u^T dgu_u
-    float *u;     // [S][r]   p_s wd[t(s)]
     float *part;  // split-K partial sums
     size_t part_cap;  // floats
 };
@@ -199,7 +198,6 @@ hipError_t lora_backward_pre(const LoraW &L, const LoraWs &w, const void *dy, in
 hipError_t lora_backward_post(const LoraW &L, const LoraWs &w, const ExpertBwdArgs &a, bool pair, hipStream_t s);
 hipError_t lora_grads(const LoraW &L, const LoraWs &w, const ExpertBwdArgs &a, float *const dA[3], float *const dB[3],
                       hipStream_t s);
-hipError_t launch_h_from_gu(const ExpertBwdArgs &a, hipStream_t s);
 hipError_t fill_zero(float *p, size_t n, hipStream_t s);
 
 // number of I-column tiles whose partial <a, h> sums the backward stores per row

@@ -265,6 +265,21 @@ __device__ __forceinline__ void gateup_pass(const ExpertFwdArgs &a, const GuBloc
         __syncthreads();
     });
 
+    // the shared adapter's per-token terms for every tile of the lane, loaded together
+    f32x4 lgv[NT][2], luv[NT][2];
+    if (a.lora_gu) {
+#pragma unroll
+        for (int tt = 0; tt < NT; tt++) {
+            const int tok = a.perm[r0 + tt0 + min(16 * tt + li, nt - 1)] / a.k;
+#pragma unroll
+            for (int t = 0; t < 2; t++) {
+                const float *p = a.lora_gu + (size_t)tok * 2 * I + b.c0 + 16 * t + 4 * g;
+                const float4 dg = *(const float4 *)p, du = *(const float4 *)(p + I);
+                lgv[tt][t] = f32x4{dg.x, dg.y, dg.z, dg.w};
+                luv[tt][t] = f32x4{du.x, du.y, du.z, du.w};
+            }
+        }
+    }
     // lane (g, li) holds I-columns c0 + 16 (t & 1) + 4 g + 0..3 of token 16 tt + li
 #pragma unroll
     for (int tt = 0; tt < NT; tt++) {
@@ -275,7 +290,10 @@ __device__ __forceinline__ void gateup_pass(const ExpertFwdArgs &a, const GuBloc
         for (int t = 0; t < 2; t++) {
             f32x4 gv = acc[t][tt], uv = acc[t + 2][tt];
             const int n = b.c0 + 16 * t + 4 * g;
-            add_lora_gu(a.lora_gu, a.perm, a.k, rr, I, n, gv, uv);
+            if (a.lora_gu) {
+                gv += lgv[tt][t];
+                uv += luv[tt][t];
+            }
             uint32_t hh[4], hl[4];
 #pragma unroll
             for (int r = 0; r < 4; r++) split_bf16(act_h(a.act, gv[r], uv[r]), hh[r], hl[r]);
@@ -428,6 +446,21 @@ __device__ __forceinline__ void gateup_pass_mx(const ExpertFwdArgs &a, const GuB
         __syncthreads();
     });
 
+    // the shared adapter's per-token terms for every tile of the lane, loaded together
+    f32x4 lgv[NT][2], luv[NT][2];
+    if (a.lora_gu) {
+#pragma unroll
+        for (int tt = 0; tt < NT; tt++) {
+            const int tok = a.perm[r0 + tt0 + min(16 * tt + li, nt - 1)] / a.k;
+#pragma unroll
+            for (int t = 0; t < 2; t++) {
+                const float *p = a.lora_gu + (size_t)tok * 2 * I + b.c0 + 16 * t + 4 * g;
+                const float4 dg = *(const float4 *)p, du = *(const float4 *)(p + I);
+                lgv[tt][t] = f32x4{dg.x, dg.y, dg.z, dg.w};
+                luv[tt][t] = f32x4{du.x, du.y, du.z, du.w};
+            }
+        }
+    }
     // lane (g, li) holds I-columns c0 + 16 (t & 1) + 4 g + 0..3 of token 16 tt + li
 #pragma unroll
     for (int tt = 0; tt < NT; tt++) {
@@ -438,7 +471,10 @@ __device__ __forceinline__ void gateup_pass_mx(const ExpertFwdArgs &a, const GuB
         for (int t = 0; t < 2; t++) {
             f32x4 gv = acc[t][tt], uv = acc[t + 2][tt];
             const int n = b.c0 + 16 * t + 4 * g;
-            add_lora_gu(a.lora_gu, a.perm, a.k, rr, I, n, gv, uv);
+            if (a.lora_gu) {
+                gv += lgv[tt][t];
+                uv += luv[tt][t];
+            }
             uint32_t hh[4], hl[4];
 #pragma unroll
             for (int r = 0; r < 4; r++) split_bf16(act_h(a.act, gv[r], uv[r]), hh[r], hl[r]);

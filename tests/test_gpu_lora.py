@@ -80,3 +80,11 @@ def test_lora_zero_tokens_gives_zero_gradients():
     torch.cuda.synchronize()
     assert all(float(t.abs().max()) == 0.0 for t in dA + dB)
     L.close()
+
+
+@pytest.mark.parametrize("T,rank", [(100, 48), (5, 64)])
+def test_lora_ranks_above_32(T, rank):
+    # ranks past 32 split the row sums and the wide products into two passes over the rank;
+    # 100 tokens take the tall products, 5 the per-output dot products
+    run_lora(_case(syn.shrink(TINY, T=T, H=512, I=256, E=8, k=4, x_dtype="bf16", with_dy=True, x_key=58 + T)),
+             f"lora-rank{rank}", rank=rank)

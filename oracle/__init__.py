@@ -72,6 +72,8 @@ def lib():
         L.oracle_topk_softmax.restype = i
         L.oracle_topk_softmax.argtypes = [i, i, i, vp, vp, vp]
         L.oracle_group.argtypes = [i, i, i, vp, vp, vp, vp, vp, vp, vp]
+        L.oracle_softmax_at.argtypes = [i, i, i, vp, vp, vp]
+        L.oracle_softmax_at.restype = None
         L.oracle_expert_forward.argtypes = [vp, i, i, i, vp, vp, vp, vp, vp]
         L.oracle_forward.argtypes = [i, i, i, i, vp, vp, vp, vp, vp, i]
         L.oracle_backward_input.argtypes = [i, i, i, i, vp, vp, vp, vp, vp, vp, vp, i]
@@ -196,10 +198,26 @@ def topk_softmax(logits: np.ndarray, k: int):
     return ids, w
 
 
-def route(x64, wr, bias, k, nthreads=None):
-    """(ids [T][k] int32, w [T][k] float64, logits [T][E] float64)."""
+def softmax_at(logits: np.ndarray, ids: np.ndarray):
+    """Softmax of each row of logits over the experts ids[t] (in that order)."""
+    logits = np.ascontiguousarray(logits, np.float64)
+    ids = np.ascontiguousarray(ids, np.int32)
+    T, E = logits.shape
+    k = ids.shape[1]
+    w = np.empty((T, k), np.float64)
+    lib().oracle_softmax_at(T, E, k, _p(logits), _p(ids), _p(w))
+    return w
+
+
+def route(x64, wr, bias, k, nthreads=None, bias_mode=1):
+    """(ids [T][k] int32, w [T][k] float64, logits [T][E] float64).  bias_mode 1: the bias is
+    part of the logits (selection and weights); 2: it selects only, the weights are the
+    softmax of the unbiased logits over the selected experts.  The returned logits are the
+    selection keys."""
     logits = router_logits(x64, wr, bias, nthreads)
     ids, w = topk_softmax(logits, k)
+    if bias is not None and bias_mode == 2:
+        w = softmax_at(router_logits(x64, wr, None, nthreads), ids)
     return ids, w, logits
 
 
@@ -269,9 +287,9 @@ def lora_grads(x64, dy64, ids, w, W: Weights, nthreads=None):
     return dA, dB
 
 
-def layer_forward(x64, wr, bias, k, W: Weights, nthreads=None):
+def layer_forward(x64, wr, bias, k, W: Weights, nthreads=None, bias_mode=1):
     """Route then run the experts: (y, ids, w)."""
-    ids, w, _ = route(x64, wr, bias, k, nthreads)
+    ids, w, _ = route(x64, wr, bias, k, nthreads, bias_mode)
     return forward(x64, ids, w, W, nthreads), ids, w
 
 

@@ -215,6 +215,25 @@ int oracle_topk_softmax(int T, int E, int k, const double *logits, int32_t *ids,
     return 0;
 }
 
+/* Softmax of each token's logits over given experts (ids[t][0..k), in their
+ * order): w[t][j] = exp(l_j - m) / sum_j' exp(l_j' - m), m the largest of
+ * them.  With a selection-only router bias the ids come from the biased
+ * logits and the weights from the unbiased ones (the bias corrects which
+ * experts are chosen, not how they are combined). */
+void oracle_softmax_at(int T, int E, int k, const double *logits, const int32_t *ids, double *w)
+{
+    for (int t = 0; t < T; t++) {
+        const double *l = logits + (size_t)t * E;
+        const int32_t *id = ids + (size_t)t * k;
+        double m = l[id[0]];
+        for (int j = 1; j < k; j++)
+            if (l[id[j]] > m) m = l[id[j]];
+        double den = 0.0;
+        for (int j = 0; j < k; j++) den += exp(l[id[j]] - m);
+        for (int j = 0; j < k; j++) w[(size_t)t * k + j] = exp(l[id[j]] - m) / den;
+    }
+}
+
 /* ------------------------------------------------------------------ */
 /* grouping                                                            */
 /* ------------------------------------------------------------------ */

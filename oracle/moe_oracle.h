@@ -40,6 +40,7 @@ void oracle_decode_matrix(const oracle_weights *W, int mat, int e, int H, int I,
 void oracle_router_logits(int T, int H, int E, const double *x, const double *wr, const double *bias,
                           double *logits, int nthreads);
 int oracle_topk_softmax(int T, int E, int k, const double *logits, int32_t *ids, double *w);
+void oracle_softmax_at(int T, int E, int k, const double *logits, const int32_t *ids, double *w);
 void oracle_group(int T, int k, int E, const int32_t *ids, int32_t *counts, int32_t *offsets, int32_t *perm,
                   int32_t *inv, int32_t *active, int32_t *n_active);
 void oracle_expert_forward(const oracle_weights *W, int e, int H, int I, const double *x, double *g_out,

@@ -142,6 +142,31 @@ def _tiny_router(seed=0, T=8, H=256, E=16):
     return x.astype(np.float64), wr
 
 
+def test_selection_only_bias():
+    """bias_mode 2: the bias picks the experts, the unbiased logits weight them.  A large
+    bias on each token's lowest-logit expert forces it into the top 2; its weight is then
+    the sigmoid of the UNBIASED logit gap (k = 2 closed form), and the selection equals the
+    one of bias_mode 1; a zero bias gives mode 1's weights bit for bit."""
+    x, wr = _tiny_router(5)
+    T, E = x.shape[0], wr.shape[0]
+    raw = oracle.router_logits(x, wr)
+    low = np.argmin(raw, axis=1)
+    for t in range(T):
+        bias = np.zeros(E, np.float32)
+        bias[low[t]] = 100.0
+        ids2, p2, keys = oracle.route(x[t:t + 1], wr, bias, 2, bias_mode=2)
+        ids1, p1, _ = oracle.route(x[t:t + 1], wr, bias, 2, bias_mode=1)
+        assert np.array_equal(ids1, ids2) and ids2[0, 0] == low[t]
+        l1, l2 = raw[t, ids2[0, 0]], raw[t, ids2[0, 1]]
+        assert abs(p2[0, 0] - 1.0 / (1.0 + math.exp(l2 - l1))) <= 1e-15
+        assert abs(p2.sum() - 1.0) <= 1e-15
+        assert p2[0, 0] < 0.5 < p1[0, 0]  # forced in by the bias, yet the smaller weight
+    z = np.zeros(E, np.float32)
+    a = oracle.route(x, wr, z, 4, bias_mode=2)
+    b = oracle.route(x, wr, z, 4, bias_mode=1)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
 def test_router_logits_against_numpy_and_fsum():
     x, wr = _tiny_router(1)
     b = np.linspace(-1, 1, wr.shape[0]).astype(np.float32)
@@ -425,25 +450,27 @@ def test_backward_is_linear_in_dy():
     assert np.allclose(a, b, rtol=1e-12, atol=1e-14 * np.abs(b).max())
 
 
-def _loss(x, dy, wr, bias, k, W):
-    y, ids, _ = oracle.layer_forward(x, wr, bias, k, W, nthreads=1)
+def _loss(x, dy, wr, bias, k, W, bias_mode=1):
+    y, ids, _ = oracle.layer_forward(x, wr, bias, k, W, nthreads=1, bias_mode=bias_mode)
     return float(np.sum(dy * y)), ids
 
 
-@pytest.mark.parametrize("with_bias,act,lora", [(False, 0, False), (True, 0, False), (False, 1, False),
-                                                (False, 0, True), (True, 1, True)])
-def test_backward_matches_central_finite_differences(with_bias, act, lora):
+@pytest.mark.parametrize("with_bias,act,lora,bias_mode", [(False, 0, False, 1), (True, 0, False, 1), (False, 1, False, 1),
+                                                          (False, 0, True, 1), (True, 1, True, 1), (True, 0, False, 2),
+                                                          (True, 1, True, 2)])
+def test_backward_matches_central_finite_differences(with_bias, act, lora, bias_mode):
     """Directional derivatives of L(x) = sum_t <dY_t, y_t(x)> by central differences in fp64,
     with a step relative to the tensor norm and routing-flip detection (a direction whose
     perturbation changes any token's expert set is retried with half the step); SwiGLU and
-    SiTU experts, with and without the shared adapter."""
+    SiTU experts, with and without the shared adapter, with the router bias in the logits or
+    in the selection only."""
     w0 = syn.WORKLOADS["tiny"]
     w, W = _tiny_layer(act=act, lora=_tiny_lora(w0) if lora else None)
     x = oracle.to_f64(syn.activations(w), "f32")
     wr = syn.router_weight(w)
     bias = np.linspace(-0.3, 0.3, w.E).astype(np.float32) if with_bias else None
     dy = oracle.to_f64(syn.upstream_grad(w), "f32") * 100.0
-    ids, p, _ = oracle.route(x, wr, bias, w.k)
+    ids, p, _ = oracle.route(x, wr, bias, w.k, bias_mode=bias_mode)
     dx = oracle.backward_input(x, dy, ids, p, wr, W)
     rng = np.random.default_rng(99)
     dirs = [rng.standard_normal(x.shape) for _ in range(6)]
@@ -455,8 +482,8 @@ def test_backward_matches_central_finite_differences(with_bias, act, lora):
     for v in dirs:
         eps = 1e-6 * np.linalg.norm(x) / np.linalg.norm(v)
         for _ in range(8):
-            lp, ip = _loss(x + eps * v, dy, wr, bias, w.k, W)
-            lm, im = _loss(x - eps * v, dy, wr, bias, w.k, W)
+            lp, ip = _loss(x + eps * v, dy, wr, bias, w.k, W, bias_mode)
+            lm, im = _loss(x - eps * v, dy, wr, bias, w.k, W, bias_mode)
             if np.array_equal(ip, ids) and np.array_equal(im, ids):
                 break
             eps /= 2

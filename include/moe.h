@@ -85,7 +85,9 @@ typedef struct {
     int32_t max_tokens;  /* largest T any call on this layer will pass; sizes the workspace */
     int32_t wfmt;        /* moe_wfmt */
     int32_t act;         /* moe_act: the gated activation h = act(gate, up) */
-    int32_t bias_mode;   /* 0: no router bias; 1: bias added to the logits (selection and weights) */
+    int32_t bias_mode;   /* 0: no router bias; 1: bias added to the logits (selection and weights);
+                            2: bias for the selection only (the weights are the softmax of the
+                            unbiased logits over the selected experts) */
     uint32_t flags;
 } moe_desc;
 
@@ -106,7 +108,7 @@ typedef struct {
  *   of a row equal the sum over the three stages s of
  *   rvq_cb[m][e][s][rvq_idx[m][e][s][row][v]].  Both 16-byte aligned.
  * router_w is [E][H] fp32; router_b is [E] fp32 or NULL (required when
- * bias_mode = 1). */
+ * bias_mode = 1 or 2). */
 typedef struct {
     const float *router_w;
     const float *router_b;

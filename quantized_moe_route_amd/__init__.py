@@ -82,21 +82,22 @@ class MoELayer:
 
     MXFP4: pass codes=[gate, up, down] ([E][out][in/2] uint8) and scales ([E][out][in/32] uint8).
     RVQ3:  pass rvq_idx=[...] ([E][3][out][in/8] uint8) and rvq_cb=[...] ([E][3][256][8] fp16 bits).
-    router_w: [E][H] fp32; router_b: [E] fp32 or None.  All tensors on the same GPU and kept
-    alive by this object.
+    router_w: [E][H] fp32; router_b: [E] fp32 or None.  bias_mode: 1 (default with a bias) adds
+    the bias to the logits, 2 uses it for the selection only.  All tensors on the same GPU and
+    kept alive by this object.
     """
 
     def __init__(self, *, hidden: int, inter: int, n_experts: int, top_k: int, max_tokens: int, router_w,
                  router_b=None, codes: Optional[Sequence] = None, scales: Optional[Sequence] = None,
                  rvq_idx: Optional[Sequence] = None, rvq_cb: Optional[Sequence] = None, flags: int = 0,
-                 act: int = 0):
+                 act: int = 0, bias_mode: Optional[int] = None):
         torch = _torch()
         L = C.lib()
         d = C.MoeDesc()
         L.moe_desc_init(ctypes.byref(d))
         d.hidden, d.inter, d.n_experts, d.top_k, d.max_tokens = hidden, inter, n_experts, top_k, max_tokens
         d.wfmt = C.MOE_W_MXFP4 if codes is not None else C.MOE_W_RVQ3
-        d.bias_mode = 1 if router_b is not None else 0
+        d.bias_mode = (1 if router_b is not None else 0) if bias_mode is None else bias_mode
         d.flags |= flags
         d.act = act
         self.desc = d

@@ -97,7 +97,7 @@ moe_status check_desc(const moe_desc *d)
     if (d->wfmt != MOE_W_MXFP4 && d->wfmt != MOE_W_RVQ3) return fail(MOE_ERR_INVALID_ARG, "unknown wfmt %d", d->wfmt);
     if (d->act != MOE_ACT_SWIGLU && d->act != MOE_ACT_SITU)
         return fail(MOE_ERR_UNSUPPORTED, "activation %d is not implemented", d->act);
-    if (d->bias_mode != 0 && d->bias_mode != 1)
+    if (d->bias_mode < 0 || d->bias_mode > 2)
         return fail(MOE_ERR_UNSUPPORTED, "bias_mode %d is not implemented", d->bias_mode);
     return MOE_OK;
 }
@@ -234,7 +234,7 @@ moe_status moe_layer_create(const moe_desc *d, const moe_weights *w, void *works
     if (!out) return fail(MOE_ERR_INVALID_ARG, "out is NULL");
     if (!w->router_w) return fail(MOE_ERR_INVALID_ARG, "router_w is NULL");
     if (!aligned(w->router_w, 16)) return fail(MOE_ERR_INVALID_ARG, "router_w must be 16-byte aligned");
-    if (d->bias_mode == 1 && !w->router_b) return fail(MOE_ERR_INVALID_ARG, "bias_mode=1 needs router_b");
+    if (d->bias_mode != 0 && !w->router_b) return fail(MOE_ERR_INVALID_ARG, "bias_mode=%d needs router_b", d->bias_mode);
     static const char *names[3] = {"gate", "up", "down"};
     for (int m = 0; m < 3; m++) {
         if (d->wfmt == MOE_W_MXFP4) {
@@ -277,7 +277,8 @@ moe_status moe_route(moe_layer *L, const void *x, int32_t xt, int32_t T, const m
     a.x = x;
     a.xt = xt;
     a.wr = L->w.router_w;
-    a.bias = L->d.bias_mode == 1 ? L->w.router_b : nullptr;
+    a.bias = L->d.bias_mode != 0 ? L->w.router_b : nullptr;
+    a.wbias = L->d.bias_mode == 2 ? L->w.router_b : nullptr;
     a.T = T;
     a.H = L->d.hidden;
     a.E = L->d.n_experts;

@@ -55,7 +55,8 @@ struct RouteArgs {
     const void *x;
     int xt;
     const float *wr;
-    const float *bias;
+    const float *bias;   // added to the logits (bias modes 1 and 2)
+    const float *wbias;  // bias mode 2: taken back out of the selected logits for the weights, else null
     int T, H, E, k;
     float *logits;  // [T][E] workspace
     float *beta;    // [T][E] workspace

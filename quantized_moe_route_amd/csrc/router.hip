@@ -450,7 +450,8 @@ __device__ __forceinline__ void topk_one(int t, const float *__restrict__ logits
                                          const void *__restrict__ x, int xt, const float *__restrict__ wr,
                                          const float *__restrict__ bias, int H, int E, int k,
                                          int32_t *__restrict__ ids, float *__restrict__ wts,
-                                         int32_t *__restrict__ refined, TopkScratch &sc, int *lds_ids = nullptr)
+                                         int32_t *__restrict__ refined, TopkScratch &sc, int *lds_ids = nullptr,
+                                         const float *__restrict__ wbias = nullptr)
 {
     const int lane = threadIdx.x & 63;
     const float NEG = -__builtin_huge_valf();
@@ -552,8 +553,11 @@ __device__ __forceinline__ void topk_one(int t, const float *__restrict__ logits
     // 5. softmax over the selected fp32 logits, in rank order (rank 0 holds the
     // largest unless the fp64 ranking reordered them)
     const int my_id = lane < k ? rank_id : 0;
-    const float lj = lane >= k ? NEG : !reranked ? rank_l : logits[(size_t)t * E + my_id];
-    const float mx = reranked ? wave_max_f32(lj) : readlane_f32(lj, 0);
+    float lj = lane >= k ? NEG : !reranked ? rank_l : logits[(size_t)t * E + my_id];
+    // a selection-only bias (wbias) is taken back out of the selected keys: the weights
+    // are the softmax of the unbiased logits, whose largest need not rank first
+    if (wbias && lane < k) lj -= wbias[my_id];
+    const float mx = reranked || wbias ? wave_max_f32(lj) : readlane_f32(lj, 0);
     const float ex = lane < k ? __expf(lj - mx) : 0.f;
     const float den = wave_sum_f32(ex);
     if (lane < k) {
@@ -569,13 +573,13 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, 
                                               const void *__restrict__ x, int xt, const float *__restrict__ wr,
                                               const float *__restrict__ bias, int T, int H, int E, int k,
                                               int32_t *__restrict__ ids, float *__restrict__ wts,
-                                              int32_t *__restrict__ refined)
+                                              int32_t *__restrict__ refined, const float *__restrict__ wbias)
 {
     __shared__ TopkScratch scs[4];
     const int wv = threadIdx.x >> 6;
     const int t = blockIdx.x * 4 + wv;
     if (t >= T) return;
-    topk_one<PL>(t, logits, beta, x, xt, wr, bias, H, E, k, ids, wts, refined, scs[wv]);
+    topk_one<PL>(t, logits, beta, x, xt, wr, bias, H, E, k, ids, wts, refined, scs[wv], nullptr, wbias);
 }
 
 // Position of q among the sorted s[0, 128) (entries past the slot count hold INT_MAX):
@@ -607,7 +611,7 @@ __global__ __launch_bounds__(256) void k_topk_group(const RouteArgs a, const Gro
     const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
     if (wv < a.T)  // T <= 4
         topk_one<PL>(wv, a.logits, a.beta, a.x, a.xt, a.wr, a.bias, a.H, a.E, a.k, a.ids, a.w, a.refined, scs[wv],
-                     sids);
+                     sids, a.wbias);
     __syncthreads();
 
     const int S = a.T * a.k, E = a.E;
@@ -736,7 +740,7 @@ static hipError_t launch_topk_pl(const RouteArgs &a, hipStream_t s)
     const dim3 grid((a.T + 3) / 4);
     ProfScope ps(a.prof, PK_ROUTER_TOPK, s);
     ps.launch(k_topk<PL>, grid, dim3(256), 0, a.logits, a.beta, a.x, a.xt, a.wr, a.bias, a.T, a.H, a.E,
-                       a.k, a.ids, a.w, a.refined);
+                       a.k, a.ids, a.w, a.refined, a.wbias);
     return hipGetLastError();
 }
 

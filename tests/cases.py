@@ -29,6 +29,7 @@ class HostCase:
     idx: Optional[List[np.ndarray]] = None
     cb: Optional[List[np.ndarray]] = None
     act: int = 0  # 0 SwiGLU, 1 SiTU
+    bias_mode: int = 1  # with a bias: 1 in the logits, 2 selection only
     lora: Optional[tuple] = None  # (A [3], B [3], scale) fp32 arrays: the shared adapter
 
     @property
@@ -67,7 +68,7 @@ def device_layer(c: HostCase, max_tokens: int, flags: int = 0):
     w = c.w
     kw = dict(hidden=w.H, inter=w.I, n_experts=w.E, top_k=w.k, max_tokens=max_tokens,
               router_w=q.to_device(c.wr), router_b=None if c.bias is None else q.to_device(c.bias), flags=flags,
-              act=c.act)
+              act=c.act, bias_mode=None if c.bias is None else c.bias_mode)
     if c.codes is not None:
         kw["codes"] = [q.to_device(a) for a in c.codes]
         kw["scales"] = [q.to_device(a) for a in c.scales]
@@ -119,7 +120,7 @@ def lora_parity(c: HostCase, L, name: str, rank: int = 16, scale: float = 2.0, s
     x = act_tensor(c.x, w.x_dtype)
     dy = act_tensor(c.dy, w.x_dtype)
     r = L.route(x)
-    ids, p, _ = oracle.route(c.x64, c.wr, c.bias, w.k)
+    ids, p, _ = oracle.route(c.x64, c.wr, c.bias, w.k, bias_mode=c.bias_mode)
     torch.cuda.synchronize()
     assert np.array_equal(np_(r.ids), ids), f"{name}: routing ids"
     W = c.oracle_weights()

@@ -104,6 +104,7 @@ def test_create_validation_and_destroy():
     w.router_w = None
     assert _create(d, w)[0] == C.MOE_ERR_INVALID_ARG
     assert _create(_desc(max_tokens=8, bias_mode=1), _fake_weights())[0] == C.MOE_ERR_INVALID_ARG
+    assert _create(_desc(max_tokens=8, bias_mode=2), _fake_weights())[0] == C.MOE_ERR_INVALID_ARG
     assert _create(d, _fake_weights(), ws_bytes=16)[0] == C.MOE_ERR_WORKSPACE
     assert _create(d, _fake_weights(), ws=0x100010)[0] == C.MOE_ERR_WORKSPACE
     assert _create(_desc(max_tokens=8, wfmt=C.MOE_W_RVQ3), _fake_weights())[0] == C.MOE_ERR_INVALID_ARG

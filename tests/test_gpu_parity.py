@@ -40,7 +40,7 @@ def run_small(c, T=None, saved=True, name="", flags=0):
     L = device_layer(c, max_tokens=max(T, 1), flags=flags)
     x = act_tensor(c.x, w.x_dtype)
     r = L.route(x)
-    ids, p, _ = oracle.route(c.x64, c.wr, c.bias, w.k)
+    ids, p, _ = oracle.route(c.x64, c.wr, c.bias, w.k, bias_mode=c.bias_mode)
     check_routing(r, ids, p, w.E, name)
     W = c.oracle_weights()
     y_ref = oracle.forward(c.x64, ids, p, W)
@@ -72,6 +72,17 @@ def test_tiny_config_full():
 def test_tiny_bf16_activations_and_bias():
     w = syn.shrink(TINY, x_dtype="bf16", bias_sd=0.5, x_key=7)
     run_small(host_case(w), name="tiny-bf16-bias")
+
+
+@pytest.mark.parametrize("T,k,E", [(1, 8, 64), (4, 16, 128), (8, 2, 16), (100, 4, 40)])
+def test_selection_only_router_bias(T, k, E):
+    """bias_mode 2: the bias (sd 1, large against the logits) decides the selection, the
+    unbiased logits the weights; the fused small-batch routing (T <= 4), the per-token
+    top-k kernel, the generic and few-token expert paths, and the router term of dX."""
+    w = syn.shrink(TINY, T=T, k=k, E=E, x_dtype="bf16", bias_sd=1.0, with_dy=True, x_key=70 + T)
+    c = host_case(w)
+    c.bias_mode = 2
+    run_small(c, name=f"bias-select-T{T}")
 
 
 def test_ragged_shapes_span_tiles():

@@ -72,6 +72,10 @@ def lib():
         L.oracle_topk_softmax.restype = i
         L.oracle_topk_softmax.argtypes = [i, i, i, vp, vp, vp]
         L.oracle_group.argtypes = [i, i, i, vp, vp, vp, vp, vp, vp, vp]
+        L.oracle_e4m3.argtypes = [ctypes.c_uint]
+        L.oracle_e4m3.restype = ctypes.c_double
+        L.oracle_quantize_mxfp8.argtypes = [i, vp, vp, vp]
+        L.oracle_quantize_mxfp8.restype = None
         L.oracle_softmax_at.argtypes = [i, i, i, vp, vp, vp]
         L.oracle_softmax_at.restype = None
         L.oracle_expert_forward.argtypes = [vp, i, i, i, vp, vp, vp, vp, vp]
@@ -196,6 +200,22 @@ def topk_softmax(logits: np.ndarray, k: int):
     if rc != 0:
         raise ValueError("oracle top-k: non-finite logit or bad k")
     return ids, w
+
+
+def e4m3(code: int) -> float:
+    """Value of an OCP MX v1.0 FP8 E4M3 code."""
+    return lib().oracle_e4m3(code)
+
+
+def quantize_mxfp8(x64: np.ndarray):
+    """OCP MX v1.0 MXFP8 (E4M3) quantization of each row in blocks of 32 consecutive
+    elements: (the represented values q * 2^shared as float64, the shared exponents)."""
+    x64 = np.ascontiguousarray(x64, np.float64)
+    assert x64.shape[-1] % 32 == 0
+    xq = np.empty_like(x64)
+    exps = np.empty(x64.size // 32, np.int32)
+    lib().oracle_quantize_mxfp8(x64.size, _p(x64), _p(xq), _p(exps))
+    return xq, exps.reshape(x64.shape[:-1] + (x64.shape[-1] // 32,))
 
 
 def softmax_at(logits: np.ndarray, ids: np.ndarray):

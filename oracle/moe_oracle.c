@@ -72,6 +72,67 @@ double oracle_fp16(uint16_t h)
     return sign ? -v : v;
 }
 
+/* OCP MX v1.0 FP8 E4M3: bit 7 sign, bits 6..3 exponent with bias 7, bits 2..0
+ * mantissa; exponent field 0 is subnormal (m/8 * 2^-6); exponent 15 with
+ * mantissa 7 is NaN, so the largest normal is 1.75 * 2^8 = 448. */
+double oracle_e4m3(unsigned code)
+{
+    unsigned sign = (code >> 7) & 1u, ef = (code >> 3) & 15u, mf = code & 7u;
+    double mag;
+    if (ef == 15u && mf == 7u)
+        mag = NAN;
+    else if (ef == 0)
+        mag = ldexp((double)mf, -9);
+    else
+        mag = ldexp(8.0 + (double)mf, (int)ef - 10);
+    return sign ? -mag : mag;
+}
+
+/* v rounded to the nearest E4M3 value, ties to the even mantissa, magnitudes
+ * past 448 saturated to 448 (the MX conversion's clamp).  v is exact here: the
+ * grid step of the binade of v is 2^(floor(log2|v|) - 3), 2^-9 below 2^-6. */
+static double round_e4m3(double v)
+{
+    double a = fabs(v);
+    if (a == 0.0) return v;
+    int ex;
+    frexp(a, &ex);                  /* a in [2^(ex-1), 2^ex) */
+    int e = ex - 1;                 /* floor(log2 a) */
+    double step = ldexp(1.0, (e < -6 ? -6 : e) - 3);
+    double q = a / step;            /* exact: step is a power of two */
+    double f = floor(q), r = q - f;
+    if (r > 0.5 || (r == 0.5 && fmod(f, 2.0) != 0.0)) f += 1.0;
+    double m = f * step;
+    if (m > 448.0) m = 448.0;
+    return v < 0 ? -m : m;
+}
+
+/* OCP MX v1.0 conversion of a row of floats to MXFP8 (E4M3), blocks of 32
+ * consecutive elements: the block's shared exponent is floor(log2 max|v|)
+ * minus E4M3's largest exponent (8), clamped to E8M0's range [-127, 127] (an
+ * all-zero block keeps exponent -127); each element is v / 2^shared rounded to
+ * E4M3 and saturated.  xq receives the represented values q * 2^shared (the
+ * activations an MXFP8 product consumes), exp the shared exponents. */
+void oracle_quantize_mxfp8(int n, const double *x, double *xq, int32_t *exps)
+{
+    for (int b = 0; b < n / 32; b++) {
+        const double *v = x + 32 * b;
+        double amax = 0.0;
+        for (int i = 0; i < 32; i++)
+            if (fabs(v[i]) > amax) amax = fabs(v[i]);
+        int se = -127;
+        if (amax > 0.0) {
+            int ex;
+            frexp(amax, &ex);
+            se = (ex - 1) - 8;
+            if (se < -127) se = -127;
+            if (se > 127) se = 127;
+        }
+        if (exps) exps[b] = se;
+        for (int i = 0; i < 32; i++) xq[32 * b + i] = ldexp(round_e4m3(ldexp(v[i], -se)), se);
+    }
+}
+
 /* ------------------------------------------------------------------ */
 /* weight access                                                       */
 /* ------------------------------------------------------------------ */

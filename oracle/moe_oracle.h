@@ -33,6 +33,8 @@ typedef struct {
 enum { ORACLE_ACT_SWIGLU = 0, ORACLE_ACT_SITU = 1 };
 
 double oracle_e2m1(unsigned code);
+double oracle_e4m3(unsigned code);
+void oracle_quantize_mxfp8(int n, const double *x, double *xq, int32_t *exps);
 double oracle_e8m0(unsigned b);
 double oracle_fp16(uint16_t h);
 void oracle_decode_row(const oracle_weights *W, int mat, int e, int H, int I, int row, double *out);

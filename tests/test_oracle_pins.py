@@ -142,6 +142,73 @@ def _tiny_router(seed=0, T=8, H=256, E=16):
     return x.astype(np.float64), wr
 
 
+def test_e4m3_table_against_ocp_mx_landmarks():
+    for row in _golden_rows("e4m3_ocp_mx_v1.txt"):
+        code, val = int(row.split()[0], 16), row.split()[1]
+        got = oracle.e4m3(code)
+        if val == "nan":
+            assert math.isnan(got), hex(code)
+        else:
+            assert got == float(val) and math.copysign(1, got) == math.copysign(1, float(val)), (hex(code), got)
+
+
+def _e4m3_finite():
+    vals = [oracle.e4m3(c) for c in range(256)]
+    return np.array(sorted({v for v in vals if not math.isnan(v) and v >= 0}))
+
+
+def test_mxfp8_quantizer_grid_ties_and_saturation():
+    """With a block whose largest magnitude lies in [256, 512) the shared exponent is 0, so
+    the quantizer rounds elements straight onto the E4M3 grid: every finite E4M3 value is a
+    fixed point, midpoints go to the even mantissa, other points to the nearest value, and
+    magnitudes past 448 saturate to 448 (the MX conversion's clamp)."""
+    grid = _e4m3_finite()
+    assert grid.size == 127 and grid[-1] == 448.0
+    mids = (grid[:-1] + grid[1:]) / 2
+    inner = grid[:-1] + (grid[1:] - grid[:-1]) * 0.3
+    for vals in (grid, mids, inner, -grid, -mids):
+        n = (len(vals) + 30) // 31 * 31
+        v = np.resize(vals, n).reshape(-1, 31)
+        blocks = np.concatenate([np.full((v.shape[0], 1), 300.0), v], axis=1)  # amax in [256, 512)
+        xq, ex = oracle.quantize_mxfp8(blocks)
+        assert np.all(ex == 0)
+        got, src = xq[:, 1:].ravel()[: len(vals)], v.ravel()[: len(vals)]
+        a = np.abs(src)
+        # reference: nearest grid value, ties to the even code (the even mantissa)
+        idx = np.searchsorted(grid, a)
+        lo, hi = grid[np.maximum(idx - 1, 0)], grid[np.minimum(idx, grid.size - 1)]
+        want = np.where(a - lo < hi - a, lo, hi)
+        tie = (a - lo) == (hi - a)
+        codes = {oracle.e4m3(c): c for c in range(128) if not math.isnan(oracle.e4m3(c))}
+        even_lo = np.array([codes[x] % 2 == 0 for x in lo])
+        want = np.where(tie, np.where(even_lo, lo, hi), want)
+        want = np.where(np.isin(a, grid), a, want)
+        assert np.array_equal(np.abs(got), want), np.argwhere(np.abs(got) != want)[:5]
+        assert np.array_equal(np.signbit(got), np.signbit(src))  # the sign is kept, also for -0
+    # saturation, the shared exponent of powers of two, an all-zero block
+    xq, ex = oracle.quantize_mxfp8(np.array([[460.0, 500.0, -511.0] + [1.0] * 29]))
+    assert ex[0, 0] == 0 and list(xq[0, :3]) == [448.0, 448.0, -448.0]
+    for k in (-20, -3, 0, 5, 40):
+        xq, ex = oracle.quantize_mxfp8(np.array([[2.0 ** k] + [0.0] * 31]))
+        assert ex[0, 0] == k - 8 and xq[0, 0] == 2.0 ** k
+    xq, ex = oracle.quantize_mxfp8(np.zeros((1, 32)))
+    assert ex[0, 0] == -127 and not xq.any()
+
+
+def test_mxfp8_quantizer_against_torch_float8():
+    """Inside the E4M3 range PyTorch's float8_e4m3fn cast rounds to nearest even, the same
+    decision the quantizer takes: compare on random blocks scaled by their shared exponent."""
+    import torch
+    rng = np.random.default_rng(3)
+    x = (rng.standard_normal((64, 32)) * np.exp2(rng.integers(-10, 10, (64, 1)))).astype(np.float32).astype(np.float64)
+    xq, ex = oracle.quantize_mxfp8(x)
+    scaled = x / np.exp2(ex)
+    assert np.abs(scaled).max() < 512
+    inside = np.minimum(np.abs(scaled), 448.0) * np.sign(scaled)
+    ref = torch.tensor(inside, dtype=torch.float32).to(torch.float8_e4m3fn).to(torch.float64).numpy() * np.exp2(ex)
+    assert np.array_equal(xq, ref)
+
+
 def test_selection_only_bias():
     """bias_mode 2: the bias picks the experts, the unbiased logits weight them.  A large
     bias on each token's lowest-logit expert forces it into the top 2; its weight is then

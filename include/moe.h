@@ -73,7 +73,14 @@ enum {
                                  scales and x as two E4M3 terms with per-32 scales (exact to about
                                  2^-20 of each block's maximum); more workspace (3H + H/16 bytes per
                                  token).  Off: exact bf16 dequantization and bf16 MFMA. */
-    MOE_F_LORA = 4u           /* workspace for a shared low-rank adapter (moe_set_lora) */
+    MOE_F_LORA = 4u,          /* workspace for a shared low-rank adapter (moe_set_lora) */
+    MOE_F_QUANT_X8 = 8u       /* moe_forward quantizes x to MXFP8 before the expert products (OCP MX
+                                 v1.0: E4M3 elements, one E8M0 scale per 32 consecutive elements,
+                                 shared exponent floor(log2 max|x|) - 8, round to nearest even,
+                                 saturation at 448): activation-quantized prefill.  The routing
+                                 (moe_route) sees x unquantized; moe_backward_input stays the exact
+                                 layer's gradient.  H must be a multiple of 32 (always).  More
+                                 workspace: 2 H bytes per token. */
 };
 
 /* Layer description.  moe_desc_init() fills the K3 defaults. */

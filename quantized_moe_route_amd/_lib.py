@@ -14,6 +14,7 @@ MOE_F_DETERMINISTIC = 1
 MOE_ACT_SWIGLU, MOE_ACT_SITU = 0, 1
 MOE_F_MX_GATEUP = 2
 MOE_F_LORA = 4
+MOE_F_QUANT_X8 = 8
 
 EXPORTED = (
     "moe_desc_init", "moe_workspace_size", "moe_layer_create", "moe_route", "moe_forward",

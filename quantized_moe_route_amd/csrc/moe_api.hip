@@ -40,6 +40,7 @@ size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 struct Layout {
     size_t logits, beta, h, ybuf, gu, dgdu, dp, xq, xqs;
     size_t l_vx, l_gu, l_hbar, l_z, l_wd, l_c, l_dgu, l_m, l_part;  // adapter (MOE_F_LORA)
+    size_t xq8;  // MXFP8-quantized activations as bf16 (MOE_F_QUANT_X8)
     size_t total;
 };
 
@@ -78,6 +79,7 @@ Layout layout_of(const moe_desc &d)
     L.l_dgu = take(Tl * 2 * I * 4);
     L.l_m = take(Tl * 2 * R * 4);
     L.l_part = take(lo ? kLoraPartFloats * 4 : 0);
+    L.xq8 = take((d.flags & MOE_F_QUANT_X8) ? T * H * 2 : 0);
     L.total = off;
     return L;
 }
@@ -346,8 +348,17 @@ moe_status moe_forward(moe_layer *L, const void *x, int32_t xt, int32_t T, const
         a.xq_s = (uint8_t *)(L->ws + L->lay.xqs);
     }
     a.prof = &L->prof;
-    moe::set_lds_staging(a);
     const hipStream_t hs = (hipStream_t)stream;
+    if (L->d.flags & MOE_F_QUANT_X8) {
+        // the experts (and the adapter) see x quantized to MXFP8; the routing came from x
+        uint16_t *xq = (uint16_t *)(L->ws + L->lay.xq8);
+        if ((st = device_status(moe::launch_quant_x8(x, xt, (size_t)T * a.H, xq, hs), "quantize x")) != MOE_OK) return st;
+        a.x = xq;
+        a.xt = MOE_DT_BF16;  // the same code as the kernels' bf16 token type
+        x = xq;
+        xt = MOE_DT_BF16;
+    }
+    moe::set_lds_staging(a);
     if (!L->has_lora) return device_status(moe::launch_expert_forward(a, hs), "forward");
     const moe::LoraWs lw = lora_ws(L);
     if ((st = device_status(moe::lora_forward_pre(L->lora, lw, x, xt, T, a.H, a.I, hs), "adapter (gate/up terms)")) != MOE_OK)

@@ -174,6 +174,10 @@ hipError_t launch_bwd_gateup_mm(const ExpertBwdArgs &a, hipStream_t s);
 // dg/du rows are bf16 hi + lo planes, the generic backward's fp32.
 inline bool bwd_uses_mm(const ExpertBwdArgs &a) { return (size_t)a.T * a.k >= (size_t)8 * a.E && bwd_mm_supported(a); }
 
+// MXFP8 quantization of n (a multiple of 32) activations x into their represented values
+// as bf16 (quant.hip).
+hipError_t launch_quant_x8(const void *x, int xt, size_t n, uint16_t *xq, hipStream_t s);
+
 // Shared low-rank adapter (lora.hip): weights (borrowed, fp32) and workspace.
 struct LoraW {
     int r;

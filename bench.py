@@ -25,6 +25,7 @@ METRIC = "MoE-layer tokens/s + achieved HBM GB/s (decode) / MFMA util (prefill),
 HBM_PEAK_GBPS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA
 BF16_MFMA_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0  # dense fp8 MFMA (an E4M3 operand against FP4 runs at the fp8 rate)
 
 
 def log(msg):
@@ -59,7 +60,7 @@ def traffic_record(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, x_pool, wr, bias, codes, scales, budget_s: float, dy_pool=None, lora=None):
+def cpu_baseline(w, x_pool, wr, bias, codes, scales, budget_s: float, dy_pool=None, lora=None, quant=False):
     """The fp64 oracle as it stands, timed on a bounded sample of the same pool: consecutive
     chunks of at most 16 tokens (route + group + forward, and the input gradient when dy_pool
     is given), until budget_s of CPU work; tokens/s over the tokens processed."""
@@ -72,11 +73,12 @@ def cpu_baseline(w, x_pool, wr, bias, codes, scales, budget_s: float, dy_pool=No
     n, t0 = 0, time.perf_counter()
     while True:
         xb = oracle.to_f64(flat[n:n + chunk], "bf16")
-        if dflat is None:
+        if dflat is None and not quant:
             oracle.layer_forward(xb, wr, bias, w.k, W, nthreads=nthreads)
         else:
             ids, p, _ = oracle.route(xb, wr, bias, w.k, nthreads=nthreads)
-            oracle.forward(xb, ids, p, W, nthreads=nthreads)
+            oracle.forward(oracle.quantize_mxfp8(xb)[0] if quant else xb, ids, p, W, nthreads=nthreads)
+        if dflat is not None:
             dyb = oracle.to_f64(dflat[n:n + chunk], "bf16")
             oracle.backward_input(xb, dyb, ids, p, wr, W, nthreads=nthreads)
             if lora is not None:
@@ -85,7 +87,8 @@ def cpu_baseline(w, x_pool, wr, bias, codes, scales, budget_s: float, dy_pool=No
         el = time.perf_counter() - t0
         if el >= budget_s or n + chunk > flat.shape[0]:
             break
-    what = "route + group + forward" + (" + input gradient" if dflat is not None else "")
+    what = "route + group + forward" + (" of MXFP8-quantized x" if quant else "") \
+        + (" + input gradient" if dflat is not None else "")
     if lora is not None:
         what += " with the adapter" + (" and its gradients" if dflat is not None else "")
     return {"value": n / el, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
@@ -104,6 +107,10 @@ def main():
     ap.add_argument("--lora", type=int, default=0, metavar="RANK",
                     help="attach a shared low-rank adapter of this rank (LazyLoRA's is 16); the training pass then "
                          "also computes the adapter gradients")
+    ap.add_argument("--mx-gateup", action="store_true",
+                    help="block-scaled gate/up (FP4 weights straight into the MFMA; grouped-GEMM workloads)")
+    ap.add_argument("--quant-x8", action="store_true",
+                    help="activation-quantized prefill: the experts take x quantized to MXFP8")
     ap.add_argument("--no-plain-read", action="store_true",
                     help="skip the reference stream (a plain read of the roofline kernel's byte count)")
     ap.add_argument("--breakdown", action="store_true", help="also time every kernel family (stderr)")
@@ -150,8 +157,8 @@ def main():
         kw["rvq_cb"] = [q.to_device(a) for a in cb]
         expert_bytes = sum(a[0].nbytes for a in idx) + sum(a[0].nbytes for a in cb)
         gateup_bytes_per_expert = sum(a[0].nbytes for a in idx[:2]) + sum(a[0].nbytes for a in cb[:2])
-    if args.lora:
-        kw["flags"] = C.MOE_F_LORA
+    kw["flags"] = ((C.MOE_F_LORA if args.lora else 0) | (C.MOE_F_MX_GATEUP if args.mx_gateup else 0)
+                   | (C.MOE_F_QUANT_X8 if args.quant_x8 else 0))
     L = q.MoELayer(**kw)
     if args.lora:
         A_h, B_h = syn.lora_adapter(w, args.lora)
@@ -225,13 +232,18 @@ def main():
               "active_experts_mean": sum(steps_U) / len(steps_U),
               "gateup_us": gu_avg_s * 1e6, "gateup_alg_bytes": gu_bytes, "gateup_GBps": achieved}
     if train:
-        # the grouped GEMM is priced against the bf16 dense MFMA peak: its operands are exact
-        # bf16 (dequantized FP4 weights, bf16 x), 2 S H (2 I) flop per launch
+        # the grouped GEMM is priced against the dense MFMA peak of its operand type: exact
+        # bf16 (dequantized FP4 weights, bf16 x; also the two-term block-scaled form, which
+        # issues fp8 MFMAs at twice bf16's rate for twice the terms), or E4M3 x against FP4
+        # weights when x arrives MXFP8-quantized; 2 S H (2 I) flop per launch
         gu_tflops = 2.0 * S * w.H * 2 * w.I / gu_avg_s / 1e12
         detail["gateup_flop"] = 2.0 * S * w.H * 2 * w.I
-        roofline = {"bound": "mfma", "kernel": ROOF_KERNEL[w.name][0] + " (dequant + gate/up + SwiGLU)",
-                    "achieved": gu_tflops, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": gu_tflops / BF16_PEAK_TFLOPS, "traffic": traffic}
+        single = args.mx_gateup and args.quant_x8
+        peak = FP8_PEAK_TFLOPS if single else BF16_PEAK_TFLOPS
+        kname = ("k_gateup_mx (block-scaled gate/up + SwiGLU)" if args.mx_gateup
+                 else ROOF_KERNEL[w.name][0] + " (dequant + gate/up + SwiGLU)")
+        roofline = {"bound": "mfma", "kernel": kname, "achieved": gu_tflops, "peak": peak, "unit": "TFLOP/s",
+                    "frac": gu_tflops / peak, "traffic": traffic if not args.mx_gateup else None}
     else:
         roofline = {"bound": "hbm", "kernel": ROOF_KERNEL[w.name][0] + " (dequant + gate/up + SwiGLU)",
                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
@@ -274,7 +286,7 @@ def main():
         log("CPU baseline: fp64 oracle")
         dy_host = syn.upstream_grad(w, w.T * POOL).reshape(POOL, w.T, w.H) if train else None
         base = (cpu_baseline(w, x_host, wr, bias, codes, scales, args.cpu_seconds, dy_host,
-                             lora=(A_h, B_h, 32.0 / args.lora) if args.lora else None)
+                             lora=(A_h, B_h, 32.0 / args.lora) if args.lora else None, quant=args.quant_x8)
                 if codes is not None else None)
 
     out = {
@@ -288,15 +300,18 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "e4m3 x mxfp4" if args.mx_gateup and args.quant_x8 else "bf16",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: K3-shaped routed-expert layer, {w.T} token(s) per step, H {w.H}, "
                                f"I {w.I}, {w.E} {w.wfmt} experts resident, top-{w.k}, bf16 activations, "
                                + ("forward + input gradient (route + group + experts + combine + dX)" if train
                                   else "forward (route + group + experts + combine)")
                                + (f", shared rank-{args.lora} adapter" + (" with its gradients" if train else "")
-                                  if args.lora else ""),
-                   "T": w.T, "H": w.H, "I": w.I, "E": w.E, "k": w.k, "weights": w.wfmt, "lora_rank": args.lora},
+                                  if args.lora else "")
+                               + (", experts fed MXFP8-quantized x" if args.quant_x8 else "")
+                               + (", block-scaled gate/up" if args.mx_gateup else ""),
+                   "T": w.T, "H": w.H, "I": w.I, "E": w.E, "k": w.k, "weights": w.wfmt, "lora_rank": args.lora,
+                   "mx_gateup": args.mx_gateup, "quant_x8": args.quant_x8},
         "roofline": roofline,
         "cpu_baseline": base,
         "detail": detail,

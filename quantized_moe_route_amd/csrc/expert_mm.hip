@@ -368,7 +368,7 @@ __device__ __forceinline__ f32x4 mfma_mx(u32x4 a, u32x4 b0, u32x4 b1, f32x4 c, u
 
 typedef u32x2 MmScl[kMmTok];
 
-template <int NT>
+template <int NT, int NTERM>
 __device__ __forceinline__ void gateup_pass_mx(const ExpertFwdArgs &a, const GuBlock &b, MmTile *xs, MmScl *xsc,
                                                int r0, int tt0, int nt)
 {
@@ -431,8 +431,10 @@ __device__ __forceinline__ void gateup_pass_mx(const ExpertFwdArgs &a, const GuB
             // term 0 on the four weight tiles, then term 1: dependent MFMAs four apart
 #pragma unroll
             for (int t = 0; t < 4; t++) acc[t][tt] = mfma_mx<0>(q[p][t], b00, b01, acc[t][tt], sc[p][t], sw);
+            if constexpr (NTERM == 2) {
 #pragma unroll
-            for (int t = 0; t < 4; t++) acc[t][tt] = mfma_mx<1>(q[p][t], b10, b11, acc[t][tt], sc[p][t], sw);
+                for (int t = 0; t < 4; t++) acc[t][tt] = mfma_mx<1>(q[p][t], b10, b11, acc[t][tt], sc[p][t], sw);
+            }
         }
         // the accumulators are pinned here: without it the compiler sinks the step's
         // MFMAs (pure operations) below the later steps and keeps all their operands live
@@ -488,6 +490,7 @@ __device__ __forceinline__ void gateup_pass_mx(const ExpertFwdArgs &a, const GuB
     }
 }
 
+template <int NTERM>
 __global__ __launch_bounds__(256, 2) void k_gateup_mx(const ExpertFwdArgs a)
 {
     __shared__ MmTile xs[2];
@@ -512,12 +515,12 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mx(const ExpertFwdArgs a)
     for (int tt0 = 0; tt0 < ntok; tt0 += kMmTok) {
         const int nt = min(kMmTok, ntok - tt0);
         switch ((nt + 15) / 16) {
-        case 1: gateup_pass_mx<1>(a, b, xs, xsc, r0, tt0, nt); break;
-        case 2: gateup_pass_mx<2>(a, b, xs, xsc, r0, tt0, nt); break;
-        case 3: gateup_pass_mx<3>(a, b, xs, xsc, r0, tt0, nt); break;
-        case 4: gateup_pass_mx<4>(a, b, xs, xsc, r0, tt0, nt); break;
-        case 5: gateup_pass_mx<5>(a, b, xs, xsc, r0, tt0, nt); break;
-        default: gateup_pass_mx<6>(a, b, xs, xsc, r0, tt0, nt); break;
+        case 1: gateup_pass_mx<1, NTERM>(a, b, xs, xsc, r0, tt0, nt); break;
+        case 2: gateup_pass_mx<2, NTERM>(a, b, xs, xsc, r0, tt0, nt); break;
+        case 3: gateup_pass_mx<3, NTERM>(a, b, xs, xsc, r0, tt0, nt); break;
+        case 4: gateup_pass_mx<4, NTERM>(a, b, xs, xsc, r0, tt0, nt); break;
+        case 5: gateup_pass_mx<5, NTERM>(a, b, xs, xsc, r0, tt0, nt); break;
+        default: gateup_pass_mx<6, NTERM>(a, b, xs, xsc, r0, tt0, nt); break;
         }
     }
 }
@@ -674,6 +677,12 @@ hipError_t launch_gateup_mm(const ExpertFwdArgs &a, hipStream_t s)
         ps.launch(k_gateup_mm, dim3(xcd_grid(maxU, a.I / 128)), dim3(256), 0, a);
         return hipGetLastError();
     }
+    if (a.xq_single) {
+        // x arrived MXFP8-quantized: its one E4M3 term is already in place
+        ProfScope ps(a.prof, PK_GATEUP, s);
+        ps.launch(k_gateup_mx<1>, dim3(xcd_grid(maxU, a.I / 128)), dim3(256), 0, a);
+        return hipGetLastError();
+    }
     {
         ProfScope ps(a.prof, PK_XTERMS, s);
         const size_t n = (size_t)a.T * (a.H / 32);
@@ -683,7 +692,7 @@ hipError_t launch_gateup_mm(const ExpertFwdArgs &a, hipStream_t s)
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
     ProfScope ps(a.prof, PK_GATEUP, s);
-    ps.launch(k_gateup_mx, dim3(xcd_grid(maxU, a.I / 128)), dim3(256), 0, a);
+    ps.launch(k_gateup_mx<2>, dim3(xcd_grid(maxU, a.I / 128)), dim3(256), 0, a);
     return hipGetLastError();
 }
 

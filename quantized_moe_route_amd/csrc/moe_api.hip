@@ -352,7 +352,10 @@ moe_status moe_forward(moe_layer *L, const void *x, int32_t xt, int32_t T, const
     if (L->d.flags & MOE_F_QUANT_X8) {
         // the experts (and the adapter) see x quantized to MXFP8; the routing came from x
         uint16_t *xq = (uint16_t *)(L->ws + L->lay.xq8);
-        if ((st = device_status(moe::launch_quant_x8(x, xt, (size_t)T * a.H, xq, hs), "quantize x")) != MOE_OK) return st;
+        // with the block-scaled gate/up the same pass writes its operand: one exact E4M3 term
+        a.xq_single = a.xq != nullptr;
+        if ((st = device_status(moe::launch_quant_x8(x, xt, T, a.H, xq, a.xq, a.xq_s, hs), "quantize x")) != MOE_OK)
+            return st;
         a.x = xq;
         a.xt = MOE_DT_BF16;  // the same code as the kernels' bf16 token type
         x = xq;

@@ -100,6 +100,7 @@ struct ExpertFwdArgs {
     int nl_x;            // experts with at most this many tokens stage their x rows in LDS
     int nl_h;            // ... and their h rows (down product)
     const float *lora_gu;  // [T][2I] per-token adapter terms added to g | u, or null
+    int xq_single;         // xq / xq_s already hold x as one exact E4M3 term (MXFP8 input)
 };
 
 struct ExpertBwdArgs {
@@ -174,9 +175,9 @@ hipError_t launch_bwd_gateup_mm(const ExpertBwdArgs &a, hipStream_t s);
 // dg/du rows are bf16 hi + lo planes, the generic backward's fp32.
 inline bool bwd_uses_mm(const ExpertBwdArgs &a) { return (size_t)a.T * a.k >= (size_t)8 * a.E && bwd_mm_supported(a); }
 
-// MXFP8 quantization of n (a multiple of 32) activations x into their represented values
-// as bf16 (quant.hip).
-hipError_t launch_quant_x8(const void *x, int xt, size_t n, uint16_t *xq, hipStream_t s);
+// MXFP8 quantization of x [T][H] into its represented values as bf16 (quant.hip); with
+// mxq / mxs also as the block-scaled gate/up's single-term operand (null: not written).
+hipError_t launch_quant_x8(const void *x, int xt, int T, int H, uint16_t *xq, uint8_t *mxq, uint8_t *mxs, hipStream_t s);
 
 // Shared low-rank adapter (lora.hip): weights (borrowed, fp32) and workspace.
 struct LoraW {

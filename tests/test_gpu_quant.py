@@ -63,19 +63,37 @@ def test_quant_grouped_gemm_and_block_scaled_gateup():
     run_quant(host_case(w), "quant-mx", flags=C.MOE_F_MX_GATEUP)
 
 
+def test_quant_block_scaled_single_term():
+    # x arrives MXFP8-quantized: the quantizer writes the block-scaled gate/up's operand as one
+    # exact E4M3 term (fp32 tokens, a ragged last tile per expert, and with the adapter)
+    from quantized_moe_route_amd import _lib as C
+    run_quant(host_case(syn.shrink(TINY, T=333, H=1024, I=512, E=16, k=3, x_key=84)), "quant-mx-f32",
+              flags=C.MOE_F_MX_GATEUP)
+    run_quant(host_case(syn.shrink(TINY, T=300, H=1024, I=512, E=16, k=3, x_dtype="bf16", x_key=85)),
+              "quant-mx-lora", flags=C.MOE_F_MX_GATEUP, lora=True)
+
+
 def test_quant_rvq3_and_adapter():
     run_quant(host_case(syn.shrink(syn.WORKLOADS["rvq16"], T=10, H=512, I=768, E=12, k=3, x_key=82)), "quant-rvq3")
     run_quant(host_case(syn.shrink(TINY, T=6, x_dtype="bf16", x_key=83)), "quant-lora", lora=True)
 
 
-def test_quant_backward_is_the_exact_layers():
+@pytest.mark.parametrize("mx", [False, True])
+def test_quant_backward_is_the_exact_layers(mx):
     """moe_backward_input ignores the forward's quantization: recomputing g, u from x it
-    returns the same bits as a layer without the flag."""
+    returns the same bits as a layer without the flag (with the block-scaled gate/up, the
+    recomputation takes x as two exact E4M3 terms again)."""
     import torch
-    w = syn.shrink(TINY, T=8, x_dtype="bf16", with_dy=True, x_key=84)
+
+    from quantized_moe_route_amd import _lib as C
+    if mx:
+        w = syn.shrink(TINY, T=300, H=1024, I=512, E=16, k=3, x_dtype="bf16", with_dy=True, x_key=86)
+    else:
+        w = syn.shrink(TINY, T=8, x_dtype="bf16", with_dy=True, x_key=84)
+    flags = C.MOE_F_MX_GATEUP if mx else 0
     c = host_case(w)
-    Lq, x, r = run_quant(c, "quant-bwd")
-    L0 = device_layer(c, max_tokens=w.T)
+    Lq, x, r = run_quant(c, "quant-bwd" + ("-mx" if mx else ""), flags=flags)
+    L0 = device_layer(c, max_tokens=w.T, flags=flags)
     dy = act_tensor(c.dy, w.x_dtype)
     r0 = L0.route(x)
     dq = Lq.backward_input(x, dy, r)

@@ -114,6 +114,66 @@ __device__ __forceinline__ void k_loop2(int n, F &&step)
     if (s0 < n) step(Stage<0>(), s0);
 }
 
+// ---------------------------------------------------------------- scale bytes in LDS
+//
+// A block's weight rows take their E8M0 scale bytes from LDS.  Read from global memory a
+// few bytes per K-step, each scale line stays live for the block's whole K loop, and with
+// two blocks on each of the XCD's CUs those lines and the half-consumed code lines
+// outgrow the L2: both are fetched from HBM again and again (1.65x the algorithmic bytes
+// measured on the 4096-token gate/up).  Instead the block copies its rows' scale bytes of
+// up to kSclRow bytes per row (one K chunk) into LDS with coalesced 16-byte loads before
+// the chunk's first step, where every step reads them.  Row pitch kSclRow = 28 dwords, so
+// the 16 rows read by one lane group land in 16 distinct banks.
+
+constexpr int kSclRow = 112;  // LDS bytes per weight row and chunk
+
+// Pieces of 16 bytes per thread for NROWS rows of at most kSclRow bytes.
+template <int NROWS>
+constexpr int scl_pieces() { return (NROWS * (kSclRow / 16) + 255) / 256; }
+
+// Loads the scale bytes [byte0, byte0 + nbytes) of NROWS consecutive rows (row stride
+// gstride bytes from boff in resource r; nbytes a multiple of 16, at most kSclRow).  The
+// resource is the same for the whole wave, so the loads are plain buffer loads.
+template <int NROWS>
+__device__ __forceinline__ void scl_load(u32x4 (&v)[scl_pieces<NROWS>()], __amdgpu_buffer_rsrc_t r, uint32_t boff,
+                                         int gstride, int byte0, int nbytes)
+{
+    const int per_row = nbytes >> 4;
+#pragma unroll
+    for (int k = 0; k < scl_pieces<NROWS>(); k++) {
+        const int i = (int)threadIdx.x + 256 * k;
+        const int row = i / per_row, j = i - row * per_row;
+        v[k] = u32x4{0u, 0u, 0u, 0u};
+        if (row < NROWS) v[k] = ld16(r, (uint32_t)row * gstride + 16 * j, boff + byte0);
+    }
+}
+
+template <int NROWS>
+__device__ __forceinline__ void scl_store(const u32x4 (&v)[scl_pieces<NROWS>()], uint8_t *scl, int nbytes)
+{
+    const int per_row = nbytes >> 4;
+#pragma unroll
+    for (int k = 0; k < scl_pieces<NROWS>(); k++) {
+        const int i = (int)threadIdx.x + 256 * k;
+        const int row = i / per_row, j = i - row * per_row;
+        if (row < NROWS) *(u32x4 *)(scl + row * kSclRow + 16 * j) = v[k];
+    }
+}
+
+// The same copy one piece at a time (four registers): for the K chunks after the first,
+// inside the K loop, where the weight and token stages hold most registers.  Each piece
+// waits for its load; it runs once per 3584 elements of K.
+__device__ __forceinline__ void scl_copy_serial(uint8_t *scl, int nrows, __amdgpu_buffer_rsrc_t r, uint32_t boff,
+                                                int gstride, int byte0, int nbytes)
+{
+    const int per_row = nbytes >> 4;
+#pragma unroll 1
+    for (int i = (int)threadIdx.x; i < nrows * per_row; i += 256) {
+        const int row = i / per_row, j = i - row * per_row;
+        *(u32x4 *)(scl + row * kSclRow + 16 * j) = ld16(r, (uint32_t)row * gstride + 16 * j, boff + byte0);
+    }
+}
+
 // ---------------------------------------------------------------- x as two E4M3 terms
 //
 // For the block-scaled gate/up, each 32-element block of a token row is written as
@@ -193,13 +253,46 @@ __global__ __launch_bounds__(256) void k_x_terms(const uint16_t *__restrict__ x,
 struct GuBlock {
     __amdgpu_buffer_rsrc_t code[2], scale[2];  // this expert's gate and up matrices
     __amdgpu_buffer_rsrc_t x;                   // the token rows
-    uint32_t coff, soff;                        // this lane's code / scale byte offsets at K-step 0
+    uint32_t coff;                              // this lane's code byte offset at K-step 0
+    uint32_t sblk;                              // the block's first scale row (byte offset)
+    uint32_t sl;                                // this lane's scale byte in LDS (gate rows, K-step 0)
     int c0;                                     // first I-column of this wave
 };
 
+constexpr int kGuSclSteps = kSclRow / 4;  // gate/up K-steps per scale chunk (4 scale bytes a step)
+
+// The block's gate (LDS rows 0..127) and up (128..255) scale bytes of the chunk at K-step
+// st0: loaded, then stored.
+struct GuScl {
+    u32x4 g[scl_pieces<128>()], u[scl_pieces<128>()];
+};
+
+__device__ __forceinline__ void gu_scl_load(GuScl &v, const GuBlock &b, int H, int st0, int nsteps)
+{
+    const int nb = 4 * min(kGuSclSteps, nsteps - st0);
+    scl_load<128>(v.g, b.scale[0], b.sblk, H / 32, 4 * st0, nb);
+    scl_load<128>(v.u, b.scale[1], b.sblk, H / 32, 4 * st0, nb);
+}
+
+__device__ __forceinline__ void gu_scl_store(const GuScl &v, uint8_t *scl, int st0, int nsteps)
+{
+    const int nb = 4 * min(kGuSclSteps, nsteps - st0);
+    scl_store<128>(v.g, scl, nb);
+    scl_store<128>(v.u, scl + 128 * kSclRow, nb);
+}
+
+__device__ __forceinline__ void gu_scl_next(uint8_t *scl, const GuBlock &b, int H, int st0, int nsteps)
+{
+    const int nb = 4 * min(kGuSclSteps, nsteps - st0);
+    __syncthreads();  // every wave is past the previous chunk's last step
+    scl_copy_serial(scl, 128, b.scale[0], b.sblk, H / 32, 4 * st0, nb);
+    scl_copy_serial(scl + 128 * kSclRow, 128, b.scale[1], b.sblk, H / 32, 4 * st0, nb);
+    __syncthreads();
+}
+
 template <int NT>
-__device__ __forceinline__ void gateup_pass(const ExpertFwdArgs &a, const GuBlock &b, MmTile *xs, int r0, int tt0,
-                                            int nt)
+__device__ __forceinline__ void gateup_pass(const ExpertFwdArgs &a, const GuBlock &b, MmTile *xs, uint8_t *scl, int r0,
+                                            int tt0, int nt)
 {
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
     const int H = a.H, I = a.I, nsteps = H / 128;
@@ -216,29 +309,38 @@ __device__ __forceinline__ void gateup_pass(const ExpertFwdArgs &a, const GuBloc
 #pragma unroll
         for (int tt = 0; tt < NT; tt++) acc[t][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
     u32x4 q[3][4];
-    uint32_t sc[3][4];
     auto load_w = [&](auto P, int st) {
         constexpr int p = decltype(P)::value;
 #pragma unroll
-        for (int t = 0; t < 4; t++) {
-            q[p][t] = ld16(b.code[t >> 1], b.coff, (t & 1) * 8 * H + 64 * st);
-            sc[p][t] = ld1(b.scale[t >> 1], b.soff, (t & 1) * (H / 2) + 4 * st);
-        }
+        for (int t = 0; t < 4; t++) q[p][t] = ld16(b.code[t >> 1], b.coff, (t & 1) * 8 * H + 64 * st);
     };
     {
+        GuScl sv;
+        gu_scl_load(sv, b, H, 0, nsteps);
         u32x4 xv[NT];
 #pragma unroll
         for (int i = 0; i < NT; i++) xv[i] = ld16(b.x, xoff[i], 0);
+        gu_scl_store(sv, scl, 0, nsteps);
         load_w(Stage<0>(), 0);
         load_w(Stage<1>(), min(1, nsteps - 1));
 #pragma unroll
         for (int i = 0; i < NT; i++) xs[0][lds_slot(xr + 16 * i, xc)] = xv[i];
     }
     __syncthreads();
+    // the scale bytes of the step are read from LDS one step ahead
+    uint32_t scn[4];
+#pragma unroll
+    for (int t = 0; t < 4; t++) scn[t] = scl[b.sl + (t >> 1) * 128 * kSclRow + (t & 1) * 16 * kSclRow + 4 * 0];
 
     k_loop3(nsteps, [&](auto P, int st) {
         constexpr int p = decltype(P)::value;
         const int buf = st & 1;
+        const int sst = st % kGuSclSteps;
+        if (sst == 0 && st != 0) {  // the next K chunk (H beyond 3584)
+            gu_scl_next(scl, b, H, st, nsteps);
+#pragma unroll
+            for (int t = 0; t < 4; t++) scn[t] = scl[b.sl + (t >> 1) * 128 * kSclRow + (t & 1) * 16 * kSclRow + 4 * 0];
+        }
         u32x4 xv[NT];  // next step's x tile, issued before the weights so waiting for it
         const int stn = min(st + 1, nsteps - 1);  // leaves the weight prefetch in flight
 #pragma unroll
@@ -247,7 +349,10 @@ __device__ __forceinline__ void gateup_pass(const ExpertFwdArgs &a, const GuBloc
         __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the step's MFMAs
         float scale[4];
 #pragma unroll
-        for (int t = 0; t < 4; t++) scale[t] = e8m0_to_f32(sc[p][t]);
+        for (int t = 0; t < 4; t++) scale[t] = e8m0_to_f32(scn[t]);
+        if (sst + 1 < kGuSclSteps && st + 1 < nsteps)
+#pragma unroll
+            for (int t = 0; t < 4; t++) scn[t] = scl[b.sl + (t >> 1) * 128 * kSclRow + (t & 1) * 16 * kSclRow + 4 * (sst + 1)];
 #pragma unroll
         for (int s = 0; s < 4; s++) {
             bf16x8 A[4], B[NT];
@@ -310,6 +415,7 @@ __device__ __forceinline__ void gateup_pass(const ExpertFwdArgs &a, const GuBloc
 __global__ __launch_bounds__(256, 2) void k_gateup_mm(const ExpertFwdArgs a)
 {
     __shared__ MmTile xs[2];
+    __shared__ __attribute__((aligned(16))) uint8_t scl[256 * kSclRow];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
     const int H = a.H, I = a.I;
     int ai, cb;
@@ -326,16 +432,17 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mm(const ExpertFwdArgs a)
     b.x = buf_rsrc(a.x, (uint32_t)((size_t)a.T * H * 2));
     b.c0 = cb * 128 + wv * 32;
     b.coff = (uint32_t)(b.c0 + li) * (H / 2) + 16 * g;
-    b.soff = (uint32_t)(b.c0 + li) * (H / 32) + g;
+    b.sblk = (uint32_t)cb * 128 * (H / 32);
+    b.sl = (uint32_t)(wv * 32 + li) * kSclRow + g;
     for (int tt0 = 0; tt0 < ntok; tt0 += kMmTok) {
         const int nt = min(kMmTok, ntok - tt0);
         switch ((nt + 15) / 16) {
-        case 1: gateup_pass<1>(a, b, xs, r0, tt0, nt); break;
-        case 2: gateup_pass<2>(a, b, xs, r0, tt0, nt); break;
-        case 3: gateup_pass<3>(a, b, xs, r0, tt0, nt); break;
-        case 4: gateup_pass<4>(a, b, xs, r0, tt0, nt); break;
-        case 5: gateup_pass<5>(a, b, xs, r0, tt0, nt); break;
-        default: gateup_pass<6>(a, b, xs, r0, tt0, nt); break;
+        case 1: gateup_pass<1>(a, b, xs, scl, r0, tt0, nt); break;
+        case 2: gateup_pass<2>(a, b, xs, scl, r0, tt0, nt); break;
+        case 3: gateup_pass<3>(a, b, xs, scl, r0, tt0, nt); break;
+        case 4: gateup_pass<4>(a, b, xs, scl, r0, tt0, nt); break;
+        case 5: gateup_pass<5>(a, b, xs, scl, r0, tt0, nt); break;
+        default: gateup_pass<6>(a, b, xs, scl, r0, tt0, nt); break;
         }
     }
 }
@@ -370,7 +477,7 @@ typedef u32x2 MmScl[kMmTok];
 
 template <int NT, int NTERM>
 __device__ __forceinline__ void gateup_pass_mx(const ExpertFwdArgs &a, const GuBlock &b, MmTile *xs, MmScl *xsc,
-                                               int r0, int tt0, int nt)
+                                               uint8_t *scl, int r0, int tt0, int nt)
 {
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
     const int H = a.H, I = a.I, nsteps = H / 128;
@@ -391,30 +498,44 @@ __device__ __forceinline__ void gateup_pass_mx(const ExpertFwdArgs &a, const GuB
 #pragma unroll
         for (int tt = 0; tt < NT; tt++) acc[t][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
     u32x4 q[2][4];
-    uint32_t sc[2][4];
     auto load_w = [&](auto P, int st) {
         constexpr int p = decltype(P)::value;
 #pragma unroll
-        for (int t = 0; t < 4; t++) {
-            q[p][t] = ld16(b.code[t >> 1], b.coff, (t & 1) * 8 * H + 64 * st);
-            sc[p][t] = ld1(b.scale[t >> 1], b.soff, (t & 1) * (H / 2) + 4 * st);
-        }
+        for (int t = 0; t < 4; t++) q[p][t] = ld16(b.code[t >> 1], b.coff, (t & 1) * 8 * H + 64 * st);
     };
     {
+        GuScl wsv;
+        gu_scl_load(wsv, b, H, 0, nsteps);
         u32x4 xv[NT];
 #pragma unroll
         for (int i = 0; i < NT; i++) xv[i] = ld16(b.x, xoff[i], 0);
         const u32x2 sv = ld8(xsr, soffx, 0);
+        gu_scl_store(wsv, scl, 0, nsteps);
         load_w(Stage<0>(), 0);
 #pragma unroll
         for (int i = 0; i < NT; i++) xs[0][lds_slot(xr + 16 * i, xc)] = xv[i];
         if (sthr) xsc[0][tid] = sv;
     }
     __syncthreads();
+    uint32_t scn[4];  // the scale bytes of the step, read from LDS one step ahead
+#pragma unroll
+    for (int t = 0; t < 4; t++) scn[t] = scl[b.sl + (t >> 1) * 128 * kSclRow + (t & 1) * 16 * kSclRow + 4 * 0];
 
     k_loop2(nsteps, [&](auto P, int st) {
         constexpr int p = decltype(P)::value;
         const int buf = st & 1;
+        const int sst = st % kGuSclSteps;
+        if (sst == 0 && st != 0) {  // the next K chunk (H beyond 3584)
+            gu_scl_next(scl, b, H, st, nsteps);
+#pragma unroll
+            for (int t = 0; t < 4; t++) scn[t] = scl[b.sl + (t >> 1) * 128 * kSclRow + (t & 1) * 16 * kSclRow + 4 * 0];
+        }
+        uint32_t sc[4];
+#pragma unroll
+        for (int t = 0; t < 4; t++) sc[t] = scn[t];
+        if (sst + 1 < kGuSclSteps && st + 1 < nsteps)
+#pragma unroll
+            for (int t = 0; t < 4; t++) scn[t] = scl[b.sl + (t >> 1) * 128 * kSclRow + (t & 1) * 16 * kSclRow + 4 * (sst + 1)];
         u32x4 xv[NT];  // next step's x tile, issued before the weights so waiting for it
         const int stn = min(st + 1, nsteps - 1);  // leaves the weight prefetch in flight
 #pragma unroll
@@ -430,10 +551,10 @@ __device__ __forceinline__ void gateup_pass_mx(const ExpertFwdArgs &a, const GuB
             const uint32_t sw = ((const uint16_t *)&xsc[buf][row])[g];
             // term 0 on the four weight tiles, then term 1: dependent MFMAs four apart
 #pragma unroll
-            for (int t = 0; t < 4; t++) acc[t][tt] = mfma_mx<0>(q[p][t], b00, b01, acc[t][tt], sc[p][t], sw);
+            for (int t = 0; t < 4; t++) acc[t][tt] = mfma_mx<0>(q[p][t], b00, b01, acc[t][tt], sc[t], sw);
             if constexpr (NTERM == 2) {
 #pragma unroll
-                for (int t = 0; t < 4; t++) acc[t][tt] = mfma_mx<1>(q[p][t], b10, b11, acc[t][tt], sc[p][t], sw);
+                for (int t = 0; t < 4; t++) acc[t][tt] = mfma_mx<1>(q[p][t], b10, b11, acc[t][tt], sc[t], sw);
             }
         }
         // the accumulators are pinned here: without it the compiler sinks the step's
@@ -495,6 +616,7 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mx(const ExpertFwdArgs a)
 {
     __shared__ MmTile xs[2];
     __shared__ MmScl xsc[2];
+    __shared__ __attribute__((aligned(16))) uint8_t scl[256 * kSclRow];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
     const int H = a.H, I = a.I;
     int ai, cb;
@@ -511,16 +633,17 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mx(const ExpertFwdArgs a)
     b.x = buf_rsrc(a.xq, (uint32_t)((size_t)a.T * H * 2));
     b.c0 = cb * 128 + wv * 32;
     b.coff = (uint32_t)(b.c0 + li) * (H / 2) + 16 * g;
-    b.soff = (uint32_t)(b.c0 + li) * (H / 32) + g;
+    b.sblk = (uint32_t)cb * 128 * (H / 32);
+    b.sl = (uint32_t)(wv * 32 + li) * kSclRow + g;
     for (int tt0 = 0; tt0 < ntok; tt0 += kMmTok) {
         const int nt = min(kMmTok, ntok - tt0);
         switch ((nt + 15) / 16) {
-        case 1: gateup_pass_mx<1, NTERM>(a, b, xs, xsc, r0, tt0, nt); break;
-        case 2: gateup_pass_mx<2, NTERM>(a, b, xs, xsc, r0, tt0, nt); break;
-        case 3: gateup_pass_mx<3, NTERM>(a, b, xs, xsc, r0, tt0, nt); break;
-        case 4: gateup_pass_mx<4, NTERM>(a, b, xs, xsc, r0, tt0, nt); break;
-        case 5: gateup_pass_mx<5, NTERM>(a, b, xs, xsc, r0, tt0, nt); break;
-        default: gateup_pass_mx<6, NTERM>(a, b, xs, xsc, r0, tt0, nt); break;
+        case 1: gateup_pass_mx<1, NTERM>(a, b, xs, xsc, scl, r0, tt0, nt); break;
+        case 2: gateup_pass_mx<2, NTERM>(a, b, xs, xsc, scl, r0, tt0, nt); break;
+        case 3: gateup_pass_mx<3, NTERM>(a, b, xs, xsc, scl, r0, tt0, nt); break;
+        case 4: gateup_pass_mx<4, NTERM>(a, b, xs, xsc, scl, r0, tt0, nt); break;
+        case 5: gateup_pass_mx<5, NTERM>(a, b, xs, xsc, scl, r0, tt0, nt); break;
+        default: gateup_pass_mx<6, NTERM>(a, b, xs, xsc, scl, r0, tt0, nt); break;
         }
     }
 }
@@ -536,13 +659,24 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mx(const ExpertFwdArgs a)
 struct DnBlock {
     __amdgpu_buffer_rsrc_t code, scale;  // this expert's down matrix
     __amdgpu_buffer_rsrc_t h;            // h_hi then h_lo (contiguous planes)
-    uint32_t coff, soff;
+    uint32_t coff;
+    uint32_t sblk;  // the block's first scale row (byte offset)
+    uint32_t sl;    // this lane's scale byte in LDS (tile 0, K-step 0)
     int m0;
 };
 
+constexpr int kDnSclSteps = kSclRow / 2;  // down K-steps per scale chunk (2 scale bytes a step)
+
+__device__ __forceinline__ void dn_scl_next(uint8_t *scl, const DnBlock &b, int I, int st0, int nsteps)
+{
+    __syncthreads();  // every wave is past the previous chunk's last step
+    scl_copy_serial(scl, 256, b.scale, b.sblk, I / 32, 2 * st0, 2 * min(kDnSclSteps, nsteps - st0));
+    __syncthreads();
+}
+
 template <int NT>
-__device__ __forceinline__ void down_pass(const ExpertFwdArgs &a, const DnBlock &b, MmTile *hs, int r0, int tt0,
-                                          int nt)
+__device__ __forceinline__ void down_pass(const ExpertFwdArgs &a, const DnBlock &b, MmTile *hs, uint8_t *scl, int r0,
+                                          int tt0, int nt)
 {
     const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
     const int H = a.H, I = a.I, nsteps = I / 64;
@@ -558,29 +692,37 @@ __device__ __forceinline__ void down_pass(const ExpertFwdArgs &a, const DnBlock 
 #pragma unroll
         for (int tt = 0; tt < NT; tt++) acc[t][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
     u32x2 q[3][4];
-    uint32_t sc[3][4];
     auto load_w = [&](auto P, int st) {
         constexpr int p = decltype(P)::value;
 #pragma unroll
-        for (int t = 0; t < 4; t++) {
-            q[p][t] = ld8(b.code, b.coff, t * 8 * I + 32 * st);
-            sc[p][t] = ld1(b.scale, b.soff, t * (I / 2) + 2 * st);
-        }
+        for (int t = 0; t < 4; t++) q[p][t] = ld8(b.code, b.coff, t * 8 * I + 32 * st);
     };
     {
+        u32x4 sv[scl_pieces<256>()];
+        scl_load<256>(sv, b.scale, b.sblk, I / 32, 0, 2 * min(kDnSclSteps, nsteps));
         u32x4 hv[NT];
 #pragma unroll
         for (int i = 0; i < NT; i++) hv[i] = ld16(b.h, hoff[i], 0);
+        scl_store<256>(sv, scl, 2 * min(kDnSclSteps, nsteps));
         load_w(Stage<0>(), 0);
         load_w(Stage<1>(), min(1, nsteps - 1));
 #pragma unroll
         for (int i = 0; i < NT; i++) hs[0][lds_slot(xr + 16 * i, xc)] = hv[i];
     }
     __syncthreads();
+    uint32_t scn[4];  // the scale bytes of the step, read from LDS one step ahead
+#pragma unroll
+    for (int t = 0; t < 4; t++) scn[t] = scl[b.sl + t * 16 * kSclRow + 2 * 0];
 
     k_loop3(nsteps, [&](auto P, int st) {
         constexpr int p = decltype(P)::value;
         const int buf = st & 1;
+        const int sst = st % kDnSclSteps;
+        if (sst == 0 && st != 0) {  // the next K chunk (I beyond 3584)
+            dn_scl_next(scl, b, I, st, nsteps);
+#pragma unroll
+            for (int t = 0; t < 4; t++) scn[t] = scl[b.sl + t * 16 * kSclRow + 2 * 0];
+        }
         u32x4 hv[NT];
         const int stn = min(st + 1, nsteps - 1);
 #pragma unroll
@@ -589,7 +731,10 @@ __device__ __forceinline__ void down_pass(const ExpertFwdArgs &a, const DnBlock 
         __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the step's MFMAs
         float scale[4];
 #pragma unroll
-        for (int t = 0; t < 4; t++) scale[t] = e8m0_to_f32(sc[p][t]);
+        for (int t = 0; t < 4; t++) scale[t] = e8m0_to_f32(scn[t]);
+        if (sst + 1 < kDnSclSteps && st + 1 < nsteps)
+#pragma unroll
+            for (int t = 0; t < 4; t++) scn[t] = scl[b.sl + t * 16 * kSclRow + 2 * (sst + 1)];
 #pragma unroll
         for (int s = 0; s < 2; s++) {
             bf16x8 A[4], Bh[NT], Bl[NT];
@@ -632,6 +777,7 @@ __device__ __forceinline__ void down_pass(const ExpertFwdArgs &a, const DnBlock 
 __global__ __launch_bounds__(256, 2) void k_down_mm(const ExpertFwdArgs a)
 {
     __shared__ MmTile hs[2];
+    __shared__ __attribute__((aligned(16))) uint8_t scl[256 * kSclRow];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
     const int H = a.H, I = a.I;
     int ai, rb;
@@ -645,16 +791,17 @@ __global__ __launch_bounds__(256, 2) void k_down_mm(const ExpertFwdArgs a)
     b.h = buf_rsrc(a.h_hi, (uint32_t)((size_t)a.T * a.k * I * 4));
     b.m0 = rb * 256 + wv * 64;
     b.coff = (uint32_t)(b.m0 + li) * (I / 2) + 8 * g;
-    b.soff = (uint32_t)(b.m0 + li) * (I / 32) + (g >> 1);
+    b.sblk = (uint32_t)rb * 256 * (I / 32);
+    b.sl = (uint32_t)(wv * 64 + li) * kSclRow + (g >> 1);
     for (int tt0 = 0; tt0 < ntok; tt0 += kMmTok) {
         const int nt = min(kMmTok, ntok - tt0);
         switch ((nt + 15) / 16) {
-        case 1: down_pass<1>(a, b, hs, r0, tt0, nt); break;
-        case 2: down_pass<2>(a, b, hs, r0, tt0, nt); break;
-        case 3: down_pass<3>(a, b, hs, r0, tt0, nt); break;
-        case 4: down_pass<4>(a, b, hs, r0, tt0, nt); break;
-        case 5: down_pass<5>(a, b, hs, r0, tt0, nt); break;
-        default: down_pass<6>(a, b, hs, r0, tt0, nt); break;
+        case 1: down_pass<1>(a, b, hs, scl, r0, tt0, nt); break;
+        case 2: down_pass<2>(a, b, hs, scl, r0, tt0, nt); break;
+        case 3: down_pass<3>(a, b, hs, scl, r0, tt0, nt); break;
+        case 4: down_pass<4>(a, b, hs, scl, r0, tt0, nt); break;
+        case 5: down_pass<5>(a, b, hs, scl, r0, tt0, nt); break;
+        default: down_pass<6>(a, b, hs, scl, r0, tt0, nt); break;
         }
     }
 }

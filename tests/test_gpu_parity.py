@@ -114,6 +114,16 @@ def test_grouped_gemm_path_skew_and_idle_experts():
     run_small(c, name="mm-skew")
 
 
+@pytest.mark.parametrize("mx", [False, True])
+def test_grouped_gemm_scale_chunks(mx):
+    # H = I = 4096: the blocks stage their weight rows' scale bytes in LDS 3584 elements of K
+    # at a time, so the gate/up (32 K-steps) and the down (64 K-steps) each cross one chunk
+    # boundary, the second chunk a short one
+    from quantized_moe_route_amd import _lib as C
+    w = syn.shrink(TINY, T=16, H=4096, I=4096, E=4, k=2, x_dtype="bf16", with_dy=not mx, x_key=27)
+    run_small(host_case(w), name="mm-scale-chunks" + ("-mx" if mx else ""), flags=C.MOE_F_MX_GATEUP if mx else 0)
+
+
 def test_block_scaled_gateup_multi_pass_and_recompute():
     # MOE_F_MX_GATEUP: the grouped-GEMM gate/up on block-scaled MFMA (FP4 weights, x as two
     # E4M3 terms); ~100 tokens per expert spans every token-tile count and a second pass;

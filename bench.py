@@ -60,13 +60,16 @@ def traffic_record(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, x_pool, wr, bias, codes, scales, budget_s: float, dy_pool=None, lora=None, quant=False):
+def cpu_baseline(w, x_pool, wr, bias, codes, scales, budget_s: float, dy_pool=None, lora=None, quant=False,
+                 shared=None):
     """The fp64 oracle as it stands, timed on a bounded sample of the same pool: consecutive
     chunks of at most 16 tokens (route + group + forward, and the input gradient when dy_pool
     is given), until budget_s of CPU work; tokens/s over the tokens processed."""
     import oracle
     nthreads = oracle.default_threads()
     W = oracle.Weights(w.H, w.I, codes=codes, scales=scales, lora=lora)
+    Ws = oracle.Weights(w.H, w.I, codes=shared[0], scales=shared[1]) if shared else None
+    n_sh = shared[0][0].shape[0] if shared else 0
     flat = x_pool.reshape(-1, w.H)
     dflat = None if dy_pool is None else dy_pool.reshape(-1, w.H)
     chunk = min(w.T, 16)
@@ -78,11 +81,15 @@ def cpu_baseline(w, x_pool, wr, bias, codes, scales, budget_s: float, dy_pool=No
         else:
             ids, p, _ = oracle.route(xb, wr, bias, w.k, nthreads=nthreads)
             oracle.forward(oracle.quantize_mxfp8(xb)[0] if quant else xb, ids, p, W, nthreads=nthreads)
+        if Ws is not None:
+            oracle.shared_forward(oracle.quantize_mxfp8(xb)[0] if quant else xb, Ws, n_sh, nthreads=nthreads)
         if dflat is not None:
             dyb = oracle.to_f64(dflat[n:n + chunk], "bf16")
             oracle.backward_input(xb, dyb, ids, p, wr, W, nthreads=nthreads)
             if lora is not None:
                 oracle.lora_grads(xb, dyb, ids, p, W, nthreads=nthreads)
+            if Ws is not None:
+                oracle.shared_backward_input(xb, dyb, Ws, n_sh, nthreads=nthreads)
         n += chunk
         el = time.perf_counter() - t0
         if el >= budget_s or n + chunk > flat.shape[0]:
@@ -91,6 +98,8 @@ def cpu_baseline(w, x_pool, wr, bias, codes, scales, budget_s: float, dy_pool=No
         + (" + input gradient" if dflat is not None else "")
     if lora is not None:
         what += " with the adapter" + (" and its gradients" if dflat is not None else "")
+    if Ws is not None:
+        what += f", {n_sh} shared experts"
     return {"value": n / el, "unit": "tokens/s", "cores": nthreads, "kind": "oracle",
             "sample": f"{n} tokens of the timed pool in chunks of {chunk} ({what} with {w.k} experts per "
                       f"token), {el:.1f} s of fp64 CPU work"}
@@ -107,6 +116,8 @@ def main():
     ap.add_argument("--lora", type=int, default=0, metavar="RANK",
                     help="attach a shared low-rank adapter of this rank (LazyLoRA's is 16); the training pass then "
                          "also computes the adapter gradients")
+    ap.add_argument("--shared", type=int, default=0, metavar="N",
+                    help="add N shared experts (K3 has 2), taken by every token with weight 1")
     ap.add_argument("--mx-gateup", action="store_true",
                     help="block-scaled gate/up (FP4 weights straight into the MFMA; grouped-GEMM workloads)")
     ap.add_argument("--quant-x8", action="store_true",
@@ -157,6 +168,14 @@ def main():
         kw["rvq_cb"] = [q.to_device(a) for a in cb]
         expert_bytes = sum(a[0].nbytes for a in idx) + sum(a[0].nbytes for a in cb)
         gateup_bytes_per_expert = sum(a[0].nbytes for a in idx[:2]) + sum(a[0].nbytes for a in cb[:2])
+    if args.shared:
+        sh = syn.shared_experts(w, args.shared)
+        kw["shared"] = ([q.to_device(a) for a in sh[0]], [q.to_device(a) for a in sh[1]])
+        # every token reads the shared experts' bytes too
+        shared_bytes = sum(a.nbytes for a in sh[0]) + sum(a.nbytes for a in sh[1])
+        shared_gateup_bytes = sum(a.nbytes for a in sh[0][:2]) + sum(a.nbytes for a in sh[1][:2])
+    else:
+        shared_bytes = shared_gateup_bytes = 0
     kw["flags"] = ((C.MOE_F_LORA if args.lora else 0) | (C.MOE_F_MX_GATEUP if args.mx_gateup else 0)
                    | (C.MOE_F_QUANT_X8 if args.quant_x8 else 0))
     L = q.MoELayer(**kw)
@@ -206,21 +225,26 @@ def main():
     # The roofline kernel is timed over a second pass of the same steps: per-launch events
     # (hipExtLaunchKernelGGL start/stop stamps) slow the step down, so they stay out of the
     # pass that gives the throughput.
-    L.prof_enable([C.PROF_GATEUP], max_launches=args.steps)
+    L.prof_enable([C.PROF_GATEUP], max_launches=args.steps * (2 if args.shared else 1))
     for i in range(args.steps):
         step(args.warmup + i)
     torch.cuda.synchronize()
     gu_ms, gu_n = L.prof_read(C.PROF_GATEUP)
     L.prof_enable([])
-    assert gu_n == args.steps
+    # one gate/up launch per step, and one more for the shared experts
+    assert gu_n == args.steps * (2 if args.shared else 1)
     steps_U = [U[(args.warmup + i) % POOL] for i in range(args.steps)]
     S = w.T * w.k
     x_bytes = w.T * w.H * 2
-    gu_alg = [u * gateup_bytes_per_expert + x_bytes + S * w.I * 4 for u in steps_U]
+    S_sh = w.T * args.shared
+    gu_alg = [u * gateup_bytes_per_expert + x_bytes + S * w.I * 4
+              + (shared_gateup_bytes + x_bytes + S_sh * w.I * 4 if args.shared else 0) for u in steps_U]
     gu_bytes = sum(gu_alg) / len(gu_alg)
-    gu_avg_s = gu_ms / gu_n / 1e3  # events stamped at the kernel's own start and end
+    # gate/up time per step (with shared experts: both launches), from events stamped at the
+    # kernels' own start and end
+    gu_avg_s = gu_ms / args.steps / 1e3
     achieved = gu_bytes / gu_avg_s / 1e9
-    step_bytes = [u * expert_bytes + wr.nbytes + x_bytes + w.T * w.H * 4 for u in steps_U]
+    step_bytes = [u * expert_bytes + shared_bytes + wr.nbytes + x_bytes + w.T * w.H * 4 for u in steps_U]
     step_s = ms / 1e3 / args.steps
     tokens_per_s = w.T * args.steps / (ms / 1e3)
     traffic = traffic_record(w.name)
@@ -236,8 +260,8 @@ def main():
         # bf16 (dequantized FP4 weights, bf16 x; also the two-term block-scaled form, which
         # issues fp8 MFMAs at twice bf16's rate for twice the terms), or E4M3 x against FP4
         # weights when x arrives MXFP8-quantized; 2 S H (2 I) flop per launch
-        gu_tflops = 2.0 * S * w.H * 2 * w.I / gu_avg_s / 1e12
-        detail["gateup_flop"] = 2.0 * S * w.H * 2 * w.I
+        gu_tflops = 2.0 * (S + S_sh) * w.H * 2 * w.I / gu_avg_s / 1e12
+        detail["gateup_flop"] = 2.0 * (S + S_sh) * w.H * 2 * w.I
         single = args.mx_gateup and args.quant_x8
         peak = FP8_PEAK_TFLOPS if single else BF16_PEAK_TFLOPS
         kname = ("k_gateup_mx (block-scaled gate/up + SwiGLU)" if args.mx_gateup
@@ -270,7 +294,7 @@ def main():
             f"reaches {roofline['plain_read']['frac']:.3f} of it")
     if args.breakdown:
         fams = list(range(len(C.PROF_NAMES)))
-        L.prof_enable(fams, max_launches=args.steps)
+        L.prof_enable(fams, max_launches=args.steps * (2 if args.shared else 1))
         for i in range(args.steps):
             step(i)
         torch.cuda.synchronize()
@@ -286,7 +310,8 @@ def main():
         log("CPU baseline: fp64 oracle")
         dy_host = syn.upstream_grad(w, w.T * POOL).reshape(POOL, w.T, w.H) if train else None
         base = (cpu_baseline(w, x_host, wr, bias, codes, scales, args.cpu_seconds, dy_host,
-                             lora=(A_h, B_h, 32.0 / args.lora) if args.lora else None, quant=args.quant_x8)
+                             lora=(A_h, B_h, 32.0 / args.lora) if args.lora else None, quant=args.quant_x8,
+                             shared=sh if args.shared else None)
                 if codes is not None else None)
 
     out = {
@@ -309,9 +334,10 @@ def main():
                                + (f", shared rank-{args.lora} adapter" + (" with its gradients" if train else "")
                                   if args.lora else "")
                                + (", experts fed MXFP8-quantized x" if args.quant_x8 else "")
-                               + (", block-scaled gate/up" if args.mx_gateup else ""),
+                               + (", block-scaled gate/up" if args.mx_gateup else "")
+                               + (f", {args.shared} shared experts" if args.shared else ""),
                    "T": w.T, "H": w.H, "I": w.I, "E": w.E, "k": w.k, "weights": w.wfmt, "lora_rank": args.lora,
-                   "mx_gateup": args.mx_gateup, "quant_x8": args.quant_x8},
+                   "mx_gateup": args.mx_gateup, "quant_x8": args.quant_x8, "n_shared": args.shared},
         "roofline": roofline,
         "cpu_baseline": base,
         "detail": detail,

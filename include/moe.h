@@ -96,6 +96,11 @@ typedef struct {
                             2: bias for the selection only (the weights are the softmax of the
                             unbiased logits over the selected experts) */
     uint32_t flags;
+    int32_t n_shared;    /* shared experts (K3: 2), 0..top_k: experts every token takes with weight 1
+                            beside the routed ones (LazyLoRA README, "The engine": 896 routed and 2
+                            shared experts in each MoE layer).  Same shape, format and activation as
+                            a routed expert; their outputs are added to y, their input gradient to
+                            dx; they get no router term and no adapter.  Default 0. */
 } moe_desc;
 
 /* Expert and router weights: BORROWED device pointers.  The caller keeps
@@ -123,6 +128,12 @@ typedef struct {
     const uint8_t *scales[3];
     const uint8_t *rvq_idx[3];
     const uint16_t *rvq_cb[3];
+    /* the n_shared shared experts, laid out like the routed ones with n_shared in place of E
+       (only those of d->wfmt; NULL when n_shared = 0) */
+    const uint8_t *shared_codes[3];
+    const uint8_t *shared_scales[3];
+    const uint8_t *shared_rvq_idx[3];
+    const uint16_t *shared_rvq_cb[3];
 } moe_weights;
 
 /* Routing record, caller-owned device buffers written by moe_route() and
@@ -170,7 +181,10 @@ moe_status moe_layer_create(const moe_desc *d, const moe_weights *w, void *works
  * T = 0 is a no-op.  0 <= T <= max_tokens. */
 moe_status moe_route(moe_layer *L, const void *x, int32_t xt, int32_t T, const moe_routing *r, void *stream);
 
-/* Expert forward and combine: y[T][H] fp32 = sum_j w[t][j] * expert_{ids[t][j]}(x[t]).
+/* Expert forward and combine: y[T][H] fp32 = sum_j w[t][j] * expert_{ids[t][j]}(x[t])
+ * + sum_s shared_s(x[t]) (s < n_shared; summed in that order after the routed slots).
+ * The shared experts' pre-activations are not saved (moe_backward_input
+ * recomputes them).
  * r must come from moe_route() on the same x and T.  If saved_gu is not
  * NULL it receives the gate and up pre-activations [T*k][2][I] fp32 in
  * grouped row order (row = inv[t*k+j]) for moe_backward_input(). */

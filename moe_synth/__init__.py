@@ -186,6 +186,14 @@ def lora_adapter(w: Workload, r: int = 16, b_sd: float = 0.05):
     return A, B
 
 
+def shared_experts(w: Workload, n: int = 2):
+    """The layer's n shared experts in its weight format (K3: 2, LazyLoRA README, "The
+    engine"), drawn like routed experts E .. E+n-1: MXFP4 (codes, scales) or RVQ3 (idx, cb),
+    each a list over gate, up, down with a leading dimension n."""
+    ids = range(w.E, w.E + n)
+    return mxfp4_layer(w, ids) if w.wfmt == "mxfp4" else rvq3_layer(w, ids)
+
+
 def shrink(w: Workload, **kw) -> Workload:
     """A workload with some fields replaced (used by tests for reduced sizes)."""
     return dataclasses.replace(w, **kw)

@@ -289,6 +289,24 @@ def backward_input(x64, dy64, ids, w, wr, W: Weights, nthreads=None) -> np.ndarr
     return dx
 
 
+def shared_forward(x64, Ws: Weights, n_shared: int, nthreads=None) -> np.ndarray:
+    """Sum over s < n_shared of shared expert s applied to every token with weight 1: the
+    shared experts of a K3 MoE layer (LazyLoRA README, "The engine": 2 shared experts beside
+    the 896 routed ones), Ws holding them as experts 0..n_shared-1.  The layer output is
+    forward(...) of the routed slots plus this."""
+    T = x64.shape[0]
+    ids = np.tile(np.arange(n_shared, dtype=np.int32), (T, 1))
+    return forward(x64, ids, np.ones((T, n_shared)), Ws, nthreads)
+
+
+def shared_backward_input(x64, dy64, Ws: Weights, n_shared: int, nthreads=None) -> np.ndarray:
+    """d/dx of sum_t <dy_t, shared_forward(x)_t>: the shared experts' input gradient.  They
+    carry no routing weight to differentiate, so the router term is zero (zero router rows)."""
+    T = x64.shape[0]
+    ids = np.tile(np.arange(n_shared, dtype=np.int32), (T, 1))
+    return backward_input(x64, dy64, ids, np.ones((T, n_shared)), np.zeros((n_shared, Ws.H)), Ws, nthreads)
+
+
 def lora_grads(x64, dy64, ids, w, W: Weights, nthreads=None):
     """Adapter gradients (dA [gate, up, down], dB [gate, up, down]) of sum_t <dy[t], y[t]>."""
     assert W.lora is not None

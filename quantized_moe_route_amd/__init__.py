@@ -83,14 +83,16 @@ class MoELayer:
     MXFP4: pass codes=[gate, up, down] ([E][out][in/2] uint8) and scales ([E][out][in/32] uint8).
     RVQ3:  pass rvq_idx=[...] ([E][3][out][in/8] uint8) and rvq_cb=[...] ([E][3][256][8] fp16 bits).
     router_w: [E][H] fp32; router_b: [E] fp32 or None.  bias_mode: 1 (default with a bias) adds
-    the bias to the logits, 2 uses it for the selection only.  All tensors on the same GPU and
-    kept alive by this object.
+    the bias to the logits, 2 uses it for the selection only.  Shared experts (taken by every
+    token with weight 1): shared=[gate, up, down] in the routed experts' format with n_shared in
+    place of E (MXFP4: a pair (codes, scales) of such lists; RVQ3: (rvq_idx, rvq_cb)).  All tensors
+    on the same GPU and kept alive by this object.
     """
 
     def __init__(self, *, hidden: int, inter: int, n_experts: int, top_k: int, max_tokens: int, router_w,
                  router_b=None, codes: Optional[Sequence] = None, scales: Optional[Sequence] = None,
                  rvq_idx: Optional[Sequence] = None, rvq_cb: Optional[Sequence] = None, flags: int = 0,
-                 act: int = 0, bias_mode: Optional[int] = None):
+                 act: int = 0, bias_mode: Optional[int] = None, shared=None):
         torch = _torch()
         L = C.lib()
         d = C.MoeDesc()
@@ -100,10 +102,11 @@ class MoELayer:
         d.bias_mode = (1 if router_b is not None else 0) if bias_mode is None else bias_mode
         d.flags |= flags
         d.act = act
+        d.n_shared = 0 if shared is None else int(shared[0][0].shape[0])
         self.desc = d
         self.H, self.I, self.E, self.k, self.max_tokens = hidden, inter, n_experts, top_k, max_tokens
         self.device = router_w.device
-        self._keep = [router_w, router_b, codes, scales, rvq_idx, rvq_cb]
+        self._keep = [router_w, router_b, codes, scales, rvq_idx, rvq_cb, shared]
         self._lora = None
         w = C.MoeWeights()
         w.router_w = router_w.data_ptr()
@@ -115,6 +118,12 @@ class MoELayer:
             else:
                 w.rvq_idx[m] = rvq_idx[m].data_ptr()
                 w.rvq_cb[m] = rvq_cb[m].data_ptr()
+            if shared is not None and codes is not None:
+                w.shared_codes[m] = shared[0][m].data_ptr()
+                w.shared_scales[m] = shared[1][m].data_ptr()
+            elif shared is not None:
+                w.shared_rvq_idx[m] = shared[0][m].data_ptr()
+                w.shared_rvq_cb[m] = shared[1][m].data_ptr()
         self.weights = w
         nbytes = ctypes.c_size_t()
         C.check(L.moe_workspace_size(ctypes.byref(d), ctypes.byref(nbytes)), "moe_workspace_size")

@@ -32,13 +32,16 @@ PROF_NAMES = ("router_logits", "router_topk", "group", "gateup", "down", "combin
 class MoeDesc(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("max_tokens", ctypes.c_int32), ("wfmt", ctypes.c_int32),
-                ("act", ctypes.c_int32), ("bias_mode", ctypes.c_int32), ("flags", ctypes.c_uint32)]
+                ("act", ctypes.c_int32), ("bias_mode", ctypes.c_int32), ("flags", ctypes.c_uint32),
+                ("n_shared", ctypes.c_int32)]
 
 
 class MoeWeights(ctypes.Structure):
     _fields_ = [("router_w", ctypes.c_void_p), ("router_b", ctypes.c_void_p),
                 ("codes", ctypes.c_void_p * 3), ("scales", ctypes.c_void_p * 3),
-                ("rvq_idx", ctypes.c_void_p * 3), ("rvq_cb", ctypes.c_void_p * 3)]
+                ("rvq_idx", ctypes.c_void_p * 3), ("rvq_cb", ctypes.c_void_p * 3),
+                ("shared_codes", ctypes.c_void_p * 3), ("shared_scales", ctypes.c_void_p * 3),
+                ("shared_rvq_idx", ctypes.c_void_p * 3), ("shared_rvq_cb", ctypes.c_void_p * 3)]
 
 
 class MoeLora(ctypes.Structure):

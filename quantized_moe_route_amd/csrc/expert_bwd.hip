@@ -293,6 +293,10 @@ __global__ __launch_bounds__(256) void k_bwd_final(const ExpertBwdArgs a)
             acc.z += v.z + d * r.z;
             acc.w += v.w + d * r.w;
         }
+        for (int j = 0; j < a.k2; j++) {  // the shared experts' rows (no router term)
+            const float4 v = *(const float4 *)(a.dxs2 + ((size_t)t * a.k2 + j) * H + i);
+            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        }
         *(float4 *)(a.dx + (size_t)t * H + i) = acc;
     }
 }
@@ -309,7 +313,7 @@ static hipError_t bwd_launch(const ExpertBwdArgs &a, hipStream_t s)
         ProfScope ps(a.prof, PK_BWD_GATEUP, s);
         ps.launch((k_bwd_gateup<WFMT, NTT>), dim3((a.H + 63) / 64, maxU), dim3(256), 0, a);
     }
-    {
+    if (!a.skip_final) {
         ProfScope ps(a.prof, PK_BWD_FINAL, s);
         ps.launch(k_bwd_final, dim3(a.T), dim3(256), 0, a);
     }
@@ -350,6 +354,7 @@ hipError_t launch_expert_backward(const ExpertBwdArgs &a0, hipStream_t s)
         f.xq = a.xq;
         f.xq_s = a.xq_s;
         f.lora_gu = a.lora_gu;
+        f.tok_chunks = a.tok_chunks;
         f.prof = a.prof;
         set_lds_staging(f);
         hipError_t err = launch_gateup_only(f, s);
@@ -359,7 +364,7 @@ hipError_t launch_expert_backward(const ExpertBwdArgs &a0, hipStream_t s)
     if (bwd_uses_mm(a)) {
         hipError_t err = launch_bwd_down_mm(a, s);
         if (err == hipSuccess) err = launch_bwd_gateup_mm(a, s);
-        if (err != hipSuccess) return err;
+        if (err != hipSuccess || a.skip_final) return err;
         ProfScope ps(a.prof, PK_BWD_FINAL, s);
         ps.launch(k_bwd_final, dim3(a.T), dim3(256), 0, a);
         return hipGetLastError();

@@ -45,6 +45,31 @@ __device__ __forceinline__ void xcd_split(int nb, int &ai, int &cb)
 
 inline int xcd_grid(int maxU, int nb) { return 8 * ((maxU + 7) / 8) * nb; }
 
+static_assert(kBtTok == kTokChunk, "token chunks are one pass");
+
+// As in the forward grouped GEMM: work unit ai is an active expert, or with tok_chunks one
+// chunk of kTokChunk tokens of expert ai / tok_chunks.
+__device__ __forceinline__ bool bt_tokens(int tok_chunks, int &ai, const int32_t *n_active, const int32_t *active,
+                                          const int32_t *offsets, int &r0, int &ntok)
+{
+    int c = 0;
+    if (tok_chunks > 0) {
+        c = ai % tok_chunks;
+        ai /= tok_chunks;
+    }
+    if (ai >= *n_active) return false;
+    const int e = active[ai];
+    r0 = offsets[e];
+    ntok = offsets[e + 1] - r0;
+    if (tok_chunks > 0) {
+        r0 += c * kTokChunk;
+        ntok = min(kTokChunk, ntok - c * kTokChunk);
+    }
+    return ntok > 0;
+}
+
+inline int bt_units(const ExpertBwdArgs &a) { return a.tok_chunks > 0 ? a.E * a.tok_chunks : min(a.E, a.T * a.k); }
+
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void *p, uint32_t bytes)
 {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, 0x00020000);
@@ -307,11 +332,10 @@ __global__ __launch_bounds__(256, 2) void k_bwdt_mm(const ExpertBwdArgs a)
     const int tid = threadIdx.x;
     const int H = a.H, I = a.I;
     const int M = GU ? H : I;
-    int ai, cb;
+    int ai, cb, r0, ntok;
     xcd_split(M / 256, ai, cb);
-    if (ai >= *a.n_active) return;
+    if (!bt_tokens(a.tok_chunks, ai, a.n_active, a.active, a.offsets, r0, ntok)) return;
     const int e = a.active[ai];
-    const int r0 = a.offsets[e], ntok = a.offsets[e + 1] - r0;
     BtBlock b;
     b.M = M;
     b.mb0 = cb * 256;
@@ -371,7 +395,7 @@ bool bwd_mm_supported(const ExpertBwdArgs &a)
 
 hipError_t launch_bwd_down_mm(const ExpertBwdArgs &a, hipStream_t s)
 {
-    const int maxU = min(a.E, a.T * a.k);
+    const int maxU = bt_units(a);
     ProfScope ps(a.prof, PK_BWD_DOWN, s);
     ps.launch(k_bwdt_mm<false>, dim3(xcd_grid(maxU, a.I / 256)), dim3(256), 0, a);
     return hipGetLastError();
@@ -379,7 +403,7 @@ hipError_t launch_bwd_down_mm(const ExpertBwdArgs &a, hipStream_t s)
 
 hipError_t launch_bwd_gateup_mm(const ExpertBwdArgs &a, hipStream_t s)
 {
-    const int maxU = min(a.E, a.T * a.k);
+    const int maxU = bt_units(a);
     ProfScope ps(a.prof, PK_BWD_GATEUP, s);
     ps.launch(k_bwdt_mm<true>, dim3(xcd_grid(maxU, a.H / 256)), dim3(256), 0, a);
     return hipGetLastError();

@@ -302,8 +302,9 @@ __global__ __launch_bounds__(256) void k_down(const ExpertFwdArgs a)
 }
 
 // y[t] = sum over j in rank order of the weighted slot rows (deterministic).
+// The k2 rows of ybuf2 (the shared experts' outputs, null: none) follow the routed slots.
 __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ ybuf, int T, int H, int k,
-                                                 float *__restrict__ y)
+                                                 const float *__restrict__ ybuf2, int k2, float *__restrict__ y)
 {
     const size_t n4 = (size_t)T * H / 4;
     for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n4; i += (size_t)gridDim.x * blockDim.x) {
@@ -322,17 +323,22 @@ __global__ __launch_bounds__(256) void k_combine(const float *__restrict__ ybuf,
                 acc.x += v[u].x; acc.y += v[u].y; acc.z += v[u].z; acc.w += v[u].w;
             }
         }
+        for (int j = 0; j < k2; j++) {
+            const float4 v = *(const float4 *)(ybuf2 + ((size_t)t * k2 + j) * H + 4 * m4);
+            acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+        }
         *(float4 *)(y + (size_t)t * H + 4 * m4) = acc;
     }
 }
 
 static hipError_t launch_combine(const ExpertFwdArgs &a, hipStream_t s)
 {
+    if (a.skip_combine) return hipSuccess;
     const size_t n4 = (size_t)a.T * a.H / 4;
     const size_t nb = (n4 + 255) / 256;
     const int blocks = (int)(nb < 4096 ? nb : 4096);
     ProfScope ps(a.prof, PK_COMBINE, s);
-    ps.launch(k_combine, dim3(blocks), dim3(256), 0, a.ybuf, a.T, a.H, a.k, a.y);
+    ps.launch(k_combine, dim3(blocks), dim3(256), 0, a.ybuf, a.T, a.H, a.k, a.ybuf2, a.ybuf2 ? a.k2 : 0, a.y);
     return hipGetLastError();
 }
 

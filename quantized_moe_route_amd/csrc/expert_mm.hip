@@ -50,6 +50,35 @@ __device__ __forceinline__ void xcd_split(int nb, int &ai, int &cb)
 
 static inline int xcd_grid(int maxU, int nb) { return 8 * ((maxU + 7) / 8) * nb; }
 
+static_assert(kMmTok == kTokChunk, "token chunks are one pass");
+
+// The slot rows [r0, r0 + ntok) of work unit ai (an active expert, or with tok_chunks
+// one chunk of kTokChunk tokens of expert ai / tok_chunks); false: nothing to do.
+__device__ __forceinline__ bool mm_tokens(int tok_chunks, int &ai, const int32_t *n_active, const int32_t *active,
+                                          const int32_t *offsets, int &r0, int &ntok)
+{
+    int c = 0;
+    if (tok_chunks > 0) {
+        c = ai % tok_chunks;
+        ai /= tok_chunks;
+    }
+    if (ai >= *n_active) return false;
+    const int e = active[ai];
+    r0 = offsets[e];
+    ntok = offsets[e + 1] - r0;
+    if (tok_chunks > 0) {
+        r0 += c * kTokChunk;
+        ntok = min(kTokChunk, ntok - c * kTokChunk);
+    }
+    return ntok > 0;
+}
+
+// Work units of a grouped-GEMM launch: active experts, or expert token chunks.
+static inline int mm_units(const ExpertFwdArgs &a)
+{
+    return a.tok_chunks > 0 ? a.E * a.tok_chunks : min(a.E, a.T * a.k);
+}
+
 __device__ __forceinline__ int lds_slot(int row, int chunk) { return row * 16 + (chunk ^ (row & 15)); }
 
 // 8 E2M1 codes (one dword) times a power-of-two scale -> 8 bf16, exact.
@@ -418,11 +447,10 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mm(const ExpertFwdArgs a)
     __shared__ __attribute__((aligned(16))) uint8_t scl[256 * kSclRow];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
     const int H = a.H, I = a.I;
-    int ai, cb;
+    int ai, cb, r0, ntok;
     xcd_split(I / 128, ai, cb);
-    if (ai >= *a.n_active) return;
+    if (!mm_tokens(a.tok_chunks, ai, a.n_active, a.active, a.offsets, r0, ntok)) return;
     const int e = a.active[ai];
-    const int r0 = a.offsets[e], ntok = a.offsets[e + 1] - r0;
     GuBlock b;
     const size_t eoc = (size_t)e * I * (H / 2), eos = (size_t)e * I * (H / 32);
     b.code[0] = buf_rsrc(a.gate.codes + eoc, I * (H / 2));
@@ -619,11 +647,10 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mx(const ExpertFwdArgs a)
     __shared__ __attribute__((aligned(16))) uint8_t scl[256 * kSclRow];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
     const int H = a.H, I = a.I;
-    int ai, cb;
+    int ai, cb, r0, ntok;
     xcd_split(I / 128, ai, cb);
-    if (ai >= *a.n_active) return;
+    if (!mm_tokens(a.tok_chunks, ai, a.n_active, a.active, a.offsets, r0, ntok)) return;
     const int e = a.active[ai];
-    const int r0 = a.offsets[e], ntok = a.offsets[e + 1] - r0;
     GuBlock b;
     const size_t eoc = (size_t)e * I * (H / 2), eos = (size_t)e * I * (H / 32);
     b.code[0] = buf_rsrc(a.gate.codes + eoc, I * (H / 2));
@@ -780,11 +807,10 @@ __global__ __launch_bounds__(256, 2) void k_down_mm(const ExpertFwdArgs a)
     __shared__ __attribute__((aligned(16))) uint8_t scl[256 * kSclRow];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
     const int H = a.H, I = a.I;
-    int ai, rb;
+    int ai, rb, r0, ntok;
     xcd_split(H / 256, ai, rb);
-    if (ai >= *a.n_active) return;
+    if (!mm_tokens(a.tok_chunks, ai, a.n_active, a.active, a.offsets, r0, ntok)) return;
     const int e = a.active[ai];
-    const int r0 = a.offsets[e], ntok = a.offsets[e + 1] - r0;
     DnBlock b;
     b.code = buf_rsrc(a.down.codes + (size_t)e * H * (I / 2), H * (I / 2));
     b.scale = buf_rsrc(a.down.scales + (size_t)e * H * (I / 32), H * (I / 32));
@@ -818,7 +844,7 @@ bool mm_supported(const ExpertFwdArgs &a)
 
 hipError_t launch_gateup_mm(const ExpertFwdArgs &a, hipStream_t s)
 {
-    const int maxU = min(a.E, a.T * a.k);
+    const int maxU = mm_units(a);
     if (!a.xq) {
         ProfScope ps(a.prof, PK_GATEUP, s);
         ps.launch(k_gateup_mm, dim3(xcd_grid(maxU, a.I / 128)), dim3(256), 0, a);
@@ -845,7 +871,7 @@ hipError_t launch_gateup_mm(const ExpertFwdArgs &a, hipStream_t s)
 
 hipError_t launch_down_mm(const ExpertFwdArgs &a, hipStream_t s)
 {
-    const int maxU = min(a.E, a.T * a.k);
+    const int maxU = mm_units(a);
     ProfScope ps(a.prof, PK_DOWN, s);
     ps.launch(k_down_mm, dim3(xcd_grid(maxU, a.H / 256)), dim3(256), 0, a);
     return hipGetLastError();

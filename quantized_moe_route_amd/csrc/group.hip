@@ -106,4 +106,38 @@ hipError_t launch_group(const GroupArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
+// Slots t n_sh + j of the dense routing: token t takes expert j with weight 1; grouped by
+// expert, expert j's rows are j T + t (token order).
+__global__ __launch_bounds__(256) void k_dense_routing(int T, int n_sh, int32_t *__restrict__ ids, float *__restrict__ w,
+                                                       int32_t *__restrict__ offsets, int32_t *__restrict__ perm,
+                                                       int32_t *__restrict__ inv, int32_t *__restrict__ active,
+                                                       int32_t *__restrict__ n_active)
+{
+    const long n = (long)T * n_sh;
+    for (long i = blockIdx.x * (long)blockDim.x + threadIdx.x; i < n; i += (long)gridDim.x * blockDim.x) {
+        const int t = (int)(i / n_sh), j = (int)(i - (long)t * n_sh);
+        const int32_t r = j * T + t;
+        ids[i] = j;
+        w[i] = 1.f;
+        inv[i] = r;
+        perm[r] = (int32_t)i;
+    }
+    if (blockIdx.x == 0 && threadIdx.x <= n_sh) {
+        offsets[threadIdx.x] = (int32_t)threadIdx.x * T;
+        if (threadIdx.x < n_sh) active[threadIdx.x] = (int32_t)threadIdx.x;
+        if (threadIdx.x == 0) *n_active = n_sh;
+    }
+}
+
+hipError_t launch_dense_routing(int T, int n_sh, int32_t *ids, float *w, int32_t *offsets, int32_t *perm, int32_t *inv,
+                                int32_t *active, int32_t *n_active, hipStream_t s)
+{
+    const long n = (long)T * n_sh;
+    const long nb = (n + 255) / 256;
+    const int blocks = (int)(nb < 1024 ? nb : 1024);
+    hipLaunchKernelGGL(k_dense_routing, dim3(blocks < 1 ? 1 : blocks), dim3(256), 0, s, T, n_sh, ids, w, offsets, perm,
+                       inv, active, n_active);
+    return hipGetLastError();
+}
+
 }  // namespace moe

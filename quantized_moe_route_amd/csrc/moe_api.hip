@@ -41,6 +41,9 @@ struct Layout {
     size_t logits, beta, h, ybuf, gu, dgdu, dp, xq, xqs;
     size_t l_vx, l_gu, l_hbar, l_z, l_wd, l_c, l_dgu, l_m, l_part;  // adapter (MOE_F_LORA)
     size_t xq8;  // MXFP8-quantized activations as bf16 (MOE_F_QUANT_X8)
+    // shared experts: their slot rows (forward outputs, backward input-gradient rows) and
+    // their dense routing; the rest of their scratch is the routed slots' (n_shared <= k)
+    size_t sh_rows, sh_ids, sh_w, sh_off, sh_perm, sh_inv, sh_act, sh_nact;
     size_t total;
 };
 
@@ -80,6 +83,15 @@ Layout layout_of(const moe_desc &d)
     L.l_m = take(Tl * 2 * R * 4);
     L.l_part = take(lo ? kLoraPartFloats * 4 : 0);
     L.xq8 = take((d.flags & MOE_F_QUANT_X8) ? T * H * 2 : 0);
+    const size_t NS = (size_t)d.n_shared, Ssh = T * NS;
+    L.sh_rows = take(Ssh * H * 4);
+    L.sh_ids = take(Ssh * 4);
+    L.sh_w = take(Ssh * 4);
+    L.sh_off = take(NS ? (NS + 1) * 4 : 0);
+    L.sh_perm = take(Ssh * 4);
+    L.sh_inv = take(Ssh * 4);
+    L.sh_act = take(NS * 4);
+    L.sh_nact = take(NS ? 4 : 0);
     L.total = off;
     return L;
 }
@@ -101,6 +113,8 @@ moe_status check_desc(const moe_desc *d)
         return fail(MOE_ERR_UNSUPPORTED, "activation %d is not implemented", d->act);
     if (d->bias_mode < 0 || d->bias_mode > 2)
         return fail(MOE_ERR_UNSUPPORTED, "bias_mode %d is not implemented", d->bias_mode);
+    if (d->n_shared < 0 || d->n_shared > d->top_k)
+        return fail(MOE_ERR_INVALID_ARG, "n_shared=%d must be in 0..top_k=%d", d->n_shared, d->top_k);
     return MOE_OK;
 }
 
@@ -197,6 +211,37 @@ moe::MatW matw(const moe_weights &w, int m)
     return r;
 }
 
+moe::MatW shared_matw(const moe_weights &w, int m)
+{
+    moe::MatW r;
+    r.codes = w.shared_codes[m];
+    r.scales = w.shared_scales[m];
+    r.idx = w.shared_rvq_idx[m];
+    r.cb = w.shared_rvq_cb[m];
+    return r;
+}
+
+// The shared experts' dense routing for T tokens, written into the workspace.
+struct DenseRouting {
+    int32_t *ids, *off, *perm, *inv, *act, *nact;
+    float *w;
+};
+
+hipError_t dense_routing(const moe_layer *L, int T, DenseRouting &r, hipStream_t s)
+{
+    char *b = L->ws;
+    r.ids = (int32_t *)(b + L->lay.sh_ids);
+    r.w = (float *)(b + L->lay.sh_w);
+    r.off = (int32_t *)(b + L->lay.sh_off);
+    r.perm = (int32_t *)(b + L->lay.sh_perm);
+    r.inv = (int32_t *)(b + L->lay.sh_inv);
+    r.act = (int32_t *)(b + L->lay.sh_act);
+    r.nact = (int32_t *)(b + L->lay.sh_nact);
+    return moe::launch_dense_routing(T, L->d.n_shared, r.ids, r.w, r.off, r.perm, r.inv, r.act, r.nact, s);
+}
+
+int tok_chunks(int T) { return (T + moe::kTokChunk - 1) / moe::kTokChunk; }
+
 }  // namespace
 
 extern "C" {
@@ -247,6 +292,18 @@ moe_status moe_layer_create(const moe_desc *d, const moe_weights *w, void *works
             if (!w->rvq_idx[m] || !w->rvq_cb[m]) return fail(MOE_ERR_INVALID_ARG, "%s rvq_idx/rvq_cb missing", names[m]);
             if (!aligned(w->rvq_idx[m], 16) || !aligned(w->rvq_cb[m], 16))
                 return fail(MOE_ERR_INVALID_ARG, "%s rvq_idx/rvq_cb must be 16-byte aligned", names[m]);
+        }
+        if (d->n_shared == 0) continue;
+        if (d->wfmt == MOE_W_MXFP4) {
+            if (!w->shared_codes[m] || !w->shared_scales[m])
+                return fail(MOE_ERR_INVALID_ARG, "shared %s codes/scales missing", names[m]);
+            if (!aligned(w->shared_codes[m], 16) || !aligned(w->shared_scales[m], 16))
+                return fail(MOE_ERR_INVALID_ARG, "shared %s codes and scales must be 16-byte aligned", names[m]);
+        } else {
+            if (!w->shared_rvq_idx[m] || !w->shared_rvq_cb[m])
+                return fail(MOE_ERR_INVALID_ARG, "shared %s rvq_idx/rvq_cb missing", names[m]);
+            if (!aligned(w->shared_rvq_idx[m], 16) || !aligned(w->shared_rvq_cb[m], 16))
+                return fail(MOE_ERR_INVALID_ARG, "shared %s rvq_idx/rvq_cb must be 16-byte aligned", names[m]);
         }
     }
     const Layout lay = layout_of(*d);
@@ -361,6 +418,30 @@ moe_status moe_forward(moe_layer *L, const void *x, int32_t xt, int32_t T, const
         x = xq;
         xt = MOE_DT_BF16;
     }
+    if (L->d.n_shared > 0) {
+        // the shared experts first: their slot rows stay in the workspace for the combine
+        DenseRouting dr;
+        if ((st = device_status(dense_routing(L, T, dr, hs), "shared-expert routing")) != MOE_OK) return st;
+        moe::ExpertFwdArgs sa = a;
+        sa.gate = shared_matw(L->w, 0);
+        sa.up = shared_matw(L->w, 1);
+        sa.down = shared_matw(L->w, 2);
+        sa.E = sa.k = L->d.n_shared;
+        sa.offsets = dr.off;
+        sa.perm = dr.perm;
+        sa.active = dr.act;
+        sa.n_active = dr.nact;
+        sa.w = dr.w;
+        sa.h_lo = sa.h_hi + (size_t)T * sa.k * sa.I;
+        sa.gu = nullptr;
+        sa.ybuf = (float *)(L->ws + L->lay.sh_rows);
+        sa.tok_chunks = tok_chunks(T);
+        sa.skip_combine = 1;
+        moe::set_lds_staging(sa);
+        if ((st = device_status(moe::launch_expert_forward(sa, hs), "shared experts")) != MOE_OK) return st;
+        a.ybuf2 = sa.ybuf;
+        a.k2 = sa.k;
+    }
     moe::set_lds_staging(a);
     if (!L->has_lora) return device_status(moe::launch_expert_forward(a, hs), "forward");
     const moe::LoraWs lw = lora_ws(L);
@@ -425,6 +506,32 @@ moe_status backward_impl(moe_layer *L, const void *x, int32_t xt, const void *dy
     }
     a.prof = &L->prof;
     const hipStream_t hs = (hipStream_t)stream;
+    if (L->d.n_shared > 0) {
+        // the shared experts' input-gradient rows first (g, u recomputed; no router term),
+        // summed into dx by the routed pass's final kernel
+        DenseRouting dr;
+        if ((st = device_status(dense_routing(L, T, dr, hs), "shared-expert routing")) != MOE_OK) return st;
+        moe::ExpertBwdArgs sb = a;
+        sb.gate = shared_matw(L->w, 0);
+        sb.up = shared_matw(L->w, 1);
+        sb.down = shared_matw(L->w, 2);
+        sb.E = sb.k = L->d.n_shared;
+        sb.ids = dr.ids;
+        sb.offsets = dr.off;
+        sb.perm = dr.perm;
+        sb.inv = dr.inv;
+        sb.active = dr.act;
+        sb.n_active = dr.nact;
+        sb.w = dr.w;
+        sb.gu = nullptr;
+        sb.h_lo = sb.h_hi + (size_t)T * sb.k * sb.I;
+        sb.dxs = (float *)(L->ws + L->lay.sh_rows);
+        sb.tok_chunks = tok_chunks(T);
+        sb.skip_final = 1;
+        if ((st = device_status(moe::launch_expert_backward(sb, hs), "shared experts (backward)")) != MOE_OK) return st;
+        a.dxs2 = sb.dxs;
+        a.k2 = sb.k;
+    }
     if (!L->has_lora) return device_status(moe::launch_expert_backward(a, hs), "backward_input");
     const moe::LoraWs lw = lora_ws(L);
     const bool grads = dA != nullptr;

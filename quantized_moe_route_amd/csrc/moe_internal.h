@@ -101,6 +101,12 @@ struct ExpertFwdArgs {
     int nl_h;            // ... and their h rows (down product)
     const float *lora_gu;  // [T][2I] per-token adapter terms added to g | u, or null
     int xq_single;         // xq / xq_s already hold x as one exact E4M3 term (MXFP8 input)
+    int tok_chunks;        // > 0: every expert holds the same token count, split into this many
+                           // chunks of kTokChunk tokens, one grouped-GEMM block per chunk and column
+                           // block (dense experts: the shared experts); 0: one block per expert
+    int skip_combine;      // leave the slot rows in ybuf (no k_combine)
+    const float *ybuf2;    // [T][k2][H] more slot rows that k_combine adds after the k routed ones
+    int k2;
 };
 
 struct ExpertBwdArgs {
@@ -127,7 +133,19 @@ struct ExpertBwdArgs {
     int act;             // ACT_SWIGLU or ACT_SITU
     const float *lora_gu;  // [T][2I] adapter terms of g | u for the recomputation, or null
     const float *lora_c;   // [T][I] adapter term added to a = Wd^T dy per token, or null
+    int tok_chunks;        // as in ExpertFwdArgs
+    int skip_final;        // leave the slot rows in dxs (no k_bwd_final)
+    const float *dxs2;     // [T][k2][H] more slot rows that k_bwd_final adds (no router term)
+    int k2;
 };
+
+// Token chunk of the grouped-GEMM kernels (one pass of a block).
+constexpr int kTokChunk = 96;
+
+// Routing of n_sh experts that every token takes with weight 1 (the shared experts):
+// expert s holds tokens 0..T-1 in order (group.hip).
+hipError_t launch_dense_routing(int T, int n_sh, int32_t *ids, float *w, int32_t *offsets, int32_t *perm, int32_t *inv,
+                                int32_t *active, int32_t *n_active, hipStream_t s);
 
 // Token rows staged in LDS by the few-token (decode) expert kernels: at most 16 rows
 // and at most 48 KB of LDS per block.

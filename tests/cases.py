@@ -31,6 +31,7 @@ class HostCase:
     act: int = 0  # 0 SwiGLU, 1 SiTU
     bias_mode: int = 1  # with a bias: 1 in the logits, 2 selection only
     lora: Optional[tuple] = None  # (A [3], B [3], scale) fp32 arrays: the shared adapter
+    shared: Optional[tuple] = None  # the shared experts: (codes, scales) or (idx, cb), n leading
 
     @property
     def x64(self):
@@ -45,6 +46,29 @@ class HostCase:
             return oracle.Weights(self.w.H, self.w.I, codes=self.codes, scales=self.scales, act=self.act,
                                   lora=self.lora)
         return oracle.Weights(self.w.H, self.w.I, idx=self.idx, cb=self.cb, act=self.act, lora=self.lora)
+
+    @property
+    def n_shared(self) -> int:
+        return 0 if self.shared is None else int(self.shared[0][0].shape[0])
+
+    def shared_weights(self):
+        a, b = self.shared
+        if self.codes is not None:
+            return oracle.Weights(self.w.H, self.w.I, codes=a, scales=b, act=self.act)
+        return oracle.Weights(self.w.H, self.w.I, idx=a, cb=b, act=self.act)
+
+    def ref_forward(self, x64, ids, p, W=None):
+        """The oracle's layer output on x64 for the given routing (routed slots + shared experts)."""
+        y = oracle.forward(x64, ids, p, W or self.oracle_weights())
+        if self.shared is not None:
+            y = y + oracle.shared_forward(x64, self.shared_weights(), self.n_shared)
+        return y
+
+    def ref_backward(self, x64, dy64, ids, p, W=None):
+        dx = oracle.backward_input(x64, dy64, ids, p, self.wr, W or self.oracle_weights())
+        if self.shared is not None:
+            dx = dx + oracle.shared_backward_input(x64, dy64, self.shared_weights(), self.n_shared)
+        return dx
 
 
 def host_case(w: syn.Workload, T: Optional[int] = None, with_dy: Optional[bool] = None) -> HostCase:
@@ -75,6 +99,8 @@ def device_layer(c: HostCase, max_tokens: int, flags: int = 0):
     else:
         kw["rvq_idx"] = [q.to_device(a) for a in c.idx]
         kw["rvq_cb"] = [q.to_device(a) for a in c.cb]
+    if c.shared is not None:
+        kw["shared"] = ([q.to_device(a) for a in c.shared[0]], [q.to_device(a) for a in c.shared[1]])
     return q.MoELayer(**kw)
 
 
@@ -124,8 +150,8 @@ def lora_parity(c: HostCase, L, name: str, rank: int = 16, scale: float = 2.0, s
     torch.cuda.synchronize()
     assert np.array_equal(np_(r.ids), ids), f"{name}: routing ids"
     W = c.oracle_weights()
-    y_ref = oracle.forward(c.x64, ids, p, W)
-    dx_ref = oracle.backward_input(c.x64, c.dy64, ids, p, c.wr, W)
+    y_ref = c.ref_forward(c.x64, ids, p, W)
+    dx_ref = c.ref_backward(c.x64, c.dy64, ids, p, W)
     dA_ref, dB_ref = oracle.lora_grads(c.x64, c.dy64, ids, p, W)
     gu = L.new_saved_gu(w.T)
     y = L.forward(x, r, saved_gu=gu)
@@ -159,4 +185,4 @@ def lora_parity(c: HostCase, L, name: str, rank: int = 16, scale: float = 2.0, s
     y0 = L.forward(x, r)
     torch.cuda.synchronize()
     c.lora = None
-    assert rel_err(np_(y0), oracle.forward(c.x64, ids, p, c.oracle_weights())) <= TOL, f"{name}: detached forward"
+    assert rel_err(np_(y0), c.ref_forward(c.x64, ids, p)) <= TOL, f"{name}: detached forward"

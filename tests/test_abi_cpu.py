@@ -217,3 +217,35 @@ def test_lora_argument_checks():
     assert L.moe_backward_lora(h, 0x1000, C.MOE_DT_BF16, 0x1000, C.MOE_DT_BF16, 1, ctypes.byref(r), None, 0x1000,
                                vp3(0x1000, 0x2008, 0x3000), dB, None) == C.MOE_ERR_INVALID_ARG
     L.moe_destroy(h)
+
+
+def test_shared_expert_argument_checks():
+    L = C.lib()
+    assert _desc().n_shared == 0
+    n0, n2 = ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.moe_workspace_size(ctypes.byref(_desc(max_tokens=8)), ctypes.byref(n0)) == C.MOE_OK
+    assert L.moe_workspace_size(ctypes.byref(_desc(max_tokens=8, n_shared=2)), ctypes.byref(n2)) == C.MOE_OK
+    assert n2.value > n0.value  # the shared experts' slot rows and routing
+    for bad in (dict(n_shared=-1), dict(n_shared=17), dict(n_experts=8, top_k=2, n_shared=3)):
+        assert L.moe_workspace_size(ctypes.byref(_desc(max_tokens=8, **bad)), ctypes.byref(n0)) == C.MOE_ERR_INVALID_ARG
+    d = _desc(max_tokens=8, n_shared=2)
+    assert _create(d, _fake_weights())[0] == C.MOE_ERR_INVALID_ARG  # shared weights missing
+    w = _fake_weights()
+    for m in range(3):
+        w.shared_codes[m] = 0x40000 + m * 256
+        w.shared_scales[m] = 0x50000 + m * 256
+    st, h = _create(d, w)
+    assert st == C.MOE_OK
+    L.moe_destroy(h)
+    w.shared_scales[1] = 0x50008
+    assert _create(d, w)[0] == C.MOE_ERR_INVALID_ARG  # misaligned
+    # RVQ3 layers take the RVQ3 arrays of the shared experts
+    d3 = _desc(max_tokens=8, n_shared=1, wfmt=C.MOE_W_RVQ3)
+    w3 = _fake_weights(C.MOE_W_RVQ3)
+    assert _create(d3, w3)[0] == C.MOE_ERR_INVALID_ARG
+    for m in range(3):
+        w3.shared_rvq_idx[m] = 0x40000 + m * 256
+        w3.shared_rvq_cb[m] = 0x50000 + m * 256
+    st, h = _create(d3, w3)
+    assert st == C.MOE_OK
+    L.moe_destroy(h)

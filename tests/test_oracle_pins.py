@@ -686,3 +686,72 @@ def test_lora_grads_match_central_finite_differences(act):
                 an = float(np.sum(G * v))
                 assert abs(fd - an) <= 1e-6 * max(abs(an), 1e-3 * np.linalg.norm(G) * np.linalg.norm(v)), \
                     (which, m, fd, an)
+
+
+# ---------------------------------------------------------------- shared experts
+
+
+def _tiny_shared(w, act=oracle.ACT_SWIGLU, n=2):
+    sc, ss = syn.shared_experts(w, n)
+    return oracle.Weights(w.H, w.I, codes=sc, scales=ss, act=act)
+
+
+@pytest.mark.parametrize("act", [oracle.ACT_SWIGLU, oracle.ACT_SITU])
+def test_shared_experts_are_dense_mlps_added_with_weight_one(act):
+    """The shared-expert term equals the textbook gated MLPs on the decoded matrices (numpy
+    products), summed over the shared experts with weight 1; one shared expert alone equals
+    the routed layer run on that expert with k = 1."""
+    w, _ = _tiny_layer(E=16)
+    Ws = _tiny_shared(w, act)
+    x = oracle.to_f64(syn.activations(w), "f32")
+    ref = np.zeros((w.T, w.H))
+    for s in range(2):
+        Wg, Wu, Wd = (oracle.decode_matrix(Ws, m, s) for m in range(3))
+        g, u = x @ Wg.T, x @ Wu.T
+        if act == oracle.ACT_SWIGLU:
+            h = scipy.special.expit(g) * g * u
+        else:
+            h = 4 * np.tanh(g / 4) * scipy.special.expit(g) * 25 * np.tanh(u / 25)
+        ref += h @ Wd.T
+    got = oracle.shared_forward(x, Ws, 2)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-14 * np.abs(ref).max())
+    one = oracle.shared_forward(x, Ws, 1)
+    k1 = oracle.forward(x, np.zeros((w.T, 1), np.int32), np.ones((w.T, 1)), Ws)
+    assert np.array_equal(one, k1)
+
+
+def test_shared_backward_matches_central_finite_differences():
+    """dX of the layer with two shared experts (routed term with its router part, plus the
+    shared experts' input gradient) against central differences of L(x) = sum <dY, y(x)>,
+    with routing-flip detection as in the routed-layer pin."""
+    w, W = _tiny_layer()
+    Ws = _tiny_shared(w)
+    x = oracle.to_f64(syn.activations(w), "f32")
+    wr = syn.router_weight(w)
+    dy = oracle.to_f64(syn.upstream_grad(w), "f32") * 100.0
+    ids, p, _ = oracle.route(x, wr, None, w.k)
+    dx = oracle.backward_input(x, dy, ids, p, wr, W) + oracle.shared_backward_input(x, dy, Ws, 2)
+
+    def loss(xx):
+        y, ii, _ = oracle.layer_forward(xx, wr, None, w.k, W, nthreads=1)
+        return float(np.sum(dy * (y + oracle.shared_forward(xx, Ws, 2, nthreads=1)))), ii
+
+    rng = np.random.default_rng(7)
+    checked = 0
+    for v in [rng.standard_normal(x.shape) for _ in range(6)]:
+        eps = 1e-6 * np.linalg.norm(x) / np.linalg.norm(v)
+        for _ in range(8):
+            lp, ip = loss(x + eps * v)
+            lm, im = loss(x - eps * v)
+            if np.array_equal(ip, ids) and np.array_equal(im, ids):
+                break
+            eps /= 2
+        else:
+            continue
+        fd = (lp - lm) / (2 * eps)
+        an = float(np.sum(dx * v))
+        assert abs(fd - an) <= 1e-7 * max(abs(an), 1e-3 * np.linalg.norm(dx) * np.linalg.norm(v)), (fd, an)
+        checked += 1
+    assert checked >= 5
+    # the shared part alone is linear in dY and has no router term: zero dY, zero gradient
+    assert not np.any(oracle.shared_backward_input(x, np.zeros_like(dy), Ws, 2))

@@ -237,7 +237,9 @@ def main():
     S = w.T * w.k
     x_bytes = w.T * w.H * 2
     S_sh = w.T * args.shared
-    gu_alg = [u * gateup_bytes_per_expert + x_bytes + S * w.I * 4
+    # weights, token rows, the h planes (bf16 hi + lo) and, in the training pass, the saved
+    # gate/up pre-activations (fp32 g and u per slot)
+    gu_alg = [u * gateup_bytes_per_expert + x_bytes + S * w.I * 4 + (S * 2 * w.I * 4 if train else 0)
               + (shared_gateup_bytes + x_bytes + S_sh * w.I * 4 if args.shared else 0) for u in steps_U]
     gu_bytes = sum(gu_alg) / len(gu_alg)
     # gate/up time per step (with shared experts: both launches), from events stamped at the

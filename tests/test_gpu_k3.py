@@ -141,3 +141,46 @@ def test_lora_k3_two_tokens(k3_mxfp4):
                     scales=scales, flags=C.MOE_F_LORA)
     lora_parity(cc, La, "lora-k3-T2", saved=(True,))
     La.close()
+
+
+def test_shared_experts_k3(k3_mxfp4):
+    """The K3 layer with its 2 shared experts (LazyLoRA README, "The engine") beside the 896
+    routed ones: one decode token in full, and the 4096-token pass (the shared experts'
+    tokens in 43 grouped-GEMM chunks) on sampled tokens, forward and dX."""
+    import quantized_moe_route_amd as q
+    c, L = k3_mxfp4
+    w = c.w
+    log("generating 2 shared experts at the K3 shape")
+    sh = syn.shared_experts(w, 2)
+    Ws = oracle.Weights(w.H, w.I, codes=sh[0], scales=sh[1])
+    Ls = q.MoELayer(hidden=w.H, inter=w.I, n_experts=w.E, top_k=w.k, max_tokens=4096, router_w=L._keep[0],
+                    codes=L._keep[2], scales=L._keep[3],
+                    shared=([q.to_device(a) for a in sh[0]], [q.to_device(a) for a in sh[1]]))
+    W = c.oracle_weights()
+    for name, T, sample, with_bwd in (("decode1", 1, 1, False), ("train4096", 4096, 3, True)):
+        wk = syn.shrink(w, T=T, x_key=syn.WORKLOADS[name].x_key)
+        assert syn.WORKLOADS[name].bias_sd in (None, 0.0)
+        x_h = syn.activations(wk, T)
+        x64 = oracle.to_f64(x_h, "bf16")
+        ids, p, _ = oracle.route(x64, c.wr, None, w.k)
+        x = act_tensor(x_h, "bf16")
+        r = Ls.route(x)
+        y = Ls.forward(x, r)
+        _sync()
+        assert np.array_equal(_np(r.ids), ids)
+        toks = np.sort(np.random.default_rng(T + 1).choice(T, size=sample, replace=False))
+        y_ref = oracle.forward(x64[toks], ids[toks], p[toks], W) + oracle.shared_forward(x64[toks], Ws, 2)
+        e = rel_err(_np(y)[toks], y_ref)
+        log(f"shared-{name}: y rel err {e:.3e} on tokens {toks.tolist()}")
+        assert e <= TOL
+        if with_bwd:
+            dy_h = syn.upstream_grad(wk, T)
+            dx = Ls.backward_input(x, act_tensor(dy_h, "bf16"), r)
+            _sync()
+            dy64 = oracle.to_f64(dy_h, "bf16")[toks]
+            dx_ref = (oracle.backward_input(x64[toks], dy64, ids[toks], p[toks], c.wr, W)
+                      + oracle.shared_backward_input(x64[toks], dy64, Ws, 2))
+            e = rel_err(_np(dx)[toks], dx_ref)
+            log(f"shared-{name}: dX rel err {e:.3e}")
+            assert e <= TOL and np.isfinite(_np(dx)).all()
+    Ls.close()

@@ -231,8 +231,9 @@ def main():
     torch.cuda.synchronize()
     gu_ms, gu_n = L.prof_read(C.PROF_GATEUP)
     L.prof_enable([])
-    # one gate/up launch per step, and one more for the shared experts
-    assert gu_n == args.steps * (2 if args.shared else 1)
+    # one gate/up launch per step; shared experts: their units join it (few tokens) or take
+    # a launch of their own
+    assert gu_n == args.steps or (args.shared and gu_n == 2 * args.steps), gu_n
     steps_U = [U[(args.warmup + i) % POOL] for i in range(args.steps)]
     S = w.T * w.k
     x_bytes = w.T * w.H * 2

@@ -158,13 +158,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     // loads go out before the block learns whether it has work.
     const int ai = blockIdx.y;
     const int nact = *a.n_active;
-    const int e = min(max(a.active[ai], 0), a.E - 1);
+    const int sh = ai - min(a.E, a.T * a.k);  // >= 0: shared expert sh (every token, weight 1)
+    const int e = sh >= 0 ? sh : min(max(a.active[ai], 0), a.E - 1);
+    const MatW &Wg = sh >= 0 ? a.sh_gate : a.gate, &Wu = sh >= 0 ? a.sh_up : a.up;
     const int H = a.H, I = a.I;
     const int row0 = blockIdx.x * 64 + wv * 16;
     const int nsteps = H / 256, spr = H / 32;
     const size_t eoc = (size_t)e * I * (H / 2), eos = (size_t)e * I * spr;
-    const __amdgpu_buffer_rsrc_t cg = buf_rsrc(a.gate.codes + eoc, I * (H / 2));
-    const __amdgpu_buffer_rsrc_t cu = buf_rsrc(a.up.codes + eoc, I * (H / 2));
+    const __amdgpu_buffer_rsrc_t cg = buf_rsrc(Wg.codes + eoc, I * (H / 2));
+    const __amdgpu_buffer_rsrc_t cu = buf_rsrc(Wu.codes + eoc, I * (H / 2));
     const uint32_t coff = (uint32_t)(row0 + li) * (H / 2) + 32 * g;
 
     Raw rg[kGuStages], ru[kGuStages];
@@ -174,13 +176,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         fetch(ru[s], cu, coff, min(s, nsteps - 1));
     }
     TileScales tg, tu;
-    get_scales(tg, buf_rsrc(a.gate.scales + eos, I * spr), (uint32_t)row0 * spr, lane);
-    get_scales(tu, buf_rsrc(a.up.scales + eos, I * spr), (uint32_t)row0 * spr, lane);
-    if (ai >= nact) return;
-    const int r0 = a.offsets[e], ntok = a.offsets[e + 1] - r0;
+    get_scales(tg, buf_rsrc(Wg.scales + eos, I * spr), (uint32_t)row0 * spr, lane);
+    get_scales(tu, buf_rsrc(Wu.scales + eos, I * spr), (uint32_t)row0 * spr, lane);
+    if (sh < 0 && ai >= nact) return;
+    const int r0 = sh >= 0 ? sh * a.T : a.offsets[e], ntok = sh >= 0 ? a.T : a.offsets[e + 1] - r0;
     // token rows to LDS while the first weight bytes are in flight
     __shared__ uint32_t xrow[16];
-    if (threadIdx.x < ntok) xrow[threadIdx.x] = (uint32_t)(a.perm[r0 + threadIdx.x] / a.k);
+    if (threadIdx.x < ntok) xrow[threadIdx.x] = sh >= 0 ? threadIdx.x : (uint32_t)(a.perm[r0 + threadIdx.x] / a.k);
     __syncthreads();
     stage_rows(xs, (const uint16_t *)a.x, [&](int r) { return (size_t)xrow[r] * H; }, ntok, H);
     uint8_t *sreg = (uint8_t *)(xs + (size_t)a.nl_x * (H + 8)) + 4096 * wv;
@@ -208,13 +210,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     if (li < ntok) {
         const size_t rr = (size_t)(r0 + li);
         const int n = row0 + 4 * g;
-        add_lora_gu(a.lora_gu, a.perm, a.k, rr, I, n, accg, accu);
+        if (sh < 0) add_lora_gu(a.lora_gu, a.perm, a.k, rr, I, n, accg, accu);
         uint32_t hh[4], hl[4];
 #pragma unroll
         for (int r = 0; r < 4; r++) split_bf16(act_h(a.act, accg[r], accu[r]), hh[r], hl[r]);
-        *(u32x2 *)(a.h_hi + rr * I + n) = u32x2{pack2(hh[0], hh[1]), pack2(hh[2], hh[3])};
-        *(u32x2 *)(a.h_lo + rr * I + n) = u32x2{pack2(hl[0], hl[1]), pack2(hl[2], hl[3])};
-        if (a.gu) {
+        uint16_t *ph = sh >= 0 ? a.sh_h_hi : a.h_hi, *pl = sh >= 0 ? a.sh_h_lo : a.h_lo;
+        *(u32x2 *)(ph + rr * I + n) = u32x2{pack2(hh[0], hh[1]), pack2(hh[2], hh[3])};
+        *(u32x2 *)(pl + rr * I + n) = u32x2{pack2(hl[0], hl[1]), pack2(hl[2], hl[3])};
+        if (a.gu && sh < 0) {
             *(float4 *)(a.gu + (rr * 2 + 0) * I + n) = float4{accg[0], accg[1], accg[2], accg[3]};
             *(float4 *)(a.gu + (rr * 2 + 1) * I + n) = float4{accu[0], accu[1], accu[2], accu[3]};
         }
@@ -233,12 +236,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
     const int ai = blockIdx.y;
     const int nact = *a.n_active;
-    const int e = min(max(a.active[ai], 0), a.E - 1);  // as in k_gateup_dec
+    const int sh = ai - min(a.E, a.T * a.k);  // as in k_gateup_dec
+    const int e = sh >= 0 ? sh : min(max(a.active[ai], 0), a.E - 1);
+    const MatW &Wd = sh >= 0 ? a.sh_down : a.down;
     const int H = a.H, I = a.I;
     const int m0 = blockIdx.x * (64 * RT) + wv * (16 * RT);
     const int nsteps = I / 256, spr = I / 32;
-    const __amdgpu_buffer_rsrc_t cd = buf_rsrc(a.down.codes + (size_t)e * H * (I / 2), H * (I / 2));
-    const __amdgpu_buffer_rsrc_t sd = buf_rsrc(a.down.scales + (size_t)e * H * spr, H * spr);
+    const __amdgpu_buffer_rsrc_t cd = buf_rsrc(Wd.codes + (size_t)e * H * (I / 2), H * (I / 2));
+    const __amdgpu_buffer_rsrc_t sd = buf_rsrc(Wd.scales + (size_t)e * H * spr, H * spr);
     uint32_t coff[RT];
 #pragma unroll
     for (int t = 0; t < RT; t++) coff[t] = (uint32_t)(m0 + 16 * t + li) * (I / 2) + 32 * g;
@@ -251,11 +256,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     TileScales ts[RT];
 #pragma unroll
     for (int t = 0; t < RT; t++) get_scales(ts[t], sd, (uint32_t)(m0 + 16 * t) * spr, lane);
-    if (ai >= nact) return;
-    const int r0 = a.offsets[e], ntok = a.offsets[e + 1] - r0;
+    if (sh < 0 && ai >= nact) return;
+    const int r0 = sh >= 0 ? sh * a.T : a.offsets[e], ntok = sh >= 0 ? a.T : a.offsets[e + 1] - r0;
     const size_t lo = (size_t)a.nl_h * (I + 8);
-    stage_rows(hs, a.h_hi, [&](int r) { return (size_t)(r0 + r) * I; }, ntok, I);
-    stage_rows(hs + lo, a.h_lo, [&](int r) { return (size_t)(r0 + r) * I; }, ntok, I);
+    stage_rows(hs, sh >= 0 ? a.sh_h_hi : a.h_hi, [&](int r) { return (size_t)(r0 + r) * I; }, ntok, I);
+    stage_rows(hs + lo, sh >= 0 ? a.sh_h_lo : a.h_lo, [&](int r) { return (size_t)(r0 + r) * I; }, ntok, I);
     uint8_t *sreg = (uint8_t *)(hs + 2 * lo) + 2048 * RT * wv;
 #pragma unroll
     for (int t = 0; t < RT; t++) put_scales(sreg + 2048 * t, ts[t], lane);
@@ -301,9 +306,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     }
     const int j = PACK ? li >> 1 : li;
     if (j < ntok && (!PACK || (li & 1) == 0)) {
-        const int slot = a.perm[r0 + j];
-        const float pw = a.w[slot];
-        float *yb = a.ybuf + (size_t)slot * H + m0 + 4 * g;
+        const int slot = sh >= 0 ? j * a.sh_n + sh : a.perm[r0 + j];
+        const float pw = sh >= 0 ? 1.f : a.w[slot];
+        float *yb = (sh >= 0 ? a.sh_ybuf : a.ybuf) + (size_t)slot * H + m0 + 4 * g;
 #pragma unroll
         for (int t = 0; t < RT; t++)
             *(float4 *)(yb + 16 * t) = float4{pw * acc[t][0], pw * acc[t][1], pw * acc[t][2], pw * acc[t][3]};
@@ -324,7 +329,7 @@ hipError_t launch_gateup_dec(const ExpertFwdArgs &a, hipStream_t s)
     const int maxU = min(a.E, a.T * a.k);
     ProfScope ps(a.prof, PK_GATEUP, s);
     const size_t lds = (size_t)a.nl_x * (a.H + 8) * 2 + 16384;
-    ps.launch(k_gateup_dec, dim3(a.I / 64, maxU), dim3(256), lds, a);
+    ps.launch(k_gateup_dec, dim3(a.I / 64, maxU + a.sh_n), dim3(256), lds, a);
     return hipGetLastError();
 }
 
@@ -334,7 +339,7 @@ hipError_t launch_down_dec(const ExpertFwdArgs &a, hipStream_t s)
     const int maxU = min(a.E, a.T * a.k);
     ProfScope ps(a.prof, PK_DOWN, s);
     const size_t lds = (size_t)a.nl_h * (a.I + 8) * 2 * 2 + 4 * 2048 * RT;
-    const dim3 grid(a.H / (64 * RT), maxU);
+    const dim3 grid(a.H / (64 * RT), maxU + a.sh_n);
     if (a.T <= 8)
         ps.launch(k_down_dec<RT, true>, grid, dim3(256), lds, a);
     else

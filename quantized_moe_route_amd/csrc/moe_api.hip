@@ -6,6 +6,7 @@
 // status and fills an out-handle, and a destroy call.  A missing input is an
 // error, never replaced (LazyLoRA README, "Three rules the engine is built
 // around").
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -43,7 +44,7 @@ struct Layout {
     size_t xq8;  // MXFP8-quantized activations as bf16 (MOE_F_QUANT_X8)
     // shared experts: their slot rows (forward outputs, backward input-gradient rows) and
     // their dense routing; the rest of their scratch is the routed slots' (n_shared <= k)
-    size_t sh_rows, sh_ids, sh_w, sh_off, sh_perm, sh_inv, sh_act, sh_nact;
+    size_t sh_rows, sh_ids, sh_w, sh_off, sh_perm, sh_inv, sh_act, sh_nact, sh_h;
     size_t total;
 };
 
@@ -92,6 +93,7 @@ Layout layout_of(const moe_desc &d)
     L.sh_inv = take(Ssh * 4);
     L.sh_act = take(NS * 4);
     L.sh_nact = take(NS ? 4 : 0);
+    L.sh_h = take(std::min<size_t>(T, 16) * NS * I * 4);  // h planes of the shared units of the few-token launch
     L.total = off;
     return L;
 }
@@ -418,7 +420,19 @@ moe_status moe_forward(moe_layer *L, const void *x, int32_t xt, int32_t T, const
         x = xq;
         xt = MOE_DT_BF16;
     }
-    if (L->d.n_shared > 0) {
+    moe::set_lds_staging(a);
+    if (L->d.n_shared > 0 && !moe::use_mm(a) && moe::dec_supported(a)) {
+        // few tokens: the shared experts are extra units of the routed stream kernels' launch
+        a.sh_n = L->d.n_shared;
+        a.sh_gate = shared_matw(L->w, 0);
+        a.sh_up = shared_matw(L->w, 1);
+        a.sh_down = shared_matw(L->w, 2);
+        a.sh_h_hi = (uint16_t *)(L->ws + L->lay.sh_h);
+        a.sh_h_lo = a.sh_h_hi + (size_t)T * a.sh_n * a.I;
+        a.sh_ybuf = (float *)(L->ws + L->lay.sh_rows);
+        a.ybuf2 = a.sh_ybuf;
+        a.k2 = a.sh_n;
+    } else if (L->d.n_shared > 0) {
         // the shared experts first: their slot rows stay in the workspace for the combine
         DenseRouting dr;
         if ((st = device_status(dense_routing(L, T, dr, hs), "shared-expert routing")) != MOE_OK) return st;

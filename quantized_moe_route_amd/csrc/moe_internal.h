@@ -107,6 +107,13 @@ struct ExpertFwdArgs {
     int skip_combine;      // leave the slot rows in ybuf (no k_combine)
     const float *ybuf2;    // [T][k2][H] more slot rows that k_combine adds after the k routed ones
     int k2;
+    // Shared experts run as extra units of the few-token stream kernels' launch (sh_n > 0):
+    // unit maxU + s is shared expert s with every token (weight 1), its h planes [s T + t]
+    // in sh_h_hi / sh_h_lo and its output rows [t sh_n + s] in sh_ybuf.
+    int sh_n;
+    MatW sh_gate, sh_up, sh_down;
+    uint16_t *sh_h_hi, *sh_h_lo;
+    float *sh_ybuf;
 };
 
 struct ExpertBwdArgs {

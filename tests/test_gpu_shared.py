@@ -143,3 +143,21 @@ def test_shared_zero_tokens():
     torch.cuda.synchronize()
     assert y.shape == (0, w.H) and dx.shape == (0, w.H)
     L.close()
+
+
+def test_shared_units_of_the_stream_kernels_situ_bias_and_k_shared():
+    # few bf16 tokens with H, I multiples of 256: the shared experts are extra units of the
+    # routed stream kernels' launch; SiTU with a selection-only bias, and as many shared
+    # experts as the top-k
+    c = _case(syn.shrink(TINY, T=3, H=512, I=512, E=16, k=4, x_dtype="bf16", bias_sd=0.5, with_dy=True, x_key=71),
+              n=4, act=1)
+    c.bias_mode = 2
+    run_shared(c, "shared-fused-situ-k")
+
+
+def test_shared_grouped_gemm_beside_generic_routed_kernels():
+    # 20 tokens over 64 experts: too few per expert for the routed grouped GEMM (generic
+    # kernels) and too many for the stream kernels, while each shared expert holds all 20
+    # tokens and takes the grouped GEMM (one chunk)
+    run_shared(_case(syn.shrink(TINY, T=20, H=512, I=512, E=64, k=2, x_dtype="bf16", with_dy=True, x_key=72)),
+               "shared-mm-beside-generic")

@@ -61,14 +61,18 @@ def traffic_record(workload: str):
 
 
 def cpu_baseline(w, x_pool, wr, bias, codes, scales, budget_s: float, dy_pool=None, lora=None, quant=False,
-                 shared=None):
+                 shared=None, rvq=None):
     """The fp64 oracle as it stands, timed on a bounded sample of the same pool: consecutive
     chunks of at most 16 tokens (route + group + forward, and the input gradient when dy_pool
     is given), until budget_s of CPU work; tokens/s over the tokens processed."""
     import oracle
     nthreads = oracle.default_threads()
-    W = oracle.Weights(w.H, w.I, codes=codes, scales=scales, lora=lora)
-    Ws = oracle.Weights(w.H, w.I, codes=shared[0], scales=shared[1]) if shared else None
+    if rvq is not None:  # RVQ3 layer: (idx, cb)
+        W = oracle.Weights(w.H, w.I, idx=rvq[0], cb=rvq[1], lora=lora)
+        Ws = oracle.Weights(w.H, w.I, idx=shared[0], cb=shared[1]) if shared else None
+    else:
+        W = oracle.Weights(w.H, w.I, codes=codes, scales=scales, lora=lora)
+        Ws = oracle.Weights(w.H, w.I, codes=shared[0], scales=shared[1]) if shared else None
     n_sh = shared[0][0].shape[0] if shared else 0
     flat = x_pool.reshape(-1, w.H)
     dflat = None if dy_pool is None else dy_pool.reshape(-1, w.H)
@@ -314,8 +318,7 @@ def main():
         dy_host = syn.upstream_grad(w, w.T * POOL).reshape(POOL, w.T, w.H) if train else None
         base = (cpu_baseline(w, x_host, wr, bias, codes, scales, args.cpu_seconds, dy_host,
                              lora=(A_h, B_h, 32.0 / args.lora) if args.lora else None, quant=args.quant_x8,
-                             shared=sh if args.shared else None)
-                if codes is not None else None)
+                             shared=sh if args.shared else None, rvq=None if codes is not None else (idx, cb)))
 
     out = {
         "metric": METRIC,

@@ -60,13 +60,30 @@ def traffic_record(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
+def host_cpu():
+    """The host's CPU model, its logical CPU count and the CPUs this process may run on."""
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    try:
+        allowed = len(os.sched_getaffinity(0))
+    except AttributeError:
+        allowed = os.cpu_count()
+    return {"model": model, "logical_cpus": os.cpu_count(), "cpus_allowed": allowed}
+
+
 def cpu_baseline(w, x_pool, wr, bias, codes, scales, budget_s: float, dy_pool=None, lora=None, quant=False,
-                 shared=None, rvq=None):
+                 shared=None, rvq=None, nthreads=None):
     """The fp64 oracle as it stands, timed on a bounded sample of the same pool: consecutive
     chunks of at most 16 tokens (route + group + forward, and the input gradient when dy_pool
     is given), until budget_s of CPU work; tokens/s over the tokens processed."""
     import oracle
-    nthreads = oracle.default_threads()
+    nthreads = oracle.default_threads() if nthreads is None else nthreads
     if rvq is not None:  # RVQ3 layer: (idx, cb)
         W = oracle.Weights(w.H, w.I, idx=rvq[0], cb=rvq[1], lora=lora)
         Ws = oracle.Weights(w.H, w.I, idx=shared[0], cb=shared[1]) if shared else None
@@ -76,7 +93,7 @@ def cpu_baseline(w, x_pool, wr, bias, codes, scales, budget_s: float, dy_pool=No
     n_sh = shared[0][0].shape[0] if shared else 0
     flat = x_pool.reshape(-1, w.H)
     dflat = None if dy_pool is None else dy_pool.reshape(-1, w.H)
-    chunk = min(w.T, 16)
+    chunk = min(w.T, 16 if nthreads > 1 else 1)
     n, t0 = 0, time.perf_counter()
     while True:
         xb = oracle.to_f64(flat[n:n + chunk], "bf16")
@@ -133,6 +150,16 @@ def main():
                     help="after the run, copy a buffer of this many MB three times (a kernel of known "
                          "traffic for calibrating hardware byte counters)")
     ap.add_argument("--print-hash", action="store_true", help="print the roofline kernel's source hash and exit")
+    ap.add_argument("--spread", type=int, default=3, metavar="N",
+                    help="run the timed measurement in N separate processes (this one and N-1 children) and "
+                         "report the spread of their ms/step; 1 = this process only")
+    ap.add_argument("--scrub-steps", type=int, default=64, metavar="K",
+                    help="also time K steps one by one, each after a 1 GiB write that flushes the last-level "
+                         "cache (decode workloads; 0 = skip)")
+    ap.add_argument("--graph", action="store_true", default=None,
+                    help="also time the steps replayed from a captured HIP graph (default on for decode)")
+    ap.add_argument("--no-graph", dest="graph", action="store_false")
+    ap.add_argument("--child", action="store_true", help=argparse.SUPPRESS)
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (every box here has one GPU, "
@@ -142,6 +169,28 @@ def main():
     if args.print_hash:
         print(kernel_source_hash(args.workload))
         return
+
+    # The other processes of the spread run first, before this one touches the GPU: each is a
+    # child that measures the same workload and prints its own JSON line.
+    spread = []
+    if args.spread > 1 and not args.child:
+        import subprocess
+        cmd = [sys.executable, os.path.abspath(__file__), "--child", "--spread", "1", "--no-cpu-baseline",
+               "--no-plain-read", "--no-graph", "--scrub-steps", "0", "--workload", args.workload,
+               "--steps", str(args.steps), "--warmup", str(args.warmup)]
+        for flag, on in (("--mx-gateup", args.mx_gateup), ("--quant-x8", args.quant_x8)):
+            if on:
+                cmd.append(flag)
+        if args.lora:
+            cmd += ["--lora", str(args.lora)]
+        if args.shared:
+            cmd += ["--shared", str(args.shared)]
+        for i in range(args.spread - 1):
+            log(f"spread: process {i + 2} of {args.spread}")
+            r = subprocess.run(cmd, stdout=subprocess.PIPE, text=True)
+            if r.returncode != 0:
+                sys.exit(f"spread process {i + 2} failed with status {r.returncode}")
+            spread.append(json.loads(r.stdout.strip().splitlines()[-1])["ms_per_step"])
 
     import numpy as np
     import torch
@@ -226,6 +275,26 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms = start.elapsed_time(end)
+    if args.child:
+        print(json.dumps({"ms_per_step": ms / args.steps}), flush=True)
+        L.close()
+        return
+
+    def pct(v):
+        v = sorted(v)
+        at = lambda q: v[min(len(v) - 1, int(round(q * (len(v) - 1))))]  # noqa: E731
+        return {"p10": at(0.10), "p50": at(0.50), "p90": at(0.90), "n": len(v)}
+
+    # Per-step distribution: the same steps again, each between its own pair of events (the
+    # event records add a little queue work, so the mean above stays the headline).
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    evs[0].record()
+    for i in range(args.steps):
+        step(args.warmup + i)
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per_step_us = pct([evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(args.steps)])
+    log(f"per-step us: p10 {per_step_us['p10']:.1f}  median {per_step_us['p50']:.1f}  p90 {per_step_us['p90']:.1f}")
     # The roofline kernel is timed over a second pass of the same steps: per-launch events
     # (hipExtLaunchKernelGGL start/stop stamps) slow the step down, so they stay out of the
     # pass that gives the throughput.
@@ -312,13 +381,72 @@ def main():
         L.prof_enable([])
         log("breakdown " + json.dumps(detail))
 
+    variants = {}
+    if not train and args.scrub_steps > 0:
+        # MALL flushed before every step: a 1 GiB write between the steps, outside the timed pairs
+        scrub = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        t = []
+        for i in range(args.scrub_steps):
+            scrub.fill_(float(i))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            step(args.warmup + i)
+            e1.record()
+            torch.cuda.synchronize()
+            t.append(e0.elapsed_time(e1) * 1e3)
+        del scrub
+        variants["mall_scrubbed_step_us"] = pct(t)
+        log(f"scrubbed steps us: median {variants['mall_scrubbed_step_us']['p50']:.1f}")
+    if args.graph is None:
+        args.graph = not train
+    if args.graph and not train:
+        # The pool's 64 steps captured once into a HIP graph (route + forward of each token),
+        # replayed as a whole: no host launch work inside; every replay's outputs are checked
+        # against eager calls of the same steps
+        ys = torch.empty((POOL, w.T, w.H), dtype=torch.float32, device="cuda")
+        rs = [L.new_routing(w.T) for _ in range(POOL)]
+        for i in range(POOL):
+            L.route(x_pool[i], rs[i])
+            L.forward(x_pool[i], rs[i], y=ys[i])
+        torch.cuda.synchronize()
+        y_eager = ys.clone()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(POOL):
+                L.route(x_pool[i], rs[i])
+                L.forward(x_pool[i], rs[i], y=ys[i])
+        reps = max(1, args.steps // POOL)
+        for _ in range(2):
+            ys.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(ys, y_eager), "graph replay differs from the eager steps"
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        assert torch.equal(ys, y_eager), "graph replay differs from the eager steps"
+        gms = e0.elapsed_time(e1) / (reps * POOL)
+        variants["hip_graph"] = {"ms_per_step": gms, "tokens_per_s": w.T / (gms / 1e3), "steps": reps * POOL}
+        log(f"graph-replayed steps: {gms * 1e3:.1f} us/step ({reps} replays of {POOL} steps)")
+        del g
+
     base = None
     if not args.no_cpu_baseline:
         log("CPU baseline: fp64 oracle")
         dy_host = syn.upstream_grad(w, w.T * POOL).reshape(POOL, w.T, w.H) if train else None
-        base = (cpu_baseline(w, x_host, wr, bias, codes, scales, args.cpu_seconds, dy_host,
-                             lora=(A_h, B_h, 32.0 / args.lora) if args.lora else None, quant=args.quant_x8,
-                             shared=sh if args.shared else None, rvq=None if codes is not None else (idx, cb)))
+        kw_cpu = dict(lora=(A_h, B_h, 32.0 / args.lora) if args.lora else None, quant=args.quant_x8,
+                      shared=sh if args.shared else None, rvq=None if codes is not None else (idx, cb))
+        base = cpu_baseline(w, x_host, wr, bias, codes, scales, args.cpu_seconds, dy_host, **kw_cpu)
+        one = cpu_baseline(w, x_host, wr, bias, codes, scales, min(5.0, args.cpu_seconds / 3), dy_host,
+                           nthreads=1, **kw_cpu)
+        host = host_cpu()
+        base["host"] = host
+        base["threads_note"] = (f"the oracle uses min(16, logical CPUs) threads: {base['cores']} here; the GPU "
+                                f"box grants each GPU a 16-CPU share of its {host['logical_cpus']} logical CPUs")
+        base["single_thread"] = {"value": one["value"], "unit": one["unit"], "sample": one["sample"]}
 
     out = {
         "metric": METRIC,
@@ -346,8 +474,15 @@ def main():
                    "mx_gateup": args.mx_gateup, "quant_x8": args.quant_x8, "n_shared": args.shared},
         "roofline": roofline,
         "cpu_baseline": base,
+        "step_us": per_step_us,
         "detail": detail,
     }
+    if variants:
+        out["variants"] = variants
+    if spread:
+        allp = [ms / args.steps] + spread
+        out["process_spread"] = {"ms_per_step": allp, "min": min(allp), "max": max(allp),
+                                 "median": sorted(allp)[len(allp) // 2], "processes": len(allp)}
     print(json.dumps(out), flush=True)
     if args.calib_copy_mb:
         n = args.calib_copy_mb * (1 << 20) // 4

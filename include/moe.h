@@ -54,7 +54,9 @@ typedef enum {
     MOE_ERR_UNSUPPORTED = 2,   /* a valid request this build does not implement */
     MOE_ERR_WORKSPACE = 3,     /* workspace smaller than moe_workspace_size() */
     MOE_ERR_DEVICE = 4,        /* a HIP call failed; text in moe_last_error() */
-    MOE_ERR_INTERNAL = 5
+    MOE_ERR_INTERNAL = 5,
+    MOE_ERR_DATA = 6           /* MOE_F_VALIDATE: an earlier call found out-of-contract data on the
+                                  device (MOE_BAD_* bits named in moe_last_error()) */
 } moe_status;
 
 typedef enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1 } moe_dtype;
@@ -70,17 +72,49 @@ enum {
     MOE_F_DETERMINISTIC = 1u, /* combine and gradient reductions in a fixed order (always on in this build) */
     MOE_F_MX_GATEUP = 2u,     /* grouped-GEMM gate/up (MXFP4, bf16 x, many tokens per expert) on the
                                  gfx950 block-scaled MFMA: weights enter as FP4 codes with their E8M0
-                                 scales and x as two E4M3 terms with per-32 scales (exact to about
-                                 2^-20 of each block's maximum); more workspace (3H + H/16 bytes per
-                                 token).  Off: exact bf16 dequantization and bf16 MFMA. */
+                                 scales and x as two E4M3 terms with per-32 scales (each element
+                                 carried to about 2^-20 of its block's maximum).  The MFMA's own
+                                 summation of the block products is coarser than bf16 MFMA's: y
+                                 measured within 2e-6 of max|y| on Gaussian x and within 6e-5 with x
+                                 spread over 2^-12..2^6 inside each 32-block.  The g, u it saves
+                                 (saved_gu) carry that deviation, and the input gradient from them
+                                 up to ~7e-4 on the spread x; with saved_gu = NULL the backward
+                                 recomputes g, u on the exact bf16 path (within 1e-4).  More
+                                 workspace (3H + H/16 bytes per token).  Off: exact bf16
+                                 dequantization and bf16 MFMA. */
     MOE_F_LORA = 4u,          /* workspace for a shared low-rank adapter (moe_set_lora) */
-    MOE_F_QUANT_X8 = 8u       /* moe_forward quantizes x to MXFP8 before the expert products (OCP MX
+    MOE_F_QUANT_X8 = 8u,      /* moe_forward quantizes x to MXFP8 before the expert products (OCP MX
                                  v1.0: E4M3 elements, one E8M0 scale per 32 consecutive elements,
                                  shared exponent floor(log2 max|x|) - 8, round to nearest even,
                                  saturation at 448): activation-quantized prefill.  The routing
-                                 (moe_route) sees x unquantized; moe_backward_input stays the exact
-                                 layer's gradient.  H must be a multiple of 32 (always).  More
-                                 workspace: 2 H bytes per token. */
+                                 (moe_route) sees x unquantized.  moe_backward_input with saved_gu
+                                 = NULL is the exact (unquantized) layer's gradient; with saved_gu
+                                 from such a forward it is the quantized layer's, the quantization
+                                 passed straight through (its derivative taken as 1).  H must be a
+                                 multiple of 32 (always).  More workspace: 2 H bytes per token. */
+    MOE_F_VALIDATE = 16u      /* device checks of the data each call consumes (below) */
+};
+
+/* MOE_F_VALIDATE (LazyLoRA README, "Three rules the engine is built around": unusable
+ * data is an error, never replaced).  Every call on the layer first scans, on the device,
+ * what it is about to consume, and ORs these bits into a status word in the workspace:
+ *   moe_route           x;
+ *   moe_forward         the scale bytes (MXFP4) or codebooks (RVQ3) of the active experts
+ *                       and of the shared experts;
+ *   moe_backward_input  dy, and the same weights.
+ * The call's kernels still run to completion on what they were given (out-of-contract
+ * inputs give meaningless outputs, never a fault).  The NEXT call on the layer, or
+ * moe_check_status(), synchronizes the stream, reads the word, clears it and returns
+ * MOE_ERR_DATA if it was nonzero (without enqueuing anything else).  So with the flag
+ * every call costs one host synchronization; without it nothing is checked and values
+ * outside the contract give undefined (but finite-time, fault-free) results. */
+enum {
+    MOE_BAD_X = 1u,           /* a non-finite activation */
+    MOE_BAD_DY = 2u,          /* a non-finite upstream gradient */
+    MOE_BAD_SCALE_NAN = 4u,   /* an E8M0 scale byte 0xFF (NaN in the format) */
+    MOE_BAD_SCALE_ZERO = 8u,  /* an E8M0 scale byte 0x00 (2^-127: the kernels carry products of
+                                 normal magnitude only; such a block would be read as zero) */
+    MOE_BAD_CODEWORD = 16u    /* a non-finite fp16 RVQ3 codeword */
 };
 
 /* Layer description.  moe_desc_init() fills the K3 defaults. */
@@ -113,8 +147,9 @@ typedef struct {
  *   (E2M1: bit 3 sign, bits 2..1 exponent with bias 1, bit 0 mantissa);
  *   scales[m] is [E][out][in/32] E8M0 bytes, one per 32 consecutive `in`
  *   elements, value 2^(byte-127).  Element = E2M1(code) * 2^(scale-127).
- *   codes and scales must be 16-byte aligned.  Scale bytes must lie in 1..254 (the
- *   all-ones byte means NaN in the format and is not supported).
+ *   codes and scales must be 16-byte aligned.  Scale bytes must lie in 1..254: 0xFF
+ *   means NaN in the format, and 0x00 (2^-127) scales every element of its block below the
+ *   smallest normal number, which the kernels do not carry; MOE_F_VALIDATE reports both.
  * RVQ3 (wfmt = MOE_W_RVQ3): rvq_idx[m] is [E][3][out][in/8] bytes (stage-
  *   planar); rvq_cb[m] is [E][3][256][8] fp16 codewords.  Elements 8v..8v+7
  *   of a row equal the sum over the three stages s of
@@ -232,6 +267,11 @@ moe_status moe_set_lora(moe_layer *L, const moe_lora *lora);
 moe_status moe_backward_lora(moe_layer *L, const void *x, int32_t xt, const void *dy, int32_t dyt, int32_t T,
                              const moe_routing *r, const float *saved_gu, float *dx, float *const dA[3],
                              float *const dB[3], void *stream);
+
+/* MOE_F_VALIDATE: synchronize stream, return the device status word in *bits (MOE_BAD_*)
+ * and clear it.  MOE_ERR_DATA if it was nonzero, MOE_OK if zero; MOE_ERR_INVALID_ARG for
+ * a NULL argument or a layer created without MOE_F_VALIDATE. */
+moe_status moe_check_status(moe_layer *L, uint32_t *bits, void *stream);
 
 /* Release the handle (NULL is a no-op).  Borrowed memory is not freed. */
 void moe_destroy(moe_layer *L);

@@ -7,7 +7,7 @@
  * its own stream.  Not needed for computing anything; the layer behaves the
  * same with timing on or off apart from the two event records per launch.
  * Sources: the LazyLoRA README ("Cost, measured" / LAZYLORA_PROFILE) and the
- * Two Desks write-up (Act IV: a cycle that cannot measure fails loudly) time
+ * Two Desks write-up (Act IV: a measurement step that cannot measure is an error, not a pass) time
  * the engine's own kernels; this is the same facility for the GPU layer.
  */
 #ifndef MOE_PROF_H

@@ -206,6 +206,13 @@ class MoELayer:
                                           _stream()), "moe_backward_lora")
         return dx, dA, dB
 
+    def check_status(self) -> int:
+        """MOE_F_VALIDATE: synchronize, return and clear the device status word (MOE_BAD_* bits);
+        raises MoeError(MOE_ERR_DATA) if it was nonzero."""
+        bits = ctypes.c_uint32()
+        C.check(C.lib().moe_check_status(self._h, ctypes.byref(bits), _stream()), "moe_check_status")
+        return bits.value
+
     def new_saved_gu(self, T: int):
         torch = _torch()
         return torch.empty((max(1, T * self.k), 2, self.I), dtype=torch.float32, device=self.device)

@@ -6,7 +6,8 @@ import os
 
 from .build import LIB_PATH
 
-MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE, MOE_ERR_INTERNAL = range(6)
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE, MOE_ERR_INTERNAL, \
+    MOE_ERR_DATA = range(7)
 MOE_DT_F32, MOE_DT_BF16 = 0, 1
 MOE_W_MXFP4, MOE_W_RVQ3 = 0, 1
 MOE_ACT_SWIGLU = 0
@@ -15,11 +16,14 @@ MOE_ACT_SWIGLU, MOE_ACT_SITU = 0, 1
 MOE_F_MX_GATEUP = 2
 MOE_F_LORA = 4
 MOE_F_QUANT_X8 = 8
+MOE_F_VALIDATE = 16
+# bits of the MOE_F_VALIDATE status word
+MOE_BAD_X, MOE_BAD_DY, MOE_BAD_SCALE_NAN, MOE_BAD_SCALE_ZERO, MOE_BAD_CODEWORD = 1, 2, 4, 8, 16
 
 EXPORTED = (
     "moe_desc_init", "moe_workspace_size", "moe_layer_create", "moe_route", "moe_forward",
     "moe_backward_input", "moe_destroy", "moe_status_string", "moe_last_error",
-    "moe_set_lora", "moe_backward_lora", "moe_prof_enable", "moe_prof_read", "moe_prof_hbm_read",
+    "moe_set_lora", "moe_backward_lora", "moe_check_status", "moe_prof_enable", "moe_prof_read", "moe_prof_hbm_read",
 )
 
 # kernel families of include/moe_prof.h
@@ -88,6 +92,8 @@ def lib() -> ctypes.CDLL:
         L.moe_backward_lora.argtypes = [vp, vp, i32, vp, i32, i32, ctypes.POINTER(MoeRouting), vp, vp,
                                         ctypes.POINTER(vp), ctypes.POINTER(vp), vp]
         L.moe_backward_lora.restype = st
+        L.moe_check_status.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), vp]
+        L.moe_check_status.restype = st
         L.moe_destroy.argtypes = [vp]
         L.moe_destroy.restype = None
         L.moe_status_string.argtypes = [st]

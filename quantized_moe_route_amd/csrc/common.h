@@ -34,6 +34,17 @@ __device__ __forceinline__ void split_bf16(float f, uint32_t &hi, uint32_t &lo)
     lo = f32_to_bf16_rne(f - bf16_bits_to_f32(hi));
 }
 
+// Split an fp32 value into three bf16 terms hi = rne(f), mid = rne(f - hi), lo = f - hi - mid.
+// Each residual is exact in fp32, and for a normal f the last one has at most 8 significant
+// bits, so hi + mid + lo == f exactly (bf16 keeps fp32's exponent range).
+__device__ __forceinline__ void split_bf16x3(float f, uint32_t &hi, uint32_t &mid, uint32_t &lo)
+{
+    hi = f32_to_bf16_rne(f);
+    const float r1 = f - bf16_bits_to_f32(hi);
+    mid = f32_to_bf16_rne(r1);
+    lo = f32_to_bf16_rne(r1 - bf16_bits_to_f32(mid));
+}
+
 __device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) { return (lo16 & 0xFFFFu) | (hi16 << 16); }
 
 // E8M0 scale byte -> fp32 power of two (bytes 1..254 are normal fp32 numbers).

@@ -351,8 +351,6 @@ hipError_t launch_expert_backward(const ExpertBwdArgs &a0, hipStream_t s)
         f.h_lo = a.h_lo;
         f.gu = a.gu_scratch;
         f.act = a.act;
-        f.xq = a.xq;
-        f.xq_s = a.xq_s;
         f.lora_gu = a.lora_gu;
         f.tok_chunks = a.tok_chunks;
         f.prof = a.prof;

@@ -285,8 +285,10 @@ struct BFrag;
 template <>
 struct BFrag<DT_BF16> {
     static constexpr bool kTwo = false;
+    static constexpr bool kThree = false;
     bf16x8 hi[8];
     bf16x8 lo[1];
+    bf16x8 mid[1];
     __device__ __forceinline__ void load(const void *src, size_t rowoff, int kk, int K, bool valid)
     {
         const uint16_t *p = (const uint16_t *)src + rowoff;
@@ -300,12 +302,16 @@ struct BFrag<DT_BF16> {
     }
 };
 
-// fp32 rows are split into bf16 hi + lo.
+// fp32 rows (tokens, upstream gradients) are split into three bf16 terms hi + mid + lo,
+// which hold all 24 significand bits of a normal fp32 value (split_bf16x3), so the
+// products with exact weights stay exact.
 template <>
 struct BFrag<DT_F32> {
     static constexpr bool kTwo = true;
+    static constexpr bool kThree = true;
     bf16x8 hi[8];
     bf16x8 lo[8];
+    bf16x8 mid[8];
     __device__ __forceinline__ void load(const void *src, size_t rowoff, int kk, int K, bool valid)
     {
         const float *p = (const float *)src + rowoff;
@@ -317,10 +323,11 @@ struct BFrag<DT_F32> {
             const bool ok = valid && kk + 32 * (s / 4) < K;
             const float f[8] = {ok ? a.x : 0.f, ok ? a.y : 0.f, ok ? a.z : 0.f, ok ? a.w : 0.f,
                                 ok ? b.x : 0.f, ok ? b.y : 0.f, ok ? b.z : 0.f, ok ? b.w : 0.f};
-            uint32_t h[8], l[8];
+            uint32_t h[8], m[8], l[8];
 #pragma unroll
-            for (int d = 0; d < 8; d++) split_bf16(f[d], h[d], l[d]);
+            for (int d = 0; d < 8; d++) split_bf16x3(f[d], h[d], m[d], l[d]);
             hi[s] = as_bf16x8(pack2(h[0], h[1]), pack2(h[2], h[3]), pack2(h[4], h[5]), pack2(h[6], h[7]));
+            mid[s] = as_bf16x8(pack2(m[0], m[1]), pack2(m[2], m[3]), pack2(m[4], m[5]), pack2(m[6], m[7]));
             lo[s] = as_bf16x8(pack2(l[0], l[1]), pack2(l[2], l[3]), pack2(l[4], l[5]), pack2(l[6], l[7]));
         }
     }
@@ -351,8 +358,10 @@ __device__ __forceinline__ void stage_rows_bf16(uint16_t *dst, const uint16_t *s
 // fp32 rows stored pre-split as two bf16 planes (hi, lo).
 struct BFragPair {
     static constexpr bool kTwo = true;
+    static constexpr bool kThree = false;
     bf16x8 hi[8];
     bf16x8 lo[8];
+    bf16x8 mid[1];
     __device__ __forceinline__ void load(const uint16_t *phi, const uint16_t *plo, size_t rowoff, int kk, int K,
                                          bool valid)
     {
@@ -377,6 +386,8 @@ __device__ __forceinline__ void mma_step(f32x4 &acc, const A &a, const B &b)
     for (int s = 0; s < 8; s++) {
         acc = mfma16(a.hi[s], b.hi[s], acc);
         if constexpr (A::kTwo) acc = mfma16(a.lo[s], b.hi[s], acc);
+        if constexpr (B::kThree) acc = mfma16(a.hi[s], b.mid[s], acc);
+        if constexpr (A::kTwo && B::kThree) acc = mfma16(a.lo[s], b.mid[s], acc);
         if constexpr (B::kTwo) acc = mfma16(a.hi[s], b.lo[s], acc);
     }
 }

@@ -1,8 +1,9 @@
 // group.hip -- token-to-expert grouping: histogram -> exclusive scan -> stable permute.
 //
-// Motivation (LazyLoRA README, "Measurement findings": for a batch the right
-// primitive is a bandwidth-optimal sequential sweep over the experts amortised
-// over the batch): the expert kernels walk experts in ascending id and read
+// Motivation (LazyLoRA README, "Measurement findings"): with a batch of tokens,
+// reading every routed expert once in expert order and serving all of its
+// tokens from that one read beats per-token reads; the expert kernels walk
+// experts in ascending id and read
 // each routed expert's bytes once for all of its tokens; this kernel builds
 // that order.  Outputs: counts[e]; offsets = exclusive scan (E+1); perm = slot
 // ids t*k+j ordered by (expert, token); inv = its inverse; active = experts

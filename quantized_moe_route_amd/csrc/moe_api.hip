@@ -45,6 +45,7 @@ struct Layout {
     // shared experts: their slot rows (forward outputs, backward input-gradient rows) and
     // their dense routing; the rest of their scratch is the routed slots' (n_shared <= k)
     size_t sh_rows, sh_ids, sh_w, sh_off, sh_perm, sh_inv, sh_act, sh_nact, sh_h;
+    size_t status;  // MOE_F_VALIDATE: the device status word
     size_t total;
 };
 
@@ -94,6 +95,7 @@ Layout layout_of(const moe_desc &d)
     L.sh_act = take(NS * 4);
     L.sh_nact = take(NS ? 4 : 0);
     L.sh_h = take(std::min<size_t>(T, 16) * NS * I * 4);  // h planes of the shared units of the few-token launch
+    L.status = take((d.flags & MOE_F_VALIDATE) ? 4 : 0);
     L.total = off;
     return L;
 }
@@ -145,6 +147,7 @@ struct moe_layer {
     moe::Prof prof;
     bool has_lora = false;
     moe::LoraW lora{};
+    bool status_armed = false;  // MOE_F_VALIDATE: the status word has been cleared once
 };
 
 namespace {
@@ -244,6 +247,62 @@ hipError_t dense_routing(const moe_layer *L, int T, DenseRouting &r, hipStream_t
 
 int tok_chunks(int T) { return (T + moe::kTokChunk - 1) / moe::kTokChunk; }
 
+bool validating(const moe_layer *L) { return (L->d.flags & MOE_F_VALIDATE) != 0; }
+
+uint32_t *status_word(const moe_layer *L) { return (uint32_t *)(L->ws + L->lay.status); }
+
+std::string bad_bits_text(uint32_t b)
+{
+    static const char *names[] = {"non-finite x", "non-finite dy", "E8M0 scale byte 0xFF (NaN)",
+                                  "E8M0 scale byte 0x00 (2^-127)", "non-finite RVQ3 codeword"};
+    std::string t;
+    for (int i = 0; i < 5; i++)
+        if ((b >> i) & 1u) t += (t.empty() ? "" : ", ") + std::string(names[i]);
+    return t;
+}
+
+// MOE_F_VALIDATE: reads (host synchronization) and clears the status word left by the
+// earlier calls; MOE_ERR_DATA if it was set.  The first call only clears it.
+moe_status take_status(moe_layer *L, hipStream_t s, uint32_t *bits_out)
+{
+    uint32_t bits = 0;
+    if (L->status_armed) {
+        hipError_t e = hipMemcpyAsync(&bits, status_word(L), 4, hipMemcpyDeviceToHost, s);
+        if (e == hipSuccess) e = hipStreamSynchronize(s);
+        if (e != hipSuccess) return device_status(e, "reading the validation status");
+    }
+    if (bits_out) *bits_out = bits;
+    if (!L->status_armed || bits) {
+        moe_status st = device_status(moe::launch_set_u32(status_word(L), 0u, s), "clearing the validation status");
+        if (st != MOE_OK) return st;
+        L->status_armed = true;
+    }
+    if (bits) return fail(MOE_ERR_DATA, "out-of-contract data found by an earlier call: %s", bad_bits_text(bits).c_str());
+    return MOE_OK;
+}
+
+size_t mat_scale_bytes(const moe_desc &d, int m)
+{
+    const size_t rows = m < 2 ? d.inter : d.hidden, cols = m < 2 ? d.hidden : d.inter;
+    return rows * (cols / 32);
+}
+
+// MOE_F_VALIDATE: scan the weights a forward or backward pass reads (active routed experts
+// of r, and the shared experts).
+moe_status check_weights(const moe_layer *L, const moe_routing *r, int T, hipStream_t s)
+{
+    const moe_desc &d = L->d;
+    const size_t sb[3] = {mat_scale_bytes(d, 0), mat_scale_bytes(d, 1), mat_scale_bytes(d, 2)};
+    const moe::MatW m[3] = {matw(L->w, 0), matw(L->w, 1), matw(L->w, 2)};
+    const int units = (int)std::min<long long>(d.n_experts, (long long)T * d.top_k);
+    moe_status st = device_status(moe::launch_check_weights(d.wfmt, m, sb, r->active, r->n_active, units,
+                                                            status_word(L), s), "validating the expert weights");
+    if (st != MOE_OK || d.n_shared == 0) return st;
+    const moe::MatW ms[3] = {shared_matw(L->w, 0), shared_matw(L->w, 1), shared_matw(L->w, 2)};
+    return device_status(moe::launch_check_weights(d.wfmt, ms, sb, nullptr, nullptr, d.n_shared, status_word(L), s),
+                         "validating the shared experts");
+}
+
 }  // namespace
 
 extern "C" {
@@ -334,6 +393,12 @@ moe_status moe_route(moe_layer *L, const void *x, int32_t xt, int32_t T, const m
     if (!x) return fail(MOE_ERR_INVALID_ARG, "x is NULL");
     if (!aligned(x, 16)) return fail(MOE_ERR_INVALID_ARG, "x must be 16-byte aligned");
     hipStream_t s = (hipStream_t)stream;
+    if (validating(L)) {
+        if ((st = take_status(L, s, nullptr)) != MOE_OK) return st;
+        if ((st = device_status(moe::launch_check_finite(x, xt, (size_t)T * L->d.hidden, status_word(L), MOE_BAD_X, s),
+                                "validating x")) != MOE_OK)
+            return st;
+    }
     moe::RouteArgs a{};
     a.x = x;
     a.xt = xt;
@@ -379,6 +444,10 @@ moe_status moe_forward(moe_layer *L, const void *x, int32_t xt, int32_t T, const
     if (!x || !y) return fail(MOE_ERR_INVALID_ARG, "x or y is NULL");
     if (!aligned(x, 16) || !aligned(y, 16)) return fail(MOE_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
     if (saved_gu && !aligned(saved_gu, 16)) return fail(MOE_ERR_INVALID_ARG, "saved_gu must be 16-byte aligned");
+    if (validating(L)) {
+        if ((st = take_status(L, (hipStream_t)stream, nullptr)) != MOE_OK) return st;
+        if ((st = check_weights(L, r, T, (hipStream_t)stream)) != MOE_OK) return st;
+    }
     moe::ExpertFwdArgs a{};
     a.wfmt = L->d.wfmt;
     a.gate = matw(L->w, 0);
@@ -483,6 +552,14 @@ moe_status backward_impl(moe_layer *L, const void *x, int32_t xt, const void *dy
     if (!aligned(x, 16) || !aligned(dy, 16) || !aligned(dx, 16))
         return fail(MOE_ERR_INVALID_ARG, "x, dy and dx must be 16-byte aligned");
     if (saved_gu && !aligned(saved_gu, 16)) return fail(MOE_ERR_INVALID_ARG, "saved_gu must be 16-byte aligned");
+    if (validating(L)) {
+        const hipStream_t s = (hipStream_t)stream;
+        if ((st = take_status(L, s, nullptr)) != MOE_OK) return st;
+        if ((st = device_status(moe::launch_check_finite(dy, dyt, (size_t)T * L->d.hidden, status_word(L), MOE_BAD_DY, s),
+                                "validating dy")) != MOE_OK)
+            return st;
+        if ((st = check_weights(L, r, T, s)) != MOE_OK) return st;
+    }
     moe::ExpertBwdArgs a{};
     a.wfmt = L->d.wfmt;
     a.gate = matw(L->w, 0);
@@ -514,10 +591,7 @@ moe_status backward_impl(moe_layer *L, const void *x, int32_t xt, const void *dy
     a.dxs = (float *)(L->ws + L->lay.ybuf);
     a.dx = dx;
     a.act = L->d.act;
-    if (L->d.flags & MOE_F_MX_GATEUP) {
-        a.xq = (uint8_t *)(L->ws + L->lay.xq);
-        a.xq_s = (uint8_t *)(L->ws + L->lay.xqs);
-    }
+    // g, u are recomputed (saved_gu = NULL) on the exact bf16 path even with MOE_F_MX_GATEUP
     a.prof = &L->prof;
     const hipStream_t hs = (hipStream_t)stream;
     if (L->d.n_shared > 0) {
@@ -635,6 +709,17 @@ moe_status moe_set_lora(moe_layer *L, const moe_lora *lora)
 
 
 
+moe_status moe_check_status(moe_layer *L, uint32_t *bits, void *stream)
+{
+    g_last_error.clear();
+    moe_status st;
+    if ((st = check_layer(L)) != MOE_OK) return st;
+    if (!bits) return fail(MOE_ERR_INVALID_ARG, "bits is NULL");
+    if (!validating(L)) return fail(MOE_ERR_INVALID_ARG, "the layer was created without MOE_F_VALIDATE");
+    *bits = 0;
+    return take_status(L, (hipStream_t)stream, bits);
+}
+
 void moe_destroy(moe_layer *L)
 {
     if (!L) return;
@@ -696,6 +781,7 @@ const char *moe_status_string(moe_status s)
     case MOE_ERR_WORKSPACE: return "workspace too small";
     case MOE_ERR_DEVICE: return "device error";
     case MOE_ERR_INTERNAL: return "internal error";
+    case MOE_ERR_DATA: return "out-of-contract data";
     }
     return "unknown status";
 }

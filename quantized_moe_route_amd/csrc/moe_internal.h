@@ -136,7 +136,6 @@ struct ExpertBwdArgs {
     float *dp_part;      // [S][ntile] partial <a, h>
     float *dxs;          // [S][H] slot rows
     float *dx;           // [T][H]
-    uint8_t *xq, *xq_s;  // x terms for the gate/up recomputation (as in ExpertFwdArgs)
     int act;             // ACT_SWIGLU or ACT_SITU
     const float *lora_gu;  // [T][2I] adapter terms of g | u for the recomputation, or null
     const float *lora_c;   // [T][I] adapter term added to a = Wd^T dy per token, or null
@@ -230,6 +229,15 @@ hipError_t lora_backward_post(const LoraW &L, const LoraWs &w, const ExpertBwdAr
 hipError_t lora_grads(const LoraW &L, const LoraWs &w, const ExpertBwdArgs &a, float *const dA[3], float *const dB[3],
                       hipStream_t s);
 hipError_t fill_zero(float *p, size_t n, hipStream_t s);
+
+// MOE_F_VALIDATE (validate.hip): OR `bit` into *status if any of the n bf16/fp32 values at
+// p (16-byte aligned, n a multiple of 8) is non-finite; OR the MOE_BAD_* bits of the scale
+// bytes (MXFP4) or codewords (RVQ3) of the experts a call reads: active[u] for u <
+// *n_active (active non-null), else experts 0..units-1; store v into *p.
+hipError_t launch_check_finite(const void *p, int dt, size_t n, uint32_t *status, uint32_t bit, hipStream_t s);
+hipError_t launch_check_weights(int wfmt, const MatW (&m)[3], const size_t (&scale_bytes)[3], const int32_t *active,
+                                const int32_t *n_active, int units, uint32_t *status, hipStream_t s);
+hipError_t launch_set_u32(uint32_t *p, uint32_t v, hipStream_t s);
 
 // number of I-column tiles whose partial <a, h> sums the backward stores per row
 __host__ __device__ inline int dp_tiles(int I) { return (I + 63) / 64; }

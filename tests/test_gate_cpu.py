@@ -1,8 +1,9 @@
 """The 1e-4 parity gate has teeth: a lossy variant of the method must fail it (CPU only).
 
-The Two Desks write-up (Act II) records a GPU expert path that computed its matmuls in
-bf16 and failed its own tolerance gate at 5.8e-3; the LazyLoRA README ("Arithmetic")
-records bf16 accumulation shifting a layer's output by about 1e-3."""
+The Two Desks write-up (Act II) reports that a GPU expert path with bf16 matmul
+arithmetic missed its precision gate (error 5.8e-3) until it moved to fp32 compute; the
+LazyLoRA README ("Arithmetic") reports a shift of about 1e-3 in a layer's output from
+bf16 accumulation."""
 import numpy as np
 
 import moe_synth as syn

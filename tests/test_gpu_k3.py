@@ -1,6 +1,8 @@
 """Parity at the K3 shapes (H 3584, I 3072, 896 experts, top-16), in the launch
 configuration the benchmark times.  Routing and grouping are compared in full for every
-token; y and dX on sampled tokens that the oracle computes one by one."""
+token; y (and dX) for every token of the 64-token and RVQ3 decode batches, and for 64 tokens
+of the 4096-token pass chosen from the grouping so that they cover the grouped GEMMs' tile
+and pass boundaries (the oracle computes them one by one)."""
 import numpy as np
 import pytest
 
@@ -45,7 +47,39 @@ def _check_full_routing(r, ids, p, E):
     return g
 
 
+def tile_tokens(g, k, T, n, seed):
+    """At least n tokens chosen from the grouping so that the compared rows cover the grouped
+    GEMMs' structure: the first and last rows of 16-token tiles, every expert's partial last
+    tile, and the second 96-token pass of the heaviest expert (its rows 96, 111, 112 and last);
+    the lightest active expert in full; the rest random."""
+    counts, off, perm = g["counts"], g["offsets"], g["perm"]
+    active = g["active"][:g["n_active"]]
+    rng = np.random.default_rng(seed)
+
+    def tok(e, r):
+        return int(perm[off[e] + r]) // k
+
+    picks = []
+    heavy = int(active[np.argmax(counts[active])])
+    for r in (0, 15, 16, 31, 95, 96, 111, 112, counts[heavy] - 1):
+        if r < counts[heavy]:
+            picks.append(tok(heavy, r))
+    light = int(active[np.argmin(counts[active])])
+    picks += [tok(light, r) for r in range(counts[light])]
+    for e in rng.choice(active, size=min(len(active), 12), replace=False):
+        c = int(counts[e])
+        picks += [tok(e, 0), tok(e, c - 1), tok(e, (c - 1) // 16 * 16)]
+    picks = sorted(set(picks))
+    if len(picks) < n:
+        rest = np.setdiff1d(np.arange(T), picks)
+        picks = sorted(set(picks) | set(rng.choice(rest, size=n - len(picks), replace=False).tolist()))
+    return np.array(picks), heavy
+
+
 def _run(c, L, name, T, sample, with_bwd):
+    """Routing in full; y (and dX with saved and recomputed g, u) on `sample` tokens, or on
+    every token when sample >= T, or on the tile-covering set of tile_tokens() when the
+    experts average many tokens."""
     w = syn.shrink(c.w, T=T, bias_sd=syn.WORKLOADS[name].bias_sd, x_key=syn.WORKLOADS[name].x_key)
     x_h = syn.activations(w, T)
     bias = syn.router_bias(w)
@@ -69,9 +103,14 @@ def _run(c, L, name, T, sample, with_bwd):
     g = _check_full_routing(r, ids, p, w.E)
     log(f"{name}: routing bit-exact; U = {g['n_active']} active experts")
     W = c.oracle_weights()
-    rng = np.random.default_rng(T)
-    toks = np.sort(rng.choice(T, size=min(sample, T), replace=False))
-    log(f"{name}: oracle forward on tokens {toks.tolist()}")
+    if sample >= T:
+        toks = np.arange(T)
+    elif T * w.k >= 8 * w.E:
+        toks, heavy = tile_tokens(g, w.k, T, sample, seed=T)
+        log(f"{name}: heaviest expert {heavy} holds {g['counts'][heavy]} tokens")
+    else:
+        toks = np.sort(np.random.default_rng(T).choice(T, size=sample, replace=False))
+    log(f"{name}: oracle forward on {len(toks)} tokens")
     y_ref = oracle.forward(x64[toks], ids[toks], p[toks], W)
     e = rel_err(_np(y)[toks], y_ref)
     log(f"{name}: y rel err {e:.3e}")
@@ -82,7 +121,7 @@ def _run(c, L, name, T, sample, with_bwd):
         dx = L2.backward_input(x, dy, r, saved_gu=gu)
         dx2 = L2.backward_input(x, dy, r, saved_gu=None)
         _sync()
-        log(f"{name}: oracle backward on the same tokens")
+        log(f"{name}: oracle backward on the same {len(toks)} tokens")
         dx_ref = oracle.backward_input(x64[toks], oracle.to_f64(dy_h, "bf16")[toks], ids[toks], p[toks], c.wr, W)
         e1, e2 = rel_err(_np(dx)[toks], dx_ref), rel_err(_np(dx2)[toks], dx_ref)
         log(f"{name}: dX rel err {e1:.3e} (saved g/u), {e2:.3e} (recomputed)")
@@ -98,12 +137,12 @@ def test_decode1_full_size(k3_mxfp4):
 
 def test_decode64_full_size(k3_mxfp4):
     c, L = k3_mxfp4
-    _run(c, L, "decode64", 64, 6, with_bwd=False)
+    _run(c, L, "decode64", 64, 64, with_bwd=False)
 
 
 def test_train4096_full_size(k3_mxfp4):
     c, L = k3_mxfp4
-    _run(c, L, "train4096", 4096, 4, with_bwd=True)
+    _run(c, L, "train4096", 4096, 64, with_bwd=True)
 
 
 def test_rvq16_full_size():
@@ -120,9 +159,8 @@ def test_rvq16_full_size():
     _sync()
     g = _check_full_routing(r, ids, p, w.E)
     log(f"rvq16: routing bit-exact; U = {g['n_active']}")
-    toks = np.array([0, 7, 15])
-    y_ref = oracle.forward(x64[toks], ids[toks], p[toks], c.oracle_weights())
-    e = rel_err(_np(y)[toks], y_ref)
+    y_ref = oracle.forward(x64, ids, p, c.oracle_weights())  # all 16 tokens
+    e = rel_err(_np(y), y_ref)
     log(f"rvq16: y rel err {e:.3e}")
     assert e <= TOL
     L.close()
@@ -157,7 +195,7 @@ def test_shared_experts_k3(k3_mxfp4):
                     codes=L._keep[2], scales=L._keep[3],
                     shared=([q.to_device(a) for a in sh[0]], [q.to_device(a) for a in sh[1]]))
     W = c.oracle_weights()
-    for name, T, sample, with_bwd in (("decode1", 1, 1, False), ("train4096", 4096, 3, True)):
+    for name, T, sample, with_bwd in (("decode1", 1, 1, False), ("train4096", 4096, 16, True)):
         wk = syn.shrink(w, T=T, x_key=syn.WORKLOADS[name].x_key)
         assert syn.WORKLOADS[name].bias_sd in (None, 0.0)
         x_h = syn.activations(wk, T)
@@ -168,7 +206,12 @@ def test_shared_experts_k3(k3_mxfp4):
         y = Ls.forward(x, r)
         _sync()
         assert np.array_equal(_np(r.ids), ids)
-        toks = np.sort(np.random.default_rng(T + 1).choice(T, size=sample, replace=False))
+        # the shared experts' tokens run in 96-token chunks: first and last rows of chunks and of
+        # 16-token tiles, the short last chunk, and random ones
+        edge = [t for t in (0, 15, 16, 95, 96, 191, 4031, 4032, 4095) if t < T]
+        rest = np.setdiff1d(np.arange(T), edge)
+        extra = np.random.default_rng(T + 1).choice(rest, size=max(0, sample - len(edge)), replace=False)
+        toks = np.sort(np.concatenate([edge, extra]).astype(np.int64))[:max(sample, 1)]
         y_ref = oracle.forward(x64[toks], ids[toks], p[toks], W) + oracle.shared_forward(x64[toks], Ws, 2)
         e = rel_err(_np(y)[toks], y_ref)
         log(f"shared-{name}: y rel err {e:.3e} on tokens {toks.tolist()}")

@@ -144,10 +144,12 @@ def test_block_scaled_gateup_skew():
 
 
 def test_block_scaled_gateup_wide_x_range_deviation():
-    """Reported, not gated at 1e-4: x elements spread over 2^-12 .. 2^6 inside each 32-block.
-    The two E4M3 terms still carry the small elements to ~2^-21 of the block maximum, but
-    the block-scaled MFMA's own accumulation then loses precision on the small products
-    (measured y ~6e-5 and dX ~6e-4 of the maximum); the bf16 path stays exact."""
+    """x elements spread over 2^-12 .. 2^6 inside each 32-block.  The two E4M3 terms still
+    carry the small elements to ~2^-21 of the block maximum, but the block-scaled MFMA's own
+    summation then loses precision on the small products.  y stays within the 1e-4 gate
+    (measured ~6e-5), and so does dX recomputed on the exact path (saved_gu = NULL); dX from
+    the g, u saved by the block-scaled forward is the gradient at those pre-activations and is
+    checked against the bound the header states (measured ~6e-4)."""
     import quantized_moe_route_amd as q
     from quantized_moe_route_amd import _lib as C
     w = syn.shrink(TINY, T=300, H=1024, I=512, E=24, k=3, x_dtype="bf16", with_dy=True, x_key=27)
@@ -166,12 +168,15 @@ def test_block_scaled_gateup_wide_x_range_deviation():
         r = L.route(x)
         gu = L.new_saved_gu(w.T)
         y = L.forward(x, r, saved_gu=gu)
-        dx = L.backward_input(x, dy, r, saved_gu=gu)
+        dx_saved = L.backward_input(x, dy, r, saved_gu=gu)
+        dx = L.backward_input(x, dy, r, saved_gu=None)
         _sync()
-        errs[name] = (rel_err(_np(y), y_ref), rel_err(_np(dx), dx_ref))
-        log(f"  wide-range x, {name} gate/up: y rel err {errs[name][0]:.3e}, dX rel err {errs[name][1]:.3e}")
+        errs[name] = (rel_err(_np(y), y_ref), rel_err(_np(dx), dx_ref), rel_err(_np(dx_saved), dx_ref))
+        log(f"  wide-range x, {name} gate/up: y rel err {errs[name][0]:.3e}, dX rel err {errs[name][1]:.3e} "
+            f"(recomputed), {errs[name][2]:.3e} (from the saved g, u)")
     assert max(errs["bf16"]) <= TOL
-    assert max(errs["mx"]) < 1e-2
+    assert errs["mx"][0] <= TOL and errs["mx"][1] <= TOL
+    assert errs["mx"][2] <= 7e-4  # the bound include/moe.h states for MOE_F_MX_GATEUP's saved g, u
 
 
 def _scale_x(c, e):
@@ -190,14 +195,14 @@ SITU_CASES = {
     # bent parts of both tanh branches.  The SiTU derivatives sech^2(g/4) and s (1 - s) change
     # by a relative amount of the order of the ABSOLUTE error of g, so dX's relative error
     # grows like max|g| times the precision x enters the products with: exact for bf16 x on
-    # the bf16 paths, about 2^-17 for fp32 x (two bf16 terms) and for the two E4M3 terms of
-    # the block-scaled gate/up.  Those two paths take 2^3 (max|g| about 75 to 110, dX error about
-    # 3e-5); at 2^5 (max|g| about 255 to 390) they reach 1.1e-4 to 1.3e-4.
-    "generic": (dict(T=37, with_dy=True), 3, 0),
+    # the bf16 paths and for fp32 x (three bf16 terms hold all 24 significand bits).  The
+    # block-scaled gate/up's forward (two E4M3 terms) is checked on y only; its backward
+    # recomputes g, u on the exact path.
+    "generic": (dict(T=37, with_dy=True), 5, 0),
     "dec-T1": (dict(T=1, H=1024, I=256, E=16, k=8, x_dtype="bf16"), 5, 0),
     "dec-few": (dict(T=6, H=512, I=768, E=12, k=3, x_dtype="bf16", with_dy=True), 5, 0),
     "mm": (dict(T=400, H=512, I=1024, E=8, k=2, x_dtype="bf16", with_dy=True), 5, 0),
-    "mm-mx": (dict(T=400, H=512, I=1024, E=8, k=2, x_dtype="bf16"), 3, 2),
+    "mm-mx": (dict(T=400, H=512, I=1024, E=8, k=2, x_dtype="bf16"), 5, 2),
 }
 
 
@@ -377,10 +382,15 @@ def test_selection_experts_closed_form_on_gpu():
     c.codes, c.scales = codes, scales
     L, x, r, y = run_small(c, name="selection")
     ids, p = _np(r.ids), _np(r.w).astype(np.float64)
+    errs = []
     for t in range(T):
         want = sum(p[t, j] * _selection_closed_form(c.x64[t], H, I, shifts, exps, exps[2][ids[t, j]])
                    for j in range(k))
-        assert rel_err(_np(y)[t], want) <= TOL
+        errs.append(rel_err(_np(y)[t], want))
+    log(f"  selection experts: max per-token rel err {max(errs):.3e}")
+    # fp32 x enters the products exactly (three bf16 terms); what remains is the fp32 sigmoid,
+    # h carried as bf16 hi + lo (2^-18) and fp32 accumulation
+    assert max(errs) <= 1e-5
 
 
 def test_repeat_calls_are_bitwise_deterministic():

@@ -100,3 +100,30 @@ def test_quant_backward_is_the_exact_layers(mx):
     d0 = L0.backward_input(x, dy, r0)
     torch.cuda.synchronize()
     assert np.array_equal(_np(dq), _np(d0))
+
+
+@pytest.mark.parametrize("mx", [False, True])
+def test_quant_backward_from_saved_preactivations(mx):
+    """saved_gu written by a quantized-input forward holds the pre-activations of the quantized
+    x; moe_backward_input from them is the input gradient of the quantized layer with the
+    quantization passed straight through (d xq / d x taken as 1): the oracle's backward run
+    on the quantized x, with the routing (and the router term's Wr) of the unquantized x."""
+    import torch
+
+    from quantized_moe_route_amd import _lib as C
+    if mx:
+        w = syn.shrink(TINY, T=300, H=1024, I=512, E=16, k=3, x_dtype="bf16", with_dy=True, x_key=87)
+    else:
+        w = syn.shrink(TINY, T=8, x_dtype="bf16", with_dy=True, x_key=88)
+    c = host_case(w)
+    Lq, x, r = run_quant(c, "quant-saved" + ("-mx" if mx else ""), flags=C.MOE_F_MX_GATEUP if mx else 0)
+    gu = Lq.new_saved_gu(w.T)
+    Lq.forward(x, r, saved_gu=gu)
+    dx = Lq.backward_input(x, act_tensor(c.dy, w.x_dtype), r, saved_gu=gu)
+    torch.cuda.synchronize()
+    ids, p, _ = oracle.route(c.x64, c.wr, c.bias, w.k)
+    xq64, _ = oracle.quantize_mxfp8(c.x64)
+    dx_ref = oracle.backward_input(xq64, c.dy64, ids, p, c.wr, c.oracle_weights())
+    e = rel_err(_np(dx), dx_ref)
+    log(f"  dX (saved g/u of the quantized forward) rel err {e:.3e}")
+    assert e <= TOL

@@ -34,7 +34,7 @@ def log(msg):
 
 # The kernel whose roofline each workload reports, and the sources that define it.
 ROOF_KERNEL = {
-    "decode1": ("k_gateup_dec", ("expert_dec.hip",)),
+    "decode1": ("k_dec_fused", ("expert_dec.hip",)),
     "decode64": ("k_gateup", ("expert_fwd.hip", "expert_frag.h")),
     "rvq16": ("k_gateup_rvq", ("expert_rvq.hip",)),
     "train4096": ("k_gateup_mm", ("expert_mm.hip",)),
@@ -311,10 +311,16 @@ def main():
     S = w.T * w.k
     x_bytes = w.T * w.H * 2
     S_sh = w.T * args.shared
-    # weights, token rows, the h planes (bf16 hi + lo) and, in the training pass, the saved
-    # gate/up pre-activations (fp32 g and u per slot)
-    gu_alg = [u * gateup_bytes_per_expert + x_bytes + S * w.I * 4 + (S * 2 * w.I * 4 if train else 0)
-              + (shared_gateup_bytes + x_bytes + S_sh * w.I * 4 if args.shared else 0) for u in steps_U]
+    fused = ROOF_KERNEL[w.name][0] == "k_dec_fused"
+    if fused:
+        # the single-token launch runs gate/up, down and the combine: every routed (and
+        # shared) expert's bytes, the token row in and y out
+        gu_alg = [u * expert_bytes + shared_bytes + x_bytes + w.T * w.H * 4 for u in steps_U]
+    else:
+        # weights, token rows, the h planes (bf16 hi + lo) and, in the training pass, the saved
+        # gate/up pre-activations (fp32 g and u per slot)
+        gu_alg = [u * gateup_bytes_per_expert + x_bytes + S * w.I * 4 + (S * 2 * w.I * 4 if train else 0)
+                  + (shared_gateup_bytes + x_bytes + S_sh * w.I * 4 if args.shared else 0) for u in steps_U]
     gu_bytes = sum(gu_alg) / len(gu_alg)
     # gate/up time per step (with shared experts: both launches), from events stamped at the
     # kernels' own start and end
@@ -325,12 +331,13 @@ def main():
     tokens_per_s = w.T * args.steps / (ms / 1e3)
     traffic = traffic_record(w.name)
     log(f"{args.steps} steps in {ms:.2f} ms (wall {wall * 1e3:.1f} ms): {step_s * 1e6:.1f} us/step, "
-        f"{tokens_per_s:.0f} tokens/s; gate/up kernel {gu_avg_s * 1e6:.1f} us avg, {achieved:.0f} GB/s")
+        f"{tokens_per_s:.0f} tokens/s; {ROOF_KERNEL[w.name][0]} {gu_avg_s * 1e6:.1f} us avg, {achieved:.0f} GB/s")
 
     detail = {"step_hbm_GBps": sum(step_bytes) / len(step_bytes) / step_s / 1e9,
               "step_alg_bytes": sum(step_bytes) / len(step_bytes),
               "active_experts_mean": sum(steps_U) / len(steps_U),
-              "gateup_us": gu_avg_s * 1e6, "gateup_alg_bytes": gu_bytes, "gateup_GBps": achieved}
+              "roofline_kernel_us": gu_avg_s * 1e6, "roofline_kernel_alg_bytes": gu_bytes,
+              "roofline_kernel_GBps": achieved}
     if train:
         # the grouped GEMM is priced against the dense MFMA peak of its operand type: exact
         # bf16 (dequantized FP4 weights, bf16 x; also the two-term block-scaled form, which
@@ -345,7 +352,8 @@ def main():
         roofline = {"bound": "mfma", "kernel": kname, "achieved": gu_tflops, "peak": peak, "unit": "TFLOP/s",
                     "frac": gu_tflops / peak, "traffic": traffic if not args.mx_gateup else None}
     else:
-        roofline = {"bound": "hbm", "kernel": ROOF_KERNEL[w.name][0] + " (dequant + gate/up + SwiGLU)",
+        what = " (dequant + gate/up + SwiGLU + down + combine)" if fused else " (dequant + gate/up + SwiGLU)"
+        roofline = {"bound": "hbm", "kernel": ROOF_KERNEL[w.name][0] + what,
                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                     "traffic": traffic}
     if not train and not args.no_plain_read:
@@ -366,7 +374,7 @@ def main():
         t_plain = sorted(t[8:])[len(t[8:]) // 2] / 1e3
         roofline["plain_read"] = {"bytes": nb, "GBps": nb / t_plain / 1e9, "us": t_plain * 1e6,
                                   "frac": achieved / (nb / t_plain / 1e9)}
-        log(f"plain read of {nb} bytes: {t_plain * 1e6:.1f} us = {nb / t_plain / 1e9:.0f} GB/s; the gate/up kernel "
+        log(f"plain read of {nb} bytes: {t_plain * 1e6:.1f} us = {nb / t_plain / 1e9:.0f} GB/s; the roofline kernel "
             f"reaches {roofline['plain_read']['frac']:.3f} of it")
     if args.breakdown:
         fams = list(range(len(C.PROF_NAMES)))

@@ -86,15 +86,24 @@ __device__ __forceinline__ void fetch(Raw &r, __amdgpu_buffer_rsrc_t code, uint3
     r.c1 = ld16(code, coff, 128 * st + 16);
 }
 
-// 8 MFMA sub-steps of one K-step for one tile: A from raw bytes and the two scale bytes
-// of the lane's blocks, B from LDS.
+// A operand of MFMA sub-step s (reduction indices 8 s .. 8 s + 7 of the lane's 64): the 8
+// E2M1 codes of word s % 4 of c0 (s < 4) or c1, times the block scale, as bf16 (exact).
+__device__ __forceinline__ bf16x8 decode_sub(const Raw &r, float scale, int s)
+{
+    const uint32_t w = s < 4 ? r.c0[s & 3] : r.c1[s & 3];
+    return as_bf16x8(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2)),
+                     __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3)));
+}
+
+// 8 MFMA sub-steps of one K-step for one tile: A decoded from the raw bytes with the two
+// scale bytes of the lane's blocks, sub-step by sub-step; B from LDS.
 __device__ __forceinline__ void mma_raw(f32x4 &acc, const Raw &r, uint32_t sc, const bf16x8 (&B)[8])
 {
-    uint32_t d[32];
-    decode_fp4x32(r.c0, e8m0_to_f32(sc & 0xFFu), d);
-    decode_fp4x32(r.c1, e8m0_to_f32(sc >> 8), d + 16);
+    const float s0 = e8m0_to_f32(sc & 0xFFu), s1 = e8m0_to_f32(sc >> 8);
 #pragma unroll
-    for (int s = 0; s < 8; s++) acc = mfma16(as_bf16x8(d[4 * s], d[4 * s + 1], d[4 * s + 2], d[4 * s + 3]), B[s], acc);
+    for (int s = 0; s < 8; s++) acc = mfma16(decode_sub(r, s < 4 ? s0 : s1, s), B[s], acc);
 }
 
 // Scale bytes of a wave's 16-row tile (16 * K/32 contiguous bytes, K <= 4096) go to a
@@ -144,41 +153,54 @@ __device__ __forceinline__ void stage_rows(uint16_t *dst, const uint16_t *src, O
     }
 }
 
-}  // namespace
+// Cache policy of the accesses that hand data from one block to another inside the fused
+// decode launch (k_dec_fused): sc1 = agent scope.  Such stores are written through to the
+// point where every XCD sees them and such loads are served from there, so a block on one
+// XCD reads what a block on another XCD wrote (each XCD has its own L2) without a fence over
+// the whole cache; a counter incremented after the stores completed (s_waitcnt) publishes
+// them.
+constexpr int kSc1 = 16;
 
-// gate/up + activation.  Block = 4 waves x 16 rows = 64 I-columns of one active expert
-// (blockIdx.y indexes the active list); all of the expert's tokens (<= nl_x) in one
-// 16-column MFMA tile.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_gateup_dec(const ExpertFwdArgs a)
+__device__ __forceinline__ u32x4 ld16_coh(__amdgpu_buffer_rsrc_t r, uint32_t voff)
 {
-    extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, 0, kSc1);
+}
+
+__device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// gate/up + activation of one block: 4 waves x 16 rows = 64 I-columns (column block bx) of
+// active unit ai; all of the unit's tokens (<= nl_x) in one 16-column MFMA tile.  COH: the h
+// planes are stored with the agent-scope policy (read by other blocks of the same launch).
+// Returns false (having done nothing else) for an unit past the active list.
+template <bool COH, int NS>
+__device__ __forceinline__ bool gateup_block(const ExpertFwdArgs &a, int bx, int ai, uint16_t *xs)
+{
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
     // The weight prefetch needs only e: the active-list entry is read together with the
     // list length (entries past it are stale but name a valid expert) and the first code
     // loads go out before the block learns whether it has work.
-    const int ai = blockIdx.y;
     const int nact = *a.n_active;
     const int sh = ai - min(a.E, a.T * a.k);  // >= 0: shared expert sh (every token, weight 1)
     const int e = sh >= 0 ? sh : min(max(a.active[ai], 0), a.E - 1);
     const MatW &Wg = sh >= 0 ? a.sh_gate : a.gate, &Wu = sh >= 0 ? a.sh_up : a.up;
     const int H = a.H, I = a.I;
-    const int row0 = blockIdx.x * 64 + wv * 16;
+    const int row0 = bx * 64 + wv * 16;
     const int nsteps = H / 256, spr = H / 32;
     const size_t eoc = (size_t)e * I * (H / 2), eos = (size_t)e * I * spr;
     const __amdgpu_buffer_rsrc_t cg = buf_rsrc(Wg.codes + eoc, I * (H / 2));
     const __amdgpu_buffer_rsrc_t cu = buf_rsrc(Wu.codes + eoc, I * (H / 2));
     const uint32_t coff = (uint32_t)(row0 + li) * (H / 2) + 32 * g;
 
-    Raw rg[kGuStages], ru[kGuStages];
+    Raw rg[NS], ru[NS];
 #pragma unroll
-    for (int s = 0; s < kGuStages - 1; s++) {
+    for (int s = 0; s < NS - 1; s++) {
         fetch(rg[s], cg, coff, min(s, nsteps - 1));
         fetch(ru[s], cu, coff, min(s, nsteps - 1));
     }
     TileScales tg, tu;
     get_scales(tg, buf_rsrc(Wg.scales + eos, I * spr), (uint32_t)row0 * spr, lane);
     get_scales(tu, buf_rsrc(Wu.scales + eos, I * spr), (uint32_t)row0 * spr, lane);
-    if (sh < 0 && ai >= nact) return;
+    if (sh < 0 && ai >= nact) return false;
     const int r0 = sh >= 0 ? sh * a.T : a.offsets[e], ntok = sh >= 0 ? a.T : a.offsets[e + 1] - r0;
     // token rows to LDS while the first weight bytes are in flight
     __shared__ uint32_t xrow[16];
@@ -194,11 +216,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     const uint16_t *slg = (const uint16_t *)(sreg + li * spr + 2 * g);
     const uint16_t *slu = (const uint16_t *)(sreg + 2048 + li * spr + 2 * g);
     f32x4 accg = {0.f, 0.f, 0.f, 0.f}, accu = {0.f, 0.f, 0.f, 0.f};
-    k_loop<kGuStages>(nsteps, [&](auto P, int st) {
+    k_loop<NS>(nsteps, [&](auto P, int st) {
         constexpr int p = decltype(P)::value;
-        const int sn = min(st + kGuStages - 1, nsteps - 1);
-        fetch(rg[(p + kGuStages - 1) % kGuStages], cg, coff, sn);
-        fetch(ru[(p + kGuStages - 1) % kGuStages], cu, coff, sn);
+        const int sn = min(st + NS - 1, nsteps - 1);
+        fetch(rg[(p + NS - 1) % NS], cg, coff, sn);
+        fetch(ru[(p + NS - 1) % NS], cu, coff, sn);
         __builtin_amdgcn_sched_barrier(0);
         bf16x8 B[8];
         lds_row8(B, xl + 256 * st);
@@ -215,15 +237,35 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
 #pragma unroll
         for (int r = 0; r < 4; r++) split_bf16(act_h(a.act, accg[r], accu[r]), hh[r], hl[r]);
         uint16_t *ph = sh >= 0 ? a.sh_h_hi : a.h_hi, *pl = sh >= 0 ? a.sh_h_lo : a.h_lo;
-        *(u32x2 *)(ph + rr * I + n) = u32x2{pack2(hh[0], hh[1]), pack2(hh[2], hh[3])};
-        *(u32x2 *)(pl + rr * I + n) = u32x2{pack2(hl[0], hl[1]), pack2(hl[2], hl[3])};
+        const u32x2 vh = {pack2(hh[0], hh[1]), pack2(hh[2], hh[3])}, vl = {pack2(hl[0], hl[1]), pack2(hl[2], hl[3])};
+        if constexpr (COH) {
+            // the planes of one unit: rows r0 .. r0 + ntok of I bf16 values each
+            const uint32_t nb = (uint32_t)((size_t)(r0 + ntok) * I * 2);
+            const uint32_t off = (uint32_t)((rr * I + n) * 2);
+            __builtin_amdgcn_raw_buffer_store_b64(vh, buf_rsrc(ph, nb), (int)off, 0, kSc1);
+            __builtin_amdgcn_raw_buffer_store_b64(vl, buf_rsrc(pl, nb), (int)off, 0, kSc1);
+        } else {
+            *(u32x2 *)(ph + rr * I + n) = vh;
+            *(u32x2 *)(pl + rr * I + n) = vl;
+        }
         if (a.gu && sh < 0) {
             *(float4 *)(a.gu + (rr * 2 + 0) * I + n) = float4{accg[0], accg[1], accg[2], accg[3]};
             *(float4 *)(a.gu + (rr * 2 + 1) * I + n) = float4{accu[0], accu[1], accu[2], accu[3]};
         }
     }
+    return true;
 }
 
+}  // namespace
+
+// gate/up + activation.  Block = 4 waves x 16 rows = 64 I-columns of one active expert
+// (blockIdx.y indexes the active list); all of the expert's tokens (<= nl_x) in one
+// 16-column MFMA tile.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k_gateup_dec(const ExpertFwdArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) uint16_t xs[];
+    gateup_block<false, kGuStages>(a, blockIdx.x, blockIdx.y, xs);
+}
 // down + routing weight.  Block = 4 waves x RT tiles x 16 rows = 64 RT H-rows of one
 // active expert; h (hi and lo planes) of its tokens (<= nl_h) staged in LDS.
 // PACK (at most 8 tokens): MFMA column 2j carries token j's h_hi and column 2j + 1 its
@@ -315,6 +357,207 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
     }
 }
 
+// ---------------------------------------------------------------------------------------
+// Fused decode launch: gate/up, down and combine of every unit in ONE grid.
+//
+// Blocks [0, ngu) are gate/up blocks as in k_gateup_dec (unit-major, I/64 column blocks per
+// unit); blocks [ngu, ngu + ndn) are down blocks (unit-major, H/64 stripes of 64 rows per
+// unit).  A down block first issues the loads of ALL its weight bytes (NST K-steps of 32
+// bytes per lane, held in registers) and of its scale bytes, and only then waits until the
+// I/64 gate/up blocks of its unit have published their h rows (a per-unit counter), so the
+// down weights stream while gate/up blocks still run.  It then publishes its p-weighted
+// slot rows of the stripe and counts itself into the stripe's counter; the block that
+// completes a stripe (n_active + n_shared arrivals) sums the stripe's slot rows of every
+// token in rank order, then the shared experts' rows: the order of k_combine, so the result
+// is the same bits as the three-launch path.  That block also zeroes the stripe's counter
+// and counts the stripe as done; the block that completes the last stripe zeroes the unit
+// counters (every down block has passed its wait by then) and the stripe count, so each
+// launch finds them at zero (the workspace region is cleared when a layer is first used).
+// Each counter has a 128-byte line of its own, and waiting blocks poll it every ~0.2 us.
+//
+// Progress: on each XCD blocks are dispatched in index order and gate/up blocks (the lower
+// indices) never wait, so every block a down block waits for is dispatched and finishes.
+// The wait is also bounded (kSpinTicks of the 100 MHz real-time clock): past it the block
+// sets kStatusSpinTimeout in the status word and goes on, so the grid always drains.
+constexpr uint64_t kSpinTicks = 20000000;  // 200 ms
+// 4 waves per SIMD (<= 128 VGPRs): all gate/up blocks and a first quarter of the down blocks
+// are resident from the start, and the rest of the down blocks as gate/up blocks finish, so
+// every down block has its weight loads in flight by the time the last unit's h is out.
+constexpr int kFusedGuStages = 3;  // gate/up register stages
+constexpr int kPre = 8;            // down K-steps loaded before the wait
+
+// stage n contiguous bf16 rows (src + r * K) written by other blocks of this launch into LDS
+// rows of stride K + 8, with the agent-scope load policy
+__device__ __forceinline__ void stage_rows_coh(uint16_t *dst, const uint16_t *src, int n, int K)
+{
+    const __amdgpu_buffer_rsrc_t r = buf_rsrc(src, (uint32_t)((size_t)n * K * 2));
+    const int per = K / 8, total = n * per;
+    for (int c0 = threadIdx.x; c0 < total; c0 += 4 * blockDim.x) {
+        u32x4 v[4];
+        int rw[4], q[4];
+#pragma unroll
+        for (int i = 0; i < 4; i++) {
+            const int c = min(c0 + i * (int)blockDim.x, total - 1);
+            rw[i] = c / per;
+            q[i] = c - rw[i] * per;
+            v[i] = ld16_coh(r, (uint32_t)(c * 16));
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) *(u32x4 *)(dst + (size_t)rw[i] * (K + 8) + 8 * q[i]) = v[i];
+    }
+}
+
+// y rows [bx * 64, bx * 64 + 64) of every token: the slot rows in rank order, then the
+// shared experts' rows (agent-scope loads: other blocks wrote them).
+__device__ __forceinline__ void combine_stripe(const ExpertFwdArgs &a, int bx)
+{
+    const int H = a.H, k = a.k, k2 = a.sh_n, T = a.T;
+    const __amdgpu_buffer_rsrc_t yb = buf_rsrc(a.ybuf, (uint32_t)((size_t)T * k * H * 4));
+    const __amdgpu_buffer_rsrc_t ys = buf_rsrc(k2 ? a.sh_ybuf : a.ybuf, (uint32_t)((size_t)T * (k2 ? k2 : k) * H * 4));
+    for (int i = threadIdx.x; i < T * 16; i += blockDim.x) {
+        const int t = i >> 4, c = bx * 64 + 4 * (i & 15);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int j0 = 0; j0 < k; j0 += 8) {
+            u32x4 v[8];
+#pragma unroll
+            for (int u = 0; u < 8; u++)
+                v[u] = j0 + u < k ? ld16_coh(yb, (uint32_t)((((size_t)t * k + j0 + u) * H + c) * 4)) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int u = 0; u < 8; u++) {
+                if (j0 + u >= k) break;
+                acc += __builtin_bit_cast(f32x4, v[u]);
+            }
+        }
+        for (int j = 0; j < k2; j++) acc += __builtin_bit_cast(f32x4, ld16_coh(ys, (uint32_t)((((size_t)t * k2 + j) * H + c) * 4)));
+        *(float4 *)(a.y + (size_t)t * H + c) = float4{acc[0], acc[1], acc[2], acc[3]};
+    }
+}
+
+// down + routing weight of one block (64 rows of stripe bx, unit ai), its slot rows
+// published to the stripe; the stripe's last block also combines it.
+template <int NST, bool PACK>
+__device__ __forceinline__ void down_block_fused(const ExpertFwdArgs &a, int bx, int ai, uint16_t *hs, int *last)
+{
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
+    const int nact = *a.n_active;
+    const int sh = ai - min(a.E, a.T * a.k);  // as in gateup_block
+    const int e = sh >= 0 ? sh : min(max(a.active[ai], 0), a.E - 1);
+    const MatW &Wd = sh >= 0 ? a.sh_down : a.down;
+    const int H = a.H, I = a.I;
+    const int m0 = bx * 64 + wv * 16;
+    const int nsteps = I / 256, spr = I / 32;
+    const __amdgpu_buffer_rsrc_t cd = buf_rsrc(Wd.codes + (size_t)e * H * (I / 2), H * (I / 2));
+    const __amdgpu_buffer_rsrc_t sd = buf_rsrc(Wd.scales + (size_t)e * H * spr, H * spr);
+    const uint32_t coff = (uint32_t)(m0 + li) * (I / 2) + 32 * g;
+    // the lane's first kPre K-steps of weight bytes in flight before the wait, the rest
+    // issued as the first steps' registers free up
+    Raw rr[NST];
+#pragma unroll
+    for (int st = 0; st < (NST < kPre ? NST : kPre); st++)
+        if (st < nsteps) fetch(rr[st], cd, coff, st);
+    TileScales ts;
+    get_scales(ts, sd, (uint32_t)m0 * spr, lane);
+    if (sh < 0 && ai >= nact) return;
+    if (threadIdx.x == 0) {
+        const uint32_t want = (uint32_t)(I / 64);
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        while (__hip_atomic_load(a.dec_sync + ai * kSyncPad, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < want) {
+            __builtin_amdgcn_s_sleep(8);
+            if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) {
+                if (a.status) atomicOr(a.status, kStatusSpinTimeout);
+                break;
+            }
+        }
+    }
+    __syncthreads();
+    const int r0 = sh >= 0 ? sh * a.T : a.offsets[e], ntok = sh >= 0 ? a.T : a.offsets[e + 1] - r0;
+    const size_t lo = (size_t)a.nl_h * (I + 8);
+    stage_rows_coh(hs, (sh >= 0 ? a.sh_h_hi : a.h_hi) + (size_t)r0 * I, ntok, I);
+    stage_rows_coh(hs + lo, (sh >= 0 ? a.sh_h_lo : a.h_lo) + (size_t)r0 * I, ntok, I);
+    uint8_t *sreg = (uint8_t *)(hs + 2 * lo) + 2048 * wv;
+    put_scales(sreg, ts, lane);
+    __syncthreads();
+
+    const int tok = PACK ? min(li >> 1, ntok - 1) : min(li, ntok - 1);
+    const uint16_t *hl = hs + (PACK && (li & 1) ? lo : 0) + (size_t)tok * (I + 8) + 64 * g;
+    const uint16_t *sl = (const uint16_t *)(sreg + li * spr + 2 * g);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < NST; st++) {
+        if (st < nsteps) {
+            bf16x8 B[8], Bl[8];
+            lds_row8(B, hl + 256 * st);
+            if constexpr (!PACK) lds_row8(Bl, hl + lo + 256 * st);
+            const uint32_t sc = sl[4 * st];
+            const float s0 = e8m0_to_f32(sc & 0xFFu), s1 = e8m0_to_f32(sc >> 8);
+#pragma unroll
+            for (int s = 0; s < 8; s++) {
+                const bf16x8 A = decode_sub(rr[st], s < 4 ? s0 : s1, s);
+                acc = mfma16(A, B[s], acc);
+                if constexpr (!PACK) acc = mfma16(A, Bl[s], acc);
+            }
+            if (st + kPre < NST && st + kPre < nsteps) fetch(rr[st + kPre], cd, coff, st + kPre);
+        }
+    }
+    if constexpr (PACK) {
+#pragma unroll
+        for (int r = 0; r < 4; r++) acc[r] += dpp_f32<kDppXor1>(acc[r]);
+    }
+    const int j = PACK ? li >> 1 : li;
+    if (j < ntok && (!PACK || (li & 1) == 0)) {
+        const int slot = sh >= 0 ? j * a.sh_n + sh : a.perm[r0 + j];
+        const float pw = sh >= 0 ? 1.f : a.w[slot];
+        float *yb = sh >= 0 ? a.sh_ybuf : a.ybuf;
+        const size_t rows = (size_t)a.T * (sh >= 0 ? a.sh_n : a.k);
+        const f32x4 v = {pw * acc[0], pw * acc[1], pw * acc[2], pw * acc[3]};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), buf_rsrc(yb, (uint32_t)(rows * H * 4)),
+                                               (int)(((size_t)slot * H + m0 + 4 * g) * 4), 0, kSc1);
+    }
+    wait_stores();
+    __syncthreads();
+    uint32_t *stripe = a.dec_sync + (kSyncUnits + bx) * kSyncPad;
+    if (threadIdx.x == 0) {
+        const uint32_t n = __hip_atomic_fetch_add(stripe, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *last = n + 1 == (uint32_t)(nact + a.sh_n);
+    }
+    __syncthreads();
+    if (!*last) return;
+    combine_stripe(a, bx);
+    if (threadIdx.x == 0) {
+        // the stripe is complete: reset its counter; the last complete stripe resets the rest
+        __hip_atomic_store(stripe, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        uint32_t *done = a.dec_sync + (kSyncUnits + kSyncStripes) * kSyncPad;
+        const uint32_t n = __hip_atomic_fetch_add(done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (n + 1 == (uint32_t)(H / 64)) {
+            const int nu = min(a.E, a.T * a.k) + a.sh_n;
+            for (int u = 0; u < nu; u++) __hip_atomic_store(a.dec_sync + u * kSyncPad, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+}
+
+template <int NST, bool PACK>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k_dec_fused(const ExpertFwdArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+    __shared__ int last;
+    const int nu = min(a.E, a.T * a.k) + a.sh_n;
+    const int gx = a.I / 64, hx = a.H / 64;
+    const int b = blockIdx.x;
+    if (b < gx * nu) {
+        const int ai = b / gx;
+        if (gateup_block<true, kFusedGuStages>(a, b - ai * gx, ai, lds)) {
+            wait_stores();
+            __syncthreads();
+            if (threadIdx.x == 0)
+                __hip_atomic_fetch_add(a.dec_sync + ai * kSyncPad, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    } else {
+        const int d = b - gx * nu;
+        down_block_fused<NST, PACK>(a, d % hx, d / hx, lds, &last);
+    }
+}
+
 // All experts hold at most nl_x (nl_h) tokens when T does; H % 256, I % 256 for the
 // full K-steps (and the 128-row down blocks); K <= 4096 for the 2 KB scale regions.
 bool dec_supported(const ExpertFwdArgs &a)
@@ -331,6 +574,34 @@ hipError_t launch_gateup_dec(const ExpertFwdArgs &a, hipStream_t s)
     const size_t lds = (size_t)a.nl_x * (a.H + 8) * 2 + 16384;
     ps.launch(k_gateup_dec, dim3(a.I / 64, maxU + a.sh_n), dim3(256), lds, a);
     return hipGetLastError();
+}
+
+bool dec_fused_ok(const ExpertFwdArgs &a)
+{
+    return a.dec_sync && dec_supported(a) && a.I / 256 <= 12 && a.H / 64 <= kSyncStripes &&
+           min(a.E, a.T * a.k) + a.sh_n <= kSyncUnits && !a.skip_combine;
+}
+
+template <int NST>
+static hipError_t launch_fused_nst(const ExpertFwdArgs &a, hipStream_t s)
+{
+    const int nu = min(a.E, a.T * a.k) + a.sh_n;
+    const size_t lds_g = (size_t)a.nl_x * (a.H + 8) * 2 + 16384, lds_d = (size_t)a.nl_h * (a.I + 8) * 2 * 2 + 4 * 2048;
+    const dim3 grid((unsigned)((a.I / 64 + a.H / 64) * nu));
+    ProfScope ps(a.prof, PK_GATEUP, s);
+    if (a.T <= 8)
+        ps.launch(k_dec_fused<NST, true>, grid, dim3(256), lds_g > lds_d ? lds_g : lds_d, a);
+    else
+        ps.launch(k_dec_fused<NST, false>, grid, dim3(256), lds_g > lds_d ? lds_g : lds_d, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_dec_fused(const ExpertFwdArgs &a, hipStream_t s)
+{
+    const int nst = a.I / 256;
+    if (nst <= 4) return launch_fused_nst<4>(a, s);
+    if (nst <= 8) return launch_fused_nst<8>(a, s);
+    return launch_fused_nst<12>(a, s);
 }
 
 hipError_t launch_down_dec(const ExpertFwdArgs &a, hipStream_t s)

@@ -418,6 +418,7 @@ hipError_t launch_expert_forward(const ExpertFwdArgs &a, hipStream_t s)
         return err;
     }
     if (dec_supported(a)) {
+        if (dec_fused_ok(a)) return launch_dec_fused(a, s);
         hipError_t err = launch_gateup_dec(a, s);
         if (err == hipSuccess) err = launch_down_dec(a, s);
         if (err == hipSuccess) err = launch_combine(a, s);

@@ -45,7 +45,8 @@ struct Layout {
     // shared experts: their slot rows (forward outputs, backward input-gradient rows) and
     // their dense routing; the rest of their scratch is the routed slots' (n_shared <= k)
     size_t sh_rows, sh_ids, sh_w, sh_off, sh_perm, sh_inv, sh_act, sh_nact, sh_h;
-    size_t status;  // MOE_F_VALIDATE: the device status word
+    size_t status;    // the device status word (MOE_F_VALIDATE findings, internal timeouts)
+    size_t dec_sync;  // counters of the fused few-token launch (zero between launches)
     size_t total;
 };
 
@@ -95,7 +96,8 @@ Layout layout_of(const moe_desc &d)
     L.sh_act = take(NS * 4);
     L.sh_nact = take(NS ? 4 : 0);
     L.sh_h = take(std::min<size_t>(T, 16) * NS * I * 4);  // h planes of the shared units of the few-token launch
-    L.status = take((d.flags & MOE_F_VALIDATE) ? 4 : 0);
+    L.status = take(4);
+    L.dec_sync = take((size_t)moe::kSyncWords * 4);
     L.total = off;
     return L;
 }
@@ -147,7 +149,8 @@ struct moe_layer {
     moe::Prof prof;
     bool has_lora = false;
     moe::LoraW lora{};
-    bool status_armed = false;  // MOE_F_VALIDATE: the status word has been cleared once
+    bool status_armed = false;  // the status word has been cleared once
+    bool sync_armed = false;    // the fused launch's counters have been cleared once
 };
 
 namespace {
@@ -258,6 +261,7 @@ std::string bad_bits_text(uint32_t b)
     std::string t;
     for (int i = 0; i < 5; i++)
         if ((b >> i) & 1u) t += (t.empty() ? "" : ", ") + std::string(names[i]);
+    if (b & moe::kStatusSpinTimeout) t += (t.empty() ? "" : ", ") + std::string("a fused decode launch gave up waiting (internal)");
     return t;
 }
 
@@ -277,6 +281,8 @@ moe_status take_status(moe_layer *L, hipStream_t s, uint32_t *bits_out)
         if (st != MOE_OK) return st;
         L->status_armed = true;
     }
+    if (bits & moe::kStatusSpinTimeout)
+        return fail(MOE_ERR_INTERNAL, "an earlier call failed on the device: %s", bad_bits_text(bits).c_str());
     if (bits) return fail(MOE_ERR_DATA, "out-of-contract data found by an earlier call: %s", bad_bits_text(bits).c_str());
     return MOE_OK;
 }
@@ -432,22 +438,14 @@ moe_status moe_route(moe_layer *L, const void *x, int32_t xt, int32_t T, const m
     return device_status(moe::launch_group(gq, s), "group");
 }
 
-moe_status moe_forward(moe_layer *L, const void *x, int32_t xt, int32_t T, const moe_routing *r, float *y,
-                       float *saved_gu, void *stream)
+}  // extern "C"
+
+namespace {
+
+// Kernel arguments of the routed forward common to every entry point: weights, shapes,
+// routing, output, activation; the scratch pointers are the caller's to fill.
+moe::ExpertFwdArgs routed_fwd_args(moe_layer *L, const void *x, int32_t xt, int32_t T, const moe_routing *r, float *y)
 {
-    g_last_error.clear();
-    moe_status st;
-    if ((st = check_layer(L)) != MOE_OK || (st = check_tokens(L, T)) != MOE_OK || (st = check_dtype(xt, "x")) != MOE_OK)
-        return st;
-    if (T == 0) return MOE_OK;
-    if ((st = check_routing(r)) != MOE_OK) return st;
-    if (!x || !y) return fail(MOE_ERR_INVALID_ARG, "x or y is NULL");
-    if (!aligned(x, 16) || !aligned(y, 16)) return fail(MOE_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
-    if (saved_gu && !aligned(saved_gu, 16)) return fail(MOE_ERR_INVALID_ARG, "saved_gu must be 16-byte aligned");
-    if (validating(L)) {
-        if ((st = take_status(L, (hipStream_t)stream, nullptr)) != MOE_OK) return st;
-        if ((st = check_weights(L, r, T, (hipStream_t)stream)) != MOE_OK) return st;
-    }
     moe::ExpertFwdArgs a{};
     a.wfmt = L->d.wfmt;
     a.gate = matw(L->w, 0);
@@ -465,18 +463,54 @@ moe_status moe_forward(moe_layer *L, const void *x, int32_t xt, int32_t T, const
     a.active = r->active;
     a.n_active = r->n_active;
     a.w = r->w;
+    a.y = y;
+    a.act = L->d.act;
+    a.prof = &L->prof;
+    return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_forward(moe_layer *L, const void *x, int32_t xt, int32_t T, const moe_routing *r, float *y,
+                       float *saved_gu, void *stream)
+{
+    g_last_error.clear();
+    moe_status st;
+    if ((st = check_layer(L)) != MOE_OK || (st = check_tokens(L, T)) != MOE_OK || (st = check_dtype(xt, "x")) != MOE_OK)
+        return st;
+    if (T == 0) return MOE_OK;
+    if ((st = check_routing(r)) != MOE_OK) return st;
+    if (!x || !y) return fail(MOE_ERR_INVALID_ARG, "x or y is NULL");
+    if (!aligned(x, 16) || !aligned(y, 16)) return fail(MOE_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
+    if (saved_gu && !aligned(saved_gu, 16)) return fail(MOE_ERR_INVALID_ARG, "saved_gu must be 16-byte aligned");
+    if (validating(L)) {
+        if ((st = take_status(L, (hipStream_t)stream, nullptr)) != MOE_OK) return st;
+        if ((st = check_weights(L, r, T, (hipStream_t)stream)) != MOE_OK) return st;
+    }
+    moe::ExpertFwdArgs a = routed_fwd_args(L, x, xt, T, r, y);
     a.h_hi = (uint16_t *)(L->ws + L->lay.h);
     a.h_lo = a.h_hi + (size_t)T * a.k * a.I;
     a.gu = saved_gu;
     a.ybuf = (float *)(L->ws + L->lay.ybuf);
-    a.y = y;
-    a.act = L->d.act;
     if (L->d.flags & MOE_F_MX_GATEUP) {
         a.xq = (uint8_t *)(L->ws + L->lay.xq);
         a.xq_s = (uint8_t *)(L->ws + L->lay.xqs);
     }
-    a.prof = &L->prof;
     const hipStream_t hs = (hipStream_t)stream;
+    a.dec_sync = (uint32_t *)(L->ws + L->lay.dec_sync);
+    a.status = status_word(L);
+    if (!L->sync_armed || !L->status_armed) {
+        // the first forward on a layer clears the counters of the fused few-token launch
+        // (which keep themselves at zero afterwards) and the status word
+        if ((st = device_status(moe::fill_zero((float *)a.dec_sync, moe::kSyncWords, hs), "clearing counters")) != MOE_OK)
+            return st;
+        if (!L->status_armed &&
+            (st = device_status(moe::launch_set_u32(a.status, 0u, hs), "clearing the status word")) != MOE_OK)
+            return st;
+        L->sync_armed = L->status_armed = true;
+    }
     if (L->d.flags & MOE_F_QUANT_X8) {
         // the experts (and the adapter) see x quantized to MXFP8; the routing came from x
         uint16_t *xq = (uint16_t *)(L->ws + L->lay.xq8);

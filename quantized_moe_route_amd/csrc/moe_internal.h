@@ -114,7 +114,19 @@ struct ExpertFwdArgs {
     MatW sh_gate, sh_up, sh_down;
     uint16_t *sh_h_hi, *sh_h_lo;
     float *sh_ybuf;
+    // Counters of the fused decode launch (kSyncWords, zero between launches; null: the
+    // three-launch path) and the status word its bounded waits report a timeout into.
+    uint32_t *dec_sync;
+    uint32_t *status;
 };
+
+// Counter layout of the fused decode launch: per-unit gate/up completions, per-stripe down
+// arrivals, completed stripes; each counter on its own 128-byte line (kSyncPad words).
+constexpr int kSyncUnits = 1152;  // >= min(E, 16 k) + n_shared for the few-token path (k <= 64)
+constexpr int kSyncStripes = 64;  // >= H / 64
+constexpr int kSyncPad = 32;
+constexpr int kSyncWords = (kSyncUnits + kSyncStripes + 1) * kSyncPad;
+constexpr uint32_t kStatusSpinTimeout = 0x80000000u;  // status-word bit: a fused launch gave up waiting
 
 struct ExpertBwdArgs {
     Prof *prof;
@@ -181,6 +193,9 @@ hipError_t launch_down_mm(const ExpertFwdArgs &a, hipStream_t s);
 bool dec_supported(const ExpertFwdArgs &a);
 hipError_t launch_gateup_dec(const ExpertFwdArgs &a, hipStream_t s);
 hipError_t launch_down_dec(const ExpertFwdArgs &a, hipStream_t s);
+// gate/up, down and combine of the few-token path in one launch (expert_dec.hip)
+bool dec_fused_ok(const ExpertFwdArgs &a);
+hipError_t launch_dec_fused(const ExpertFwdArgs &a, hipStream_t s);
 // Few-token RVQ3 kernels (expert_rvq.hip): codeword gathers as fp16 MFMA operands.
 bool rvq_dec_supported(const ExpertFwdArgs &a);
 hipError_t launch_gateup_rvq(const ExpertFwdArgs &a, hipStream_t s);

@@ -58,11 +58,15 @@ def run_small(c, T=None, saved=True, name="", flags=0):
             _sync()
             e = rel_err(_np(dx), dx_ref)
             log(f"  dX rel err {e:.3e} (saved_gu={'yes' if g is not None else 'no'})")
-            assert e <= TOL, f"{name}: dX rel err {e}"
+            # g, u saved by the block-scaled gate/up carry its summation deviation: the bound
+            # include/moe.h states for MOE_F_MX_GATEUP; recomputed ones are exact
+            bound = MX_SAVED_BOUND if g is not None and flags & 2 else TOL
+            assert e <= bound, f"{name}: dX rel err {e}"
     return L, x, r, y
 
 
 TINY = syn.WORKLOADS["tiny"]
+MX_SAVED_BOUND = 7e-4  # dX from the g, u a MOE_F_MX_GATEUP forward saved (include/moe.h)
 
 
 def test_tiny_config_full():
@@ -176,7 +180,7 @@ def test_block_scaled_gateup_wide_x_range_deviation():
             f"(recomputed), {errs[name][2]:.3e} (from the saved g, u)")
     assert max(errs["bf16"]) <= TOL
     assert errs["mx"][0] <= TOL and errs["mx"][1] <= TOL
-    assert errs["mx"][2] <= 7e-4  # the bound include/moe.h states for MOE_F_MX_GATEUP's saved g, u
+    assert errs["mx"][2] <= MX_SAVED_BOUND
 
 
 def _scale_x(c, e):

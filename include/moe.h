@@ -268,6 +268,21 @@ moe_status moe_backward_lora(moe_layer *L, const void *x, int32_t xt, const void
                              const moe_routing *r, const float *saved_gu, float *dx, float *const dA[3],
                              float *const dB[3], void *stream);
 
+/* moe_forward() with saved_gu = NULL, for callers that cannot allocate device memory:
+ * code under HIP graph capture, serving loops that must not call the allocator, harnesses
+ * that forbid it.  Same arguments, semantics and results (the same kernels); the scratch the
+ * kernels use (h, the weighted slot rows, counters) is not the layer's workspace but one
+ * array of 32 MiB compiled into the library, one copy per GPU, held until the process ends.
+ * The call allocates nothing and calls no allocating routine; it clears that array's
+ * counters with a fill kernel on `stream` (no memset).  Limits: T k (4 I + 4 H) bytes plus
+ * ~157 KB must fit in 32 MiB (K3 shape: T <= 78 at k = 16), else MOE_ERR_WORKSPACE and
+ * nothing is enqueued; layers with shared experts, an attached adapter, MOE_F_MX_GATEUP,
+ * MOE_F_QUANT_X8 or MOE_F_VALIDATE give MOE_ERR_UNSUPPORTED.  Every call on one GPU uses the
+ * same array: calls that overlap on one GPU (other streams, other threads, other layers)
+ * race and give wrong results; serialize them. */
+moe_status moe_forward_static(moe_layer *L, const void *x, int32_t xt, int32_t T, const moe_routing *r, float *y,
+                              void *stream);
+
 /* MOE_F_VALIDATE: synchronize stream, return the device status word in *bits (MOE_BAD_*)
  * and clear it.  MOE_ERR_DATA if it was nonzero, MOE_OK if zero; MOE_ERR_INVALID_ARG for
  * a NULL argument or a layer created without MOE_F_VALIDATE. */

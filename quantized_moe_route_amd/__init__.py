@@ -162,6 +162,19 @@ class MoELayer:
                                     _ptr(saved_gu), _stream()), "moe_forward")
         return y
 
+    def forward_static(self, x, routing: Routing, y=None):
+        """moe_forward_static: the forward with the library's own per-GPU scratch (no
+        workspace, no allocation by the library; y must be preallocated for an
+        allocation-free call)."""
+        torch = _torch()
+        T = x.shape[0]
+        if y is None:
+            y = torch.empty((T, self.H), dtype=torch.float32, device=self.device)
+        rs = routing.c_struct()
+        C.check(C.lib().moe_forward_static(self._h, x.data_ptr(), _dtype_code(x), T, ctypes.byref(rs), y.data_ptr(),
+                                           _stream()), "moe_forward_static")
+        return y
+
     def backward_input(self, x, dy, routing: Routing, saved_gu=None, dx=None):
         torch = _torch()
         T = x.shape[0]

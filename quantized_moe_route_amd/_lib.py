@@ -23,7 +23,7 @@ MOE_BAD_X, MOE_BAD_DY, MOE_BAD_SCALE_NAN, MOE_BAD_SCALE_ZERO, MOE_BAD_CODEWORD =
 EXPORTED = (
     "moe_desc_init", "moe_workspace_size", "moe_layer_create", "moe_route", "moe_forward",
     "moe_backward_input", "moe_destroy", "moe_status_string", "moe_last_error",
-    "moe_set_lora", "moe_backward_lora", "moe_check_status", "moe_prof_enable", "moe_prof_read", "moe_prof_hbm_read",
+    "moe_set_lora", "moe_backward_lora", "moe_check_status", "moe_forward_static", "moe_prof_enable", "moe_prof_read", "moe_prof_hbm_read",
 )
 
 # kernel families of include/moe_prof.h
@@ -92,6 +92,8 @@ def lib() -> ctypes.CDLL:
         L.moe_backward_lora.argtypes = [vp, vp, i32, vp, i32, i32, ctypes.POINTER(MoeRouting), vp, vp,
                                         ctypes.POINTER(vp), ctypes.POINTER(vp), vp]
         L.moe_backward_lora.restype = st
+        L.moe_forward_static.argtypes = [vp, vp, i32, i32, ctypes.POINTER(MoeRouting), vp, vp]
+        L.moe_forward_static.restype = st
         L.moe_check_status.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), vp]
         L.moe_check_status.restype = st
         L.moe_destroy.argtypes = [vp]

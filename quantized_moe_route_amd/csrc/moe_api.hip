@@ -11,6 +11,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 
@@ -440,6 +441,64 @@ moe_status moe_route(moe_layer *L, const void *x, int32_t xt, int32_t T, const m
 
 }  // extern "C"
 
+// ---------------------------------------------------------------------------------------
+// Scratch of moe_forward_static: one array per GPU, part of the library's code object, so
+// that call allocates nothing.  Every call on a GPU uses that GPU's copy, which keeps the last
+// call's contents; calls that overlap on one GPU race on it.
+constexpr size_t kStaticScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device, once looked up
+
+// The device address of the current device's copy of `scratch`, looked up once per device
+// with that device current (in host code the array's name is only a stand-in for it).
+moe_status static_scratch(char **out)
+{
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return device_status(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(MOE_ERR_UNSUPPORTED, "device %d is beyond the %d tracked", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return device_status(e, "hipGetSymbolAddress(scratch)");
+        g_scratch_ptr[dev] = p;
+    }
+    *out = (char *)g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
+// Carving of `scratch` for T tokens: status word, counters of the fused few-token launch,
+// h as bf16 hi + lo planes [S][I], weighted slot rows [S][H] fp32 (S = T k).
+struct StaticLayout {
+    size_t status, sync, h, ybuf, total;
+};
+
+StaticLayout static_layout(const moe_desc &d, int T)
+{
+    StaticLayout l{};
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = off;
+        off += align256(bytes);
+        return at;
+    };
+    const size_t S = (size_t)T * d.top_k;
+    l.status = take(4);
+    l.sync = take((size_t)moe::kSyncWords * 4);
+    l.h = take(S * d.inter * 4);
+    l.ybuf = take(S * d.hidden * 4);
+    l.total = off;
+    return l;
+}
+
+}  // namespace
+
 namespace {
 
 // Kernel arguments of the routed forward common to every entry point: weights, shapes,
@@ -742,6 +801,43 @@ moe_status moe_set_lora(moe_layer *L, const moe_lora *lora)
 }
 
 
+
+moe_status moe_forward_static(moe_layer *L, const void *x, int32_t xt, int32_t T, const moe_routing *r, float *y,
+                              void *stream)
+{
+    g_last_error.clear();
+    moe_status st;
+    if ((st = check_layer(L)) != MOE_OK || (st = check_tokens(L, T)) != MOE_OK || (st = check_dtype(xt, "x")) != MOE_OK)
+        return st;
+    if (L->d.n_shared || L->has_lora || (L->d.flags & (MOE_F_MX_GATEUP | MOE_F_QUANT_X8 | MOE_F_VALIDATE)))
+        return fail(MOE_ERR_UNSUPPORTED,
+                    "moe_forward_static serves the routed layer without shared experts, an attached adapter, "
+                    "MOE_F_MX_GATEUP, MOE_F_QUANT_X8 or MOE_F_VALIDATE");
+    const StaticLayout sl = static_layout(L->d, T);
+    if (sl.total > kStaticScratchBytes)
+        return fail(MOE_ERR_WORKSPACE, "T=%d needs %zu bytes of scratch; moe_forward_static has %zu", T, sl.total,
+                    kStaticScratchBytes);
+    if (T == 0) return MOE_OK;
+    if ((st = check_routing(r)) != MOE_OK) return st;
+    if (!x || !y) return fail(MOE_ERR_INVALID_ARG, "x or y is NULL");
+    if (!aligned(x, 16) || !aligned(y, 16)) return fail(MOE_ERR_INVALID_ARG, "x and y must be 16-byte aligned");
+    char *base = nullptr;
+    if ((st = static_scratch(&base)) != MOE_OK) return st;
+    const hipStream_t hs = (hipStream_t)stream;
+    moe::ExpertFwdArgs a = routed_fwd_args(L, x, xt, T, r, y);
+    a.h_hi = (uint16_t *)(base + sl.h);
+    a.h_lo = a.h_hi + (size_t)T * a.k * a.I;
+    a.ybuf = (float *)(base + sl.ybuf);
+    a.status = (uint32_t *)(base + sl.status);
+    a.dec_sync = (uint32_t *)(base + sl.sync);
+    // the array keeps the previous call's contents: the status word and the counters of the
+    // fused launch must start at zero (a fill kernel, no memset node under graph capture)
+    if ((st = device_status(moe::fill_zero((float *)(base + sl.status), (sl.h - sl.status) / 4, hs),
+                            "clearing the static scratch")) != MOE_OK)
+        return st;
+    moe::set_lds_staging(a);
+    return device_status(moe::launch_expert_forward(a, hs), "forward (static scratch)");
+}
 
 moe_status moe_check_status(moe_layer *L, uint32_t *bits, void *stream)
 {

@@ -274,3 +274,24 @@ def test_validate_argument_checks():
     assert L.moe_status_string(C.MOE_ERR_DATA) == b"out-of-contract data"
     L.moe_destroy(h)
 
+
+def test_static_forward_argument_checks():
+    """moe_forward_static refuses, before touching the device, token counts whose scratch
+    exceeds its 32 MiB array and layers it does not serve."""
+    L = C.lib()
+    st, h = _create(_desc(max_tokens=4096), _fake_weights())
+    assert st == C.MOE_OK
+    r = C.MoeRouting()
+    for i, n in enumerate(("ids", "w", "counts", "offsets", "perm", "inv", "active", "n_active")):
+        setattr(r, n, 0x40000 + 256 * i)
+    x, y = 0x50000, 0x60000
+    # K3 shape: 26,624 bytes per slot, 16 slots per token: 79 tokens no longer fit
+    assert L.moe_forward_static(h, x, C.MOE_DT_BF16, 79, ctypes.byref(r), y, None) == C.MOE_ERR_WORKSPACE
+    assert b"32" in L.moe_last_error() or b"33554432" in L.moe_last_error()
+    assert L.moe_forward_static(h, x, C.MOE_DT_BF16, 1, None, y, None) == C.MOE_ERR_INVALID_ARG
+    assert L.moe_forward_static(h, x, C.MOE_DT_BF16, 1, ctypes.byref(r), y + 4, None) == C.MOE_ERR_INVALID_ARG
+    assert L.moe_forward_static(h, None, C.MOE_DT_BF16, 0, ctypes.byref(r), None, None) == C.MOE_OK
+    L.moe_destroy(h)
+    st, h = _create(_desc(max_tokens=8, flags=C.MOE_F_QUANT_X8), _fake_weights())
+    assert L.moe_forward_static(h, x, C.MOE_DT_BF16, 1, ctypes.byref(r), y, None) == C.MOE_ERR_UNSUPPORTED
+    L.moe_destroy(h)

@@ -135,6 +135,9 @@ typedef struct {
                             shared experts in each MoE layer).  Same shape, format and activation as
                             a routed expert; their outputs are added to y, their input gradient to
                             dx; they get no router term and no adapter.  Default 0. */
+    int32_t model_width; /* D: width of the model around the MoE's latent space, 0 = none (default).
+                            With D > 0 the layer also holds the latent in/out projections
+                            (moe_project_in/out below); D and H multiples of 64. */
 } moe_desc;
 
 /* Expert and router weights: BORROWED device pointers.  The caller keeps
@@ -169,6 +172,10 @@ typedef struct {
     const uint8_t *shared_scales[3];
     const uint8_t *shared_rvq_idx[3];
     const uint16_t *shared_rvq_cb[3];
+    /* latent projections (model_width D > 0; NULL otherwise): bf16 bit patterns, 16-byte
+       aligned, proj_in [H][D] (model -> latent), proj_out [D][H] (latent -> model) */
+    const uint16_t *proj_in;
+    const uint16_t *proj_out;
 } moe_weights;
 
 /* Routing record, caller-owned device buffers written by moe_route() and
@@ -234,6 +241,27 @@ moe_status moe_forward(moe_layer *L, const void *x, int32_t xt, int32_t T, const
  * inputs, or NULL to recompute it. */
 moe_status moe_backward_input(moe_layer *L, const void *x, int32_t xt, const void *dy, int32_t dyt, int32_t T,
                               const moe_routing *r, const float *saved_gu, float *dx, void *stream);
+
+/* Latent projections (LazyLoRA README, "The engine": the latent MoE projections are dense
+ * weights beside the router gates; Two Desks, Act II: the experts run in a latent space of
+ * width 3,584).  The layer's input and output live in the model width D; the router, the
+ * routed and the shared experts work in the latent width H:
+ *   x_latent = x_model proj_in^T   -> moe_route / moe_forward on x_latent -> y_latent
+ *   out      = y_latent proj_out^T
+ * and the input gradient runs the chain backwards (moe_project_out_backward, then
+ * moe_backward_input with dy = its result, then moe_project_in_backward).  Products of the
+ * bf16 weights with bf16 or fp32 activations (fp32 carried exactly), fp32 accumulation,
+ * fp32 results; all buffers caller-owned device memory, 16-byte aligned.  Errors as for the
+ * other calls; MOE_ERR_INVALID_ARG if the layer has no projections (model_width = 0).
+ *   moe_project_in           x_model [T][D] (dtype xt) -> x_latent [T][H] fp32
+ *   moe_project_out          y_latent [T][H] fp32      -> out [T][D] fp32
+ *   moe_project_out_backward dout [T][D] (dtype dt)    -> dy_latent [T][H] fp32 = dout proj_out
+ *   moe_project_in_backward  dx_latent [T][H] fp32     -> dx_model [T][D] fp32 = dx_latent proj_in */
+moe_status moe_project_in(moe_layer *L, const void *x_model, int32_t xt, int32_t T, float *x_latent, void *stream);
+moe_status moe_project_out(moe_layer *L, const float *y_latent, int32_t T, float *out, void *stream);
+moe_status moe_project_out_backward(moe_layer *L, const void *dout, int32_t dt, int32_t T, float *dy_latent,
+                                    void *stream);
+moe_status moe_project_in_backward(moe_layer *L, const float *dx_latent, int32_t T, float *dx_model, void *stream);
 
 /* Shared low-rank adapter on the routed experts (LazyLoRA README, "LoRA": one
  * adapter per MoE layer in the latent space, shared by every routed expert, on

@@ -29,6 +29,7 @@ _T_X, _T_WR, _T_BIAS, _T_DY = 1, 2, 3, 4
 _T_CODES, _T_SCALES = 10, 20          # + matrix index (0 gate, 1 up, 2 down)
 _T_RVQ_IDX, _T_RVQ_CB = 30, 40        # + matrix index
 _T_LORA_A, _T_LORA_B = 50, 60         # + matrix index
+_T_PROJ_IN, _T_PROJ_OUT, _T_XM, _T_DOUT = 70, 71, 72, 73  # latent projections, model-width x and dout
 
 # family ids: the K3-shaped MXFP4 layer is shared by the three MXFP4 K3 workloads
 FAMILY_TINY, FAMILY_K3_MXFP4, FAMILY_K3_RVQ = 1, 2, 4
@@ -197,3 +198,30 @@ def shared_experts(w: Workload, n: int = 2):
 def shrink(w: Workload, **kw) -> Workload:
     """A workload with some fields replaced (used by tests for reduced sizes)."""
     return dataclasses.replace(w, **kw)
+
+
+# K3's model width around the 3,584-wide latent space is not on the pages; this stands in for it
+# (twice the latent width) where a K3-shaped test needs one.
+K3_MODEL_WIDTH_ASSUMED = 7168
+
+
+def latent_projections(w: Workload, D: int):
+    """proj_in [H][D] and proj_out [D][H] as bf16 bit patterns: N(0, 1/in_width), so the
+    projected activations keep unit scale."""
+    pin = _rng(w.family, _T_PROJ_IN, D).standard_normal((w.H, D), dtype=np.float32) * np.float32(1.0 / np.sqrt(D))
+    pout = _rng(w.family, _T_PROJ_OUT, D).standard_normal((D, w.H), dtype=np.float32) * np.float32(1.0 / np.sqrt(w.H))
+    return f32_to_bf16_bits(pin), f32_to_bf16_bits(pout)
+
+
+def model_activations(w: Workload, D: int, T: Optional[int] = None) -> np.ndarray:
+    """x_model [T][D]: N(0,1) rounded to bf16 bits (fp32 for the fp32-activation workload)."""
+    T = w.T if T is None else T
+    x = _rng(w.family, _T_XM, w.x_key).standard_normal((T, D), dtype=np.float32)
+    return x if w.x_dtype == "f32" else f32_to_bf16_bits(x)
+
+
+def model_upstream_grad(w: Workload, D: int, T: Optional[int] = None) -> np.ndarray:
+    """dout [T][D]: N(0, 0.01^2) rounded to bf16 bits (fp32 for the fp32-activation workload)."""
+    T = w.T if T is None else T
+    d = _rng(w.family, _T_DOUT, w.x_key).standard_normal((T, D), dtype=np.float32) * np.float32(0.01)
+    return d if w.x_dtype == "f32" else f32_to_bf16_bits(d)

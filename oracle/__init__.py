@@ -82,6 +82,7 @@ def lib():
         L.oracle_forward.argtypes = [i, i, i, i, vp, vp, vp, vp, vp, i]
         L.oracle_backward_input.argtypes = [i, i, i, i, vp, vp, vp, vp, vp, vp, vp, i]
         L.oracle_lora_grads.argtypes = [i, i, i, i, vp, vp, vp, vp, vp, vp * 3, vp * 3, i]
+        L.oracle_dense.argtypes = [i, i, i, vp, vp, vp, i, i]
         _lib = L
     return _lib
 
@@ -323,6 +324,18 @@ def lora_grads(x64, dy64, ids, w, W: Weights, nthreads=None):
                             vp3(*[a.ctypes.data for a in dA]), vp3(*[b.ctypes.data for b in dB]),
                             nthreads or default_threads())
     return dA, dB
+
+
+def dense(a64: np.ndarray, w_bits: np.ndarray, transposed: bool = False, nthreads=None) -> np.ndarray:
+    """Latent projection with bf16 weights w [N][K] (uint16 bits): a [T][K] -> a w^T [T][N], or
+    with transposed a [T][N] -> a w [T][K]."""
+    a64 = np.ascontiguousarray(a64, np.float64)
+    w_bits = np.ascontiguousarray(w_bits, np.uint16)
+    N, K = w_bits.shape
+    T = a64.shape[0]
+    out = np.zeros((T, K if transposed else N))
+    lib().oracle_dense(T, N, K, _p(a64), _p(w_bits), _p(out), int(transposed), nthreads or default_threads())
+    return out
 
 
 def layer_forward(x64, wr, bias, k, W: Weights, nthreads=None, bias_mode=1):

@@ -638,3 +638,47 @@ void oracle_lora_grads(int T, int H, int I, int k, const double *x, const double
     free(dp);
     free(keep);
 }
+
+/* ------------------------------------------------------------------ */
+/* latent projections (dense bf16 matrices around the MoE)             */
+/* ------------------------------------------------------------------ */
+
+/* LazyLoRA README, "The engine": the latent MoE projections sit beside the
+ * router gates among the dense (non-expert) weights; Two Desks, Act II: the
+ * experts run in a latent space of width 3,584.  A projection is a plain
+ * matrix product with bf16 weights w stored [N][K] (K contiguous):
+ *   forward     out[t][n] = sum_k a[t][k] w[n][k]      (T x N)
+ *   transposed  out[t][k] = sum_n a[t][n] w[n][k]      (T x K)
+ * in fp64, each sum taken sequentially in index order. */
+typedef struct { int T, N, K, transposed; const double *a; const uint16_t *w; double *out; } dense_ctx;
+
+static double bf16_value(uint16_t b)
+{
+    union { uint32_t u; float f; } v;
+    v.u = (uint32_t)b << 16;
+    return (double)v.f;
+}
+
+static void dense_row(void *vctx, long t)
+{
+    const dense_ctx *c = (const dense_ctx *)vctx;
+    if (!c->transposed) {
+        for (int n = 0; n < c->N; n++) {
+            double s = 0.0;
+            for (int k = 0; k < c->K; k++) s += c->a[(size_t)t * c->K + k] * bf16_value(c->w[(size_t)n * c->K + k]);
+            c->out[(size_t)t * c->N + n] = s;
+        }
+    } else {
+        for (int k = 0; k < c->K; k++) {
+            double s = 0.0;
+            for (int n = 0; n < c->N; n++) s += c->a[(size_t)t * c->N + n] * bf16_value(c->w[(size_t)n * c->K + k]);
+            c->out[(size_t)t * c->K + k] = s;
+        }
+    }
+}
+
+void oracle_dense(int T, int N, int K, const double *a, const uint16_t *w, double *out, int transposed, int nthreads)
+{
+    dense_ctx c = {T, N, K, transposed, a, w, out};
+    parallel_for(T, nthreads, dense_row, &c);
+}

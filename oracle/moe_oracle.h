@@ -55,4 +55,7 @@ void oracle_backward_input(int T, int H, int I, int k, const double *x, const do
  * (same layouts as oracle_lora), routing held fixed.  W->lora must be set. */
 void oracle_lora_grads(int T, int H, int I, int k, const double *x, const double *dy, const int32_t *ids,
                        const double *w, const oracle_weights *W, double *dA[3], double *dB[3], int nthreads);
+/* Latent projection with bf16 weights w [N][K]: out [T][N] = a [T][K] w^T, or with
+ * transposed != 0 out [T][K] = a [T][N] w. */
+void oracle_dense(int T, int N, int K, const double *a, const uint16_t *w, double *out, int transposed, int nthreads);
 #endif

@@ -85,14 +85,15 @@ class MoELayer:
     router_w: [E][H] fp32; router_b: [E] fp32 or None.  bias_mode: 1 (default with a bias) adds
     the bias to the logits, 2 uses it for the selection only.  Shared experts (taken by every
     token with weight 1): shared=[gate, up, down] in the routed experts' format with n_shared in
-    place of E (MXFP4: a pair (codes, scales) of such lists; RVQ3: (rvq_idx, rvq_cb)).  All tensors
-    on the same GPU and kept alive by this object.
+    place of E (MXFP4: a pair (codes, scales) of such lists; RVQ3: (rvq_idx, rvq_cb)).  Latent
+    projections: proj=(proj_in [H][D], proj_out [D][H]) bf16 (uint16 bits or torch.bfloat16), D the
+    model width.  All tensors on the same GPU and kept alive by this object.
     """
 
     def __init__(self, *, hidden: int, inter: int, n_experts: int, top_k: int, max_tokens: int, router_w,
                  router_b=None, codes: Optional[Sequence] = None, scales: Optional[Sequence] = None,
                  rvq_idx: Optional[Sequence] = None, rvq_cb: Optional[Sequence] = None, flags: int = 0,
-                 act: int = 0, bias_mode: Optional[int] = None, shared=None):
+                 act: int = 0, bias_mode: Optional[int] = None, shared=None, proj=None):
         torch = _torch()
         L = C.lib()
         d = C.MoeDesc()
@@ -103,10 +104,12 @@ class MoELayer:
         d.flags |= flags
         d.act = act
         d.n_shared = 0 if shared is None else int(shared[0][0].shape[0])
+        d.model_width = 0 if proj is None else int(proj[0].shape[1])
+        self.D = d.model_width
         self.desc = d
         self.H, self.I, self.E, self.k, self.max_tokens = hidden, inter, n_experts, top_k, max_tokens
         self.device = router_w.device
-        self._keep = [router_w, router_b, codes, scales, rvq_idx, rvq_cb, shared]
+        self._keep = [router_w, router_b, codes, scales, rvq_idx, rvq_cb, shared, proj]
         self._lora = None
         w = C.MoeWeights()
         w.router_w = router_w.data_ptr()
@@ -124,6 +127,8 @@ class MoELayer:
             elif shared is not None:
                 w.shared_rvq_idx[m] = shared[0][m].data_ptr()
                 w.shared_rvq_cb[m] = shared[1][m].data_ptr()
+        if proj is not None:
+            w.proj_in, w.proj_out = proj[0].data_ptr(), proj[1].data_ptr()
         self.weights = w
         nbytes = ctypes.c_size_t()
         C.check(L.moe_workspace_size(ctypes.byref(d), ctypes.byref(nbytes)), "moe_workspace_size")
@@ -218,6 +223,32 @@ class MoELayer:
                                           vp3(*[a.data_ptr() for a in dA]), vp3(*[b.data_ptr() for b in dB]),
                                           _stream()), "moe_backward_lora")
         return dx, dA, dB
+
+    def _project(self, fn, a, T, width, dtype=None):
+        torch = _torch()
+        out = torch.empty((T, width), dtype=torch.float32, device=self.device)
+        L = C.lib()
+        if dtype is None:
+            C.check(getattr(L, fn)(self._h, a.data_ptr(), T, out.data_ptr(), _stream()), fn)
+        else:
+            C.check(getattr(L, fn)(self._h, a.data_ptr(), dtype, T, out.data_ptr(), _stream()), fn)
+        return out
+
+    def project_in(self, x_model):
+        """Latent input x_model proj_in^T [T][H] fp32 (x_model [T][D] bf16 or fp32)."""
+        return self._project("moe_project_in", x_model, x_model.shape[0], self.H, _dtype_code(x_model))
+
+    def project_out(self, y_latent):
+        """Model-width output y_latent proj_out^T [T][D] fp32 (y_latent [T][H] fp32)."""
+        return self._project("moe_project_out", y_latent, y_latent.shape[0], self.D)
+
+    def project_out_backward(self, dout):
+        """dy_latent = dout proj_out [T][H] fp32 (dout [T][D] bf16 or fp32)."""
+        return self._project("moe_project_out_backward", dout, dout.shape[0], self.H, _dtype_code(dout))
+
+    def project_in_backward(self, dx_latent):
+        """dx_model = dx_latent proj_in [T][D] fp32 (dx_latent [T][H] fp32)."""
+        return self._project("moe_project_in_backward", dx_latent, dx_latent.shape[0], self.D)
 
     def check_status(self) -> int:
         """MOE_F_VALIDATE: synchronize, return and clear the device status word (MOE_BAD_* bits);

@@ -23,7 +23,8 @@ MOE_BAD_X, MOE_BAD_DY, MOE_BAD_SCALE_NAN, MOE_BAD_SCALE_ZERO, MOE_BAD_CODEWORD =
 EXPORTED = (
     "moe_desc_init", "moe_workspace_size", "moe_layer_create", "moe_route", "moe_forward",
     "moe_backward_input", "moe_destroy", "moe_status_string", "moe_last_error",
-    "moe_set_lora", "moe_backward_lora", "moe_check_status", "moe_forward_static", "moe_prof_enable", "moe_prof_read", "moe_prof_hbm_read",
+    "moe_set_lora", "moe_backward_lora", "moe_check_status", "moe_forward_static",
+    "moe_project_in", "moe_project_out", "moe_project_out_backward", "moe_project_in_backward", "moe_prof_enable", "moe_prof_read", "moe_prof_hbm_read",
 )
 
 # kernel families of include/moe_prof.h
@@ -37,7 +38,7 @@ class MoeDesc(ctypes.Structure):
     _fields_ = [("hidden", ctypes.c_int32), ("inter", ctypes.c_int32), ("n_experts", ctypes.c_int32),
                 ("top_k", ctypes.c_int32), ("max_tokens", ctypes.c_int32), ("wfmt", ctypes.c_int32),
                 ("act", ctypes.c_int32), ("bias_mode", ctypes.c_int32), ("flags", ctypes.c_uint32),
-                ("n_shared", ctypes.c_int32)]
+                ("n_shared", ctypes.c_int32), ("model_width", ctypes.c_int32)]
 
 
 class MoeWeights(ctypes.Structure):
@@ -45,7 +46,8 @@ class MoeWeights(ctypes.Structure):
                 ("codes", ctypes.c_void_p * 3), ("scales", ctypes.c_void_p * 3),
                 ("rvq_idx", ctypes.c_void_p * 3), ("rvq_cb", ctypes.c_void_p * 3),
                 ("shared_codes", ctypes.c_void_p * 3), ("shared_scales", ctypes.c_void_p * 3),
-                ("shared_rvq_idx", ctypes.c_void_p * 3), ("shared_rvq_cb", ctypes.c_void_p * 3)]
+                ("shared_rvq_idx", ctypes.c_void_p * 3), ("shared_rvq_cb", ctypes.c_void_p * 3),
+                ("proj_in", ctypes.c_void_p), ("proj_out", ctypes.c_void_p)]
 
 
 class MoeLora(ctypes.Structure):
@@ -94,6 +96,12 @@ def lib() -> ctypes.CDLL:
         L.moe_backward_lora.restype = st
         L.moe_forward_static.argtypes = [vp, vp, i32, i32, ctypes.POINTER(MoeRouting), vp, vp]
         L.moe_forward_static.restype = st
+        for fn in ("moe_project_in", "moe_project_out_backward"):
+            getattr(L, fn).argtypes = [vp, vp, i32, i32, vp, vp]
+            getattr(L, fn).restype = st
+        for fn in ("moe_project_out", "moe_project_in_backward"):
+            getattr(L, fn).argtypes = [vp, vp, i32, vp, vp]
+            getattr(L, fn).restype = st
         L.moe_check_status.argtypes = [vp, ctypes.POINTER(ctypes.c_uint32), vp]
         L.moe_check_status.restype = st
         L.moe_destroy.argtypes = [vp]

@@ -122,6 +122,9 @@ moe_status check_desc(const moe_desc *d)
         return fail(MOE_ERR_UNSUPPORTED, "bias_mode %d is not implemented", d->bias_mode);
     if (d->n_shared < 0 || d->n_shared > d->top_k)
         return fail(MOE_ERR_INVALID_ARG, "n_shared=%d must be in 0..top_k=%d", d->n_shared, d->top_k);
+    if (d->model_width < 0 || d->model_width % 64 || (d->model_width > 0 && d->hidden % 64))
+        return fail(MOE_ERR_INVALID_ARG, "model_width=%d must be 0 or a multiple of 64 (with hidden a multiple of 64)",
+                    d->model_width);
     return MOE_OK;
 }
 
@@ -373,6 +376,11 @@ moe_status moe_layer_create(const moe_desc *d, const moe_weights *w, void *works
             if (!aligned(w->shared_rvq_idx[m], 16) || !aligned(w->shared_rvq_cb[m], 16))
                 return fail(MOE_ERR_INVALID_ARG, "shared %s rvq_idx/rvq_cb must be 16-byte aligned", names[m]);
         }
+    }
+    if (d->model_width > 0) {
+        if (!w->proj_in || !w->proj_out) return fail(MOE_ERR_INVALID_ARG, "model_width > 0 needs proj_in and proj_out");
+        if (!aligned(w->proj_in, 16) || !aligned(w->proj_out, 16))
+            return fail(MOE_ERR_INVALID_ARG, "proj_in and proj_out must be 16-byte aligned");
     }
     const Layout lay = layout_of(*d);
     if (!workspace && lay.total > 0) return fail(MOE_ERR_WORKSPACE, "workspace is NULL");
@@ -837,6 +845,60 @@ moe_status moe_forward_static(moe_layer *L, const void *x, int32_t xt, int32_t T
         return st;
     moe::set_lds_staging(a);
     return device_status(moe::launch_expert_forward(a, hs), "forward (static scratch)");
+}
+
+}  // extern "C"
+
+namespace {
+
+// One latent projection call: argument checks, then the dense product on the stream.
+moe_status project(moe_layer *L, const void *a, int32_t at, int32_t T, float *out, bool in, bool backward, void *stream)
+{
+    g_last_error.clear();
+    moe_status st;
+    if ((st = check_layer(L)) != MOE_OK || (st = check_tokens(L, T)) != MOE_OK || (st = check_dtype(at, "input")) != MOE_OK)
+        return st;
+    if (L->d.model_width <= 0) return fail(MOE_ERR_INVALID_ARG, "the layer has no latent projections (model_width = 0)");
+    if (T == 0) return MOE_OK;
+    if (!a || !out) return fail(MOE_ERR_INVALID_ARG, "input or output is NULL");
+    if (!aligned(a, 16) || !aligned(out, 16)) return fail(MOE_ERR_INVALID_ARG, "input and output must be 16-byte aligned");
+    const int D = L->d.model_width, H = L->d.hidden;
+    // forward in: [T][D] -> [T][H] with proj_in [H][D]; forward out: [T][H] -> [T][D] with
+    // proj_out [D][H]; the backward products take the same matrices untransposed
+    const uint16_t *w = in ? L->w.proj_in : L->w.proj_out;
+    int N, R;
+    if (!backward) {
+        N = in ? H : D;
+        R = in ? D : H;
+    } else {
+        N = in ? D : H;
+        R = in ? H : D;
+    }
+    return device_status(moe::launch_dense(a, at, w, backward, T, N, R, out, (hipStream_t)stream), "latent projection");
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_project_in(moe_layer *L, const void *x_model, int32_t xt, int32_t T, float *x_latent, void *stream)
+{
+    return project(L, x_model, xt, T, x_latent, true, false, stream);
+}
+
+moe_status moe_project_out(moe_layer *L, const float *y_latent, int32_t T, float *out, void *stream)
+{
+    return project(L, y_latent, MOE_DT_F32, T, out, false, false, stream);
+}
+
+moe_status moe_project_out_backward(moe_layer *L, const void *dout, int32_t dt, int32_t T, float *dy_latent, void *stream)
+{
+    return project(L, dout, dt, T, dy_latent, false, true, stream);
+}
+
+moe_status moe_project_in_backward(moe_layer *L, const float *dx_latent, int32_t T, float *dx_model, void *stream)
+{
+    return project(L, dx_latent, MOE_DT_F32, T, dx_model, true, true, stream);
 }
 
 moe_status moe_check_status(moe_layer *L, uint32_t *bits, void *stream)

@@ -254,6 +254,10 @@ hipError_t launch_check_weights(int wfmt, const MatW (&m)[3], const size_t (&sca
                                 const int32_t *n_active, int units, uint32_t *status, hipStream_t s);
 hipError_t launch_set_u32(uint32_t *p, uint32_t v, hipStream_t s);
 
+// Latent projection (dense.hip): out[T][N] = a[T][R] w^T with w [N][R] (nn = false) or
+// a[T][R] w with w [R][N] (nn = true); a bf16 or fp32 (at), w bf16; N % 64 == 0, R % 32 == 0.
+hipError_t launch_dense(const void *a, int at, const uint16_t *w, bool nn, int T, int N, int R, float *out, hipStream_t s);
+
 // number of I-column tiles whose partial <a, h> sums the backward stores per row
 __host__ __device__ inline int dp_tiles(int I) { return (I + 63) / 64; }
 

@@ -87,7 +87,7 @@ def act_tensor(a: np.ndarray, dtype: str):
     return q.bf16_tensor(a) if dtype == "bf16" else q.to_device(np.asarray(a, np.float32))
 
 
-def device_layer(c: HostCase, max_tokens: int, flags: int = 0):
+def device_layer(c: HostCase, max_tokens: int, flags: int = 0, proj=None):
     import quantized_moe_route_amd as q
     w = c.w
     kw = dict(hidden=w.H, inter=w.I, n_experts=w.E, top_k=w.k, max_tokens=max_tokens,
@@ -101,6 +101,8 @@ def device_layer(c: HostCase, max_tokens: int, flags: int = 0):
         kw["rvq_cb"] = [q.to_device(a) for a in c.cb]
     if c.shared is not None:
         kw["shared"] = ([q.to_device(a) for a in c.shared[0]], [q.to_device(a) for a in c.shared[1]])
+    if proj is not None:
+        kw["proj"] = proj
     return q.MoELayer(**kw)
 
 

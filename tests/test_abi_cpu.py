@@ -295,3 +295,29 @@ def test_static_forward_argument_checks():
     st, h = _create(_desc(max_tokens=8, flags=C.MOE_F_QUANT_X8), _fake_weights())
     assert L.moe_forward_static(h, x, C.MOE_DT_BF16, 1, ctypes.byref(r), y, None) == C.MOE_ERR_UNSUPPORTED
     L.moe_destroy(h)
+
+
+def test_latent_projection_argument_checks():
+    """model_width: 0 or a multiple of 64 (with H a multiple of 64); a layer with it needs both
+    projection matrices, 16-byte aligned; projection calls on a layer without them fail."""
+    L = C.lib()
+    n = ctypes.c_size_t()
+    for mw in (-64, 100, 32):
+        assert L.moe_workspace_size(ctypes.byref(_desc(model_width=mw)), ctypes.byref(n)) == C.MOE_ERR_INVALID_ARG
+    assert L.moe_workspace_size(ctypes.byref(_desc(model_width=512, hidden=3552)), ctypes.byref(n)) == C.MOE_ERR_INVALID_ARG
+    d = _desc(max_tokens=8, model_width=7168)
+    assert _create(d, _fake_weights())[0] == C.MOE_ERR_INVALID_ARG  # no projections given
+    w = _fake_weights()
+    w.proj_in, w.proj_out = 0x70000, 0x80008  # proj_out misaligned
+    assert _create(d, w)[0] == C.MOE_ERR_INVALID_ARG
+    w.proj_out = 0x80000
+    st, h = _create(d, w)
+    assert st == C.MOE_OK
+    assert L.moe_project_in(h, None, C.MOE_DT_BF16, 1, 0x90000, None) == C.MOE_ERR_INVALID_ARG
+    assert L.moe_project_out(h, 0x90000, 9, 0xA0000, None) == C.MOE_ERR_INVALID_ARG  # T > max_tokens
+    assert L.moe_project_out(h, None, 0, None, None) == C.MOE_OK  # T = 0
+    L.moe_destroy(h)
+    st, h = _create(_desc(max_tokens=8), _fake_weights())
+    assert L.moe_project_in(h, 0x90000, C.MOE_DT_BF16, 1, 0xA0000, None) == C.MOE_ERR_INVALID_ARG
+    assert b"model_width" in L.moe_last_error()
+    L.moe_destroy(h)

@@ -227,3 +227,21 @@ def test_shared_experts_k3(k3_mxfp4):
             log(f"shared-{name}: dX rel err {e:.3e}")
             assert e <= TOL and np.isfinite(_np(dx)).all()
     Ls.close()
+
+
+def test_latent_projections_k3(k3_mxfp4):
+    """The K3 layer (896 routed experts in the 3,584-wide latent space) inside latent
+    projections of an assumed model width of 7,168 (the pages do not give it): four tokens,
+    forward and input gradient through the whole chain against the oracle."""
+    import quantized_moe_route_amd as q
+    from test_gpu_latent import chain_parity
+    c, L = k3_mxfp4
+    D = syn.K3_MODEL_WIDTH_ASSUMED
+    w = syn.shrink(c.w, T=4, x_key=71)
+    cc = type(c)(w, syn.activations(w, 4), c.wr, None, None, codes=c.codes, scales=c.scales)
+    pin, pout = syn.latent_projections(w, D)
+    router_w, _, codes, scales = L._keep[:4]
+    Lp = q.MoELayer(hidden=w.H, inter=w.I, n_experts=w.E, top_k=w.k, max_tokens=4, router_w=router_w, codes=codes,
+                    scales=scales, proj=(q.to_device(pin), q.to_device(pout)))
+    chain_parity(cc, D, "latent-k3-T4", L=Lp)
+    Lp.close()

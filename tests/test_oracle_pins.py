@@ -755,3 +755,85 @@ def test_shared_backward_matches_central_finite_differences():
     assert checked >= 5
     # the shared part alone is linear in dY and has no router term: zero dY, zero gradient
     assert not np.any(oracle.shared_backward_input(x, np.zeros_like(dy), Ws, 2))
+
+
+# ---------------------------------------------------------------- latent projections
+
+
+def _bf16_f64(bits):
+    return oracle.to_f64(bits, "bf16")
+
+
+def test_dense_projection_against_numpy_both_orientations():
+    """oracle.dense against numpy float64 products of the decoded bf16 matrix, in both
+    orientations, with a non-square matrix so that a transposed operand cannot pass."""
+    rng = np.random.default_rng(31)
+    w = syn.f32_to_bf16_bits(rng.standard_normal((96, 160), dtype=np.float32))  # [N][K]
+    a = rng.standard_normal((5, 160))
+    wf = _bf16_f64(w)
+    assert np.abs(oracle.dense(a, w) - a @ wf.T).max() <= 1e-12 * np.abs(a @ wf.T).max()
+    b = rng.standard_normal((5, 96))
+    got = oracle.dense(b, w, transposed=True)
+    assert got.shape == (5, 160)
+    assert np.abs(got - b @ wf).max() <= 1e-12 * np.abs(b @ wf).max()
+
+
+def test_dense_projection_identity_and_permutation():
+    """Closed forms: the identity matrix returns the input exactly; a permutation matrix
+    permutes it, forward (w^T applied) and transposed (w applied, the inverse permutation)."""
+    n = 64
+    perm = np.random.default_rng(5).permutation(n)
+    eye = syn.f32_to_bf16_bits(np.eye(n, dtype=np.float32))
+    P = np.zeros((n, n), np.float32)
+    P[np.arange(n), perm] = 1.0  # row i picks input perm[i]
+    Pb = syn.f32_to_bf16_bits(P)
+    a = np.random.default_rng(6).standard_normal((3, n))
+    assert np.array_equal(oracle.dense(a, eye), a)
+    assert np.array_equal(oracle.dense(a, Pb), a[:, perm])
+    back = np.empty_like(a)
+    back[:, perm] = a
+    assert np.array_equal(oracle.dense(a, Pb, transposed=True), back)
+
+
+def test_latent_chain_gradient_by_finite_differences():
+    """The layer inside its latent projections: out = proj_out(moe(proj_in(x_model))).  dX_model
+    composed as proj_in-backward(backward_input(proj_out-backward(dout))) matches central
+    differences of L(x_model) = sum <dout, out(x_model)>, with routing-flip detection."""
+    w0 = syn.WORKLOADS["tiny"]
+    w, W = _tiny_layer()
+    D = 192
+    pin, pout = syn.latent_projections(w, D)
+    xm = oracle.to_f64(syn.model_activations(w, D), "f32")
+    wr = syn.router_weight(w)
+    dout = oracle.to_f64(syn.model_upstream_grad(w, D), "f32") * 100.0
+
+    def out_of(xx):
+        xl = oracle.dense(xx, pin)
+        y, ii, _ = oracle.layer_forward(xl, wr, None, w.k, W, nthreads=1)
+        return oracle.dense(y, pout), ii, xl
+
+    _, ids, xl = out_of(xm)
+    ids_, p, _ = oracle.route(xl, wr, None, w.k)
+    assert np.array_equal(ids, ids_)
+    dyl = oracle.dense(dout, pout, transposed=True)
+    dxl = oracle.backward_input(xl, dyl, ids, p, wr, W)
+    dxm = oracle.dense(dxl, pin, transposed=True)
+    assert dxm.shape == xm.shape
+    rng = np.random.default_rng(17)
+    checked = 0
+    for v in [rng.standard_normal(xm.shape) for _ in range(6)]:
+        eps = 1e-6 * np.linalg.norm(xm) / np.linalg.norm(v)
+        for _ in range(8):
+            op, ip, _ = out_of(xm + eps * v)
+            om, im, _ = out_of(xm - eps * v)
+            if np.array_equal(ip, ids) and np.array_equal(im, ids):
+                break
+            eps /= 2
+        else:
+            continue
+        fd = float(np.sum(dout * op) - np.sum(dout * om)) / (2 * eps)
+        an = float(np.sum(dxm * v))
+        assert abs(fd - an) <= 1e-7 * max(abs(an), 1e-3 * np.linalg.norm(dxm) * np.linalg.norm(v)), (fd, an)
+        checked += 1
+    assert checked >= 5
+    assert w0.H == w.H

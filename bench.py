@@ -32,12 +32,13 @@ def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-# The kernel whose roofline each workload reports, and the sources that define it.
+# The kernel whose roofline each workload reports, the sources that define it, and what it
+# does.
 ROOF_KERNEL = {
-    "decode1": ("k_dec_fused", ("expert_dec.hip",)),
-    "decode64": ("k_gateup", ("expert_fwd.hip", "expert_frag.h")),
-    "rvq16": ("k_gateup_rvq", ("expert_rvq.hip",)),
-    "train4096": ("k_gateup_mm", ("expert_mm.hip",)),
+    "decode1": ("k_dec_fused", ("expert_dec.hip",), "dequant + gate/up + SwiGLU + down + combine"),
+    "decode64": ("k_gateup", ("expert_fwd.hip", "expert_frag.h"), "dequant + gate/up + SwiGLU"),
+    "rvq16": ("k_gu_lut", ("expert_rvq_lut.hip",), "RVQ3 gate/up as codeword-table lookups"),
+    "train4096": ("k_gateup_mm", ("expert_mm.hip",), "dequant + gate/up + SwiGLU"),
 }
 
 
@@ -348,12 +349,11 @@ def main():
         single = args.mx_gateup and args.quant_x8
         peak = FP8_PEAK_TFLOPS if single else BF16_PEAK_TFLOPS
         kname = ("k_gateup_mx (block-scaled gate/up + SwiGLU)" if args.mx_gateup
-                 else ROOF_KERNEL[w.name][0] + " (dequant + gate/up + SwiGLU)")
+                 else f"{ROOF_KERNEL[w.name][0]} ({ROOF_KERNEL[w.name][2]})")
         roofline = {"bound": "mfma", "kernel": kname, "achieved": gu_tflops, "peak": peak, "unit": "TFLOP/s",
                     "frac": gu_tflops / peak, "traffic": traffic if not args.mx_gateup else None}
     else:
-        what = " (dequant + gate/up + SwiGLU + down + combine)" if fused else " (dequant + gate/up + SwiGLU)"
-        roofline = {"bound": "hbm", "kernel": ROOF_KERNEL[w.name][0] + what,
+        roofline = {"bound": "hbm", "kernel": f"{ROOF_KERNEL[w.name][0]} ({ROOF_KERNEL[w.name][2]})",
                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                     "traffic": traffic}
     if not train and not args.no_plain_read:

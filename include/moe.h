@@ -299,11 +299,12 @@ moe_status moe_backward_lora(moe_layer *L, const void *x, int32_t xt, const void
 /* moe_forward() with saved_gu = NULL, for callers that cannot allocate device memory:
  * code under HIP graph capture, serving loops that must not call the allocator, harnesses
  * that forbid it.  Same arguments, semantics and results (the same kernels); the scratch the
- * kernels use (h, the weighted slot rows, counters) is not the layer's workspace but one
- * array of 32 MiB compiled into the library, one copy per GPU, held until the process ends.
- * The call allocates nothing and calls no allocating routine; it clears that array's
- * counters with a fill kernel on `stream` (no memset).  Limits: T k (4 I + 4 H) bytes plus
- * ~157 KB must fit in 32 MiB (K3 shape: T <= 78 at k = 16), else MOE_ERR_WORKSPACE and
+ * kernels use (h or, for RVQ3, g and u, the weighted slot rows, counters) is not the layer's
+ * workspace but one array of 32 MiB compiled into the library, one copy per GPU, held until
+ * the process ends.  The call allocates nothing and calls no allocating routine; it clears
+ * that array's counters with a fill kernel on `stream` (no memset).  Limits: T k (4 I + 4 H)
+ * bytes (RVQ3: T k (8 I + 4 H)) plus ~157 KB must fit in 32 MiB (K3 shape: T <= 78 at
+ * k = 16; RVQ3 at the K3 shape: T <= 53), else MOE_ERR_WORKSPACE and
  * nothing is enqueued; layers with shared experts, an attached adapter, MOE_F_MX_GATEUP,
  * MOE_F_QUANT_X8 or MOE_F_VALIDATE give MOE_ERR_UNSUPPORTED.  Every call on one GPU uses the
  * same array: calls that overlap on one GPU (other streams, other threads, other layers)

@@ -424,6 +424,11 @@ hipError_t launch_expert_forward(const ExpertFwdArgs &a, hipStream_t s)
         if (err == hipSuccess) err = launch_combine(a, s);
         return err;
     }
+    if (a.tok_chunks == 0 && rvq_lut_supported(a)) {
+        hipError_t err = launch_rvq_lut(a, s);
+        if (err == hipSuccess) err = launch_combine(a, s);
+        return err;
+    }
     if (rvq_dec_supported(a)) {
         hipError_t err = launch_gateup_rvq(a, s);
         if (err == hipSuccess) err = launch_down_rvq(a, s);

@@ -482,7 +482,9 @@ moe_status static_scratch(char **out)
 }
 
 // Carving of `scratch` for T tokens: status word, counters of the fused few-token launch,
-// h as bf16 hi + lo planes [S][I], weighted slot rows [S][H] fp32 (S = T k).
+// h as bf16 hi + lo planes [S][I] (RVQ3: the same region, twice the size, holds g and u
+// [S][2][I] fp32 for the table-lookup kernels, which take no h planes), weighted slot rows
+// [S][H] fp32 (S = T k).
 struct StaticLayout {
     size_t status, sync, h, ybuf, total;
 };
@@ -499,7 +501,7 @@ StaticLayout static_layout(const moe_desc &d, int T)
     const size_t S = (size_t)T * d.top_k;
     l.status = take(4);
     l.sync = take((size_t)moe::kSyncWords * 4);
-    l.h = take(S * d.inter * 4);
+    l.h = take(S * d.inter * (d.wfmt == MOE_W_RVQ3 ? 8 : 4));
     l.ybuf = take(S * d.hidden * 4);
     l.total = off;
     return l;
@@ -560,6 +562,7 @@ moe_status moe_forward(moe_layer *L, const void *x, int32_t xt, int32_t T, const
     a.h_hi = (uint16_t *)(L->ws + L->lay.h);
     a.h_lo = a.h_hi + (size_t)T * a.k * a.I;
     a.gu = saved_gu;
+    a.gu_ws = (float *)(L->ws + L->lay.gu);
     a.ybuf = (float *)(L->ws + L->lay.ybuf);
     if (L->d.flags & MOE_F_MX_GATEUP) {
         a.xq = (uint8_t *)(L->ws + L->lay.xq);
@@ -618,6 +621,7 @@ moe_status moe_forward(moe_layer *L, const void *x, int32_t xt, int32_t T, const
         sa.w = dr.w;
         sa.h_lo = sa.h_hi + (size_t)T * sa.k * sa.I;
         sa.gu = nullptr;
+        sa.gu_ws = nullptr;  // sized for the routed slots; the shared units take other kernels
         sa.ybuf = (float *)(L->ws + L->lay.sh_rows);
         sa.tok_chunks = tok_chunks(T);
         sa.skip_combine = 1;
@@ -835,6 +839,7 @@ moe_status moe_forward_static(moe_layer *L, const void *x, int32_t xt, int32_t T
     moe::ExpertFwdArgs a = routed_fwd_args(L, x, xt, T, r, y);
     a.h_hi = (uint16_t *)(base + sl.h);
     a.h_lo = a.h_hi + (size_t)T * a.k * a.I;
+    if (L->d.wfmt == MOE_W_RVQ3) a.gu_ws = (float *)(base + sl.h);
     a.ybuf = (float *)(base + sl.ybuf);
     a.status = (uint32_t *)(base + sl.status);
     a.dec_sync = (uint32_t *)(base + sl.sync);

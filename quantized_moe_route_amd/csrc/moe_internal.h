@@ -118,6 +118,7 @@ struct ExpertFwdArgs {
     // three-launch path) and the status word its bounded waits report a timeout into.
     uint32_t *dec_sync;
     uint32_t *status;
+    float *gu_ws;  // [S][2][I] workspace for g, u when gu is null (the RVQ3 table-lookup path), or null
 };
 
 // Counter layout of the fused decode launch: per-unit gate/up completions, per-stripe down
@@ -200,6 +201,9 @@ hipError_t launch_dec_fused(const ExpertFwdArgs &a, hipStream_t s);
 bool rvq_dec_supported(const ExpertFwdArgs &a);
 hipError_t launch_gateup_rvq(const ExpertFwdArgs &a, hipStream_t s);
 hipError_t launch_down_rvq(const ExpertFwdArgs &a, hipStream_t s);
+// Few-token RVQ3 as table lookups (expert_rvq_lut.hip): gate and up into g, u, then down.
+bool rvq_lut_supported(const ExpertFwdArgs &a);
+hipError_t launch_rvq_lut(const ExpertFwdArgs &a, hipStream_t s);
 // taken when the experts average at least 8 tokens each
 inline bool use_mm(const ExpertFwdArgs &a) { return (size_t)a.T * a.k >= (size_t)8 * a.E && mm_supported(a); }
 hipError_t launch_expert_backward(const ExpertBwdArgs &a, hipStream_t s);

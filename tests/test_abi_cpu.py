@@ -295,6 +295,14 @@ def test_static_forward_argument_checks():
     st, h = _create(_desc(max_tokens=8, flags=C.MOE_F_QUANT_X8), _fake_weights())
     assert L.moe_forward_static(h, x, C.MOE_DT_BF16, 1, ctypes.byref(r), y, None) == C.MOE_ERR_UNSUPPORTED
     L.moe_destroy(h)
+    # RVQ3 holds g and u (8 I bytes per slot) where the other formats hold h (4 I): at the K3
+    # shape 38,912 bytes per slot, so 53 tokens fit and 54 do not (53 passes the size check
+    # and stops at the missing routing)
+    st, h = _create(_desc(max_tokens=4096, wfmt=C.MOE_W_RVQ3), _fake_weights(C.MOE_W_RVQ3))
+    assert st == C.MOE_OK
+    assert L.moe_forward_static(h, x, C.MOE_DT_BF16, 54, ctypes.byref(r), y, None) == C.MOE_ERR_WORKSPACE
+    assert L.moe_forward_static(h, x, C.MOE_DT_BF16, 53, None, y, None) == C.MOE_ERR_INVALID_ARG
+    L.moe_destroy(h)
 
 
 def test_latent_projection_argument_checks():

@@ -62,6 +62,10 @@ def test_lora_rvq3_paths():
              "lora-rvq3-gather")
     run_lora(_case(syn.shrink(syn.WORKLOADS["rvq16"], T=24, H=256, I=128, E=12, k=3, with_dy=True, x_key=56), act=1),
              "lora-rvq3-generic-situ", rank=4)
+    # ~13 tokens per expert with an adapter: the codeword-gather kernels in four passes of up
+    # to 4 tokens, the weights re-read per pass
+    run_lora(_case(syn.shrink(syn.WORKLOADS["rvq16"], T=40, H=256, I=512, E=6, k=2, with_dy=True, x_key=57)),
+             "lora-rvq3-gather-passes")
 
 
 def test_lora_zero_tokens_gives_zero_gradients():

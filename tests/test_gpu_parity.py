@@ -268,16 +268,24 @@ def test_rvq3_small():
     run_small(host_case(w), name="rvq3-small")
 
 
-def test_rvq3_fp16_gather_path():
-    # bf16 x, H and I multiples of 256, T <= 64: codewords gathered as fp16 MFMA operands
+def test_rvq3_table_lookup_path():
+    # bf16 x, H and I multiples of 256, T <= 64, no adapter: the table-lookup kernels (one row
+    # block per matrix, a half table group for H = 512 and a three-quarter one for I = 768)
     w = syn.shrink(syn.WORKLOADS["rvq16"], T=10, H=512, I=768, E=12, k=3, with_dy=True, x_key=21)
-    run_small(host_case(w), name="rvq3-gather")
+    run_small(host_case(w), name="rvq3-lut")
 
 
-def test_rvq3_fp16_gather_multi_pass():
-    # ~13 tokens per expert: four passes of up to 4 tokens, the weights re-read per pass
+def test_rvq3_table_lookup_many_tokens_per_unit():
+    # ~13 tokens per expert: one pass per token, the index bytes re-read per pass
     w = syn.shrink(syn.WORKLOADS["rvq16"], T=40, H=256, I=512, E=6, k=2, with_dy=True, x_key=22)
-    run_small(host_case(w), name="rvq3-gather-passes")
+    run_small(host_case(w), name="rvq3-lut-passes")
+
+
+def test_rvq3_table_lookup_row_blocks():
+    # two row blocks per matrix (gate/up: 7 slots x 128 rows = 896, I = 1792; down: 5 slots,
+    # 640 rows, H = 1280), groups of 128 + 32 and 128 + 96 vectors
+    w = syn.shrink(syn.WORKLOADS["rvq16"], T=6, H=1280, I=1792, E=10, k=4, with_dy=True, x_key=23)
+    run_small(host_case(w), name="rvq3-lut-blocks")
 
 
 def test_single_token_and_k1():

@@ -102,19 +102,23 @@ struct LutGeom {
     int k, r;          // lane in team, lookup order (vector 16k + (i xor r) at step i)
 };
 
-// This thread's 16 index bytes of each slot's row for stage-group step st (lanes past the
-// row's last vector, and rows past the matrix, read bytes that are never looked up or
-// stored; offsets past the buffer read zero).
+// This thread's 16 index bytes of each slot's row for stage-group step st.  The whole offset
+// within the unit's index bytes is in the per-lane operand, which is all the buffer range
+// check sees: lanes past the group's last vector and slots past the matrix's last row take
+// offset 2^31, past the range (index planes are below 2^31 bytes), and read zeros without
+// touching memory.
 template <int NS>
 __device__ __forceinline__ void load_idx(uint32_t (&dst)[NS][4], __amdgpu_buffer_rsrc_t ir, const LutGeom &G,
-                                         uint32_t rowoff, int st)
+                                         uint32_t rowoff, uint32_t slot_ok, int st)
 {
     const int s = st / G.ng, g = st - s * G.ng;
-    const uint32_t off = rowoff + (uint32_t)(kGV * g + 16 * G.k), soff = (uint32_t)s * G.plane;
+    const bool lane_ok = 16 * G.k < G.V - kGV * g;
+    const uint32_t off = (uint32_t)s * G.plane + rowoff + (uint32_t)(kGV * g + 16 * G.k);
     const uint32_t slot_stride = (uint32_t)kTeams * (uint32_t)G.V;
 #pragma unroll
     for (int j = 0; j < NS; j++) {
-        const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(ir, (int)off, (int)(soff + j * slot_stride), 0);
+        const uint32_t o = lane_ok && ((slot_ok >> j) & 1u) ? off + j * slot_stride : 0x80000000u;
+        const u32x4 a = __builtin_amdgcn_raw_buffer_load_b128(ir, (int)o, 0, 0);
         dst[j][0] = a[0]; dst[j][1] = a[1]; dst[j][2] = a[2]; dst[j][3] = a[3];
     }
 }
@@ -199,19 +203,23 @@ __device__ __forceinline__ float lut_rows(const uint8_t *__restrict__ idx, int N
     G.k = tid & 7;
     G.r = 4 * ((lane >> 3) & 3) + (G.k >> 1);
     const __amdgpu_buffer_rsrc_t ir = lrsrc(idx, 3 * G.plane);
-    const uint32_t rowoff = (uint32_t)(rb * NS * kTeams + (tid >> 3)) * (uint32_t)G.V;  // slot 0's row
+    const int row0 = rb * NS * kTeams + (tid >> 3);  // slot 0's row
+    const uint32_t rowoff = (uint32_t)row0 * (uint32_t)G.V;
+    uint32_t slot_ok = 0;  // bit j: slot j's row is in the matrix
+#pragma unroll
+    for (int j = 0; j < NS; j++) slot_ok |= (row0 + j * kTeams < NR ? 1u : 0u) << j;
     float acc[NS];
 #pragma unroll
     for (int j = 0; j < NS; j++) acc[j] = 0.f;
     uint32_t ia[NS][4], ib[NS][4];  // index bytes of two consecutive steps
     // The prefetch is unconditional (the last step re-reads itself): a conditional load makes
     // the wait before the current step's first use cover the prefetch as well.
-    load_idx<NS>(ia, ir, G, rowoff, 0);
+    load_idx<NS>(ia, ir, G, rowoff, slot_ok, 0);
     for (int st = 0; st < G.nstep; st += 2) {
         const int s1 = min(st + 1, G.nstep - 1), s2 = min(st + 2, G.nstep - 1);
-        load_idx<NS>(ib, ir, G, rowoff, s1);
+        load_idx<NS>(ib, ir, G, rowoff, slot_ok, s1);
         lut_step<NS, NTERM>(ia, acc, G, st, K, xs, cbl, lut);
-        load_idx<NS>(ia, ir, G, rowoff, s2);
+        load_idx<NS>(ia, ir, G, rowoff, slot_ok, s2);
         if (st + 1 < G.nstep) lut_step<NS, NTERM>(ib, acc, G, s1, K, xs, cbl, lut);
     }
     // the team's 8 partial sums of each row; lane k keeps slot k's

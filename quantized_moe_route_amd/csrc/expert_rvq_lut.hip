@@ -10,7 +10,8 @@
 // of expert_rvq.hip are bound by the bank conflicts of those gathers when experts hold one
 // token, and read each row's index bytes 32 at a time).
 //
-// Block = 1024 threads, one matrix of one unit, NS x 128 rows, one token per pass.  Rows are
+// Block = 1024 threads, one matrix of one unit, NS x 128 rows, up to two tokens (gate/up) or
+// one token (down) per pass, the index bytes read once per pass.  Rows are
 // worked by teams of 8 lanes: for each stage s and group of 128 vectors (one 128-byte line of
 // a row's index bytes) the 8 lanes of a team load the line together, 16 bytes each, so one
 // wave-wide load covers 8 whole lines (reading a row 64 or 32 bytes at a time, strided by the
@@ -123,19 +124,15 @@ __device__ __forceinline__ void load_idx(uint32_t (&dst)[NS][4], __amdgpu_buffer
     }
 }
 
-// Build the table of stage-group step st, then add the entries picked by the slots' index
-// bytes (idx, permuted in place) to acc.
-template <int NS, int NTERM>
-__device__ __forceinline__ void lut_step(uint32_t (&idx)[NS][4], float (&acc)[NS], const LutGeom &G, int st, int K,
-                                         const _Float16 *xs, const _Float16 *cbl, char *lut)
+// Build the table of stage s, group g (gw vectors) for one token (xs: its NTERM fp16 planes
+// [NTERM][K]): 32 tiles of 32 codewords x 32 vectors, two per wave; lane supplies codeword /
+// vector lane mod 32, dimensions 4 (lane / 32) .. + 3, and gets back rows 8 (i / 4) +
+// 4 (lane / 32) + i mod 4 of the tile's column lane mod 32.
+template <int NTERM>
+__device__ __forceinline__ void build_table(int s, int g, int gw, int K, const _Float16 *xs, const _Float16 *cbl,
+                                            char *lut)
 {
-    const int s = st / G.ng, g = st - s * G.ng;
-    const int gw = min(kGV, G.V - kGV * g);  // vectors in this group (a multiple of 32)
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-    __syncthreads();  // the previous step's lookups are done
-    // 32 tiles of 32 codewords x 32 vectors, two per wave: lane supplies codeword / vector
-    // lane mod 32, dimensions 4 (lane / 32) .. + 3, and gets back rows 8 (i / 4) + 4 (lane / 32)
-    // + i mod 4 of the tile's column lane mod 32
 #pragma unroll 1
     for (int h = 0; h < 2; h++) {
         const int t = wv + 16 * h, ct = t & 7, vt = t >> 3;
@@ -153,15 +150,17 @@ __device__ __forceinline__ void lut_step(uint32_t (&idx)[NS][4], float (&acc)[NS
 #pragma unroll
         for (int i = 0; i < 16; i++) *(float *)(dst + 256 * (8 * (i >> 2) + (i & 3))) = d[i];
     }
-    __syncthreads();
-    if (16 * G.k >= gw) return;
-#pragma unroll
-    for (int j = 0; j < NS; j++) xor_dwords(idx[j], G.r >> 2);
-    // step i: vector v = 16k + (i xor r) at byte (v / 64) * 64 KB + 256 c + 4 (v mod 64), whose
-    // bytes 0 and 2 are those of toff = tb xor 4i (the base and the selectors are opaque
-    // copies, so that they stay five registers and the per-step offsets are one xor each); the
-    // lookups of step i + 1 are issued before the adds of step i
-    const char *lb = lut;
+}
+
+// Add to acc the table entries picked by the slots' index bytes (already permuted by
+// r / 4).  Step i takes vector v = 16k + (i xor r) at byte (v / 64) * 64 KB + 256 c +
+// 4 (v mod 64), whose bytes 0 and 2 are those of toff = tb xor 4i (the base and the selectors
+// are opaque copies, so that they stay five registers and the per-step offsets are one xor
+// each); the lookups of step i + 1 are issued before the adds of step i.
+template <int NS>
+__device__ __forceinline__ void lookups(const uint32_t (&idx)[NS][4], float (&acc)[NS], const LutGeom &G,
+                                        const char *lb)
+{
     uint32_t tb = ((uint32_t)(G.k >> 2) << 16) | (64u * (uint32_t)(G.k & 3) + 4u * (uint32_t)G.r);
     uint32_t sel[4];
 #pragma unroll
@@ -186,13 +185,40 @@ __device__ __forceinline__ void lut_step(uint32_t (&idx)[NS][4], float (&acc)[NS
     }
 }
 
-// One matrix of one unit for one token: slot j of team t is row rb * NS * 128 + j * 128 + t
-// of NR, K inputs.  Returns, in lane k of each team, the whole sum of its slot k's row
-// (scaled by the token's 2^-se).  xs: the token as NTERM fp16 planes [NTERM][K] (LDS); cbl:
-// the matrix's codebooks [3][256][8] fp16 (LDS); lut: 128 KB of LDS at address 0.
-template <int NS, int NTERM>
-__device__ __forceinline__ float lut_rows(const uint8_t *__restrict__ idx, int NR, int K, int rb, const _Float16 *xs,
-                                          const _Float16 *cbl, char *lut)
+// Stage-group step st for nt <= NT tokens (xs: [NT][NTERM][K]): per token, build the table,
+// then add the entries picked by the slots' index bytes (idx, permuted in place once) to
+// that token's acc.
+template <int NS, int NTERM, int NT>
+__device__ __forceinline__ void lut_step(uint32_t (&idx)[NS][4], float (&acc)[NT][NS], const LutGeom &G, int st, int K,
+                                         int nt, const _Float16 *xs, const _Float16 *cbl, char *lut)
+{
+    const int s = st / G.ng, g = st - s * G.ng;
+    const int gw = min(kGV, G.V - kGV * g);  // vectors in this group (a multiple of 32)
+    const bool active = 16 * G.k < gw;
+#pragma unroll
+    for (int t = 0; t < NT; t++) {
+        if (t > 0 && t >= nt) break;
+        __syncthreads();  // the previous lookups are done
+        build_table<NTERM>(s, g, gw, K, xs + (size_t)t * NTERM * K, cbl, lut);
+        __syncthreads();
+        if (active) {
+            if (t == 0) {
+#pragma unroll
+                for (int j = 0; j < NS; j++) xor_dwords(idx[j], G.r >> 2);
+            }
+            lookups<NS>(idx, acc[t], G, lut);
+        }
+    }
+}
+
+// One matrix of one unit for nt <= NT tokens: slot j of team t is row rb * NS * 128 + j * 128
+// + t of NR, K inputs.  On return, out[u] in lane k of each team is the whole sum of its slot
+// k's row for token u (scaled by that token's 2^-se).  xs: the tokens as NTERM fp16 planes
+// each, [NT][NTERM][K] (LDS); cbl: the matrix's codebooks [3][256][8] fp16 (LDS); lut: 128
+// KB of LDS at address 0.
+template <int NS, int NTERM, int NT>
+__device__ __forceinline__ void lut_rows(const uint8_t *__restrict__ idx, int NR, int K, int rb, int nt, const _Float16 *xs,
+                                         const _Float16 *cbl, char *lut, float (&out)[NT])
 {
     const int tid = threadIdx.x, lane = tid & 63;
     LutGeom G;
@@ -208,9 +234,11 @@ __device__ __forceinline__ float lut_rows(const uint8_t *__restrict__ idx, int N
     uint32_t slot_ok = 0;  // bit j: slot j's row is in the matrix
 #pragma unroll
     for (int j = 0; j < NS; j++) slot_ok |= (row0 + j * kTeams < NR ? 1u : 0u) << j;
-    float acc[NS];
+    float acc[NT][NS];
 #pragma unroll
-    for (int j = 0; j < NS; j++) acc[j] = 0.f;
+    for (int t = 0; t < NT; t++)
+#pragma unroll
+        for (int j = 0; j < NS; j++) acc[t][j] = 0.f;
     uint32_t ia[NS][4], ib[NS][4];  // index bytes of two consecutive steps
     // The prefetch is unconditional (the last step re-reads itself): a conditional load makes
     // the wait before the current step's first use cover the prefetch as well.
@@ -218,21 +246,23 @@ __device__ __forceinline__ float lut_rows(const uint8_t *__restrict__ idx, int N
     for (int st = 0; st < G.nstep; st += 2) {
         const int s1 = min(st + 1, G.nstep - 1), s2 = min(st + 2, G.nstep - 1);
         load_idx<NS>(ib, ir, G, rowoff, slot_ok, s1);
-        lut_step<NS, NTERM>(ia, acc, G, st, K, xs, cbl, lut);
+        lut_step<NS, NTERM, NT>(ia, acc, G, st, K, nt, xs, cbl, lut);
         load_idx<NS>(ia, ir, G, rowoff, slot_ok, s2);
-        if (st + 1 < G.nstep) lut_step<NS, NTERM>(ib, acc, G, s1, K, xs, cbl, lut);
+        if (st + 1 < G.nstep) lut_step<NS, NTERM, NT>(ib, acc, G, s1, K, nt, xs, cbl, lut);
     }
     // the team's 8 partial sums of each row; lane k keeps slot k's
-    float out = 0.f;
 #pragma unroll
-    for (int j = 0; j < NS; j++) {
-        float v = acc[j];
-        v += dpp_f32<kDppXor1>(v);
-        v += dpp_f32<kDppXor2>(v);
-        v += dpp_f32<kDppHalfMirror>(v);
-        if (G.k == j) out = v;
+    for (int t = 0; t < NT; t++) {
+        out[t] = 0.f;
+#pragma unroll
+        for (int j = 0; j < NS; j++) {
+            float v = acc[t][j];
+            v += dpp_f32<kDppXor1>(v);
+            v += dpp_f32<kDppXor2>(v);
+            v += dpp_f32<kDppHalfMirror>(v);
+            if (G.k == j) out[t] = v;
+        }
     }
-    return out;
 }
 
 // Stage the codebooks of one matrix of expert e ([3][256][8] fp16 = 768 x 16 B) in LDS.
@@ -244,8 +274,9 @@ __device__ __forceinline__ void stage_cb(_Float16 *dst, const uint16_t *cb, int 
 
 }  // namespace
 
-// gate (blockIdx.y = 0) or up (1) rows of one active unit (blockIdx.z), one token per pass:
-// g or u = row . x for every token of the unit, written to gu [S][2][I] (grouped rows).
+// gate (blockIdx.y = 0) or up (1) rows of one active unit (blockIdx.z), up to two tokens per
+// pass (the index bytes are read once per pass): g or u = row . x for every token of the unit,
+// written to gu [S][2][I] (grouped rows).
 template <int NS>
 __global__ __launch_bounds__(kLutThreads, 1) void k_gu_lut(const ExpertFwdArgs a)
 {
@@ -257,24 +288,32 @@ __global__ __launch_bounds__(kLutThreads, 1) void k_gu_lut(const ExpertFwdArgs a
     const MatW &W = m == 0 ? a.gate : a.up;
     char *lut = (char *)lds_u;
     _Float16 *cbl = (_Float16 *)((char *)lds_u + kLutBytes);
-    _Float16 *xs = (_Float16 *)((char *)lds_u + kLutBytes + kCbBytes);
-    float *red = (float *)(xs + H);
+    _Float16 *xs = (_Float16 *)((char *)lds_u + kLutBytes + kCbBytes);  // [2][H] fp16
+    float *red = (float *)(xs + 2 * H);
     stage_cb(cbl, W.cb, e);
     const int r0 = a.offsets[e], ntok = a.offsets[e + 1] - r0;
     float *gu = a.gu ? a.gu : a.gu_ws;
     const uint8_t *idx = W.idx + (size_t)e * 3 * I * (H / 8);
     const int n = rb * NS * kTeams + (threadIdx.x & 7) * kTeams + (threadIdx.x >> 3);  // slot k's row
-    for (int j = 0; j < ntok; j++) {
-        const uint16_t *xr = (const uint16_t *)a.x + (size_t)(a.perm[r0 + j] / a.k) * H;
-        float mx = 0.f;
-        for (int c = threadIdx.x; c < H; c += kLutThreads) mx = fmaxf(mx, fabsf(bf16_bits_to_f32(xr[c])));
-        const int se = lut_scale_exp(block_max(mx, red));
-        for (int c = threadIdx.x; c < H / 2; c += kLutThreads) {
-            const uint32_t v = ((const uint32_t *)xr)[c];
-            ((uint32_t *)xs)[c] = pack_h2f(ldexpf(bf16_bits_to_f32(v & 0xFFFFu), -se), ldexpf(bf16_bits_to_f32(v >> 16), -se));
+    for (int j0 = 0; j0 < ntok; j0 += 2) {
+        const int nt = min(2, ntok - j0);
+        int se[2] = {0, 0};
+        for (int t = 0; t < nt; t++) {
+            const uint16_t *xr = (const uint16_t *)a.x + (size_t)(a.perm[r0 + j0 + t] / a.k) * H;
+            float mx = 0.f;
+            for (int c = threadIdx.x; c < H; c += kLutThreads) mx = fmaxf(mx, fabsf(bf16_bits_to_f32(xr[c])));
+            se[t] = lut_scale_exp(block_max(mx, red));
+            for (int c = threadIdx.x; c < H / 2; c += kLutThreads) {
+                const uint32_t v = ((const uint32_t *)xr)[c];
+                ((uint32_t *)(xs + (size_t)t * H))[c] =
+                    pack_h2f(ldexpf(bf16_bits_to_f32(v & 0xFFFFu), -se[t]), ldexpf(bf16_bits_to_f32(v >> 16), -se[t]));
+            }
         }
-        const float o = lut_rows<NS, 1>(idx, I, H, rb, xs, cbl, lut);
-        if ((threadIdx.x & 7) < NS && n < I) gu[((size_t)(r0 + j) * 2 + m) * I + n] = ldexpf(o, se);
+        float o[2];
+        lut_rows<NS, 1, 2>(idx, I, H, rb, nt, xs, cbl, lut, o);
+        if ((threadIdx.x & 7) < NS && n < I) {
+            for (int t = 0; t < nt; t++) gu[((size_t)(r0 + j0 + t) * 2 + m) * I + n] = ldexpf(o[t], se[t]);
+        }
     }
 }
 
@@ -309,9 +348,10 @@ __global__ __launch_bounds__(kLutThreads, 1) void k_down_lut(const ExpertFwdArgs
             hs[c] = hi;
             hs[I + c] = (_Float16)(h - (float)hi);
         }
-        const float o = lut_rows<NS, 2>(idx, H, I, rb, hs, cbl, lut);
+        float o[1];
+        lut_rows<NS, 2, 1>(idx, H, I, rb, 1, hs, cbl, lut, o);
         const int slot = a.perm[r0 + j];
-        if ((threadIdx.x & 7) < NS && n < H) a.ybuf[(size_t)slot * H + n] = ldexpf(a.w[slot], se) * o;
+        if ((threadIdx.x & 7) < NS && n < H) a.ybuf[(size_t)slot * H + n] = ldexpf(a.w[slot], se) * o[0];
     }
 }
 
@@ -319,7 +359,7 @@ namespace {
 
 // Dynamic LDS: the table first (at LDS address 0: the kernels have no static LDS, so table
 // addresses need no base added), codebooks, token slice, block-maximum scratch.
-size_t lds_gu(const ExpertFwdArgs &a) { return (size_t)kLutBytes + kCbBytes + (size_t)2 * a.H + 4 * kLutThreads / 64; }
+size_t lds_gu(const ExpertFwdArgs &a) { return (size_t)kLutBytes + kCbBytes + (size_t)4 * a.H + 4 * kLutThreads / 64; }
 size_t lds_down(const ExpertFwdArgs &a) { return (size_t)kLutBytes + kCbBytes + (size_t)4 * a.I + 4 * kLutThreads / 64; }
 
 // Largest dynamic LDS a block of the current device may take (cached per device).

@@ -31,8 +31,13 @@
 //    is one v_perm_b32 per lookup: byte 1 is the index byte (picked by a per-lane selector
 //    that applies r mod 4), bytes 0 and 2 come from the step's offset.
 // Index bytes of the next (stage, group) are loaded while the current one is looked up.
-// gate/up write g or u (fp32, grouped rows [S][2][I]); down reads them, forms h = act(g, u)
-// and writes the p-weighted slot rows for the fixed-order combine.
+// The launches are persistent, one block per CU: work items (a unit's row block of one
+// matrix, all of the unit's tokens) are handed out by an atomic counter, units with the most
+// tokens first, so the long items start early and the CUs run out of work together (blocks
+// that dispatch in a fixed order to the XCDs left about a sixth of the CU time idle).  A
+// one-block launch before them sorts the active units by token count into a shared order
+// and zeroes the counters.  The order decides only which block computes an item, not any
+// arithmetic, so results do not depend on it.
 #include "common.h"
 #include "moe_internal.h"
 
@@ -216,9 +221,11 @@ __device__ __forceinline__ void lut_step(uint32_t (&idx)[NS][4], float (&acc)[NT
 // k's row for token u (scaled by that token's 2^-se).  xs: the tokens as NTERM fp16 planes
 // each, [NT][NTERM][K] (LDS); cbl: the matrix's codebooks [3][256][8] fp16 (LDS); lut: 128
 // KB of LDS at address 0.
-template <int NS, int NTERM, int NT>
+// prep() (which stages the tokens and codebooks in LDS) runs after the first two steps' index
+// bytes are requested, so their latency overlaps it.
+template <int NS, int NTERM, int NT, typename Prep>
 __device__ __forceinline__ void lut_rows(const uint8_t *__restrict__ idx, int NR, int K, int rb, int nt, const _Float16 *xs,
-                                         const _Float16 *cbl, char *lut, float (&out)[NT])
+                                         const _Float16 *cbl, char *lut, float (&out)[NT], Prep &&prep)
 {
     const int tid = threadIdx.x, lane = tid & 63;
     LutGeom G;
@@ -246,6 +253,7 @@ __device__ __forceinline__ void lut_rows(const uint8_t *__restrict__ idx, int NR
     for (int st = 0; st < G.nstep; st += 2) {
         const int s1 = min(st + 1, G.nstep - 1), s2 = min(st + 2, G.nstep - 1);
         load_idx<NS>(ib, ir, G, rowoff, slot_ok, s1);
+        if (st == 0) prep();
         lut_step<NS, NTERM, NT>(ia, acc, G, st, K, nt, xs, cbl, lut);
         load_idx<NS>(ia, ir, G, rowoff, slot_ok, s2);
         if (st + 1 < G.nstep) lut_step<NS, NTERM, NT>(ib, acc, G, s1, K, nt, xs, cbl, lut);
@@ -265,6 +273,15 @@ __device__ __forceinline__ void lut_rows(const uint8_t *__restrict__ idx, int NR
     }
 }
 
+// The block's next work item from the launch's counter ctr.
+__device__ __forceinline__ int next_item(uint32_t *ctr, int *sh)
+{
+    __syncthreads();  // every thread has read the previous item
+    if (threadIdx.x == 0) *sh = (int)__hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    return *sh;
+}
+
 // Stage the codebooks of one matrix of expert e ([3][256][8] fp16 = 768 x 16 B) in LDS.
 __device__ __forceinline__ void stage_cb(_Float16 *dst, const uint16_t *cb, int e)
 {
@@ -274,93 +291,154 @@ __device__ __forceinline__ void stage_cb(_Float16 *dst, const uint16_t *cb, int 
 
 }  // namespace
 
-// gate (blockIdx.y = 0) or up (1) rows of one active unit (blockIdx.z), up to two tokens per
-// pass (the index bytes are read once per pass): g or u = row . x for every token of the unit,
-// written to gu [S][2][I] (grouped rows).
+// The active units sorted by token count, descending, into ord[0 .. n_active) (one block;
+// counts above 64 share the top bin; positions within a bin are taken by atomics, in no fixed
+// order, which only moves work between blocks), and the table-lookup counters zeroed.
+__global__ __launch_bounds__(1024) void k_lut_order(const ExpertFwdArgs a)
+{
+    __shared__ int hist[65];
+    const int n = *a.n_active;
+    for (int i = threadIdx.x; i < 65; i += blockDim.x) hist[i] = 0;
+    if (threadIdx.x < 2) a.dec_sync[kSyncLut + threadIdx.x * kSyncPad] = 0u;
+    __syncthreads();
+    for (int u = threadIdx.x; u < n; u += blockDim.x) {
+        const int e = a.active[u];
+        atomicAdd(&hist[min(a.offsets[e + 1] - a.offsets[e], 64)], 1);
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int run = 0;
+        for (int c = 64; c >= 0; c--) {
+            const int h = hist[c];
+            hist[c] = run;
+            run += h;
+        }
+    }
+    __syncthreads();
+    for (int u = threadIdx.x; u < n; u += blockDim.x) {
+        const int e = a.active[u];
+        a.lut_ord[atomicAdd(&hist[min(a.offsets[e + 1] - a.offsets[e], 64)], 1)] = u;
+    }
+}
+
+// gate and up rows: work item (unit u in the heavy-first order, matrix m, row block rb) is
+// item (u * 2 + m) * nrb + rb; up to two tokens per pass (the index bytes are read once per
+// pass): g or u = row . x for every token of the unit, written to gu [S][2][I] (grouped rows).
 template <int NS>
 __global__ __launch_bounds__(kLutThreads, 1) void k_gu_lut(const ExpertFwdArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) u32x4 lds_u[];
-    const int ai = blockIdx.z, m = blockIdx.y, rb = blockIdx.x;
-    if (ai >= *a.n_active) return;
-    const int e = a.active[ai];
     const int H = a.H, I = a.I;
-    const MatW &W = m == 0 ? a.gate : a.up;
     char *lut = (char *)lds_u;
     _Float16 *cbl = (_Float16 *)((char *)lds_u + kLutBytes);
     _Float16 *xs = (_Float16 *)((char *)lds_u + kLutBytes + kCbBytes);  // [2][H] fp16
     float *red = (float *)(xs + 2 * H);
-    stage_cb(cbl, W.cb, e);
-    const int r0 = a.offsets[e], ntok = a.offsets[e + 1] - r0;
+    int *sh = (int *)(red + kLutThreads / 64);
+    uint32_t *ctr = a.dec_sync + kSyncLut;
+    const int nact = *a.n_active, nrb = (I + NS * kTeams - 1) / (NS * kTeams);
     float *gu = a.gu ? a.gu : a.gu_ws;
-    const uint8_t *idx = W.idx + (size_t)e * 3 * I * (H / 8);
-    const int n = rb * NS * kTeams + (threadIdx.x & 7) * kTeams + (threadIdx.x >> 3);  // slot k's row
-    for (int j0 = 0; j0 < ntok; j0 += 2) {
-        const int nt = min(2, ntok - j0);
-        int se[2] = {0, 0};
-        for (int t = 0; t < nt; t++) {
-            const uint16_t *xr = (const uint16_t *)a.x + (size_t)(a.perm[r0 + j0 + t] / a.k) * H;
-            float mx = 0.f;
-            for (int c = threadIdx.x; c < H; c += kLutThreads) mx = fmaxf(mx, fabsf(bf16_bits_to_f32(xr[c])));
-            se[t] = lut_scale_exp(block_max(mx, red));
-            for (int c = threadIdx.x; c < H / 2; c += kLutThreads) {
-                const uint32_t v = ((const uint32_t *)xr)[c];
-                ((uint32_t *)(xs + (size_t)t * H))[c] =
-                    pack_h2f(ldexpf(bf16_bits_to_f32(v & 0xFFFFu), -se[t]), ldexpf(bf16_bits_to_f32(v >> 16), -se[t]));
+    for (;;) {
+        const int item = next_item(ctr, sh);
+        if (item >= nact * 2 * nrb) break;
+        const int e = a.active[a.lut_ord[item / (2 * nrb)]], m = (item / nrb) & 1, rb = item % nrb;
+        const MatW &W = m == 0 ? a.gate : a.up;
+        const int r0 = a.offsets[e], ntok = a.offsets[e + 1] - r0;
+        const uint8_t *idx = W.idx + (size_t)e * 3 * I * (H / 8);
+        const int n = rb * NS * kTeams + (threadIdx.x & 7) * kTeams + (threadIdx.x >> 3);  // slot k's row
+        for (int j0 = 0; j0 < ntok; j0 += 2) {
+            const int nt = min(2, ntok - j0);
+            int se[2] = {0, 0};
+            auto prep = [&]() {
+                if (j0 == 0) stage_cb(cbl, W.cb, e);
+                for (int t = 0; t < nt; t++) {
+                    const uint16_t *xr = (const uint16_t *)a.x + (size_t)(a.perm[r0 + j0 + t] / a.k) * H;
+                    float mx = 0.f;
+                    for (int c = threadIdx.x; c < H; c += kLutThreads) mx = fmaxf(mx, fabsf(bf16_bits_to_f32(xr[c])));
+                    se[t] = lut_scale_exp(block_max(mx, red));
+                    for (int c = threadIdx.x; c < H / 2; c += kLutThreads) {
+                        const uint32_t v = ((const uint32_t *)xr)[c];
+                        ((uint32_t *)(xs + (size_t)t * H))[c] =
+                            pack_h2f(ldexpf(bf16_bits_to_f32(v & 0xFFFFu), -se[t]), ldexpf(bf16_bits_to_f32(v >> 16), -se[t]));
+                    }
+                }
+            };
+            float o[2];
+            lut_rows<NS, 1, 2>(idx, I, H, rb, nt, xs, cbl, lut, o, prep);
+            if ((threadIdx.x & 7) < NS && n < I) {
+                for (int t = 0; t < nt; t++) gu[((size_t)(r0 + j0 + t) * 2 + m) * I + n] = ldexpf(o[t], se[t]);
             }
-        }
-        float o[2];
-        lut_rows<NS, 1, 2>(idx, I, H, rb, nt, xs, cbl, lut, o);
-        if ((threadIdx.x & 7) < NS && n < I) {
-            for (int t = 0; t < nt; t++) gu[((size_t)(r0 + j0 + t) * 2 + m) * I + n] = ldexpf(o[t], se[t]);
         }
     }
 }
 
-// down rows of one active unit: h = act(g, u) of each token (from gu), o = row . h, and the
-// p-weighted slot rows for the combine.
+// down rows: work item (unit u in the heavy-first order, row block rb) is u * nrb + rb; per
+// token h = act(g, u) (from gu), o = row . h, and the p-weighted slot rows for the combine.
 template <int NS>
 __global__ __launch_bounds__(kLutThreads, 1) void k_down_lut(const ExpertFwdArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) u32x4 lds_u[];
-    const int ai = blockIdx.y, rb = blockIdx.x;
-    if (ai >= *a.n_active) return;
-    const int e = a.active[ai];
     const int H = a.H, I = a.I;
     char *lut = (char *)lds_u;
     _Float16 *cbl = (_Float16 *)((char *)lds_u + kLutBytes);
     _Float16 *hs = (_Float16 *)((char *)lds_u + kLutBytes + kCbBytes);  // [2][I] fp16: hi, lo
     float *red = (float *)(hs + 2 * I);
-    stage_cb(cbl, a.down.cb, e);
-    const int r0 = a.offsets[e], ntok = a.offsets[e + 1] - r0;
+    int *sh = (int *)(red + kLutThreads / 64);
+    uint32_t *ctr = a.dec_sync + kSyncLut + kSyncPad;
+    const int nact = *a.n_active, nrb = (H + NS * kTeams - 1) / (NS * kTeams);
     const float *gu = a.gu ? a.gu : a.gu_ws;
-    const uint8_t *idx = a.down.idx + (size_t)e * 3 * H * (I / 8);
-    const int n = rb * NS * kTeams + (threadIdx.x & 7) * kTeams + (threadIdx.x >> 3);  // slot k's row
-    for (int j = 0; j < ntok; j++) {
-        const size_t rr = (size_t)(r0 + j);
-        const float *g = gu + rr * 2 * I, *u = g + I;
-        float mx = 0.f;
-        for (int c = threadIdx.x; c < I; c += kLutThreads) mx = fmaxf(mx, fabsf(act_h(a.act, g[c], u[c])));
-        const int se = lut_scale_exp(block_max(mx, red));
-        for (int c = threadIdx.x; c < I; c += kLutThreads) {
-            const float h = ldexpf(act_h(a.act, g[c], u[c]), -se);
-            const _Float16 hi = (_Float16)h;
-            hs[c] = hi;
-            hs[I + c] = (_Float16)(h - (float)hi);
+    for (;;) {
+        const int item = next_item(ctr, sh);
+        if (item >= nact * nrb) break;
+        const int e = a.active[a.lut_ord[item / nrb]], rb = item % nrb;
+        const int r0 = a.offsets[e], ntok = a.offsets[e + 1] - r0;
+        const uint8_t *idx = a.down.idx + (size_t)e * 3 * H * (I / 8);
+        const int n = rb * NS * kTeams + (threadIdx.x & 7) * kTeams + (threadIdx.x >> 3);  // slot k's row
+        for (int j = 0; j < ntok; j++) {
+            const size_t rr = (size_t)(r0 + j);
+            int se = 0;
+            auto prep = [&]() {
+                if (j == 0) stage_cb(cbl, a.down.cb, e);
+                const float *g = gu + rr * 2 * I, *u = g + I;
+                float mx = 0.f;
+                for (int c = threadIdx.x; c < I; c += kLutThreads) mx = fmaxf(mx, fabsf(act_h(a.act, g[c], u[c])));
+                se = lut_scale_exp(block_max(mx, red));
+                for (int c = threadIdx.x; c < I; c += kLutThreads) {
+                    const float h = ldexpf(act_h(a.act, g[c], u[c]), -se);
+                    const _Float16 hi = (_Float16)h;
+                    hs[c] = hi;
+                    hs[I + c] = (_Float16)(h - (float)hi);
+                }
+            };
+            float o[1];
+            lut_rows<NS, 2, 1>(idx, H, I, rb, 1, hs, cbl, lut, o, prep);
+            const int slot = a.perm[r0 + j];
+            if ((threadIdx.x & 7) < NS && n < H) a.ybuf[(size_t)slot * H + n] = ldexpf(a.w[slot], se) * o[0];
         }
-        float o[1];
-        lut_rows<NS, 2, 1>(idx, H, I, rb, 1, hs, cbl, lut, o);
-        const int slot = a.perm[r0 + j];
-        if ((threadIdx.x & 7) < NS && n < H) a.ybuf[(size_t)slot * H + n] = ldexpf(a.w[slot], se) * o[0];
     }
 }
 
 namespace {
 
 // Dynamic LDS: the table first (at LDS address 0: the kernels have no static LDS, so table
-// addresses need no base added), codebooks, token slice, block-maximum scratch.
-size_t lds_gu(const ExpertFwdArgs &a) { return (size_t)kLutBytes + kCbBytes + (size_t)4 * a.H + 4 * kLutThreads / 64; }
-size_t lds_down(const ExpertFwdArgs &a) { return (size_t)kLutBytes + kCbBytes + (size_t)4 * a.I + 4 * kLutThreads / 64; }
+// addresses need no base added), codebooks, token slices, block-maximum scratch, the item
+// broadcast word.
+size_t lds_sched(const ExpertFwdArgs &) { return 4 * kLutThreads / 64 + 4; }
+size_t lds_gu(const ExpertFwdArgs &a) { return (size_t)kLutBytes + kCbBytes + (size_t)4 * a.H + lds_sched(a); }
+size_t lds_down(const ExpertFwdArgs &a) { return (size_t)kLutBytes + kCbBytes + (size_t)4 * a.I + lds_sched(a); }
+
+// Compute units of the current device (cached per device).
+int device_cus()
+{
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cached[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) return 0;
+        cached[dev] = v;
+    }
+    return cached[dev];
+}
 
 // Largest dynamic LDS a block of the current device may take (cached per device).
 size_t max_lds_per_block()
@@ -376,13 +454,13 @@ size_t max_lds_per_block()
     return (size_t)cached[dev];
 }
 
-// Slots per team for NR rows: the fewest padded rows, then the most slots (eight slots
-// would not fit the 128 registers a thread of a 1024-thread block may hold).
-int pick_slots(int NR)
+// Slots per team for NR rows: the fewest padded rows, then the most slots, at most max_ns
+// (seven slots would not fit the 128 registers a thread of a 1024-thread block may hold).
+int pick_slots(int NR, int max_ns)
 {
-    int best = 7;
+    int best = max_ns;
     long bw = -1;
-    for (int ns = 7; ns >= 5; ns--) {
+    for (int ns = max_ns; ns >= 5; ns--) {
         const long rows = (long)ns * kTeams, w = ((NR + rows - 1) / rows) * rows - NR;
         if (bw < 0 || w < bw) {
             bw = w;
@@ -398,8 +476,9 @@ hipError_t launch_gu(const ExpertFwdArgs &a, int maxU, hipStream_t s)
     const size_t lds = lds_gu(a);
     hipError_t err = hipFuncSetAttribute((const void *)k_gu_lut<NS>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
+    const int items = maxU * 2 * ((a.I + NS * kTeams - 1) / (NS * kTeams));
     ProfScope ps(a.prof, PK_GATEUP, s);
-    ps.launch(k_gu_lut<NS>, dim3((a.I + NS * kTeams - 1) / (NS * kTeams), 2, maxU), dim3(kLutThreads), lds, a);
+    ps.launch(k_gu_lut<NS>, dim3(min(items, device_cus())), dim3(kLutThreads), lds, a);
     return hipGetLastError();
 }
 
@@ -409,20 +488,21 @@ hipError_t launch_down(const ExpertFwdArgs &a, int maxU, hipStream_t s)
     const size_t lds = lds_down(a);
     hipError_t err = hipFuncSetAttribute((const void *)k_down_lut<NS>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
+    const int items = maxU * ((a.H + NS * kTeams - 1) / (NS * kTeams));
     ProfScope ps(a.prof, PK_DOWN, s);
-    ps.launch(k_down_lut<NS>, dim3((a.H + NS * kTeams - 1) / (NS * kTeams), maxU), dim3(kLutThreads), lds, a);
+    ps.launch(k_down_lut<NS>, dim3(min(items, device_cus())), dim3(kLutThreads), lds, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
 // bf16 tokens, no adapter, both widths multiples of 256 (whole 32 x 32 table tiles),
-// index planes addressable with 31-bit offsets, the table, codebooks and token slice within
-// the device's LDS per block.
+// index planes addressable with 31-bit offsets, the launch counters and unit order present,
+// the table, codebooks and token slices within the device's LDS per block.
 bool rvq_lut_supported(const ExpertFwdArgs &a)
 {
-    if (!(a.wfmt == FMT_RVQ3 && a.xt == DT_BF16 && a.T <= 64 && !a.lora_gu && a.gu_ws && a.H % 256 == 0 &&
-          a.I % 256 == 0 && (size_t)3 * a.H * (a.I / 8) < ((size_t)1 << 31)))
+    if (!(a.wfmt == FMT_RVQ3 && a.xt == DT_BF16 && a.T <= 64 && !a.lora_gu && a.gu_ws && a.dec_sync && a.lut_ord &&
+          a.H % 256 == 0 && a.I % 256 == 0 && (size_t)3 * a.H * (a.I / 8) < ((size_t)1 << 31) && device_cus() > 0))
         return false;
     const size_t need = lds_gu(a) > lds_down(a) ? lds_gu(a) : lds_down(a);
     return need <= max_lds_per_block();
@@ -432,17 +512,11 @@ hipError_t launch_rvq_lut(const ExpertFwdArgs &a, hipStream_t s)
 {
     const int maxU = min(a.E, a.T * a.k);
     hipError_t err;
-    switch (pick_slots(a.I)) {
-        case 7: err = launch_gu<7>(a, maxU, s); break;
-        case 6: err = launch_gu<6>(a, maxU, s); break;
-        default: err = launch_gu<5>(a, maxU, s); break;
-    }
+    hipLaunchKernelGGL(k_lut_order, dim3(1), dim3(1024), 0, s, a);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    err = pick_slots(a.I, 6) == 6 ? launch_gu<6>(a, maxU, s) : launch_gu<5>(a, maxU, s);
     if (err != hipSuccess) return err;
-    switch (pick_slots(a.H)) {
-        case 7: return launch_down<7>(a, maxU, s);
-        case 6: return launch_down<6>(a, maxU, s);
-        default: return launch_down<5>(a, maxU, s);
-    }
+    return pick_slots(a.H, 6) == 6 ? launch_down<6>(a, maxU, s) : launch_down<5>(a, maxU, s);
 }
 
 }  // namespace moe

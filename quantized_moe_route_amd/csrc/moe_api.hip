@@ -48,6 +48,7 @@ struct Layout {
     size_t sh_rows, sh_ids, sh_w, sh_off, sh_perm, sh_inv, sh_act, sh_nact, sh_h;
     size_t status;    // the device status word (MOE_F_VALIDATE findings, internal timeouts)
     size_t dec_sync;  // counters of the fused few-token launch (zero between launches)
+    size_t lut_ord;   // the RVQ3 table-lookup launches' unit order [S] int32
     size_t total;
 };
 
@@ -99,6 +100,7 @@ Layout layout_of(const moe_desc &d)
     L.sh_h = take(std::min<size_t>(T, 16) * NS * I * 4);  // h planes of the shared units of the few-token launch
     L.status = take(4);
     L.dec_sync = take((size_t)moe::kSyncWords * 4);
+    L.lut_ord = take(S * 4);
     L.total = off;
     return L;
 }
@@ -481,12 +483,12 @@ moe_status static_scratch(char **out)
     return MOE_OK;
 }
 
-// Carving of `scratch` for T tokens: status word, counters of the fused few-token launch,
-// h as bf16 hi + lo planes [S][I] (RVQ3: the same region, twice the size, holds g and u
-// [S][2][I] fp32 for the table-lookup kernels, which take no h planes), weighted slot rows
-// [S][H] fp32 (S = T k).
+// Carving of `scratch` for T tokens: status word, counters of the fused few-token launch
+// and of the table-lookup launches, h as bf16 hi + lo planes [S][I] (RVQ3: the same region,
+// twice the size, holds g and u [S][2][I] fp32 for the table-lookup kernels, which take no h
+// planes), weighted slot rows [S][H] fp32, the table-lookup unit order [S] (S = T k).
 struct StaticLayout {
-    size_t status, sync, h, ybuf, total;
+    size_t status, sync, h, ybuf, ord, total;
 };
 
 StaticLayout static_layout(const moe_desc &d, int T)
@@ -503,6 +505,7 @@ StaticLayout static_layout(const moe_desc &d, int T)
     l.sync = take((size_t)moe::kSyncWords * 4);
     l.h = take(S * d.inter * (d.wfmt == MOE_W_RVQ3 ? 8 : 4));
     l.ybuf = take(S * d.hidden * 4);
+    l.ord = take(S * 4);
     l.total = off;
     return l;
 }
@@ -563,6 +566,7 @@ moe_status moe_forward(moe_layer *L, const void *x, int32_t xt, int32_t T, const
     a.h_lo = a.h_hi + (size_t)T * a.k * a.I;
     a.gu = saved_gu;
     a.gu_ws = (float *)(L->ws + L->lay.gu);
+    a.lut_ord = (int32_t *)(L->ws + L->lay.lut_ord);
     a.ybuf = (float *)(L->ws + L->lay.ybuf);
     if (L->d.flags & MOE_F_MX_GATEUP) {
         a.xq = (uint8_t *)(L->ws + L->lay.xq);
@@ -622,6 +626,7 @@ moe_status moe_forward(moe_layer *L, const void *x, int32_t xt, int32_t T, const
         sa.h_lo = sa.h_hi + (size_t)T * sa.k * sa.I;
         sa.gu = nullptr;
         sa.gu_ws = nullptr;  // sized for the routed slots; the shared units take other kernels
+        sa.lut_ord = nullptr;
         sa.ybuf = (float *)(L->ws + L->lay.sh_rows);
         sa.tok_chunks = tok_chunks(T);
         sa.skip_combine = 1;
@@ -839,7 +844,10 @@ moe_status moe_forward_static(moe_layer *L, const void *x, int32_t xt, int32_t T
     moe::ExpertFwdArgs a = routed_fwd_args(L, x, xt, T, r, y);
     a.h_hi = (uint16_t *)(base + sl.h);
     a.h_lo = a.h_hi + (size_t)T * a.k * a.I;
-    if (L->d.wfmt == MOE_W_RVQ3) a.gu_ws = (float *)(base + sl.h);
+    if (L->d.wfmt == MOE_W_RVQ3) {
+        a.gu_ws = (float *)(base + sl.h);
+        a.lut_ord = (int32_t *)(base + sl.ord);
+    }
     a.ybuf = (float *)(base + sl.ybuf);
     a.status = (uint32_t *)(base + sl.status);
     a.dec_sync = (uint32_t *)(base + sl.sync);

@@ -114,19 +114,24 @@ struct ExpertFwdArgs {
     MatW sh_gate, sh_up, sh_down;
     uint16_t *sh_h_hi, *sh_h_lo;
     float *sh_ybuf;
-    // Counters of the fused decode launch (kSyncWords, zero between launches; null: the
-    // three-launch path) and the status word its bounded waits report a timeout into.
+    // Counters of the fused decode launch and of the RVQ3 table-lookup launches (kSyncWords,
+    // zero between launches; null: the three-launch path, no table lookups) and the status
+    // word the fused launch's bounded waits report a timeout into.
     uint32_t *dec_sync;
     uint32_t *status;
     float *gu_ws;  // [S][2][I] workspace for g, u when gu is null (the RVQ3 table-lookup path), or null
+    int32_t *lut_ord;  // [S] the table-lookup launches' unit order (workspace), or null
 };
 
 // Counter layout of the fused decode launch: per-unit gate/up completions, per-stripe down
-// arrivals, completed stripes; each counter on its own 128-byte line (kSyncPad words).
+// arrivals, completed stripes; then the RVQ3 table-lookup launches' work counters (gate/up,
+// down; zeroed by the launch before them); each counter on its own 128-byte line (kSyncPad
+// words).
 constexpr int kSyncUnits = 1152;  // >= min(E, 16 k) + n_shared for the few-token path (k <= 64)
 constexpr int kSyncStripes = 64;  // >= H / 64
 constexpr int kSyncPad = 32;
-constexpr int kSyncWords = (kSyncUnits + kSyncStripes + 1) * kSyncPad;
+constexpr int kSyncLut = (kSyncUnits + kSyncStripes + 1) * kSyncPad;  // first table-lookup counter
+constexpr int kSyncWords = kSyncLut + 2 * kSyncPad;
 constexpr uint32_t kStatusSpinTimeout = 0x80000000u;  // status-word bit: a fused launch gave up waiting
 
 struct ExpertBwdArgs {

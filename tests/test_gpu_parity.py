@@ -288,6 +288,13 @@ def test_rvq3_table_lookup_row_blocks():
     run_small(host_case(w), name="rvq3-lut-blocks")
 
 
+def test_rvq3_table_lookup_blocks_take_several_items():
+    # 128 active experts x 2 matrices x 2 row blocks = 512 gate/up work items and 256 down
+    # items for a launch of one block per CU: blocks draw several items each
+    w = syn.shrink(syn.WORKLOADS["rvq16"], T=48, H=1024, I=1024, E=128, k=8, with_dy=True, x_key=24)
+    run_small(host_case(w), name="rvq3-lut-persistent")
+
+
 def test_single_token_and_k1():
     w = syn.shrink(TINY, T=1, k=1, x_key=10)
     run_small(host_case(w), name="T1-k1")

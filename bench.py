@@ -142,6 +142,8 @@ def main():
                     help="add N shared experts (K3 has 2), taken by every token with weight 1")
     ap.add_argument("--mx-gateup", action="store_true",
                     help="block-scaled gate/up (FP4 weights straight into the MFMA; grouped-GEMM workloads)")
+    ap.add_argument("--rvq-gather", action="store_true",
+                    help="RVQ3 few-token experts on the codeword-gather kernels instead of the table lookups")
     ap.add_argument("--quant-x8", action="store_true",
                     help="activation-quantized prefill: the experts take x quantized to MXFP8")
     ap.add_argument("--no-plain-read", action="store_true",
@@ -231,7 +233,7 @@ def main():
     else:
         shared_bytes = shared_gateup_bytes = 0
     kw["flags"] = ((C.MOE_F_LORA if args.lora else 0) | (C.MOE_F_MX_GATEUP if args.mx_gateup else 0)
-                   | (C.MOE_F_QUANT_X8 if args.quant_x8 else 0))
+                   | (C.MOE_F_QUANT_X8 if args.quant_x8 else 0) | (C.MOE_F_RVQ_GATHER if args.rvq_gather else 0))
     L = q.MoELayer(**kw)
     if args.lora:
         A_h, B_h = syn.lora_adapter(w, args.lora)
@@ -312,7 +314,10 @@ def main():
     S = w.T * w.k
     x_bytes = w.T * w.H * 2
     S_sh = w.T * args.shared
-    fused = ROOF_KERNEL[w.name][0] == "k_dec_fused"
+    roof = ROOF_KERNEL[w.name]
+    if args.rvq_gather and w.wfmt == "rvq3":
+        roof = ("k_gateup_rvq", ("expert_rvq.hip",), "RVQ3 gate/up as codeword gathers into fp16 MFMAs + SwiGLU")
+    fused = roof[0] == "k_dec_fused"
     if fused:
         # the single-token launch runs gate/up, down and the combine: every routed (and
         # shared) expert's bytes, the token row in and y out
@@ -330,9 +335,9 @@ def main():
     step_bytes = [u * expert_bytes + shared_bytes + wr.nbytes + x_bytes + w.T * w.H * 4 for u in steps_U]
     step_s = ms / 1e3 / args.steps
     tokens_per_s = w.T * args.steps / (ms / 1e3)
-    traffic = traffic_record(w.name)
+    traffic = traffic_record(w.name) if roof is ROOF_KERNEL[w.name] else None
     log(f"{args.steps} steps in {ms:.2f} ms (wall {wall * 1e3:.1f} ms): {step_s * 1e6:.1f} us/step, "
-        f"{tokens_per_s:.0f} tokens/s; {ROOF_KERNEL[w.name][0]} {gu_avg_s * 1e6:.1f} us avg, {achieved:.0f} GB/s")
+        f"{tokens_per_s:.0f} tokens/s; {roof[0]} {gu_avg_s * 1e6:.1f} us avg, {achieved:.0f} GB/s")
 
     detail = {"step_hbm_GBps": sum(step_bytes) / len(step_bytes) / step_s / 1e9,
               "step_alg_bytes": sum(step_bytes) / len(step_bytes),
@@ -349,11 +354,11 @@ def main():
         single = args.mx_gateup and args.quant_x8
         peak = FP8_PEAK_TFLOPS if single else BF16_PEAK_TFLOPS
         kname = ("k_gateup_mx (block-scaled gate/up + SwiGLU)" if args.mx_gateup
-                 else f"{ROOF_KERNEL[w.name][0]} ({ROOF_KERNEL[w.name][2]})")
+                 else f"{roof[0]} ({roof[2]})")
         roofline = {"bound": "mfma", "kernel": kname, "achieved": gu_tflops, "peak": peak, "unit": "TFLOP/s",
                     "frac": gu_tflops / peak, "traffic": traffic if not args.mx_gateup else None}
     else:
-        roofline = {"bound": "hbm", "kernel": f"{ROOF_KERNEL[w.name][0]} ({ROOF_KERNEL[w.name][2]})",
+        roofline = {"bound": "hbm", "kernel": f"{roof[0]} ({roof[2]})",
                     "achieved": achieved, "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
                     "traffic": traffic}
     if not train and not args.no_plain_read:

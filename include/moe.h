@@ -92,7 +92,11 @@ enum {
                                  from such a forward it is the quantized layer's, the quantization
                                  passed straight through (its derivative taken as 1).  H must be a
                                  multiple of 32 (always).  More workspace: 2 H bytes per token. */
-    MOE_F_VALIDATE = 16u      /* device checks of the data each call consumes (below) */
+    MOE_F_VALIDATE = 16u,     /* device checks of the data each call consumes (below) */
+    MOE_F_RVQ_GATHER = 32u    /* RVQ3 with few tokens per expert on the codeword-gather kernels
+                                 (each stage's codeword an fp16 MFMA operand) instead of the
+                                 codeword-table lookups; for comparing the two forms (same
+                                 results to the parity bar, different rounding order) */
 };
 
 /* MOE_F_VALIDATE (LazyLoRA README, "Three rules the engine is built around": unusable

@@ -17,6 +17,7 @@ MOE_F_MX_GATEUP = 2
 MOE_F_LORA = 4
 MOE_F_QUANT_X8 = 8
 MOE_F_VALIDATE = 16
+MOE_F_RVQ_GATHER = 32
 # bits of the MOE_F_VALIDATE status word
 MOE_BAD_X, MOE_BAD_DY, MOE_BAD_SCALE_NAN, MOE_BAD_SCALE_ZERO, MOE_BAD_CODEWORD = 1, 2, 4, 8, 16
 

@@ -103,10 +103,23 @@ __device__ __forceinline__ float block_max(float v, float *red)
 
 // Per-thread geometry of one block.
 struct LutGeom {
-    int V, ng, nstep;  // index bytes per row and stage, groups per row, stage-group steps
-    uint32_t plane;    // bytes per stage plane
-    int k, r;          // lane in team, lookup order (vector 16k + (i xor r) at step i)
+    int V, s0, ng, nstep;  // index bytes per row and stage; window g covers vectors 128 g - s0
+                           // .. 128 g - s0 + 127 (clipped to the row); windows; steps
+    uint32_t plane;        // bytes per stage plane
+    int k, r;              // lane in team, lookup order (position 16k + (i xor r) at step i)
 };
+
+// Rows fall into P = 128 / gcd(V, 128) phases by where they start within a 128-byte line
+// (row r starts at byte r V of its plane); a block takes rows of one phase c, r = c mod P,
+// and shifts its table windows by s0 = c V mod 128 vectors so that every window of every
+// row is whole 128-byte lines (a window that straddled two lines would read each of them
+// half, a step apart, and the other half often after the L2 has dropped the line).
+__device__ __host__ __forceinline__ int lut_phases(int V)
+{
+    int p = 128;
+    while (p > 1 && V % (128 / p * 2) == 0) p >>= 1;
+    return p;
+}
 
 // This thread's 16 index bytes of each slot's row for stage-group step st.  The whole offset
 // within the unit's index bytes is in the per-lane operand, which is all the buffer range
@@ -114,13 +127,14 @@ struct LutGeom {
 // offset 2^31, past the range (index planes are below 2^31 bytes), and read zeros without
 // touching memory.
 template <int NS>
-__device__ __forceinline__ void load_idx(uint32_t (&dst)[NS][4], __amdgpu_buffer_rsrc_t ir, const LutGeom &G,
+__device__ __forceinline__ void load_idx(uint32_t (&dst)[NS][4], __amdgpu_buffer_rsrc_t ir, const LutGeom &G, int P,
                                          uint32_t rowoff, uint32_t slot_ok, int st)
 {
     const int s = st / G.ng, g = st - s * G.ng;
-    const bool lane_ok = 16 * G.k < G.V - kGV * g;
-    const uint32_t off = (uint32_t)s * G.plane + rowoff + (uint32_t)(kGV * g + 16 * G.k);
-    const uint32_t slot_stride = (uint32_t)kTeams * (uint32_t)G.V;
+    const int v0 = kGV * g - G.s0 + 16 * G.k;  // this lane's first vector
+    const bool lane_ok = v0 >= 0 && v0 + 16 <= G.V;
+    const uint32_t off = (uint32_t)s * G.plane + rowoff + (uint32_t)v0;
+    const uint32_t slot_stride = (uint32_t)(kTeams * P) * (uint32_t)G.V;
 #pragma unroll
     for (int j = 0; j < NS; j++) {
         const uint32_t o = lane_ok && ((slot_ok >> j) & 1u) ? off + j * slot_stride : 0x80000000u;
@@ -129,25 +143,26 @@ __device__ __forceinline__ void load_idx(uint32_t (&dst)[NS][4], __amdgpu_buffer
     }
 }
 
-// Build the table of stage s, group g (gw vectors) for one token (xs: its NTERM fp16 planes
-// [NTERM][K]): 32 tiles of 32 codewords x 32 vectors, two per wave; lane supplies codeword /
-// vector lane mod 32, dimensions 4 (lane / 32) .. + 3, and gets back rows 8 (i / 4) +
-// 4 (lane / 32) + i mod 4 of the tile's column lane mod 32.
+// Build the table of stage s for the window starting at vector w0, positions plo .. phi - 1
+// (those inside the row), for one token (xs: its NTERM fp16 planes [NTERM][K]): 32 tiles
+// of 32 codewords x 32 positions, two per wave; lane supplies codeword / position lane mod
+// 32, dimensions 4 (lane / 32) .. + 3, and gets back rows 8 (i / 4) + 4 (lane / 32) + i mod 4
+// of the tile's column lane mod 32.
 template <int NTERM>
-__device__ __forceinline__ void build_table(int s, int g, int gw, int K, const _Float16 *xs, const _Float16 *cbl,
-                                            char *lut)
+__device__ __forceinline__ void build_table(int s, int w0, int plo, int phi, int K, const _Float16 *xs,
+                                            const _Float16 *cbl, char *lut)
 {
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
 #pragma unroll 1
     for (int h = 0; h < 2; h++) {
         const int t = wv + 16 * h, ct = t & 7, vt = t >> 3;
-        if (32 * vt >= gw) continue;
+        if (32 * vt < plo || 32 * vt + 32 > phi) continue;
         const int hl = lane >> 5, li = lane & 31;
         const h4v A = *(const h4v *)(cbl + (size_t)(256 * s + 32 * ct + li) * 8 + 4 * hl);
         f32x16 d = {};
 #pragma unroll
         for (int q = 0; q < NTERM; q++) {
-            const h4v B = *(const h4v *)(xs + (size_t)q * K + 8 * (kGV * g + 32 * vt + li) + 4 * hl);
+            const h4v B = *(const h4v *)(xs + (size_t)q * K + 8 * (w0 + 32 * vt + li) + 4 * hl);
             d = __builtin_amdgcn_mfma_f32_32x32x8f16(A, B, d, 0, 0, 0);
         }
         const int v = 32 * vt + li;
@@ -198,13 +213,14 @@ __device__ __forceinline__ void lut_step(uint32_t (&idx)[NS][4], float (&acc)[NT
                                          int nt, const _Float16 *xs, const _Float16 *cbl, char *lut)
 {
     const int s = st / G.ng, g = st - s * G.ng;
-    const int gw = min(kGV, G.V - kGV * g);  // vectors in this group (a multiple of 32)
-    const bool active = 16 * G.k < gw;
+    const int w0 = kGV * g - G.s0;                                     // the window's first vector
+    const int plo = max(0, -w0), phi = min(kGV, G.V - w0);             // positions inside the row
+    const bool active = 16 * G.k >= plo && 16 * G.k + 16 <= phi;       // (multiples of 32)
 #pragma unroll
     for (int t = 0; t < NT; t++) {
         if (t > 0 && t >= nt) break;
         __syncthreads();  // the previous lookups are done
-        build_table<NTERM>(s, g, gw, K, xs + (size_t)t * NTERM * K, cbl, lut);
+        build_table<NTERM>(s, w0, plo, phi, K, xs + (size_t)t * NTERM * K, cbl, lut);
         __syncthreads();
         if (active) {
             if (t == 0) {
@@ -216,31 +232,33 @@ __device__ __forceinline__ void lut_step(uint32_t (&idx)[NS][4], float (&acc)[NT
     }
 }
 
-// One matrix of one unit for nt <= NT tokens: slot j of team t is row rb * NS * 128 + j * 128
-// + t of NR, K inputs.  On return, out[u] in lane k of each team is the whole sum of its slot
+// One matrix of one unit for nt <= NT tokens, rows of phase c: slot j of team t is row
+// P (rb * NS * 128 + j * 128 + t) + c of NR, K inputs.  On return, out[u] in lane k of each team is the whole sum of its slot
 // k's row for token u (scaled by that token's 2^-se).  xs: the tokens as NTERM fp16 planes
 // each, [NT][NTERM][K] (LDS); cbl: the matrix's codebooks [3][256][8] fp16 (LDS); lut: 128
 // KB of LDS at address 0.
 // prep() (which stages the tokens and codebooks in LDS) runs after the first two steps' index
 // bytes are requested, so their latency overlaps it.
 template <int NS, int NTERM, int NT, typename Prep>
-__device__ __forceinline__ void lut_rows(const uint8_t *__restrict__ idx, int NR, int K, int rb, int nt, const _Float16 *xs,
-                                         const _Float16 *cbl, char *lut, float (&out)[NT], Prep &&prep)
+__device__ __forceinline__ void lut_rows(const uint8_t *__restrict__ idx, int NR, int K, int c, int rb, int nt,
+                                         const _Float16 *xs, const _Float16 *cbl, char *lut, float (&out)[NT], Prep &&prep)
 {
     const int tid = threadIdx.x, lane = tid & 63;
     LutGeom G;
     G.V = K / 8;
-    G.ng = (G.V + kGV - 1) / kGV;
+    const int P = lut_phases(G.V);
+    G.s0 = (c * G.V) & (kGV - 1);
+    G.ng = (G.V + G.s0 + kGV - 1) / kGV;
     G.nstep = 3 * G.ng;
     G.plane = (uint32_t)NR * G.V;
     G.k = tid & 7;
     G.r = 4 * ((lane >> 3) & 3) + (G.k >> 1);
     const __amdgpu_buffer_rsrc_t ir = lrsrc(idx, 3 * G.plane);
-    const int row0 = rb * NS * kTeams + (tid >> 3);  // slot 0's row
+    const int row0 = P * (rb * NS * kTeams + (tid >> 3)) + c;  // slot 0's row
     const uint32_t rowoff = (uint32_t)row0 * (uint32_t)G.V;
     uint32_t slot_ok = 0;  // bit j: slot j's row is in the matrix
 #pragma unroll
-    for (int j = 0; j < NS; j++) slot_ok |= (row0 + j * kTeams < NR ? 1u : 0u) << j;
+    for (int j = 0; j < NS; j++) slot_ok |= (row0 + j * P * kTeams < NR ? 1u : 0u) << j;
     float acc[NT][NS];
 #pragma unroll
     for (int t = 0; t < NT; t++)
@@ -249,13 +267,13 @@ __device__ __forceinline__ void lut_rows(const uint8_t *__restrict__ idx, int NR
     uint32_t ia[NS][4], ib[NS][4];  // index bytes of two consecutive steps
     // The prefetch is unconditional (the last step re-reads itself): a conditional load makes
     // the wait before the current step's first use cover the prefetch as well.
-    load_idx<NS>(ia, ir, G, rowoff, slot_ok, 0);
+    load_idx<NS>(ia, ir, G, P, rowoff, slot_ok, 0);
     for (int st = 0; st < G.nstep; st += 2) {
         const int s1 = min(st + 1, G.nstep - 1), s2 = min(st + 2, G.nstep - 1);
-        load_idx<NS>(ib, ir, G, rowoff, slot_ok, s1);
+        load_idx<NS>(ib, ir, G, P, rowoff, slot_ok, s1);
         if (st == 0) prep();
         lut_step<NS, NTERM, NT>(ia, acc, G, st, K, nt, xs, cbl, lut);
-        load_idx<NS>(ia, ir, G, rowoff, slot_ok, s2);
+        load_idx<NS>(ia, ir, G, P, rowoff, slot_ok, s2);
         if (st + 1 < G.nstep) lut_step<NS, NTERM, NT>(ib, acc, G, s1, K, nt, xs, cbl, lut);
     }
     // the team's 8 partial sums of each row; lane k keeps slot k's
@@ -321,8 +339,8 @@ __global__ __launch_bounds__(1024) void k_lut_order(const ExpertFwdArgs a)
     }
 }
 
-// gate and up rows: work item (unit u in the heavy-first order, matrix m, row block rb) is
-// item (u * 2 + m) * nrb + rb; up to two tokens per pass (the index bytes are read once per
+// gate and up rows: work item (unit u in the heavy-first order, matrix m, row phase c, row
+// block rb) is item ((u * 2 + m) * P + c) * nrb + rb; up to two tokens per pass (the index bytes are read once per
 // pass): g or u = row . x for every token of the unit, written to gu [S][2][I] (grouped rows).
 template <int NS>
 __global__ __launch_bounds__(kLutThreads, 1) void k_gu_lut(const ExpertFwdArgs a)
@@ -335,16 +353,18 @@ __global__ __launch_bounds__(kLutThreads, 1) void k_gu_lut(const ExpertFwdArgs a
     float *red = (float *)(xs + 2 * H);
     int *sh = (int *)(red + kLutThreads / 64);
     uint32_t *ctr = a.dec_sync + kSyncLut;
-    const int nact = *a.n_active, nrb = (I + NS * kTeams - 1) / (NS * kTeams);
+    const int P = lut_phases(H / 8), nrb = ((I + P - 1) / P + NS * kTeams - 1) / (NS * kTeams);
+    const int nact = *a.n_active, per = 2 * P * nrb;
     float *gu = a.gu ? a.gu : a.gu_ws;
     for (;;) {
         const int item = next_item(ctr, sh);
-        if (item >= nact * 2 * nrb) break;
-        const int e = a.active[a.lut_ord[item / (2 * nrb)]], m = (item / nrb) & 1, rb = item % nrb;
+        if (item >= nact * per) break;
+        const int e = a.active[a.lut_ord[item / per]], m = (item % per) / (P * nrb);
+        const int c = (item % (P * nrb)) / nrb, rb = item % nrb;
         const MatW &W = m == 0 ? a.gate : a.up;
         const int r0 = a.offsets[e], ntok = a.offsets[e + 1] - r0;
         const uint8_t *idx = W.idx + (size_t)e * 3 * I * (H / 8);
-        const int n = rb * NS * kTeams + (threadIdx.x & 7) * kTeams + (threadIdx.x >> 3);  // slot k's row
+        const int n = P * (rb * NS * kTeams + (threadIdx.x & 7) * kTeams + (threadIdx.x >> 3)) + c;  // slot k's row
         for (int j0 = 0; j0 < ntok; j0 += 2) {
             const int nt = min(2, ntok - j0);
             int se[2] = {0, 0};
@@ -363,7 +383,7 @@ __global__ __launch_bounds__(kLutThreads, 1) void k_gu_lut(const ExpertFwdArgs a
                 }
             };
             float o[2];
-            lut_rows<NS, 1, 2>(idx, I, H, rb, nt, xs, cbl, lut, o, prep);
+            lut_rows<NS, 1, 2>(idx, I, H, c, rb, nt, xs, cbl, lut, o, prep);
             if ((threadIdx.x & 7) < NS && n < I) {
                 for (int t = 0; t < nt; t++) gu[((size_t)(r0 + j0 + t) * 2 + m) * I + n] = ldexpf(o[t], se[t]);
             }
@@ -371,7 +391,8 @@ __global__ __launch_bounds__(kLutThreads, 1) void k_gu_lut(const ExpertFwdArgs a
     }
 }
 
-// down rows: work item (unit u in the heavy-first order, row block rb) is u * nrb + rb; per
+// down rows: work item (unit u in the heavy-first order, row phase c, row block rb) is
+// (u * P + c) * nrb + rb; per
 // token h = act(g, u) (from gu), o = row . h, and the p-weighted slot rows for the combine.
 template <int NS>
 __global__ __launch_bounds__(kLutThreads, 1) void k_down_lut(const ExpertFwdArgs a)
@@ -384,15 +405,16 @@ __global__ __launch_bounds__(kLutThreads, 1) void k_down_lut(const ExpertFwdArgs
     float *red = (float *)(hs + 2 * I);
     int *sh = (int *)(red + kLutThreads / 64);
     uint32_t *ctr = a.dec_sync + kSyncLut + kSyncPad;
-    const int nact = *a.n_active, nrb = (H + NS * kTeams - 1) / (NS * kTeams);
+    const int P = lut_phases(I / 8), nrb = ((H + P - 1) / P + NS * kTeams - 1) / (NS * kTeams);
+    const int nact = *a.n_active, per = P * nrb;
     const float *gu = a.gu ? a.gu : a.gu_ws;
     for (;;) {
         const int item = next_item(ctr, sh);
-        if (item >= nact * nrb) break;
-        const int e = a.active[a.lut_ord[item / nrb]], rb = item % nrb;
+        if (item >= nact * per) break;
+        const int e = a.active[a.lut_ord[item / per]], c = (item % per) / nrb, rb = item % nrb;
         const int r0 = a.offsets[e], ntok = a.offsets[e + 1] - r0;
         const uint8_t *idx = a.down.idx + (size_t)e * 3 * H * (I / 8);
-        const int n = rb * NS * kTeams + (threadIdx.x & 7) * kTeams + (threadIdx.x >> 3);  // slot k's row
+        const int n = P * (rb * NS * kTeams + (threadIdx.x & 7) * kTeams + (threadIdx.x >> 3)) + c;  // slot k's row
         for (int j = 0; j < ntok; j++) {
             const size_t rr = (size_t)(r0 + j);
             int se = 0;
@@ -410,7 +432,7 @@ __global__ __launch_bounds__(kLutThreads, 1) void k_down_lut(const ExpertFwdArgs
                 }
             };
             float o[1];
-            lut_rows<NS, 2, 1>(idx, H, I, rb, 1, hs, cbl, lut, o, prep);
+            lut_rows<NS, 2, 1>(idx, H, I, c, rb, 1, hs, cbl, lut, o, prep);
             const int slot = a.perm[r0 + j];
             if ((threadIdx.x & 7) < NS && n < H) a.ybuf[(size_t)slot * H + n] = ldexpf(a.w[slot], se) * o[0];
         }
@@ -476,7 +498,7 @@ hipError_t launch_gu(const ExpertFwdArgs &a, int maxU, hipStream_t s)
     const size_t lds = lds_gu(a);
     hipError_t err = hipFuncSetAttribute((const void *)k_gu_lut<NS>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
-    const int items = maxU * 2 * ((a.I + NS * kTeams - 1) / (NS * kTeams));
+    const int P = lut_phases(a.H / 8), items = maxU * 2 * P * (((a.I + P - 1) / P + NS * kTeams - 1) / (NS * kTeams));
     ProfScope ps(a.prof, PK_GATEUP, s);
     ps.launch(k_gu_lut<NS>, dim3(min(items, device_cus())), dim3(kLutThreads), lds, a);
     return hipGetLastError();
@@ -488,7 +510,7 @@ hipError_t launch_down(const ExpertFwdArgs &a, int maxU, hipStream_t s)
     const size_t lds = lds_down(a);
     hipError_t err = hipFuncSetAttribute((const void *)k_down_lut<NS>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (err != hipSuccess) return err;
-    const int items = maxU * ((a.H + NS * kTeams - 1) / (NS * kTeams));
+    const int P = lut_phases(a.I / 8), items = maxU * P * (((a.H + P - 1) / P + NS * kTeams - 1) / (NS * kTeams));
     ProfScope ps(a.prof, PK_DOWN, s);
     ps.launch(k_down_lut<NS>, dim3(min(items, device_cus())), dim3(kLutThreads), lds, a);
     return hipGetLastError();
@@ -514,9 +536,10 @@ hipError_t launch_rvq_lut(const ExpertFwdArgs &a, hipStream_t s)
     hipError_t err;
     hipLaunchKernelGGL(k_lut_order, dim3(1), dim3(1024), 0, s, a);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    err = pick_slots(a.I, 6) == 6 ? launch_gu<6>(a, maxU, s) : launch_gu<5>(a, maxU, s);
+    const int pg = lut_phases(a.H / 8), pd = lut_phases(a.I / 8);  // rows per phase: ceil(NR / P)
+    err = pick_slots((a.I + pg - 1) / pg, 6) == 6 ? launch_gu<6>(a, maxU, s) : launch_gu<5>(a, maxU, s);
     if (err != hipSuccess) return err;
-    return pick_slots(a.H, 6) == 6 ? launch_down<6>(a, maxU, s) : launch_down<5>(a, maxU, s);
+    return pick_slots((a.H + pd - 1) / pd, 6) == 6 ? launch_down<6>(a, maxU, s) : launch_down<5>(a, maxU, s);
 }
 
 }  // namespace moe

@@ -566,7 +566,7 @@ moe_status moe_forward(moe_layer *L, const void *x, int32_t xt, int32_t T, const
     a.h_lo = a.h_hi + (size_t)T * a.k * a.I;
     a.gu = saved_gu;
     a.gu_ws = (float *)(L->ws + L->lay.gu);
-    a.lut_ord = (int32_t *)(L->ws + L->lay.lut_ord);
+    if (!(L->d.flags & MOE_F_RVQ_GATHER)) a.lut_ord = (int32_t *)(L->ws + L->lay.lut_ord);
     a.ybuf = (float *)(L->ws + L->lay.ybuf);
     if (L->d.flags & MOE_F_MX_GATEUP) {
         a.xq = (uint8_t *)(L->ws + L->lay.xq);
@@ -846,7 +846,7 @@ moe_status moe_forward_static(moe_layer *L, const void *x, int32_t xt, int32_t T
     a.h_lo = a.h_hi + (size_t)T * a.k * a.I;
     if (L->d.wfmt == MOE_W_RVQ3) {
         a.gu_ws = (float *)(base + sl.h);
-        a.lut_ord = (int32_t *)(base + sl.ord);
+        if (!(L->d.flags & MOE_F_RVQ_GATHER)) a.lut_ord = (int32_t *)(base + sl.ord);
     }
     a.ybuf = (float *)(base + sl.ybuf);
     a.status = (uint32_t *)(base + sl.status);

@@ -2,6 +2,8 @@
 
   stats    kernel-trace statistics (the *_kernel_stats.csv of `rocprofv3 --stats`)
            -> a short text table;
+  counters per-dispatch means of every counter in one or more `rocprofv3 --pmc` runs, per
+           kernel family (given as name=regex pairs) -> a short text table;
   traffic  HBM bytes per launch of one kernel from two `rocprofv3 --pmc` runs
            (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the
            same counter reads for a copy kernel of known size run in the same process
@@ -43,6 +45,27 @@ def counter_avg(path: str, counter: str, name_re: str, min_value: float = 0.0):
     return (statistics.fmean(vals) if vals else None), len(vals)
 
 
+def counter_table(paths, kernels) -> str:
+    """Mean per-dispatch value of every counter found in the csv files, per kernel family
+    (kernels: list of (name, regex)); SQ counters are totals over the device."""
+    vals = {}
+    for p in paths:
+        for r in _rows(p):
+            for name, rx in kernels:
+                if re.search(rx, r["Kernel_Name"]):
+                    vals.setdefault((r["Counter_Name"], name), []).append(float(r["Counter_Value"]))
+    counters = sorted({c for c, _ in vals})
+    names = [n for n, _ in kernels]
+    out = [f"{'counter (mean per dispatch)':30s}" + "".join(f"{n:>18s}" for n in names)]
+    for c in counters:
+        row = f"{c:30s}"
+        for n in names:
+            v = vals.get((c, n))
+            row += f"{statistics.fmean(v):18.4g}" if v else f"{'-':>18s}"
+        out.append(row)
+    return "\n".join(out)
+
+
 def traffic(fetch_csv, write_csv, kernel_re, copy_re, copy_bytes):
     kf, nkf = counter_avg(fetch_csv, "FETCH_SIZE", kernel_re)
     kw, nkw = counter_avg(write_csv, "WRITE_SIZE", kernel_re)
@@ -71,6 +94,9 @@ def main(argv=None):
     a = sub.add_parser("stats")
     a.add_argument("csv")
     a.add_argument("--top", type=int, default=12)
+    c = sub.add_parser("counters")
+    c.add_argument("csv", nargs="+")
+    c.add_argument("--kernel", action="append", required=True, help="name=regex of a kernel family (repeatable)")
     b = sub.add_parser("traffic")
     b.add_argument("--fetch", required=True)
     b.add_argument("--write", required=True)
@@ -82,6 +108,9 @@ def main(argv=None):
     args = ap.parse_args(argv)
     if args.cmd == "stats":
         print(kernel_stats(args.csv, args.top))
+        return
+    if args.cmd == "counters":
+        print(counter_table(args.csv, [tuple(k.split("=", 1)) for k in args.kernel]))
         return
     rec = traffic(args.fetch, args.write, args.kernel, args.copy, args.copy_bytes)
     rec["kernel_source_hash"] = args.hash

@@ -131,6 +131,27 @@ __device__ __forceinline__ void k_loop3(int n, F &&step)
     if (s0 + 1 < n) step(Stage<1>(), s0 + 1);
 }
 
+// Runs step(Stage<st % 6>, st) for st = 0 .. n-1, so that both st % 3 (a register stage)
+// and st % 2 (an LDS buffer) are known at compile time in each copy of the body.
+template <typename F>
+__device__ __forceinline__ void k_loop6(int n, F &&step)
+{
+    int s0 = 0;
+    for (; s0 + 6 <= n; s0 += 6) {
+        step(Stage<0>(), s0);
+        step(Stage<1>(), s0 + 1);
+        step(Stage<2>(), s0 + 2);
+        step(Stage<3>(), s0 + 3);
+        step(Stage<4>(), s0 + 4);
+        step(Stage<5>(), s0 + 5);
+    }
+    if (s0 < n) step(Stage<0>(), s0);
+    if (s0 + 1 < n) step(Stage<1>(), s0 + 1);
+    if (s0 + 2 < n) step(Stage<2>(), s0 + 2);
+    if (s0 + 3 < n) step(Stage<3>(), s0 + 3);
+    if (s0 + 4 < n) step(Stage<4>(), s0 + 4);
+}
+
 // Runs step(Stage<st % 2>, st) for st = 0 .. n-1: two register stages.
 template <typename F>
 __device__ __forceinline__ void k_loop2(int n, F &&step)
@@ -319,19 +340,41 @@ __device__ __forceinline__ void gu_scl_next(uint8_t *scl, const GuBlock &b, int 
     __syncthreads();
 }
 
-template <int NT>
-__device__ __forceinline__ void gateup_pass(const ExpertFwdArgs &a, const GuBlock &b, MmTile *xs, uint8_t *scl, int r0,
-                                            int tt0, int nt)
+// s_waitcnt with only the vector-memory count: vmcnt(n), no wait on the other counters.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
 {
-    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// xs0, xs1: the two x-tile buffers, separate LDS arrays (step st reads buffer st % 2 while
+// the next tile streams into the other; as distinct objects the compiler can see that the
+// stream does not alias the reads, and need not wait for it before them).
+template <int NT>
+__device__ __forceinline__ void gateup_pass(const ExpertFwdArgs &a, const GuBlock &b, u32x4 *xs0, u32x4 *xs1,
+                                            uint8_t *scl, int r0, int tt0, int nt)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, li = lane & 15;
     const int H = a.H, I = a.I, nsteps = H / 128;
-    const int xr = tid >> 4, xc = tid & 15;  // this thread's x-tile row (+16 i) and chunk
-    uint32_t xoff[NT];                       // byte offsets at K-step 0
+    // The x tile goes straight from memory to LDS (buffer loads with the LDS flag): piece i
+    // of wave wv fills the 64 slots 64 (wv + 4 i) .. +63, slot s = 16 row + (chunk ^ (row &
+    // 15)), so lane l loads row 16 i + 4 wv + l / 16, chunk (l % 16) ^ (row % 16).  Nothing
+    // of it passes through registers.
+    uint32_t xoff[NT];  // byte offsets at K-step 0
 #pragma unroll
     for (int i = 0; i < NT; i++) {
-        const int tok = a.perm[r0 + tt0 + min(xr + 16 * i, nt - 1)] / a.k;
-        xoff[i] = ((uint32_t)tok * H + 8 * xc) * 2;
+        const int row = 16 * i + 4 * wv + (lane >> 4), chunk = (lane & 15) ^ (row & 15);
+        const int tok = a.perm[r0 + tt0 + min(row, nt - 1)] / a.k;
+        xoff[i] = ((uint32_t)tok * H + 8 * chunk) * 2;
     }
+    auto load_x = [&](u32x4 *dst, int st) {
+#pragma unroll
+        for (int i = 0; i < NT; i++)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                b.x, (__attribute__((address_space(3))) void *)((char *)dst + 1024 * (wv + 4 * i)), 16, xoff[i],
+                256 * st, 0, 0);
+    };
     f32x4 acc[4][NT];
 #pragma unroll
     for (int t = 0; t < 4; t++)
@@ -346,14 +389,13 @@ __device__ __forceinline__ void gateup_pass(const ExpertFwdArgs &a, const GuBloc
     {
         GuScl sv;
         gu_scl_load(sv, b, H, 0, nsteps);
-        u32x4 xv[NT];
-#pragma unroll
-        for (int i = 0; i < NT; i++) xv[i] = ld16(b.x, xoff[i], 0);
-        gu_scl_store(sv, scl, 0, nsteps);
+        load_x(xs0, 0);
+        __builtin_amdgcn_sched_barrier(0);
         load_w(Stage<0>(), 0);
         load_w(Stage<1>(), min(1, nsteps - 1));
-#pragma unroll
-        for (int i = 0; i < NT; i++) xs[0][lds_slot(xr + 16 * i, xc)] = xv[i];
+        __builtin_amdgcn_sched_barrier(0);
+        gu_scl_store(sv, scl, 0, nsteps);
+        wait_vmcnt<8>();  // the x tile (issued before the eight weight loads)
     }
     __syncthreads();
     // the scale bytes of the step are read from LDS one step ahead
@@ -361,19 +403,19 @@ __device__ __forceinline__ void gateup_pass(const ExpertFwdArgs &a, const GuBloc
 #pragma unroll
     for (int t = 0; t < 4; t++) scn[t] = scl[b.sl + (t >> 1) * 128 * kSclRow + (t & 1) * 16 * kSclRow + 4 * 0];
 
-    k_loop3(nsteps, [&](auto P, int st) {
-        constexpr int p = decltype(P)::value;
-        const int buf = st & 1;
+    k_loop6(nsteps, [&](auto P6, int st) {
+        constexpr int p = decltype(P6)::value % 3, parity = decltype(P6)::value & 1;
+        u32x4 *const xcur = parity ? xs1 : xs0, *const xnxt = parity ? xs0 : xs1;
         const int sst = st % kGuSclSteps;
         if (sst == 0 && st != 0) {  // the next K chunk (H beyond 3584)
             gu_scl_next(scl, b, H, st, nsteps);
 #pragma unroll
             for (int t = 0; t < 4; t++) scn[t] = scl[b.sl + (t >> 1) * 128 * kSclRow + (t & 1) * 16 * kSclRow + 4 * 0];
         }
-        u32x4 xv[NT];  // next step's x tile, issued before the weights so waiting for it
-        const int stn = min(st + 1, nsteps - 1);  // leaves the weight prefetch in flight
-#pragma unroll
-        for (int i = 0; i < NT; i++) xv[i] = ld16(b.x, xoff[i], 256 * stn);
+        // next step's x tile into the other buffer, issued before the weights so that waiting
+        // for it leaves the weight prefetch in flight
+        load_x(xnxt, min(st + 1, nsteps - 1));
+        __builtin_amdgcn_sched_barrier(0);
         load_w(Stage<(p + 2) % 3>(), min(st + 2, nsteps - 1));
         __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the step's MFMAs
         float scale[4];
@@ -386,7 +428,7 @@ __device__ __forceinline__ void gateup_pass(const ExpertFwdArgs &a, const GuBloc
         for (int s = 0; s < 4; s++) {
             bf16x8 A[4], B[NT];
 #pragma unroll
-            for (int tt = 0; tt < NT; tt++) B[tt] = as_bf16x8(xs[buf][lds_slot(16 * tt + li, 4 * g + s)]);
+            for (int tt = 0; tt < NT; tt++) B[tt] = as_bf16x8(xcur[lds_slot(16 * tt + li, 4 * g + s)]);
 #pragma unroll
             for (int t = 0; t < 4; t++) A[t] = fp4x8_to_bf16(q[p][t][s], scale[t]);
 #pragma unroll
@@ -394,8 +436,7 @@ __device__ __forceinline__ void gateup_pass(const ExpertFwdArgs &a, const GuBloc
 #pragma unroll
                 for (int t = 0; t < 4; t++) acc[t][tt] = mfma16(A[t], B[tt], acc[t][tt]);
         }
-#pragma unroll
-        for (int i = 0; i < NT; i++) xs[buf ^ 1][lds_slot(xr + 16 * i, xc)] = xv[i];
+        wait_vmcnt<4>();  // this thread's part of the next x tile (the 4 weight loads came after)
         __syncthreads();
     });
 
@@ -443,7 +484,7 @@ __device__ __forceinline__ void gateup_pass(const ExpertFwdArgs &a, const GuBloc
 
 __global__ __launch_bounds__(256, 2) void k_gateup_mm(const ExpertFwdArgs a)
 {
-    __shared__ MmTile xs[2];
+    __shared__ MmTile xs0, xs1;
     __shared__ __attribute__((aligned(16))) uint8_t scl[256 * kSclRow];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
     const int H = a.H, I = a.I;
@@ -465,12 +506,12 @@ __global__ __launch_bounds__(256, 2) void k_gateup_mm(const ExpertFwdArgs a)
     for (int tt0 = 0; tt0 < ntok; tt0 += kMmTok) {
         const int nt = min(kMmTok, ntok - tt0);
         switch ((nt + 15) / 16) {
-        case 1: gateup_pass<1>(a, b, xs, scl, r0, tt0, nt); break;
-        case 2: gateup_pass<2>(a, b, xs, scl, r0, tt0, nt); break;
-        case 3: gateup_pass<3>(a, b, xs, scl, r0, tt0, nt); break;
-        case 4: gateup_pass<4>(a, b, xs, scl, r0, tt0, nt); break;
-        case 5: gateup_pass<5>(a, b, xs, scl, r0, tt0, nt); break;
-        default: gateup_pass<6>(a, b, xs, scl, r0, tt0, nt); break;
+        case 1: gateup_pass<1>(a, b, xs0, xs1, scl, r0, tt0, nt); break;
+        case 2: gateup_pass<2>(a, b, xs0, xs1, scl, r0, tt0, nt); break;
+        case 3: gateup_pass<3>(a, b, xs0, xs1, scl, r0, tt0, nt); break;
+        case 4: gateup_pass<4>(a, b, xs0, xs1, scl, r0, tt0, nt); break;
+        case 5: gateup_pass<5>(a, b, xs0, xs1, scl, r0, tt0, nt); break;
+        default: gateup_pass<6>(a, b, xs0, xs1, scl, r0, tt0, nt); break;
         }
     }
 }

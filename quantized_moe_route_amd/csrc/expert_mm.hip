@@ -742,18 +742,30 @@ __device__ __forceinline__ void dn_scl_next(uint8_t *scl, const DnBlock &b, int 
     __syncthreads();
 }
 
+// hs0, hs1: the two h-tile buffers (separate LDS arrays, as for the gate/up's x tile).
 template <int NT>
-__device__ __forceinline__ void down_pass(const ExpertFwdArgs &a, const DnBlock &b, MmTile *hs, uint8_t *scl, int r0,
-                                          int tt0, int nt)
+__device__ __forceinline__ void down_pass(const ExpertFwdArgs &a, const DnBlock &b, u32x4 *hs0, u32x4 *hs1,
+                                          uint8_t *scl, int r0, int tt0, int nt)
 {
-    const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, li = lane & 15;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6, g = lane >> 4, li = lane & 15;
     const int H = a.H, I = a.I, nsteps = I / 64;
-    const int xr = tid >> 4, xc = tid & 15;
-    const uint32_t plane = xc < 8 ? 0u : (uint32_t)(a.h_lo - a.h_hi) * 2;  // this thread's plane
-    uint32_t hoff[NT];                                                      // byte offsets at K-step 0
+    // The h tile goes straight from memory to LDS, as the gate/up's x tile: lane l of wave
+    // wv, piece i, loads row 16 i + 4 wv + l / 16, chunk c = (l % 16) ^ (row % 16) (chunks
+    // 0..7 from h_hi, 8..15 from h_lo).
+    uint32_t hoff[NT];  // byte offsets at K-step 0
 #pragma unroll
-    for (int i = 0; i < NT; i++)
-        hoff[i] = plane + ((uint32_t)(r0 + tt0 + min(xr + 16 * i, nt - 1)) * I + 8 * (xc & 7)) * 2;
+    for (int i = 0; i < NT; i++) {
+        const int row = 16 * i + 4 * wv + (lane >> 4), chunk = (lane & 15) ^ (row & 15);
+        const uint32_t plane = chunk < 8 ? 0u : (uint32_t)(a.h_lo - a.h_hi) * 2;
+        hoff[i] = plane + ((uint32_t)(r0 + tt0 + min(row, nt - 1)) * I + 8 * (chunk & 7)) * 2;
+    }
+    auto load_h = [&](u32x4 *dst, int st) {
+#pragma unroll
+        for (int i = 0; i < NT; i++)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                b.h, (__attribute__((address_space(3))) void *)((char *)dst + 1024 * (wv + 4 * i)), 16, hoff[i],
+                128 * st, 0, 0);
+    };
     f32x4 acc[4][NT];
 #pragma unroll
     for (int t = 0; t < 4; t++)
@@ -768,33 +780,30 @@ __device__ __forceinline__ void down_pass(const ExpertFwdArgs &a, const DnBlock 
     {
         u32x4 sv[scl_pieces<256>()];
         scl_load<256>(sv, b.scale, b.sblk, I / 32, 0, 2 * min(kDnSclSteps, nsteps));
-        u32x4 hv[NT];
-#pragma unroll
-        for (int i = 0; i < NT; i++) hv[i] = ld16(b.h, hoff[i], 0);
-        scl_store<256>(sv, scl, 2 * min(kDnSclSteps, nsteps));
+        load_h(hs0, 0);
+        __builtin_amdgcn_sched_barrier(0);
         load_w(Stage<0>(), 0);
         load_w(Stage<1>(), min(1, nsteps - 1));
-#pragma unroll
-        for (int i = 0; i < NT; i++) hs[0][lds_slot(xr + 16 * i, xc)] = hv[i];
+        __builtin_amdgcn_sched_barrier(0);
+        scl_store<256>(sv, scl, 2 * min(kDnSclSteps, nsteps));
+        wait_vmcnt<8>();  // the h tile (issued before the eight weight loads)
     }
     __syncthreads();
     uint32_t scn[4];  // the scale bytes of the step, read from LDS one step ahead
 #pragma unroll
     for (int t = 0; t < 4; t++) scn[t] = scl[b.sl + t * 16 * kSclRow + 2 * 0];
 
-    k_loop3(nsteps, [&](auto P, int st) {
-        constexpr int p = decltype(P)::value;
-        const int buf = st & 1;
+    k_loop6(nsteps, [&](auto P6, int st) {
+        constexpr int p = decltype(P6)::value % 3, parity = decltype(P6)::value & 1;
+        u32x4 *const hcur = parity ? hs1 : hs0, *const hnxt = parity ? hs0 : hs1;
         const int sst = st % kDnSclSteps;
         if (sst == 0 && st != 0) {  // the next K chunk (I beyond 3584)
             dn_scl_next(scl, b, I, st, nsteps);
 #pragma unroll
             for (int t = 0; t < 4; t++) scn[t] = scl[b.sl + t * 16 * kSclRow + 2 * 0];
         }
-        u32x4 hv[NT];
-        const int stn = min(st + 1, nsteps - 1);
-#pragma unroll
-        for (int i = 0; i < NT; i++) hv[i] = ld16(b.h, hoff[i], 128 * stn);
+        load_h(hnxt, min(st + 1, nsteps - 1));  // next step's h tile, before the weights
+        __builtin_amdgcn_sched_barrier(0);
         load_w(Stage<(p + 2) % 3>(), min(st + 2, nsteps - 1));
         __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the step's MFMAs
         float scale[4];
@@ -808,8 +817,8 @@ __device__ __forceinline__ void down_pass(const ExpertFwdArgs &a, const DnBlock 
             bf16x8 A[4], Bh[NT], Bl[NT];
 #pragma unroll
             for (int tt = 0; tt < NT; tt++) {
-                Bh[tt] = as_bf16x8(hs[buf][lds_slot(16 * tt + li, 2 * g + s)]);
-                Bl[tt] = as_bf16x8(hs[buf][lds_slot(16 * tt + li, 8 + 2 * g + s)]);
+                Bh[tt] = as_bf16x8(hcur[lds_slot(16 * tt + li, 2 * g + s)]);
+                Bl[tt] = as_bf16x8(hcur[lds_slot(16 * tt + li, 8 + 2 * g + s)]);
             }
 #pragma unroll
             for (int t = 0; t < 4; t++) A[t] = fp4x8_to_bf16(q[p][t][s], scale[t]);
@@ -821,8 +830,7 @@ __device__ __forceinline__ void down_pass(const ExpertFwdArgs &a, const DnBlock 
                     acc[t][tt] = mfma16(A[t], Bl[tt], acc[t][tt]);
                 }
         }
-#pragma unroll
-        for (int i = 0; i < NT; i++) hs[buf ^ 1][lds_slot(xr + 16 * i, xc)] = hv[i];
+        wait_vmcnt<4>();  // this thread's part of the next h tile (the 4 weight loads came after)
         __syncthreads();
     });
 
@@ -844,7 +852,7 @@ __device__ __forceinline__ void down_pass(const ExpertFwdArgs &a, const DnBlock 
 
 __global__ __launch_bounds__(256, 2) void k_down_mm(const ExpertFwdArgs a)
 {
-    __shared__ MmTile hs[2];
+    __shared__ MmTile hs0, hs1;
     __shared__ __attribute__((aligned(16))) uint8_t scl[256 * kSclRow];
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6, g = lane >> 4, li = lane & 15;
     const int H = a.H, I = a.I;
@@ -863,12 +871,12 @@ __global__ __launch_bounds__(256, 2) void k_down_mm(const ExpertFwdArgs a)
     for (int tt0 = 0; tt0 < ntok; tt0 += kMmTok) {
         const int nt = min(kMmTok, ntok - tt0);
         switch ((nt + 15) / 16) {
-        case 1: down_pass<1>(a, b, hs, scl, r0, tt0, nt); break;
-        case 2: down_pass<2>(a, b, hs, scl, r0, tt0, nt); break;
-        case 3: down_pass<3>(a, b, hs, scl, r0, tt0, nt); break;
-        case 4: down_pass<4>(a, b, hs, scl, r0, tt0, nt); break;
-        case 5: down_pass<5>(a, b, hs, scl, r0, tt0, nt); break;
-        default: down_pass<6>(a, b, hs, scl, r0, tt0, nt); break;
+        case 1: down_pass<1>(a, b, hs0, hs1, scl, r0, tt0, nt); break;
+        case 2: down_pass<2>(a, b, hs0, hs1, scl, r0, tt0, nt); break;
+        case 3: down_pass<3>(a, b, hs0, hs1, scl, r0, tt0, nt); break;
+        case 4: down_pass<4>(a, b, hs0, hs1, scl, r0, tt0, nt); break;
+        case 5: down_pass<5>(a, b, hs0, hs1, scl, r0, tt0, nt); break;
+        default: down_pass<6>(a, b, hs0, hs1, scl, r0, tt0, nt); break;
         }
     }
 }

@@ -47,32 +47,38 @@ __device__ __forceinline__ float bound_of(float eb, float l)
     return 1.001f * kU * eb + kU * fabsf(l) + 1e-30f;
 }
 
-// GEMV form for up to 64 tokens and H <= 4096: one block per (expert, group of 8
-// tokens).  Thread tid owns the float4 chunks tid + 256 m of the router row (held in
-// registers) and runs one FMA chain per token over them; the 64 lanes of a wave are
-// summed by the DPP tree and the four wave sums in a fixed order.  Grid: (E, ceil(T/8)).
+// GEMV form for up to 64 tokens and H <= 4096: one block per (pair of experts, group of 8
+// tokens).  Thread tid owns the float4 chunks tid + 256 m of both router rows (held in
+// registers, all eight loads issued together) and runs one FMA chain per (expert, token)
+// over them; the 64 lanes of a wave are summed by the DPP tree and the four wave sums in a
+// fixed order.  Grid: (ceil(E / 2), ceil(T / 8)).
 constexpr int kGemvMaxT = 64;
 constexpr int kGemvMaxH = 4096;
+constexpr int kGemvE = 2;  // experts per block
 
 __global__ __launch_bounds__(256) void k_router_gemv(const void *__restrict__ x, int xt, const float *__restrict__ wr,
                                                      const float *__restrict__ bias, int T, int H, int E,
                                                      float *__restrict__ logits, float *__restrict__ beta)
 {
-    __shared__ float ps[4][8], pe[4][8];
+    __shared__ float ps[kGemvE][4][8], pe[kGemvE][4][8];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int e = blockIdx.x, t0 = blockIdx.y * 8;
+    const int e0 = blockIdx.x * kGemvE, t0 = blockIdx.y * 8;
     const int n4 = H / 4;
-    const float *wrow = wr + (size_t)e * H;
-    float4 w4[4];
+    float4 w4[kGemvE][4];
 #pragma unroll
-    for (int m = 0; m < 4; m++) {
-        const int c = tid + 256 * m;
-        w4[m] = c < n4 ? *(const float4 *)(wrow + 4 * c) : float4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < kGemvE; j++) {
+        const float *wrow = wr + (size_t)min(e0 + j, E - 1) * H;
+#pragma unroll
+        for (int m = 0; m < 4; m++) {
+            const int c = tid + 256 * m;
+            w4[j][m] = c < n4 ? *(const float4 *)(wrow + 4 * c) : float4{0.f, 0.f, 0.f, 0.f};
+        }
     }
-    float acc[8], eb[8];
+    float acc[kGemvE][8], eb[kGemvE][8];
 #pragma unroll
     for (int u = 0; u < 8; u++) {
-        acc[u] = eb[u] = 0.f;
+#pragma unroll
+        for (int j = 0; j < kGemvE; j++) acc[j][u] = eb[j][u] = 0.f;
         const int t = t0 + u;
         if (t >= T) continue;
         float xv[4][4];
@@ -85,36 +91,44 @@ __global__ __launch_bounds__(256) void k_router_gemv(const void *__restrict__ x,
                 xv[m][0] = xv[m][1] = xv[m][2] = xv[m][3] = 0.f;
         }
 #pragma unroll
-        for (int m = 0; m < 4; m++) {
-            if (tid + 256 * m >= n4) break;
-            acc[u] = fmaf(xv[m][0], w4[m].x, acc[u]);
-            eb[u] += fabsf(acc[u]);
-            acc[u] = fmaf(xv[m][1], w4[m].y, acc[u]);
-            eb[u] += fabsf(acc[u]);
-            acc[u] = fmaf(xv[m][2], w4[m].z, acc[u]);
-            eb[u] += fabsf(acc[u]);
-            acc[u] = fmaf(xv[m][3], w4[m].w, acc[u]);
-            eb[u] += fabsf(acc[u]);
+        for (int j = 0; j < kGemvE; j++) {
+#pragma unroll
+            for (int m = 0; m < 4; m++) {
+                if (tid + 256 * m >= n4) break;
+                acc[j][u] = fmaf(xv[m][0], w4[j][m].x, acc[j][u]);
+                eb[j][u] += fabsf(acc[j][u]);
+                acc[j][u] = fmaf(xv[m][1], w4[j][m].y, acc[j][u]);
+                eb[j][u] += fabsf(acc[j][u]);
+                acc[j][u] = fmaf(xv[m][2], w4[j][m].z, acc[j][u]);
+                eb[j][u] += fabsf(acc[j][u]);
+                acc[j][u] = fmaf(xv[m][3], w4[j][m].w, acc[j][u]);
+                eb[j][u] += fabsf(acc[j][u]);
+            }
         }
     }
 #pragma unroll
     for (int u = 0; u < 8; u++) {
         if (t0 + u >= T) break;
-        float ebt = eb[u];
-        const float sv = wave_sum_f32_eb(acc[u], ebt);
-        if (lane == 0) {
-            ps[wv][u] = sv;
-            pe[wv][u] = ebt;
+#pragma unroll
+        for (int j = 0; j < kGemvE; j++) {
+            float ebt = eb[j][u];
+            const float sv = wave_sum_f32_eb(acc[j][u], ebt);
+            if (lane == 0) {
+                ps[j][wv][u] = sv;
+                pe[j][wv][u] = ebt;
+            }
         }
     }
     __syncthreads();
-    if (tid < 8 && t0 + tid < T) {
-        const int u = tid, t = t0 + u;
-        const float s01 = ps[0][u] + ps[1][u], s23 = ps[2][u] + ps[3][u], r = s01 + s23;
-        const float ebt = ((pe[0][u] + pe[1][u]) + fabsf(s01)) + ((pe[2][u] + pe[3][u]) + fabsf(s23)) + fabsf(r);
-        const float l = r + (bias ? bias[e] : 0.f);
-        logits[(size_t)t * E + e] = l;
-        beta[(size_t)t * E + e] = bound_of(ebt, l);
+    if (tid < 8 * kGemvE) {
+        const int u = tid & 7, j = tid >> 3, t = t0 + u, e = e0 + j;
+        if (t < T && e < E) {
+            const float s01 = ps[j][0][u] + ps[j][1][u], s23 = ps[j][2][u] + ps[j][3][u], r = s01 + s23;
+            const float ebt = ((pe[j][0][u] + pe[j][1][u]) + fabsf(s01)) + ((pe[j][2][u] + pe[j][3][u]) + fabsf(s23)) + fabsf(r);
+            const float l = r + (bias ? bias[e] : 0.f);
+            logits[(size_t)t * E + e] = l;
+            beta[(size_t)t * E + e] = bound_of(ebt, l);
+        }
     }
 }
 
@@ -712,7 +726,7 @@ static hipError_t launch_small_pl(const RouteArgs &a, const GroupArgs &g, hipStr
 {
     {
         ProfScope ps(a.prof, PK_ROUTER_LOGITS, s);
-        ps.launch(k_router_gemv, dim3(a.E, (a.T + 7) / 8), dim3(256), 0, a.x, a.xt, a.wr,
+        ps.launch(k_router_gemv, dim3((a.E + kGemvE - 1) / kGemvE, (a.T + 7) / 8), dim3(256), 0, a.x, a.xt, a.wr,
                            a.bias, a.T, a.H, a.E, a.logits, a.beta);
     }
     const hipError_t err = hipGetLastError();
@@ -749,7 +763,7 @@ hipError_t launch_router(const RouteArgs &a, hipStream_t s)
     {
     ProfScope ps(a.prof, PK_ROUTER_LOGITS, s);
     if (a.T <= kGemvMaxT && a.H <= kGemvMaxH) {
-        ps.launch(k_router_gemv, dim3(a.E, (a.T + 7) / 8), dim3(256), 0, a.x, a.xt, a.wr, a.bias,
+        ps.launch(k_router_gemv, dim3((a.E + kGemvE - 1) / kGemvE, (a.T + 7) / 8), dim3(256), 0, a.x, a.xt, a.wr, a.bias,
                            a.T, a.H, a.E, a.logits, a.beta);
     } else {
         ps.launch(k_router_f64, dim3((a.E + kRfTile - 1) / kRfTile, (a.T + kRfTile - 1) / kRfTile), dim3(256), 0,

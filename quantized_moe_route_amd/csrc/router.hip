@@ -596,17 +596,6 @@ __global__ __launch_bounds__(256) void k_topk(const float *__restrict__ logits, 
     topk_one<PL>(t, logits, beta, x, xt, wr, bias, H, E, k, ids, wts, refined, scs[wv], nullptr, wbias);
 }
 
-// Position of q among the sorted s[0, 128) (entries past the slot count hold INT_MAX):
-// the number of entries below q.  Fixed steps and no branch, so that the searches of
-// one thread interleave.
-__device__ __forceinline__ int lower_bound128(const int *s, int q)
-{
-    int pos = 0;
-#pragma unroll
-    for (int step = 64; step > 0; step >>= 1) pos += s[pos + step - 1] < q ? step : 0;
-    return pos;
-}
-
 // Small batches (T <= 4, T k <= 256): top-k of every token and the grouping of the
 // T k slots in one single-block launch (the logits come from k_router_gemv, whose
 // kernel boundary makes them visible).  Wave w ranks token w; then the block groups
@@ -658,13 +647,27 @@ __global__ __launch_bounds__(256) void k_topk_group(const RouteArgs a, const Gro
             }
         }
         __syncthreads();
+        // offsets[q] = the slots of experts below q, counts[q] = those of q: counted against
+        // the sorted list read in 16-entry pieces (independent LDS reads, no dependent search;
+        // entries past S hold INT_MAX and count for no expert)
         for (int q0 = 0; q0 < E; q0 += 1024) {
-            int lo[4], hi[4];
+            int lo[4] = {0, 0, 0, 0}, hi[4] = {0, 0, 0, 0};
+            for (int c0 = 0; c0 < S; c0 += 16) {
+                int v[16];
 #pragma unroll
-            for (int r = 0; r < 4; r++) {
-                const int q = q0 + tid + 256 * r;
-                lo[r] = lower_bound128(se, q);
-                hi[r] = lower_bound128(se, q + 1);
+                for (int i = 0; i < 4; i++) {
+                    const int4 w = *(const int4 *)(se + c0 + 4 * i);
+                    v[4 * i] = w.x; v[4 * i + 1] = w.y; v[4 * i + 2] = w.z; v[4 * i + 3] = w.w;
+                }
+#pragma unroll
+                for (int r = 0; r < 4; r++) {
+                    const int q = q0 + tid + 256 * r;
+#pragma unroll
+                    for (int i = 0; i < 16; i++) {
+                        lo[r] += v[i] < q;
+                        hi[r] += v[i] <= q;
+                    }
+                }
             }
 #pragma unroll
             for (int r = 0; r < 4; r++) {

@@ -324,8 +324,10 @@ def main():
         gu_alg = [u * expert_bytes + shared_bytes + x_bytes + w.T * w.H * 4 for u in steps_U]
     else:
         # weights, token rows, the h planes (bf16 hi + lo) and, in the training pass, the saved
-        # gate/up pre-activations (fp32 g and u per slot)
-        gu_alg = [u * gateup_bytes_per_expert + x_bytes + S * w.I * 4 + (S * 2 * w.I * 4 if train else 0)
+        # gate/up pre-activations (fp32 g and u per slot); the RVQ3 table-lookup gate/up writes
+        # g and u (fp32) instead of h, and its down pass forms h
+        out_b = 8 if roof[0] == "k_gu_lut" else 4
+        gu_alg = [u * gateup_bytes_per_expert + x_bytes + S * w.I * out_b + (S * 2 * w.I * 4 if train else 0)
                   + (shared_gateup_bytes + x_bytes + S_sh * w.I * 4 if args.shared else 0) for u in steps_U]
     gu_bytes = sum(gu_alg) / len(gu_alg)
     # gate/up time per step (with shared experts: both launches), from events stamped at the

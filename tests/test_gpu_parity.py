@@ -275,6 +275,13 @@ def test_rvq3_table_lookup_path():
     run_small(host_case(w), name="rvq3-lut")
 
 
+def test_rvq3_codeword_gather_flag():
+    # MOE_F_RVQ_GATHER: the layer of test_rvq3_table_lookup_path on the codeword-gather kernels
+    from quantized_moe_route_amd import _lib as C
+    w = syn.shrink(syn.WORKLOADS["rvq16"], T=10, H=512, I=768, E=12, k=3, with_dy=True, x_key=21)
+    run_small(host_case(w), name="rvq3-gather-flag", flags=C.MOE_F_RVQ_GATHER)
+
+
 def test_rvq3_table_lookup_many_tokens_per_unit():
     # ~13 tokens per expert: one pass per token, the index bytes re-read per pass
     w = syn.shrink(syn.WORKLOADS["rvq16"], T=40, H=256, I=512, E=6, k=2, with_dy=True, x_key=22)

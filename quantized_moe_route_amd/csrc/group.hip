@@ -96,9 +96,10 @@ __global__ __launch_bounds__(1024) void k_group(const int32_t *__restrict__ ids,
 
 hipError_t launch_group(const GroupArgs &a, hipStream_t s)
 {
-    // one wave per 512 slots (at most 16), within 64 KB of LDS
-    int nw = 1;
-    while (nw < 16 && (long)nw * 512 < (long)a.T * a.k) nw <<= 1;
+    // 16 waves (fewer when their histograms would exceed 64 KB of LDS): the per-expert
+    // sums and scans run over E whatever the slot count, so small batches gain from the
+    // waves too
+    int nw = 16;
     while (nw > 1 && (size_t)nw * a.E * 4 + (size_t)nw * 64 * 4 > 64 * 1024) nw >>= 1;
     const size_t lds = ((size_t)nw * a.E + (size_t)nw * 64) * sizeof(int);
     ProfScope ps(a.prof, PK_GROUP, s);

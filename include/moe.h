@@ -51,7 +51,7 @@ extern "C" {
 typedef enum {
     MOE_OK = 0,
     MOE_ERR_INVALID_ARG = 1,   /* a null pointer, a bad size, a bad dtype, misalignment */
-    MOE_ERR_UNSUPPORTED = 2,   /* a valid request this build does not implement */
+    MOE_ERR_UNSUPPORTED = 2,   /* a valid request the library does not implement */
     MOE_ERR_WORKSPACE = 3,     /* workspace smaller than moe_workspace_size() */
     MOE_ERR_DEVICE = 4,        /* a HIP call failed; text in moe_last_error() */
     MOE_ERR_INTERNAL = 5,
@@ -69,7 +69,7 @@ typedef enum {
 
 /* flags */
 enum {
-    MOE_F_DETERMINISTIC = 1u, /* combine and gradient reductions in a fixed order (always on in this build) */
+    MOE_F_DETERMINISTIC = 1u, /* combine and gradient reductions in a fixed order (always on: the library has no unordered mode) */
     MOE_F_MX_GATEUP = 2u,     /* grouped-GEMM gate/up (MXFP4, bf16 x, many tokens per expert) on the
                                  gfx950 block-scaled MFMA: weights enter as FP4 codes with their E8M0
                                  scales and x as two E4M3 terms with per-32 scales (each element

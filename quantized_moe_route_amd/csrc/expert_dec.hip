@@ -168,6 +168,31 @@ __device__ __forceinline__ u32x4 ld16_coh(__amdgpu_buffer_rsrc_t r, uint32_t vof
 
 __device__ __forceinline__ void wait_stores() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// sum_q v[q] b[q] for q < R (v, b 16-byte aligned when R % 4 == 0): four-wide loads, all of a
+// group of up to 8 issued before the products.
+__device__ __forceinline__ float dot_r(const float *v, const float *b, int R)
+{
+    float acc = 0.f;
+    if (R % 4 == 0) {
+        for (int q0 = 0; q0 < R; q0 += 32) {
+            float4 va[8], ba[8];
+#pragma unroll
+            for (int i = 0; i < 8; i++) {
+                const int q = min(q0 + 4 * i, R - 4);
+                va[i] = *(const float4 *)(v + q);
+                ba[i] = *(const float4 *)(b + q);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; i++)
+                if (q0 + 4 * i < R)
+                    acc = fmaf(va[i].w, ba[i].w, fmaf(va[i].z, ba[i].z, fmaf(va[i].y, ba[i].y, fmaf(va[i].x, ba[i].x, acc))));
+        }
+    } else {
+        for (int q = 0; q < R; q++) acc = fmaf(v[q], b[q], acc);
+    }
+    return acc;
+}
+
 // gate/up + activation of one block: 4 waves x 16 rows = 64 I-columns (column block bx) of
 // active unit ai; all of the unit's tokens (<= nl_x) in one 16-column MFMA tile.  COH: the h
 // planes are stored with the agent-scope policy (read by other blocks of the same launch).
@@ -210,6 +235,19 @@ __device__ __forceinline__ bool gateup_block(const ExpertFwdArgs &a, int bx, int
     uint8_t *sreg = (uint8_t *)(xs + (size_t)a.nl_x * (H + 8)) + 4096 * wv;
     put_scales(sreg, tg, lane);
     put_scales(sreg + 2048, tu, lane);
+    // the fused launch's adapter: lt[t][m][c] = s (B_m vx_m of token t) at the block's column c
+    // (m = 0 gate, 1 up), formed while the first weight bytes are in flight
+    float *lt = (float *)((uint8_t *)(xs + (size_t)a.nl_x * (H + 8)) + 16384), *hz = lt + a.nl_x * 128;
+    const bool lora = a.lora_vx && sh < 0;
+    if (lora) {
+        const int R = a.lora_r;
+        for (int o = threadIdx.x; o < ntok * 128; o += blockDim.x) {
+            const int t = o >> 7, m = (o >> 6) & 1, col = o & 63;
+            const float *v = a.lora_vx + (size_t)xrow[t] * 2 * R + m * R;
+            const float *bm = (m ? a.lora_Bu : a.lora_Bg) + (size_t)(bx * 64 + col) * R;
+            lt[o] = a.lora_scale * dot_r(v, bm, R);
+        }
+    }
     __syncthreads();
 
     const uint16_t *xl = xs + (size_t)min(li, ntok - 1) * (H + 8) + 64 * g;
@@ -232,10 +270,22 @@ __device__ __forceinline__ bool gateup_block(const ExpertFwdArgs &a, int bx, int
     if (li < ntok) {
         const size_t rr = (size_t)(r0 + li);
         const int n = row0 + 4 * g;
-        if (sh < 0) add_lora_gu(a.lora_gu, a.perm, a.k, rr, I, n, accg, accu);
+        if (lora) {
+            const float4 dg = *(const float4 *)(lt + (li * 2) * 64 + wv * 16 + 4 * g);
+            const float4 du = *(const float4 *)(lt + (li * 2 + 1) * 64 + wv * 16 + 4 * g);
+            accg += f32x4{dg.x, dg.y, dg.z, dg.w};
+            accu += f32x4{du.x, du.y, du.z, du.w};
+        } else if (sh < 0) {
+            add_lora_gu(a.lora_gu, a.perm, a.k, rr, I, n, accg, accu);
+        }
         uint32_t hh[4], hl[4];
+        float hv[4];
 #pragma unroll
-        for (int r = 0; r < 4; r++) split_bf16(act_h(a.act, accg[r], accu[r]), hh[r], hl[r]);
+        for (int r = 0; r < 4; r++) {
+            hv[r] = act_h(a.act, accg[r], accu[r]);
+            split_bf16(hv[r], hh[r], hl[r]);
+        }
+        if (lora) *(float4 *)(hz + li * 64 + wv * 16 + 4 * g) = float4{hv[0], hv[1], hv[2], hv[3]};
         uint16_t *ph = sh >= 0 ? a.sh_h_hi : a.h_hi, *pl = sh >= 0 ? a.sh_h_lo : a.h_lo;
         const u32x2 vh = {pack2(hh[0], hh[1]), pack2(hh[2], hh[3])}, vl = {pack2(hl[0], hl[1]), pack2(hl[2], hl[3])};
         if constexpr (COH) {
@@ -251,6 +301,31 @@ __device__ __forceinline__ bool gateup_block(const ExpertFwdArgs &a, int bx, int
         if (a.gu && sh < 0) {
             *(float4 *)(a.gu + (rr * 2 + 0) * I + n) = float4{accg[0], accg[1], accg[2], accg[3]};
             *(float4 *)(a.gu + (rr * 2 + 1) * I + n) = float4{accu[0], accu[1], accu[2], accu[3]};
+        }
+    }
+    if (lora) {
+        // partials of z = A_d hbar over the block's 64 columns: lora_zp[(slot r + q) I/64 + bx]
+        // = p_slot sum_c A_d[q][bx 64 + c] h(slot, c), agent-scope stores (another block sums them)
+        __syncthreads();
+        const int R = a.lora_r, gx = I / 64;
+        const __amdgpu_buffer_rsrc_t zr = buf_rsrc(a.lora_zp, (uint32_t)((size_t)a.T * a.k * R * gx * 4));
+        for (int o = threadIdx.x; o < ntok * R; o += blockDim.x) {
+            const int t = o / R, q = o - t * R;
+            const float *ad = a.lora_Ad + (size_t)q * I + bx * 64;
+            const float *hr = hz + t * 64;
+            float4 av[16];
+#pragma unroll
+            for (int c = 0; c < 16; c++) av[c] = *(const float4 *)(ad + 4 * c);
+            float acc = 0.f;
+#pragma unroll
+            for (int c = 0; c < 16; c++) {
+                const float4 hv4 = *(const float4 *)(hr + 4 * c);
+                acc = fmaf(av[c].x, hv4.x, fmaf(av[c].y, hv4.y, fmaf(av[c].z, hv4.z, fmaf(av[c].w, hv4.w, acc))));
+            }
+            const int slot = a.perm[r0 + t];
+            const float v = a.w[slot] * acc;
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), zr,
+                                                  (int)((((size_t)slot * R + q) * gx + bx) * 4), 0, kSc1);
         }
     }
     return true;
@@ -407,9 +482,47 @@ __device__ __forceinline__ void stage_rows_coh(uint16_t *dst, const uint16_t *sr
     }
 }
 
+// The adapter's down term for y rows [bx 64, bx 64 + 64) in the fused launch: thread (m, part)
+// loads B_d[bx 64 + m][q] for ranks q = part, part + 4, ... before it waits for z (reduced by
+// the last routed gate/up block, lora_z_last), then writes pd[part][t][m] = sum over its ranks
+// of z[t][q] B_d[bx 64 + m][q] to LDS (scr: T r + 4 T 64 floats).  Returns pd.
+__device__ __forceinline__ const float *lora_stripe(const ExpertFwdArgs &a, int bx, float *scr)
+{
+    const int R = a.lora_r, T = a.T, m = threadIdx.x & 63, part = threadIdx.x >> 6;
+    float b[16];
+    const float *brow = a.lora_Bd + (size_t)(bx * 64 + m) * R;
+#pragma unroll
+    for (int i = 0; i < 16; i++) b[i] = part + 4 * i < R ? brow[part + 4 * i] : 0.f;
+    if (threadIdx.x == 0) {
+        const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+        while (__hip_atomic_load(a.dec_sync + kSyncLoraZ, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+            __builtin_amdgcn_s_sleep(2);
+            if (__builtin_amdgcn_s_memrealtime() - t0 > kSpinTicks) {
+                if (a.status) atomicOr(a.status, kStatusSpinTimeout);
+                break;
+            }
+        }
+    }
+    __syncthreads();
+    float *zs = scr, *pd = scr + ((T * R + 3) & ~3);
+    const __amdgpu_buffer_rsrc_t zr = buf_rsrc(a.lora_z, (uint32_t)((size_t)T * R * 4));
+    for (int o = threadIdx.x; o < T * R; o += blockDim.x)
+        zs[o] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(zr, o * 4, 0, kSc1));
+    __syncthreads();
+    for (int t = 0; t < T; t++) {
+        float d = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; i++)
+            if (part + 4 * i < R) d = fmaf(zs[t * R + part + 4 * i], b[i], d);
+        pd[(part * T + t) * 64 + m] = d;
+    }
+    __syncthreads();
+    return pd;
+}
+
 // y rows [bx * 64, bx * 64 + 64) of every token: the slot rows in rank order, then the
 // shared experts' rows (agent-scope loads: other blocks wrote them).
-__device__ __forceinline__ void combine_stripe(const ExpertFwdArgs &a, int bx)
+__device__ __forceinline__ void combine_stripe(const ExpertFwdArgs &a, int bx, const float *pd = nullptr)
 {
     const int H = a.H, k = a.k, k2 = a.sh_n, T = a.T;
     const __amdgpu_buffer_rsrc_t yb = buf_rsrc(a.ybuf, (uint32_t)((size_t)T * k * H * 4));
@@ -429,6 +542,15 @@ __device__ __forceinline__ void combine_stripe(const ExpertFwdArgs &a, int bx)
             }
         }
         for (int j = 0; j < k2; j++) acc += __builtin_bit_cast(f32x4, ld16_coh(ys, (uint32_t)((((size_t)t * k2 + j) * H + c) * 4)));
+        if (pd) {
+            // the adapter's down term s B_d z: four rank-partial sums per output (lora_stripe)
+            const int m = c - bx * 64;
+#pragma unroll
+            for (int i = 0; i < 4; i++) {
+                const f32x4 d = *(const f32x4 *)(pd + (i * T + t) * 64 + m);
+                acc += a.lora_scale * d;
+            }
+        }
         *(float4 *)(a.y + (size_t)t * H + c) = float4{acc[0], acc[1], acc[2], acc[3]};
     }
 }
@@ -522,7 +644,8 @@ __device__ __forceinline__ void down_block_fused(const ExpertFwdArgs &a, int bx,
     }
     __syncthreads();
     if (!*last) return;
-    combine_stripe(a, bx);
+    const float *pd = a.lora_vx ? lora_stripe(a, bx, (float *)hs) : nullptr;
+    combine_stripe(a, bx, pd);
     if (threadIdx.x == 0) {
         // the stripe is complete: reset its counter; the last complete stripe resets the rest
         __hip_atomic_store(stripe, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -532,8 +655,64 @@ __device__ __forceinline__ void down_block_fused(const ExpertFwdArgs &a, int bx,
             const int nu = min(a.E, a.T * a.k) + a.sh_n;
             for (int u = 0; u < nu; u++) __hip_atomic_store(a.dec_sync + u * kSyncPad, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(a.dec_sync + kSyncLoraGu, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(a.dec_sync + kSyncLoraZ, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
+}
+
+// The adapter in the fused launch: a routed gate/up block counts itself (its z partials are
+// stored); the last of them sums the partials into z[t][q] = sum over the token's slots j in
+// rank order and the column blocks c of lora_zp[((t k + j) r + q) I/64 + c] (thread group gi
+// of an output takes slots j = gi, gi + ng, ..., each with all its column blocks in one round
+// of loads; the groups are then summed in order), stores z [T][r] and raises the flag the
+// combining blocks wait for.  scr: 256 + 16 x 64 floats of LDS.
+__device__ __forceinline__ void lora_z_last(const ExpertFwdArgs &a, int gx, int *flag, float *scr)
+{
+    if (threadIdx.x == 0) {
+        const uint32_t n = __hip_atomic_fetch_add(a.dec_sync + kSyncLoraGu, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *flag = n + 1 == (uint32_t)(*a.n_active * gx);
+    }
+    __syncthreads();
+    if (!*flag) return;
+    float *zs = scr, *zl = scr + 256;
+    const int R = a.lora_r, T = a.T, k = a.k;
+    const int nout = T * R;  // <= 16 x 64
+    const __amdgpu_buffer_rsrc_t zr = buf_rsrc(a.lora_zp, (uint32_t)((size_t)T * k * R * gx * 4));
+    for (int o0 = 0; o0 < nout; o0 += 256) {
+        const int nb = min(256, nout - o0);  // outputs of this round
+        const int ng = min(256 / nb, k);     // thread groups per output
+        const int o = o0 + threadIdx.x % nb, gi = threadIdx.x / nb;
+        float acc = 0.f;
+        if (gi < ng) {
+            const int t = o / R, q = o - t * R;
+            for (int j = gi; j < k; j += ng) {
+                // the gx <= 64 column-block partials of (slot, q): up to 16 loads issued together
+                const uint32_t base = (uint32_t)((((size_t)(t * k + j) * R + q) * gx) * 4);
+                f32x4 v[16];
+#pragma unroll
+                for (int i = 0; i < 16; i++)
+                    v[i] = 4 * i < gx ? __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(zr, (int)(base + 16 * i), 0, kSc1))
+                                      : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int i = 0; i < 16; i++) acc += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
+            }
+        }
+        zs[threadIdx.x] = acc;
+        __syncthreads();
+        if (threadIdx.x < nb) {
+            float z = zs[threadIdx.x];
+            for (int g2 = 1; g2 < ng; g2++) z += zs[g2 * nb + threadIdx.x];
+            zl[o0 + threadIdx.x] = z;
+        }
+        __syncthreads();
+    }
+    const __amdgpu_buffer_rsrc_t zo = buf_rsrc(a.lora_z, (uint32_t)((size_t)nout * 4));
+    for (int o = threadIdx.x; o < nout; o += blockDim.x)
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, zl[o]), zo, (int)(o * 4), 0, kSc1);
+    wait_stores();
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_store(a.dec_sync + kSyncLoraZ, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int NST, bool PACK>
@@ -551,6 +730,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void k
             __syncthreads();
             if (threadIdx.x == 0)
                 __hip_atomic_fetch_add(a.dec_sync + ai * kSyncPad, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            // scratch: the block's scale regions (16 KB past the x rows), free after its K loop
+            if (a.lora_vx && ai < min(a.E, a.T * a.k))
+                lora_z_last(a, gx, &last, (float *)(lds + (size_t)a.nl_x * (a.H + 8)));
         }
     } else {
         const int d = b - gx * nu;
@@ -586,7 +768,9 @@ template <int NST>
 static hipError_t launch_fused_nst(const ExpertFwdArgs &a, hipStream_t s)
 {
     const int nu = min(a.E, a.T * a.k) + a.sh_n;
-    const size_t lds_g = (size_t)a.nl_x * (a.H + 8) * 2 + 16384, lds_d = (size_t)a.nl_h * (a.I + 8) * 2 * 2 + 4 * 2048;
+    // gate/up blocks: x rows, 16 KB of scales, and with the adapter its terms and h (768 B a token)
+    const size_t lds_g = (size_t)a.nl_x * (a.H + 8) * 2 + 16384 + (a.lora_vx ? (size_t)a.nl_x * 768 : 0),
+                 lds_d = (size_t)a.nl_h * (a.I + 8) * 2 * 2 + 4 * 2048;
     const dim3 grid((unsigned)((a.I / 64 + a.H / 64) * nu));
     ProfScope ps(a.prof, PK_GATEUP, s);
     if (a.T <= 8)

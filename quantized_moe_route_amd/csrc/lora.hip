@@ -485,6 +485,15 @@ hipError_t lora_forward_pre(const LoraW &L, const LoraWs &w, const void *x, int 
     return e;
 }
 
+hipError_t lora_forward_vx(const LoraW &L, const LoraWs &w, const void *x, int xt, int T, int H, hipStream_t s)
+{
+    const int r = L.r;
+    if (T <= 64) return dot2(xt, true, x, H, L.A[0], L.A[1], r, T, H, w.vx, 2 * r, 1.f, s);
+    hipError_t e = hipSuccess;
+    for (int m = 0; m < 2 && e == hipSuccess; m++) e = tall(xt, true, x, H, L.A[m], r, T, H, w.vx + m * r, 2 * r, 1.f, s);
+    return e;
+}
+
 // hbar and z = hbar A_d^T  [T][r]; h from its planes (gu == nullptr) or from g, u.
 hipError_t lora_down_z(const LoraW &L, const LoraWs &w, const uint16_t *h_hi, const uint16_t *h_lo, const float *gu, int act,
                        const int32_t *inv, const float *pw, int T, int k, int I, hipStream_t s)

@@ -638,6 +638,23 @@ moe_status moe_forward(moe_layer *L, const void *x, int32_t xt, int32_t T, const
     moe::set_lds_staging(a);
     if (!L->has_lora) return device_status(moe::launch_expert_forward(a, hs), "forward");
     const moe::LoraWs lw = lora_ws(L);
+    if (!moe::use_mm(a) && moe::dec_supported(a) && moe::dec_fused_ok(a) &&
+        (size_t)T * a.k * L->lora.r * (a.I / 64) <= lw.part_cap) {
+        // the fused few-token launch forms the adapter's gate/up and down terms itself from
+        // vx = [A_g x | A_u x]; its partials of A_d hbar go to the adapter's split-K region
+        if ((st = device_status(moe::lora_forward_vx(L->lora, lw, x, xt, T, a.H, hs), "adapter (A x)")) != MOE_OK)
+            return st;
+        a.lora_vx = lw.vx;
+        a.lora_Bg = L->lora.B[0];
+        a.lora_Bu = L->lora.B[1];
+        a.lora_Ad = L->lora.A[2];
+        a.lora_Bd = L->lora.B[2];
+        a.lora_r = L->lora.r;
+        a.lora_scale = L->lora.scale;
+        a.lora_zp = lw.part;
+        a.lora_z = lw.z;
+        return device_status(moe::launch_expert_forward(a, hs), "forward");
+    }
     if ((st = device_status(moe::lora_forward_pre(L->lora, lw, x, xt, T, a.H, a.I, hs), "adapter (gate/up terms)")) != MOE_OK)
         return st;
     a.lora_gu = lw.gu;

@@ -121,6 +121,15 @@ struct ExpertFwdArgs {
     uint32_t *status;
     float *gu_ws;  // [S][2][I] workspace for g, u when gu is null (the RVQ3 table-lookup path), or null
     int32_t *lut_ord;  // [S] the table-lookup launches' unit order (workspace), or null
+    // The shared adapter inside the fused few-token launch (lora_vx non-null; lora_gu is then
+    // null): the gate/up blocks add s B_g vx_g, s B_u vx_u to g and u themselves, and write the
+    // partials p_j A_d[:, block columns] h_j of z = A_d hbar to lora_zp [S][r][I / 64]; the last
+    // gate/up block reduces them into lora_z [T][r] and the combining blocks add s B_d z to y.
+    const float *lora_vx;  // [T][2r]: A_g x | A_u x
+    const float *lora_Bg, *lora_Bu, *lora_Ad, *lora_Bd;
+    int lora_r;
+    float lora_scale;
+    float *lora_zp, *lora_z;
 };
 
 // Counter layout of the fused decode launch: per-unit gate/up completions, per-stripe down
@@ -131,7 +140,10 @@ constexpr int kSyncUnits = 1152;  // >= min(E, 16 k) + n_shared for the few-toke
 constexpr int kSyncStripes = 64;  // >= H / 64
 constexpr int kSyncPad = 32;
 constexpr int kSyncLut = (kSyncUnits + kSyncStripes + 1) * kSyncPad;  // first table-lookup counter
-constexpr int kSyncWords = kSyncLut + 2 * kSyncPad;
+// the fused launch with the adapter: finished routed gate/up blocks, then the flag that z is out
+constexpr int kSyncLoraGu = kSyncLut + 2 * kSyncPad;
+constexpr int kSyncLoraZ = kSyncLoraGu + kSyncPad;
+constexpr int kSyncWords = kSyncLoraZ + kSyncPad;
 constexpr uint32_t kStatusSpinTimeout = 0x80000000u;  // status-word bit: a fused launch gave up waiting
 
 struct ExpertBwdArgs {
@@ -247,6 +259,8 @@ struct LoraWs {
     size_t part_cap;  // floats
 };
 hipError_t lora_forward_pre(const LoraW &L, const LoraWs &w, const void *x, int xt, int T, int H, int I, hipStream_t s);
+// vx = [A_g x | A_u x] only (the fused few-token launch forms the rest itself)
+hipError_t lora_forward_vx(const LoraW &L, const LoraWs &w, const void *x, int xt, int T, int H, hipStream_t s);
 hipError_t lora_forward_post(const LoraW &L, const LoraWs &w, const ExpertFwdArgs &a, const int32_t *inv, hipStream_t s);
 hipError_t lora_backward_pre(const LoraW &L, const LoraWs &w, const void *dy, int dyt, int T, int H, int I, hipStream_t s);
 hipError_t lora_backward_post(const LoraW &L, const LoraWs &w, const ExpertBwdArgs &a, bool pair, hipStream_t s);

@@ -44,6 +44,14 @@ def test_lora_few_tokens_decode_kernels():
              "lora-dec-few")
 
 
+@pytest.mark.parametrize("rank", [1, 6])
+def test_lora_fused_decode_odd_ranks_situ(rank):
+    # the single few-token launch forms the adapter's gate/up and down terms itself: ranks
+    # that are not a multiple of four (scalar rank sums), SiTU, a router bias, three tokens
+    run_lora(_case(syn.shrink(TINY, T=3, H=768, I=512, E=10, k=4, x_dtype="bf16", bias_sd=0.5, with_dy=True,
+                              x_key=59 + rank), act=1), f"lora-fused-rank{rank}", rank=rank)
+
+
 def test_lora_grouped_gemm_paths():
     # T k >= 8 E with H, I multiples of 512: grouped-GEMM forward and backward (dg/du as bf16
     # hi + lo planes); rank 32 takes the square GEMM tiles

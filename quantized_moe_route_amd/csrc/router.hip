@@ -448,6 +448,67 @@ __device__ __noinline__ int rerank_f64(int t, const void *__restrict__ x, int xt
     return rank_id;
 }
 
+// fp64 re-ranking when the candidate set (bit q of cand: expert lane + 64 q) has at most 64
+// members.  Candidate i goes to entry i of a compacted list (expert, fp32 logit, bound); only
+// the candidates whose interval [l - b, l + b] meets another candidate's get their logit
+// recomputed in fp64 (exact products, as in rerank_f64): every other candidate's exact logit
+// lies in an interval disjoint from all the others', so its fp32 logit orders it correctly
+// against any candidate's exact (or fp64) value.  Ranks are then counted under (value desc,
+// id asc).  Returns, on lane j < k, the expert ranked j-th.  Called by a whole wave; uses
+// sc's candidate and rank arrays.
+template <int PL>
+__device__ __noinline__ int rerank_overlap(int t, const void *__restrict__ x, int xt, const float *__restrict__ wr,
+                                           const float *__restrict__ bias, const float *__restrict__ logits,
+                                           const float *__restrict__ beta, int H, int E, int k, uint32_t cand,
+                                           int rank_id, TopkScratch &sc)
+{
+    const int lane = threadIdx.x & 63;
+    float *cl = (float *)sc.ckey, *cb = cl + 64;
+    int *cid = (int *)(cl + 128);
+    int n = 0;
+#pragma unroll
+    for (int q = 0; q < PL; q++) {
+        const bool c = (cand >> q) & 1u;
+        const unsigned long long m = __ballot(c);
+        const int pos = n + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        if (c) {
+            const int e = lane + 64 * q;
+            const float lv = logits[(size_t)t * E + e];
+            cl[pos] = lv != lv ? -__builtin_huge_valf() : lv;
+            cb[pos] = beta[(size_t)t * E + e];
+            cid[pos] = e;
+        }
+        n += __popcll(m);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    const bool mine = lane < n;
+    const double li = mine ? (double)cl[lane] : 0.0, bi = mine ? (double)cb[lane] : 0.0;
+    bool unc = false;  // differences and sums of two floats are exact in fp64
+    for (int j = 0; j < n; j++) unc |= j != lane && fabs(li - (double)cl[j]) <= bi + (double)cb[j];
+    unc = unc && mine && li > -__builtin_huge_val();
+    double v = mine ? li : -__builtin_huge_val();
+    unsigned long long mu = __ballot(unc);
+    while (mu) {
+        const int owner = __ffsll((long long)mu) - 1;
+        mu &= mu - 1;
+        const double d = logit_f64(x, xt, wr, bias, t, cid[owner], H, lane);
+        if (lane == owner) v = d != d ? -__builtin_huge_val() : d;
+    }
+    double *cv = (double *)sc.rkey;
+    int *rk = (int *)sc.rb;
+    if (mine) cv[lane] = v;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    const int myid = mine ? cid[lane] : 0x7FFFFFFF;
+    int r = 0;
+    for (int j = 0; j < n; j++) {
+        const double vj = cv[j];
+        r += vj > v || (vj == v && cid[j] < myid);
+    }
+    if (mine && r < k) rk[r] = myid;
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    return lane < k ? rk[lane] : rank_id;
+}
+
 // Top-k + softmax of token t by one wave.  PL = logits held per lane (E <= 64 PL).
 // No block-level barrier inside, so waves of one block may run it for different
 // numbers of tokens.
@@ -559,8 +620,10 @@ __device__ __forceinline__ void topk_one(int t, const float *__restrict__ logits
     int rank_id = key_expert(rank_key);
     bool reranked = false;
     if (ncand2 > k || overlap) {
-        // 4. re-rank every candidate on fp64 logits (rare: kept out of line)
-        rank_id = rerank_f64<PL>(t, x, xt, wr, bias, H, k, cand, rank_id);
+        // 4. re-rank on fp64 logits (rare: kept out of line): those of the candidates whose
+        // intervals overlap (at most 64 candidates), else of every candidate
+        rank_id = ncand2 <= 64 ? rerank_overlap<PL>(t, x, xt, wr, bias, logits, beta, H, E, k, cand, rank_id, sc)
+                               : rerank_f64<PL>(t, x, xt, wr, bias, H, k, cand, rank_id);
         if (lane == 0 && refined) atomicAdd(refined, 1);
         reranked = true;
     }

@@ -428,6 +428,9 @@ moe_status moe_route(moe_layer *L, const void *x, int32_t xt, int32_t T, const m
     a.k = L->d.top_k;
     a.logits = (float *)(L->ws + L->lay.logits);
     a.beta = (float *)(L->ws + L->lay.beta);
+    // the backward's dg/du region is free while routing: the split-K router's partial sums
+    a.rpart = (double *)(L->ws + L->lay.dgdu);
+    a.rpart_bytes = (size_t)L->d.max_tokens * L->d.top_k * 2 * L->d.inter * 4;
     a.ids = r->ids;
     a.w = r->w;
     a.refined = nullptr;

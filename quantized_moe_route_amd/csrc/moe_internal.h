@@ -58,6 +58,8 @@ struct RouteArgs {
     const float *bias;   // added to the logits (bias modes 1 and 2)
     const float *wbias;  // bias mode 2: taken back out of the selected logits for the weights, else null
     int T, H, E, k;
+    double *rpart;       // workspace for the split-K fp64 router (null: no split)
+    size_t rpart_bytes;
     float *logits;  // [T][E] workspace
     float *beta;    // [T][E] workspace
     int32_t *ids;

@@ -148,9 +148,14 @@ __global__ __launch_bounds__(256) void k_router_gemv(const void *__restrict__ x,
 typedef __attribute__((ext_vector_type(4))) double f64x4;
 constexpr int kRfTile = 64, kRfK = 32, kRfStride = 36;
 
+// Split over H (part non-null, gridDim.z slices of whole 32-chunks): slice z writes its
+// fp64 partial sums part[z][t][e] and the sums of squares of its x and Wr values,
+// part[Z T E + z T + t] and part[Z T E + Z T + z E + e] (identical in every block that stages
+// the same row), and k_router_f64_sum forms the logits and bounds.
 __global__ __launch_bounds__(256, 2) void k_router_f64(const void *__restrict__ x, int xt, const float *__restrict__ wr,
                                                        const float *__restrict__ bias, int T, int H, int E,
-                                                       float *__restrict__ logits, float *__restrict__ beta)
+                                                       float *__restrict__ logits, float *__restrict__ beta,
+                                                       double *__restrict__ part)
 {
     __shared__ __attribute__((aligned(16))) float xs[2][kRfTile * kRfStride];
     __shared__ __attribute__((aligned(16))) float ws[2][kRfTile * kRfStride];
@@ -200,13 +205,14 @@ __global__ __launch_bounds__(256, 2) void k_router_f64(const void *__restrict__ 
         for (int b = 0; b < 2; b++) acc[a][b] = f64x4{0.0, 0.0, 0.0, 0.0};
     const int mr = 32 * (wv & 1), mc = 32 * (wv >> 1);  // this wave's tokens / experts in the tile
     const int fr = lane & 15, fk = lane >> 4;           // fragment row (or column) and k
-    const int nchunks = H / kRfK;
-    load(0);
+    const int Z = gridDim.z, z = blockIdx.z;
+    const int nall = H / kRfK, per = nall / Z, cbeg = z * per, nchunks = per;
+    load(cbeg * kRfK);
     store(0);
     __syncthreads();
     for (int c = 0; c < nchunks; c++) {
         const int buf = c & 1;
-        if (c + 1 < nchunks) load((c + 1) * kRfK);
+        if (c + 1 < nchunks) load((cbeg + c + 1) * kRfK);
 #pragma unroll
         for (int ks = 0; ks < kRfK / 4; ks++) {
             double A[2], B[2];
@@ -228,6 +234,23 @@ __global__ __launch_bounds__(256, 2) void k_router_f64(const void *__restrict__ 
     sx += __shfl_xor(sx, 2, 64);
     sw += __shfl_xor(sw, 1, 64);
     sw += __shfl_xor(sw, 2, 64);
+    if (part) {
+        const size_t TE = (size_t)T * E;
+        if ((tid & 3) == 0) {
+            if (tok_ok) part[(size_t)Z * TE + (size_t)z * T + t0 + sr] = sx;
+            if (exp_ok) part[(size_t)Z * TE + (size_t)Z * T + (size_t)z * E + e0 + sr] = sw;
+        }
+#pragma unroll
+        for (int a = 0; a < 2; a++)
+#pragma unroll
+            for (int b = 0; b < 2; b++)
+#pragma unroll
+                for (int i = 0; i < 4; i++) {
+                    const int t = t0 + mr + 16 * a + 4 * i + fk, e = e0 + mc + 16 * b + fr;
+                    if (t < T && e < E) part[(size_t)z * TE + (size_t)t * E + e] = acc[a][b][i];
+                }
+        return;
+    }
     if ((tid & 3) == 0) {
         nx[sr] = sqrt(sx);
         nw[sr] = sqrt(sw);
@@ -249,6 +272,40 @@ __global__ __launch_bounds__(256, 2) void k_router_f64(const void *__restrict__ 
                 logits[(size_t)t * E + e] = l32;
                 beta[(size_t)t * E + e] = (float)(bd * (1.0 + 0x1p-20)) + 1e-30f;
             }
+}
+
+// Logits and bounds of the split fp64 router: l64 = the Z slice sums added in slice order
+// (+ bias), the norms from the slices' sums of squares, the bound as in k_router_f64 (any
+// order of fp64 additions of the H exact products is covered).  One thread per (t, e).
+__global__ __launch_bounds__(256) void k_router_f64_sum(const double *__restrict__ part, int Z, const float *__restrict__ bias,
+                                                        int T, int H, int E, float *__restrict__ logits,
+                                                        float *__restrict__ beta)
+{
+    const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x, TE = (size_t)T * E;
+    if (i >= TE) return;
+    const int t = (int)(i / E), e = (int)(i - (size_t)t * E);
+    double pl[16], px[16], pw[16];  // Z <= 16: every load issued before the sums
+#pragma unroll
+    for (int z = 0; z < 16; z++) {
+        const int zz = min(z, Z - 1);
+        pl[z] = part[(size_t)zz * TE + i];
+        px[z] = part[(size_t)Z * TE + (size_t)zz * T + t];
+        pw[z] = part[(size_t)Z * TE + (size_t)Z * T + (size_t)zz * E + e];
+    }
+    double l64 = 0.0, sx = 0.0, sw = 0.0;
+#pragma unroll
+    for (int z = 0; z < 16; z++) {
+        if (z >= Z) break;
+        l64 += pl[z];
+        sx += px[z];
+        sw += pw[z];
+    }
+    if (bias) l64 += (double)bias[e];
+    const double g2 = 2.0 * (double)(H + 1) * 0x1p-53 * (1.0 + 0x1p-20);  // 2 gamma_{H+1}, rounded up
+    const float l32 = (float)l64;
+    const double bd = g2 * sqrt(sx) * sqrt(sw) + fabs(l64 - (double)l32) + 0x1p-52 * fabs(l64);
+    logits[i] = l32;
+    beta[i] = (float)(bd * (1.0 + 0x1p-20)) + 1e-30f;
 }
 
 // fp64 logit of expert c for token t: lane l sums its inputs 4l + 256 m in order
@@ -824,16 +881,44 @@ static hipError_t launch_topk_pl(const RouteArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
+// Slices of H for the fp64 router: up to 16, so that tiles x slices reaches ~256 blocks, each
+// slice a whole number of 32-chunks, the partials within the workspace given.
+constexpr int kGemvSplitT = 8;  // more tokens than this take the fp64 router (split when its tiles are few)
+static int rf64_slices(const RouteArgs &a, int tiles)
+{
+    if (!a.rpart || a.H % kRfK || tiles >= 256) return 1;
+    const int nch = a.H / kRfK;
+    int Z = 1;
+    for (int c = 2; c <= 16; c++) {
+        const size_t need = ((size_t)c * a.T * a.E + (size_t)c * (a.T + a.E)) * 8;
+        if (nch % c || need > a.rpart_bytes) continue;
+        Z = c;
+        if (tiles * c >= 256) break;
+    }
+    return Z;
+}
+
 hipError_t launch_router(const RouteArgs &a, hipStream_t s)
 {
     {
     ProfScope ps(a.prof, PK_ROUTER_LOGITS, s);
-    if (a.T <= kGemvMaxT && a.H <= kGemvMaxH) {
+    const int tiles = ((a.E + kRfTile - 1) / kRfTile) * ((a.T + kRfTile - 1) / kRfTile);
+    const int Z = rf64_slices(a, tiles);
+    if (a.T <= kGemvMaxT && a.H <= kGemvMaxH && (a.T <= kGemvSplitT || Z == 1)) {
         ps.launch(k_router_gemv, dim3((a.E + kGemvE - 1) / kGemvE, (a.T + 7) / 8), dim3(256), 0, a.x, a.xt, a.wr, a.bias,
                            a.T, a.H, a.E, a.logits, a.beta);
+    } else if (Z > 1) {
+        // few tiles: H split into Z slices so the grid fills the chip, then the slice sums
+        ps.launch(k_router_f64, dim3((a.E + kRfTile - 1) / kRfTile, (a.T + kRfTile - 1) / kRfTile, Z), dim3(256), 0,
+                  a.x, a.xt, a.wr, a.bias, a.T, a.H, a.E, a.logits, a.beta, a.rpart);
+        const hipError_t e1 = hipGetLastError();
+        if (e1 != hipSuccess) return e1;
+        const size_t TE = (size_t)a.T * a.E;
+        hipLaunchKernelGGL(k_router_f64_sum, dim3((unsigned)((TE + 255) / 256)), dim3(256), 0, s, (const double *)a.rpart, Z,
+                           a.bias, a.T, a.H, a.E, a.logits, a.beta);
     } else {
         ps.launch(k_router_f64, dim3((a.E + kRfTile - 1) / kRfTile, (a.T + kRfTile - 1) / kRfTile), dim3(256), 0,
-                  a.x, a.xt, a.wr, a.bias, a.T, a.H, a.E, a.logits, a.beta);
+                  a.x, a.xt, a.wr, a.bias, a.T, a.H, a.E, a.logits, a.beta, (double *)nullptr);
     }
     }
     hipError_t err = hipGetLastError();

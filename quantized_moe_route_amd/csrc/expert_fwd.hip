@@ -342,14 +342,31 @@ static hipError_t launch_combine(const ExpertFwdArgs &a, hipStream_t s)
     return hipGetLastError();
 }
 
+// Token rows the gate/up kernel stages in LDS (experts with more tokens read theirs from
+// the L2 each step): no more than keep three blocks per CU, the kernel's register bound, in
+// the CU's 160 KB beside its static LDS (the staged scale bytes or the RVQ3 codebooks).
+// With the six rows of 48 KB at the K3 shape only two blocks fit: the 64-token gate/up
+// took 1,180 µs with six rows staged, 1,000-1,003 µs with four or five.
+template <int WFMT, bool FULL>
+static ExpertFwdArgs gateup_staging(const ExpertFwdArgs &a)
+{
+    ExpertFwdArgs b = a;
+    const size_t stat = WFMT == FMT_RVQ3 ? (size_t)2 * 3 * 256 * 8 * 2 : FULL ? (size_t)2 * 64 * kMaxScaleRow : 0;
+    const size_t per_block = (size_t)160 * 1024 / 3;
+    const int cap = per_block > stat ? (int)((per_block - stat) / ((size_t)(a.H + 8) * 2)) : 0;
+    b.nl_x = min(a.nl_x, cap);
+    return b;
+}
+
 template <int WFMT, int XT, int NTT, bool FULLG, bool FULLD>
 static hipError_t fwd_launch(const ExpertFwdArgs &a, hipStream_t s)
 {
     const int maxU = min(a.E, a.T * a.k);
     {
         ProfScope ps(a.prof, PK_GATEUP, s);
-        const size_t lds = NTT == 1 && XT == DT_BF16 ? (size_t)a.nl_x * (a.H + 8) * 2 : 0;
-        ps.launch((k_gateup<WFMT, XT, NTT, FULLG>), dim3((a.I + 63) / 64, maxU), dim3(256), lds, a);
+        const ExpertFwdArgs b = gateup_staging<WFMT, FULLG>(a);
+        const size_t lds = NTT == 1 && XT == DT_BF16 ? (size_t)b.nl_x * (b.H + 8) * 2 : 0;
+        ps.launch((k_gateup<WFMT, XT, NTT, FULLG>), dim3((a.I + 63) / 64, maxU), dim3(256), lds, b);
     }
     {
         ProfScope ps(a.prof, PK_DOWN, s);
@@ -381,14 +398,15 @@ static hipError_t gateup_only(const ExpertFwdArgs &a, hipStream_t s)
 {
     const int maxU = min(a.E, a.T * a.k);
     ProfScope ps(a.prof, PK_GATEUP, s);
-    const size_t lds = XT == DT_BF16 ? (size_t)a.nl_x * (a.H + 8) * 2 : 0;
     const dim3 grid((a.I + 63) / 64, maxU);
     const bool f = a.H % 256 == 0 && a.H <= 32 * kMaxScaleRow;
     if (a.T <= 64) {
+        const ExpertFwdArgs b = f ? gateup_staging<WFMT, true>(a) : gateup_staging<WFMT, false>(a);
+        const size_t lds = XT == DT_BF16 ? (size_t)b.nl_x * (b.H + 8) * 2 : 0;
         if (f)
-            ps.launch((k_gateup<WFMT, XT, 1, true>), grid, dim3(256), lds, a);
+            ps.launch((k_gateup<WFMT, XT, 1, true>), grid, dim3(256), lds, b);
         else
-            ps.launch((k_gateup<WFMT, XT, 1, false>), grid, dim3(256), lds, a);
+            ps.launch((k_gateup<WFMT, XT, 1, false>), grid, dim3(256), lds, b);
     } else {
         if (f)
             ps.launch((k_gateup<WFMT, XT, 4, true>), grid, dim3(256), 0, a);

@@ -728,10 +728,12 @@ template <int PL>
 __global__ __launch_bounds__(256) void k_topk_group(const RouteArgs a, const GroupArgs gq)
 {
     __shared__ TopkScratch scs[4];
-    __shared__ int cnt[kSmallE];
-    __shared__ int sids[kSmallS];
+    __shared__ __attribute__((aligned(16))) int cnt[kSmallE];
+    __shared__ __attribute__((aligned(16))) int sids[kSmallS];
     __shared__ int scr[256];
     const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63;
+    // slot-list entries past the T k slots read as INT_MAX by the 16-entry counting below
+    if (tid < 16 && a.T * a.k + tid < kSmallS) sids[a.T * a.k + tid] = 0x7FFFFFFF;
     if (wv < a.T)  // T <= 4
         topk_one<PL>(wv, a.logits, a.beta, a.x, a.xt, a.wr, a.bias, a.H, a.E, a.k, a.ids, a.w, a.refined, scs[wv],
                      sids, a.wbias);
@@ -740,8 +742,8 @@ __global__ __launch_bounds__(256) void k_topk_group(const RouteArgs a, const Gro
     const int S = a.T * a.k, E = a.E;
     if (S <= 64) {
         // Up to 64 slots: slot s's grouped row is the number of slots ordered before it
-        // (counted by wave 0 against the broadcast slot list); offsets and counts of
-        // every expert are then searches in the sorted expert list.
+        // (counted by wave 0 against the broadcast slot list); meanwhile every thread counts
+        // the offsets and counts of its experts against the same list.
         int *se = cnt;  // sorted experts
         if (wv == 0) {
             const int e = lane < S ? sids[lane] : 0x7FFFFFFF;
@@ -766,17 +768,16 @@ __global__ __launch_bounds__(256) void k_topk_group(const RouteArgs a, const Gro
                 gq.offsets[E] = S;
             }
         }
-        __syncthreads();
         // offsets[q] = the slots of experts below q, counts[q] = those of q: counted against
-        // the sorted list read in 16-entry pieces (independent LDS reads, no dependent search;
-        // entries past S hold INT_MAX and count for no expert)
+        // the slot list (a count needs no order) read in 16-entry pieces (independent LDS
+        // reads; entries past S hold INT_MAX and count for no expert)
         for (int q0 = 0; q0 < E; q0 += 1024) {
             int lo[4] = {0, 0, 0, 0}, hi[4] = {0, 0, 0, 0};
             for (int c0 = 0; c0 < S; c0 += 16) {
                 int v[16];
 #pragma unroll
                 for (int i = 0; i < 4; i++) {
-                    const int4 w = *(const int4 *)(se + c0 + 4 * i);
+                    const int4 w = *(const int4 *)(sids + c0 + 4 * i);
                     v[4 * i] = w.x; v[4 * i + 1] = w.y; v[4 * i + 2] = w.z; v[4 * i + 3] = w.w;
                 }
 #pragma unroll

@@ -9,7 +9,8 @@
 // The quantized weights are dequantized in registers straight from HBM (each
 // active expert's bytes are read once per token tile) and fed to bf16 MFMA
 // with fp32 accumulation.  MXFP4 dequantizes exactly to bf16; bf16 tokens are
-// exact; fp32 operands (fp32 tokens, h) are split into bf16 hi + lo.
+// exact; fp32 tokens enter as three bf16 terms (hi + mid + lo, all 24 significand bits),
+// h as two (hi + lo).
 //
 // Block = 4 waves x 16 rows = 64 rows of one active expert (blockIdx.y indexes
 // the device-side active list; blocks past *n_active exit), all of that

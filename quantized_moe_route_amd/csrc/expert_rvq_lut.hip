@@ -24,7 +24,8 @@
 //    block of token slices is a 32 x 32 tile of the table (fp16 products are exact, sums in
 //    fp32).  The token enters as fp16 times a power of two that puts its maximum magnitude
 //    in [2^13, 2^14), so bf16 tokens are exact; fp32 h for the down product as two fp16
-//    terms hi + lo (two MFMAs into the same tile);
+//    terms hi + lo, both in one v_mfma_f32_32x32x16_f16 (reduction length 16: the codeword
+//    against each term);
 //  - lookups: lane (team j of its half-wave, k) takes at step i vector 16k + (i xor r) with
 //    r = 4j + k / 2, so at every step the 32 lanes of a half-wave read 32 distinct banks.
 //    Its 16 index bytes per row have their dwords permuted by r / 4 once; the table address
@@ -46,6 +47,7 @@ namespace moe {
 namespace {
 
 typedef _Float16 h4v __attribute__((ext_vector_type(4)));
+typedef _Float16 h8v __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kLutThreads = 1024;
@@ -158,11 +160,17 @@ __device__ __forceinline__ void build_table(int s, int w0, int plo, int phi, int
         const int t = wv + 16 * h, ct = t & 7, vt = t >> 3;
         if (32 * vt < plo || 32 * vt + 32 > phi) continue;
         const int hl = lane >> 5, li = lane & 31;
-        const h4v A = *(const h4v *)(cbl + (size_t)(256 * s + 32 * ct + li) * 8 + 4 * hl);
         f32x16 d = {};
-#pragma unroll
-        for (int q = 0; q < NTERM; q++) {
-            const h4v B = *(const h4v *)(xs + (size_t)q * K + 8 * (w0 + 32 * vt + li) + 4 * hl);
+        if constexpr (NTERM == 2) {
+            // both terms in one product of reduction length 16: lanes 0..31 pair the codeword
+            // with the hi plane, lanes 32..63 with the lo plane (A and B share the lane-to-
+            // reduction-index map, so the sum is C . hi + C . lo whatever that map is)
+            const h8v A = *(const h8v *)(cbl + (size_t)(256 * s + 32 * ct + li) * 8);
+            const h8v B = *(const h8v *)(xs + (size_t)hl * K + 8 * (w0 + 32 * vt + li));
+            d = __builtin_amdgcn_mfma_f32_32x32x16_f16(A, B, d, 0, 0, 0);
+        } else {
+            const h4v A = *(const h4v *)(cbl + (size_t)(256 * s + 32 * ct + li) * 8 + 4 * hl);
+            const h4v B = *(const h4v *)(xs + 8 * (w0 + 32 * vt + li) + 4 * hl);
             d = __builtin_amdgcn_mfma_f32_32x32x8f16(A, B, d, 0, 0, 0);
         }
         const int v = 32 * vt + li;

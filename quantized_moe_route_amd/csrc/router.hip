@@ -152,7 +152,8 @@ constexpr int kRfTile = 64, kRfK = 32, kRfStride = 36;
 // fp64 partial sums part[z][t][e] and the sums of squares of its x and Wr values,
 // part[Z T E + z T + t] and part[Z T E + Z T + z E + e] (identical in every block that stages
 // the same row), and k_router_f64_sum forms the logits and bounds.
-__global__ __launch_bounds__(256, 2) void k_router_f64(const void *__restrict__ x, int xt, const float *__restrict__ wr,
+template <int XT>
+__global__ __launch_bounds__(256, 2) void k_router_f64(const void *__restrict__ x, const float *__restrict__ wr,
                                                        const float *__restrict__ bias, int T, int H, int E,
                                                        float *__restrict__ logits, float *__restrict__ beta,
                                                        double *__restrict__ part)
@@ -167,25 +168,40 @@ __global__ __launch_bounds__(256, 2) void k_router_f64(const void *__restrict__ 
     const int st_t = min(t0 + sr, T - 1), st_e = min(e0 + sr, E - 1);
     const bool tok_ok = t0 + sr < T, exp_ok = e0 + sr < E;
     double sx = 0.0, sw = 0.0;  // sums of squares of this thread's staged values
-    float xv[8], wv8[8];
+    // The next chunk's raw bits (x: bf16 in xa, or fp32 in xa and xb; Wr in wa, wb) stay in
+    // registers, untouched, until the chunk is staged: converting the bf16 x at the load
+    // would wait for it right there, one memory round trip per chunk.
+    u32x4 xa, xb, wa, wb;
     auto load = [&](int k0) {
-        if (xt == DT_BF16) {
-            const u32x4 v = *(const u32x4 *)((const uint16_t *)x + (size_t)st_t * H + k0 + sk);
-#pragma unroll
-            for (int j = 0; j < 4; j++) {
-                xv[2 * j] = __uint_as_float(v[j] << 16);
-                xv[2 * j + 1] = __uint_as_float(v[j] & 0xFFFF0000u);
-            }
+        if constexpr (XT == DT_BF16) {
+            xa = *(const u32x4 *)((const uint16_t *)x + (size_t)st_t * H + k0 + sk);
         } else {
-            const float4 a = *(const float4 *)((const float *)x + (size_t)st_t * H + k0 + sk);
-            const float4 b = *(const float4 *)((const float *)x + (size_t)st_t * H + k0 + sk + 4);
-            xv[0] = a.x; xv[1] = a.y; xv[2] = a.z; xv[3] = a.w; xv[4] = b.x; xv[5] = b.y; xv[6] = b.z; xv[7] = b.w;
+            xa = *(const u32x4 *)((const float *)x + (size_t)st_t * H + k0 + sk);
+            xb = *(const u32x4 *)((const float *)x + (size_t)st_t * H + k0 + sk + 4);
         }
-        const float4 a = *(const float4 *)(wr + (size_t)st_e * H + k0 + sk);
-        const float4 b = *(const float4 *)(wr + (size_t)st_e * H + k0 + sk + 4);
-        wv8[0] = a.x; wv8[1] = a.y; wv8[2] = a.z; wv8[3] = a.w; wv8[4] = b.x; wv8[5] = b.y; wv8[6] = b.z; wv8[7] = b.w;
+        wa = *(const u32x4 *)(wr + (size_t)st_e * H + k0 + sk);
+        wb = *(const u32x4 *)(wr + (size_t)st_e * H + k0 + sk + 4);
     };
     auto store = [&](int buf) {
+        float xv[8], wv8[8];
+        if constexpr (XT == DT_BF16) {
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                xv[2 * j] = __uint_as_float(xa[j] << 16);
+                xv[2 * j + 1] = __uint_as_float(xa[j] & 0xFFFF0000u);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                xv[j] = __uint_as_float(xa[j]);
+                xv[4 + j] = __uint_as_float(xb[j]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < 4; j++) {
+            wv8[j] = __uint_as_float(wa[j]);
+            wv8[4 + j] = __uint_as_float(wb[j]);
+        }
         float4 *xd = (float4 *)&xs[buf][sr * kRfStride + sk], *wd = (float4 *)&ws[buf][sr * kRfStride + sk];
         const float m = tok_ok ? 1.f : 0.f, n = exp_ok ? 1.f : 0.f;  // rows past T or E are zero
         xd[0] = float4{m * xv[0], m * xv[1], m * xv[2], m * xv[3]};
@@ -910,16 +926,24 @@ hipError_t launch_router(const RouteArgs &a, hipStream_t s)
                            a.T, a.H, a.E, a.logits, a.beta);
     } else if (Z > 1) {
         // few tiles: H split into Z slices so the grid fills the chip, then the slice sums
-        ps.launch(k_router_f64, dim3((a.E + kRfTile - 1) / kRfTile, (a.T + kRfTile - 1) / kRfTile, Z), dim3(256), 0,
-                  a.x, a.xt, a.wr, a.bias, a.T, a.H, a.E, a.logits, a.beta, a.rpart);
+        const dim3 grid((a.E + kRfTile - 1) / kRfTile, (a.T + kRfTile - 1) / kRfTile, Z);
+        if (a.xt == DT_BF16)
+            ps.launch(k_router_f64<DT_BF16>, grid, dim3(256), 0, a.x, a.wr, a.bias, a.T, a.H, a.E, a.logits, a.beta, a.rpart);
+        else
+            ps.launch(k_router_f64<DT_F32>, grid, dim3(256), 0, a.x, a.wr, a.bias, a.T, a.H, a.E, a.logits, a.beta, a.rpart);
         const hipError_t e1 = hipGetLastError();
         if (e1 != hipSuccess) return e1;
         const size_t TE = (size_t)a.T * a.E;
         hipLaunchKernelGGL(k_router_f64_sum, dim3((unsigned)((TE + 255) / 256)), dim3(256), 0, s, (const double *)a.rpart, Z,
                            a.bias, a.T, a.H, a.E, a.logits, a.beta);
     } else {
-        ps.launch(k_router_f64, dim3((a.E + kRfTile - 1) / kRfTile, (a.T + kRfTile - 1) / kRfTile), dim3(256), 0,
-                  a.x, a.xt, a.wr, a.bias, a.T, a.H, a.E, a.logits, a.beta, (double *)nullptr);
+        const dim3 grid((a.E + kRfTile - 1) / kRfTile, (a.T + kRfTile - 1) / kRfTile);
+        if (a.xt == DT_BF16)
+            ps.launch(k_router_f64<DT_BF16>, grid, dim3(256), 0, a.x, a.wr, a.bias, a.T, a.H, a.E, a.logits, a.beta,
+                      (double *)nullptr);
+        else
+            ps.launch(k_router_f64<DT_F32>, grid, dim3(256), 0, a.x, a.wr, a.bias, a.T, a.H, a.E, a.logits, a.beta,
+                      (double *)nullptr);
     }
     }
     hipError_t err = hipGetLastError();

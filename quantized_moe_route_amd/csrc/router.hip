@@ -56,7 +56,8 @@ constexpr int kGemvMaxT = 64;
 constexpr int kGemvMaxH = 4096;
 constexpr int kGemvE = 2;  // experts per block
 
-__global__ __launch_bounds__(256) void k_router_gemv(const void *__restrict__ x, int xt, const float *__restrict__ wr,
+template <int XT>
+__global__ __launch_bounds__(256) void k_router_gemv(const void *__restrict__ x, const float *__restrict__ wr,
                                                      const float *__restrict__ bias, int T, int H, int E,
                                                      float *__restrict__ logits, float *__restrict__ beta)
 {
@@ -64,6 +65,24 @@ __global__ __launch_bounds__(256) void k_router_gemv(const void *__restrict__ x,
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int e0 = blockIdx.x * kGemvE, t0 = blockIdx.y * 8;
     const int n4 = H / 4;
+    // A token's x pieces (4 values each, 4 per thread) are loaded as raw bits and widened only
+    // when the token is multiplied: widening at the load would wait for it there.  The first
+    // token's pieces go out before the Wr rows, each later token's while the one before it is
+    // multiplied (unconditionally, which keeps the compiler from moving pending registers at
+    // a branch; clamped in bounds, pieces past H count as 0).
+    using XRaw = std::conditional_t<XT == DT_BF16, u32x2, u32x4>;
+    XRaw xr[4];
+    auto load_xr = [&](int t) {
+#pragma unroll
+        for (int m = 0; m < 4; m++) {
+            const size_t off = (size_t)min(t, T - 1) * H + 4 * min(tid + 256 * m, n4 - 1);
+            if constexpr (XT == DT_BF16)
+                xr[m] = *(const u32x2 *)((const uint16_t *)x + off);
+            else
+                xr[m] = *(const u32x4 *)((const float *)x + off);
+        }
+    };
+    load_xr(t0);
     float4 w4[kGemvE][4];
 #pragma unroll
     for (int j = 0; j < kGemvE; j++) {
@@ -84,12 +103,18 @@ __global__ __launch_bounds__(256) void k_router_gemv(const void *__restrict__ x,
         float xv[4][4];
 #pragma unroll
         for (int m = 0; m < 4; m++) {
-            const int c = tid + 256 * m;
-            if (c < n4)
-                load_x4(x, xt, (size_t)t * H + 4 * c, xv[m][0], xv[m][1], xv[m][2], xv[m][3]);
-            else
-                xv[m][0] = xv[m][1] = xv[m][2] = xv[m][3] = 0.f;
+            const bool in = tid + 256 * m < n4;
+            if constexpr (XT == DT_BF16) {
+                xv[m][0] = in ? __uint_as_float(xr[m][0] << 16) : 0.f;
+                xv[m][1] = in ? __uint_as_float(xr[m][0] & 0xFFFF0000u) : 0.f;
+                xv[m][2] = in ? __uint_as_float(xr[m][1] << 16) : 0.f;
+                xv[m][3] = in ? __uint_as_float(xr[m][1] & 0xFFFF0000u) : 0.f;
+            } else {
+#pragma unroll
+                for (int q = 0; q < 4; q++) xv[m][q] = in ? __uint_as_float(xr[m][q]) : 0.f;
+            }
         }
+        if (u + 1 < 8) load_xr(t + 1);
 #pragma unroll
         for (int j = 0; j < kGemvE; j++) {
 #pragma unroll
@@ -866,7 +891,8 @@ static hipError_t launch_small_pl(const RouteArgs &a, const GroupArgs &g, hipStr
 {
     {
         ProfScope ps(a.prof, PK_ROUTER_LOGITS, s);
-        ps.launch(k_router_gemv, dim3((a.E + kGemvE - 1) / kGemvE, (a.T + 7) / 8), dim3(256), 0, a.x, a.xt, a.wr,
+        ps.launch(a.xt == DT_BF16 ? k_router_gemv<DT_BF16> : k_router_gemv<DT_F32>,
+                  dim3((a.E + kGemvE - 1) / kGemvE, (a.T + 7) / 8), dim3(256), 0, a.x, a.wr,
                            a.bias, a.T, a.H, a.E, a.logits, a.beta);
     }
     const hipError_t err = hipGetLastError();
@@ -922,7 +948,8 @@ hipError_t launch_router(const RouteArgs &a, hipStream_t s)
     const int tiles = ((a.E + kRfTile - 1) / kRfTile) * ((a.T + kRfTile - 1) / kRfTile);
     const int Z = rf64_slices(a, tiles);
     if (a.T <= kGemvMaxT && a.H <= kGemvMaxH && (a.T <= kGemvSplitT || Z == 1)) {
-        ps.launch(k_router_gemv, dim3((a.E + kGemvE - 1) / kGemvE, (a.T + 7) / 8), dim3(256), 0, a.x, a.xt, a.wr, a.bias,
+        ps.launch(a.xt == DT_BF16 ? k_router_gemv<DT_BF16> : k_router_gemv<DT_F32>,
+                  dim3((a.E + kGemvE - 1) / kGemvE, (a.T + 7) / 8), dim3(256), 0, a.x, a.wr, a.bias,
                            a.T, a.H, a.E, a.logits, a.beta);
     } else if (Z > 1) {
         // few tiles: H split into Z slices so the grid fills the chip, then the slice sums
